@@ -1,0 +1,74 @@
+"""Reference GEMM over dequantized operands, and the acceptance bound.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What is computed: C[i, j] = sum_k A_hat[i, k] * B_hat[j, k] in float64,
+where both operands are stored with the contraction axis last (A_hat is
+[M', K'], B_hat is [N', K']) and hold the exact dequantized values (code
+value times exactly the scale(s) the recipe defines).  This is the plain
+definition of the product the quantize-then-GEMM path approximates ("How to
+optimize Transformer-based models for low-precision training", "Model
+configuration and training inputs": each linear layer's work is an M x K x N
+matrix product).  float64 over at most 2**15-term sums of products with at
+most 60 significant bits differs from the exact sum by far less than the
+tolerance below.
+
+Acceptance (the tolerance the target states): |C_gpu - C_ref| <=
+1e-5 * sum_k |A_hat[i, k] * B_hat[j, k]|, plus one bf16 unit in the last
+place of C_ref when the GPU output is bf16.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+REL_TOL = 1e-5
+
+
+def gemm_ref(a_hat, b_hat):
+    """Returns (C_ref, bound_base) with bound_base = sum_k |a_ik * b_jk|."""
+    a = np.asarray(a_hat, dtype=np.float64)
+    b = np.asarray(b_hat, dtype=np.float64)
+    if a.shape[1] != b.shape[1]:
+        raise ValueError("contraction dims differ")
+    return a @ b.T, np.abs(a) @ np.abs(b).T
+
+
+def gemm_ref_bruteforce(a_hat, b_hat):
+    """Triple loop in float64, for tiny inputs only."""
+    a = np.asarray(a_hat, dtype=np.float64)
+    b = np.asarray(b_hat, dtype=np.float64)
+    m, k = a.shape
+    n = b.shape[0]
+    c = np.zeros((m, n))
+    for i in range(m):
+        for j in range(n):
+            acc = 0.0
+            for kk in range(k):
+                acc += a[i, kk] * b[j, kk]
+            c[i, j] = acc
+    return c
+
+
+def ulp_bf16(y):
+    """Spacing of bf16 numbers at |y|: 2**(floor(log2|y|) - 7) for normal y.
+
+    Below the normal range (and at 0) the spacing is the subnormal one, 2**-133.
+    """
+    y = np.abs(np.asarray(y, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(y > 0, y, 1.0)))
+    # floor(log2) from float64 log2 can be off by one next to powers of two;
+    # correct it exactly with ldexp comparisons.
+    e = np.where(np.ldexp(1.0, e.astype(np.int64)) > y, e - 1, e)
+    e = np.where(np.ldexp(1.0, (e + 1).astype(np.int64)) <= y, e + 1, e)
+    u = np.ldexp(1.0, (e - 7).astype(np.int64))
+    return np.where((y > 0) & (e >= -126), u, 2.0 ** -133)
+
+
+def check_gemm(c_gpu, c_ref, bound_base, bf16_out):
+    """Boolean mask of elements inside the acceptance bound, and the bound."""
+    tol = REL_TOL * bound_base
+    if bf16_out:
+        tol = tol + ulp_bf16(c_ref)
+    err = np.abs(np.asarray(c_gpu, dtype=np.float64) - c_ref)
+    return err <= tol, tol, err

@@ -1,0 +1,632 @@
+"""Pins for the oracle's recipes (CPU only).
+
+Every check ties the oracle to something other than itself: exact rational
+arithmetic, closed forms, invariants that follow from the definitions,
+brute force over tiny inputs, rocRAND's Philox, or the numbers the pages
+print.
+"""
+import json
+import math
+import os
+import shutil
+import subprocess
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import recipes as R
+from oracle.formats import E2M1, E4M3, E5M2, bf16_to_f32, e8m0_decode
+from oracle.philox import philox4x32_10, philox_word0_for_index
+from oracle.gemm_ref import gemm_ref, gemm_ref_bruteforce, check_gemm, ulp_bf16
+from oracle.passes import pass_operands, RECIPES
+
+HERE = os.path.dirname(__file__)
+GOLDEN = json.load(open(os.path.join(HERE, "golden", "page_facts.json")))
+FLT_MAX = float(np.finfo(np.float32).max)
+
+
+# ---------------------------------------------------------------------------
+# exact helpers (independent of NumPy float32 arithmetic)
+# ---------------------------------------------------------------------------
+def frac_to_f32(q):
+    """Round an exact rational to the nearest float32 (ties to even), as a float."""
+    if q == 0:
+        return 0.0
+    neg = q < 0
+    q = abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    if Fraction(2) ** e > q:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= q:
+        e += 1
+    spacing = Fraction(2) ** (max(e, -126) - 23)
+    n = q / spacing
+    fl = math.floor(n)
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    val = fl * spacing
+    if val >= Fraction(2) ** 128:
+        return math.inf
+    out = float(val)
+    return -out if neg else out
+
+
+def positive_finite_bf16():
+    b = np.arange(1, 0x7F80, dtype=np.uint16)
+    return b, bf16_to_f32(b)
+
+
+# ---------------------------------------------------------------------------
+# per-tensor scale and cast
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmax", [448.0, 57344.0, 2688.0])
+def test_scale_division_exact_over_all_bf16_amax(fmax):
+    _, a = positive_finite_bf16()
+    s, s_inv = R.scale_from_amax(a, fmax)
+    for ai, si, sii in zip(a[::1], s, s_inv):
+        want = frac_to_f32(Fraction(fmax) / Fraction(float(ai)))
+        if want == math.inf:
+            want = FLT_MAX
+        assert float(si) == want
+        assert float(sii) == frac_to_f32(1 / Fraction(want))
+
+
+def test_scale_corner_cases():
+    s, s_inv = R.scale_from_amax(np.float32(0.0), 448.0)
+    assert s == 1.0 and s_inv == 1.0
+    s, _ = R.scale_from_amax(np.float32(1e-40), 448.0)   # overflow -> FLT_MAX
+    assert s == np.float32(FLT_MAX)
+
+
+@pytest.mark.parametrize("s", [np.float32(1.0), np.float32(448.0 / 3.0), np.float32(2.0 ** 40 / 7)])
+def test_pertensor_product_rounding_all_bf16_patterns(s):
+    x = W.all_bf16_patterns().reshape(-1)
+    t = bf16_to_f32(x)
+    v = (t * s).astype(np.float32)
+    sel = np.isfinite(v)
+    for ti, vi in zip(t[sel][::7], v[sel][::7]):
+        want = frac_to_f32(Fraction(float(ti)) * Fraction(float(s)))
+        assert float(vi) == want or (want == 0.0 and float(vi) == 0.0)
+
+
+def test_pertensor_cast_amax_element_maps_to_max_and_bounds():
+    x = W.all_bf16_patterns()
+    for fmt, F in (("e4m3", 448.0), ("e5m2", 57344.0)):
+        codes, s_inv, a = R.quantize_current(x, fmt)
+        fm = {"e4m3": E4M3, "e5m2": E5M2}[fmt]
+        t = bf16_to_f32(x)
+        i = np.unravel_index(np.argmax(np.abs(t)), t.shape)
+        assert (codes[i] & (fm.sign_bit - 1)) == fm.max_code
+        deq = fm.decode(codes) * float(s_inv)
+        # relative error of a normal-range element is at most half a unit of the format
+        big = np.abs(t) * (F / float(a)) >= fm.magnitudes[1 << fm.mbits]
+        rel = np.abs(deq[big] - t[big]) / np.abs(t[big])
+        assert rel.max() <= 2.0 ** -(fm.mbits + 1) * 1.0001
+
+
+def test_pertensor_col_copy_is_transpose():
+    x = W.activations(64, 96, seed=7)
+    c_row, si_r, _ = R.quantize_current(x, "e4m3", "row")
+    c_col, si_c, _ = R.quantize_current(x, "e4m3", "col")
+    assert si_r == si_c and (c_col == c_row.T).all()
+
+
+# ---------------------------------------------------------------------------
+# delayed scaling
+# ---------------------------------------------------------------------------
+def test_delayed_closed_form_16_steps():
+    base = W.activations(64, 128, seed=4)
+    a0 = float(bf16_to_f32(base).__abs__().max())
+    st = R.DelayedScaling("e4m3", 16)
+    scales = []
+    for step in range(17):
+        x = W.drift(base, step)
+        codes, s_inv, a = st.cast(x)
+        scales.append(float(st.scale))
+        # closed form of this step's amax: rounding is monotone, so the max of
+        # the drifted tensor is the drifted max
+        want = float(bf16_to_f32(W.f32_to_bf16_bits(np.float32(a0) * W.drift_factor(step))).reshape(-1)[0])
+        assert float(a) == want
+        if step < 16:
+            st.update(a)
+    assert scales[0] == 1.0
+    hist, pos, s16, s16_inv = st.state_words()
+    assert pos == 0
+    amaxes = [float(bf16_to_f32(W.f32_to_bf16_bits(np.float32(a0) * W.drift_factor(k))).reshape(-1)[0])
+              for k in range(16)]
+    assert list(map(float, hist)) == amaxes
+    # scale used at step 16 comes from the largest amax in the history: step 15's
+    assert float(s16) == frac_to_f32(Fraction(448) / Fraction(amaxes[15]))
+    # at step 16 the tensor grew by 1.1 over the history's max: its largest
+    # element saturates, and count of saturated codes equals count of
+    # elements whose exact scaled value rounds above 448
+    x16 = bf16_to_f32(W.drift(base, 16)).astype(np.float64)
+    codes, s_inv, _ = st.cast(W.drift(base, 16))
+    n_sat = int(((codes & 0x7F) == 0x7E).sum())
+    exact = np.abs(x16) * float(s16)
+    assert n_sat == int((exact >= 416.0).sum())   # 416 = midpoint of 384 and 448
+
+
+def test_delayed_history_wraps():
+    st = R.DelayedScaling("e5m2", 4)
+    for k, a in enumerate([1.0, 8.0, 2.0, 3.0, 4.0, 0.5]):
+        st.update(np.float32(a))
+    # window holds the last four: 2, 3, 4, 0.5
+    assert sorted(map(float, st.hist)) == [0.5, 2.0, 3.0, 4.0]
+    assert float(st.scale) == 57344.0 / 4.0
+
+
+# ---------------------------------------------------------------------------
+# sub-channel FP8
+# ---------------------------------------------------------------------------
+def _brute_e4m3(v):
+    m = E4M3.magnitudes
+    a = np.abs(v.astype(np.float64))[..., None]
+    d = np.abs(a - m[None, :])
+    best = d.min(axis=-1, keepdims=True)
+    cand = np.where(d == best, np.arange(len(m)), 10 ** 6)
+    even = np.where(cand % 2 == 0, cand, 10 ** 6).min(axis=-1)
+    code = np.where(even < 10 ** 6, even, cand.min(axis=-1))
+    code = np.where(a[..., 0] > 448.0, 0x7E, code)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("weight_2d,shape", [(False, (3, 256)), (True, (128, 256))])
+def test_block128_bruteforce(weight_2d, shape):
+    x = W.activations(*shape, seed=9)
+    codes, s_inv = R.quantize_block128(x, "row", weight_2d)
+    t = bf16_to_f32(x)
+    br, bc = (128, 128) if weight_2d else (1, 128)
+    for bi in range(shape[0] // br):
+        for bj in range(shape[1] // bc):
+            blk = t[bi * br:(bi + 1) * br, bj * bc:(bj + 1) * bc]
+            a = max(abs(float(z)) for z in blk.reshape(-1))
+            s = frac_to_f32(Fraction(448) / Fraction(a)) if a else 1.0
+            assert float(s_inv[bi, bj]) == frac_to_f32(1 / Fraction(s))
+            v = np.array([frac_to_f32(Fraction(float(z)) * Fraction(s)) for z in blk.reshape(-1)],
+                         dtype=np.float32).reshape(blk.shape)
+            assert (codes[bi * br:(bi + 1) * br, bj * bc:(bj + 1) * bc] == _brute_e4m3(v)).all()
+            # the block maximum lands on 448
+            assert (np.abs(E4M3.decode(codes[bi * br:(bi + 1) * br, bj * bc:(bj + 1) * bc])).max()
+                    == 448.0)
+
+
+def test_block128_outlier_stays_in_its_blocks():
+    x = W.activations(4, 512, seed=2, n_outlier_channels=0)
+    t = bf16_to_f32(x).copy()
+    t[1, 300] = 1e4
+    xo = W.f32_to_bf16_bits(t)
+    c0, s0 = R.quantize_block128(x, "row")
+    c1, s1 = R.quantize_block128(xo, "row")
+    diff = c0 != c1
+    diff_blocks = set(zip(*np.nonzero(diff)))
+    assert all(r == 1 and 256 <= c < 384 for r, c in diff_blocks)
+    assert (s0 != s1).sum() == 1 and s0[1, 2] != s1[1, 2]
+
+
+def test_block128_2d_col_is_transpose():
+    x = W.weights(256, 384, seed=5)
+    cr, sr_ = R.quantize_block128(x, "row", weight_2d=True)
+    cc, sc = R.quantize_block128(x, "col", weight_2d=True)
+    assert (cc == cr.T).all() and (sc == sr_.T).all()
+
+
+# ---------------------------------------------------------------------------
+# MXFP8
+# ---------------------------------------------------------------------------
+def test_mx_exponent_closed_form_all_bf16():
+    _, a = positive_finite_bf16()
+    got = R.mx_block_exponent_code(a).astype(np.int64) - 127
+    f, ex = np.frexp(a.astype(np.float64))          # a = f * 2**ex, f in [0.5, 1)
+    mant = 2 * f                                     # in [1, 2)
+    E = ex - 1
+    want = np.clip(E - 8 + (mant > 1.75), -127, 127)
+    assert (got == want).all()
+    assert R.mx_block_exponent_code(np.float32(0.0)) == 0
+
+
+def test_mx_no_saturation_and_half_scale_would():
+    x = W.activations(16, 512, seed=12)
+    codes, e8 = R.quantize_mxfp8(x)
+    t = bf16_to_f32(x).astype(np.float64).reshape(16, 16, 32)
+    scale = e8m0_decode(e8)[..., None]
+    assert (np.abs(t) / scale <= 448.0).all()
+    bm = np.abs(t).max(axis=-1)
+    e = e8.astype(np.int64) - 127
+    assert ((bm / np.ldexp(1.0, e - 1) > 448.0) | (e == -127)).all()
+    deq = R.dequant_mxfp8(codes, e8).reshape(16, 16, 32)
+    assert np.all(np.abs(deq - t) <= scale * 2.0 ** -4 * np.maximum(np.abs(t) / scale, 2.0 ** -6) + 1e-300)
+
+
+# ---------------------------------------------------------------------------
+# NVFP4
+# ---------------------------------------------------------------------------
+def test_nvfp4_block_scale_bruteforce_and_global_block():
+    x = W.activations(32, 256, seed=13)
+    t = bf16_to_f32(x)
+    A = R.amax(t)
+    S_enc, S_dec = R.nvfp4_tensor_scales(A)
+    assert float(S_enc) == frac_to_f32(Fraction(2688) / Fraction(float(A)))
+    packed, d = R.quantize_nvfp4(t, S_enc)
+    a_b = np.abs(t).reshape(32, 16, 16).max(axis=-1)
+    for i in range(32):
+        for j in range(16):
+            q = frac_to_f32(Fraction(frac_to_f32(Fraction(float(a_b[i, j])) / 6)) * Fraction(float(S_enc)))
+            assert d[i, j] == _brute_e4m3(np.array([q], dtype=np.float32))[0]
+    # the block holding the tensor amax gets the largest E4M3 scale
+    i, j = np.unravel_index(np.argmax(a_b), a_b.shape)
+    assert d[i, j] == 0x7E
+
+
+def test_nvfp4_storage_matches_page_accounting():
+    n_facts = GOLDEN["nvfp4"]
+    for rows, cols in ((16, 4096), (64, 16384)):
+        x = W.activations(rows, cols, seed=1)
+        t = bf16_to_f32(x)
+        packed, d = R.quantize_nvfp4(t, R.nvfp4_tensor_scales(R.amax(t))[0])
+        n = rows * cols
+        nbytes = packed.nbytes + d.nbytes + 4
+        assert nbytes == n // 2 + n // 16 + 4
+        bits = 8 * nbytes / n
+        assert abs(bits - (4.5 + 32 / n)) < 1e-12
+        assert round(bits, 2) == n_facts["approx_bits_per_value"]
+    assert round(16 / 4.5, 1) in (3.5, 3.6) and abs(16 / 4.5 - n_facts["approx_memory_reduction_vs_fp16"]) < 0.1
+    assert round(8 / 4.5, 1) == n_facts["approx_memory_reduction_vs_fp8"]
+
+
+def test_nvfp4_dequant_error_within_half_unit():
+    x = W.activations(16, 512, seed=21)
+    t = bf16_to_f32(x)
+    S_enc, S_dec = R.nvfp4_tensor_scales(R.amax(t))
+    packed, d = R.quantize_nvfp4(t, S_enc)
+    deq = R.dequant_nvfp4(packed, d, S_dec)
+    # each element is within half an E2M1 step (at most 1 unit for the 4..6
+    # gap) of its scaled value, up to the fp32 roundings of the scales
+    dd = np.repeat(E4M3.decode(d), 16, axis=1) * float(S_dec)
+    err = np.abs(deq - t) / np.where(dd > 0, dd, 1)
+    assert err.max() <= 1.0 + 1e-5
+
+
+def test_nvfp4_zero_block_and_sign():
+    t = np.zeros((2, 32), dtype=np.float32)
+    t[0, :16] = -0.0
+    t[1, 16:] = 5.0
+    packed, d = R.quantize_nvfp4(t, R.nvfp4_tensor_scales(R.amax(t))[0])
+    codes = R.unpack_e2m1(packed)
+    assert (d[0] == 0).all() and (codes[0, :16] == 8).all() and (codes[0, 16:] == 0).all()
+    assert d[1, 1] == 0x7E and (codes[1, 16:] == 7).all()
+
+
+def test_nvfp4_2d_col_is_transpose():
+    x = W.weights(64, 96, seed=8)
+    t = bf16_to_f32(x)
+    S_enc = R.nvfp4_tensor_scales(R.amax(t))[0]
+    pr, dr = R.quantize_nvfp4(t, S_enc, weight_2d=True)
+    pc, dc = R.quantize_nvfp4(np.ascontiguousarray(t.T), S_enc, weight_2d=True)
+    assert (R.unpack_e2m1(pc) == R.unpack_e2m1(pr).T).all() and (dc == dr.T).all()
+
+
+# ---------------------------------------------------------------------------
+# Philox and stochastic rounding
+# ---------------------------------------------------------------------------
+def _rocrand_helper():
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available to build the rocRAND cross-check")
+    d = tempfile.mkdtemp(prefix="pbs_philox_")
+    exe = os.path.join(d, "philox_rocrand")
+    subprocess.run([hipcc, "-O1", os.path.join(HERE, "helpers", "philox_rocrand.cpp"), "-o", exe],
+                   check=True, capture_output=True)
+    return exe
+
+
+def test_philox_matches_rocrand():
+    exe = _rocrand_helper()
+    rng = np.random.default_rng(77)
+    cases = [(42, 0, i, 0, 0, 0) for i in range(64)]
+    cases += [(42, 0, j, 0, 1, 0) for j in range(16)]
+    cases += [(42, 0, 5, 3, 0, 0), (42, 0, 0xFFFFFFFF, 1, 0, 0)]
+    for _ in range(64):
+        k0, k1, c0, c2, c3 = (int(v) for v in rng.integers(0, 2 ** 32, 5))
+        cases.append((k0, k1, c0, int(rng.integers(0, 2 ** 28)), c2, c3))
+    inp = "\n".join(" ".join(str(v) for v in c) for c in cases) + "\n"
+    out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout.split("\n")
+    for c, line in zip(cases, out):
+        k0, k1, c0, c1, c2, c3 = c
+        ours = philox4x32_10(c0, c1, c2, c3, k0, k1)
+        assert " ".join("%08x" % int(w) for w in ours) == line.strip(), c
+
+
+def test_philox_word0_statistics():
+    r = philox_word0_for_index(np.arange(1 << 20), 42)
+    # 16-bin chi-square on the top 4 bits; 15 dof, p = 1e-6 cut ~ 55
+    counts = np.bincount((r >> 28).astype(np.int64), minlength=16)
+    exp = len(r) / 16
+    chi2 = ((counts - exp) ** 2 / exp).sum()
+    assert chi2 < 55
+    bits = np.unpackbits(r.view(np.uint8)).reshape(-1, 32).mean(axis=0)
+    assert np.all(np.abs(bits - 0.5) < 5 * 0.5 / math.sqrt(len(r)))
+
+
+def test_sr_threshold_exact():
+    vals = np.array([0.1, 0.3, 0.7, 1.2, 1.6, 2.2, 2.9, 3.3, 4.4, 5.9, 1e-30, 4.000001],
+                    dtype=np.float32)
+    mags = [Fraction(float(m)) for m in E2M1.magnitudes]
+    for v in vals:
+        a = Fraction(float(v))
+        lo = max(m for m in mags if m <= a)
+        hi = min(m for m in mags if m > a)
+        T = math.ceil((a - lo) / (hi - lo) * 2 ** 32)
+        lo_code = int(E2M1.encode(np.float32(float(lo)))[()])
+        hi_code = int(E2M1.encode(np.float32(float(hi)))[()])
+        if T >= 1:
+            assert R.sr_e2m1(np.array([v]), np.array([T - 1], dtype=np.uint32))[0] == hi_code
+        if T <= 2 ** 32 - 1:
+            assert R.sr_e2m1(np.array([v]), np.array([T], dtype=np.uint32))[0] == lo_code
+        # sign symmetry
+        assert R.sr_e2m1(np.array([-v]), np.array([0], dtype=np.uint32))[0] == (hi_code | 8)
+
+
+def test_sr_grid_fixed_and_unbiased():
+    grid = E2M1.magnitudes.astype(np.float32)
+    r = philox_word0_for_index(np.arange(4096), 42)
+    for g in grid:
+        assert (E2M1.decode(R.sr_e2m1(np.full(4096, g, dtype=np.float32), r)) == g).all()
+    assert (R.sr_e2m1(np.full(8, 7.5, np.float32), r[:8]) == 7).all()
+    n = 1 << 20
+    r = philox_word0_for_index(np.arange(n), 42)
+    for v in (0.3, 1.3, 2.6, 4.9):
+        out = E2M1.decode(R.sr_e2m1(np.full(n, v, dtype=np.float32), r))
+        mags = E2M1.magnitudes
+        lo = mags[mags <= v].max()
+        hi = mags[mags > v].min()
+        p = (np.float32(v) - lo) / (hi - lo)
+        sigma = (hi - lo) * math.sqrt(p * (1 - p) / n)
+        assert abs(out.mean() - float(np.float32(v))) < 4 * sigma
+
+
+def test_sr_counter_is_logical_index_in_both_copies():
+    r_row = R.sr_random_for((32, 48), "row")
+    r_col = R.sr_random_for((32, 48), "col")
+    assert (r_col == r_row.T).all()
+    assert r_row[3, 5] == philox_word0_for_index(3 * 48 + 5, 42)
+
+
+# ---------------------------------------------------------------------------
+# RHT16
+# ---------------------------------------------------------------------------
+def test_rht_matches_hadamard_popcount_formula():
+    eye = np.eye(16, dtype=np.float32)
+    y = R.rht16_along_rows(eye)                 # column j = 1/4 H D e_j
+    sig = R.rht_signs(42)
+    for i in range(16):
+        for j in range(16):
+            h = (-1) ** bin(i & j).count("1")
+            assert y[i, j] == np.float32(0.25 * h * sig[j])
+    # signs: bit 0 of word 0 of Philox(key (42,0), counter (j, 0, 1, 0))
+    w = philox4x32_10(np.arange(16), 0, 1, 0, 42, 0)[0]
+    assert (sig == np.where(w & 1, -1.0, 1.0)).all()
+    assert set(np.unique(sig)) <= {-1.0, 1.0}
+    # orthogonal: T T^T = I exactly
+    assert (y.astype(np.float64) @ y.T.astype(np.float64) == np.eye(16)).all()
+
+
+def test_rht_preserves_wgrad_product():
+    x = bf16_to_f32(W.activations(256, 8, seed=3)).astype(np.float32)
+    dy = bf16_to_f32(W.grads(256, 6, seed=4)).astype(np.float32)
+    tx = R.rht16_along_rows(x).astype(np.float64)
+    td = R.rht16_along_rows(dy).astype(np.float64)
+    ref = x.astype(np.float64).T @ dy.astype(np.float64)
+    got = tx.T @ td
+    bound = np.abs(x.astype(np.float64)).T @ np.abs(dy.astype(np.float64))
+    assert np.all(np.abs(got - ref) <= 1e-6 * bound + 1e-30)
+
+
+def test_rht_inverse():
+    x = bf16_to_f32(W.activations(32, 4, seed=6))
+    y = R.rht16_along_rows(x).astype(np.float64)
+    H = np.array([[(-1) ** bin(i & j).count("1") for j in range(16)] for i in range(16)], float)
+    D = np.diag(R.rht_signs(42).astype(np.float64))
+    back = np.concatenate([D @ H @ y[g * 16:(g + 1) * 16] / 4 for g in range(2)])
+    assert np.allclose(back, x, rtol=1e-6, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# GEMM reference
+# ---------------------------------------------------------------------------
+def test_gemm_ref_bruteforce_and_special_cases():
+    rng = np.random.default_rng(0)
+    a = rng.standard_normal((7, 33))
+    b = rng.standard_normal((5, 33))
+    c, bnd = gemm_ref(a, b)
+    assert np.allclose(c, gemm_ref_bruteforce(a, b), rtol=1e-13, atol=1e-13)
+    assert (bnd >= np.abs(c)).all()
+    perm = np.eye(33)[rng.permutation(33)]
+    c2, _ = gemm_ref(a, perm)          # B = permutation: exact copy of permuted A
+    assert (c2 == a @ perm.T).all() and (np.sort(c2, axis=1) == np.sort(a, axis=1)).all()
+    ok, tol, err = check_gemm(c * (1 + 5e-6), c, bnd, False)
+    assert ok.all()
+    ok, _, _ = check_gemm(c + 2e-5 * bnd, c, bnd, False)
+    assert not ok.any()
+
+
+def test_ulp_bf16():
+    assert ulp_bf16(1.0) == 2.0 ** -7
+    assert ulp_bf16(1.99) == 2.0 ** -7
+    assert ulp_bf16(2.0) == 2.0 ** -6
+    assert ulp_bf16(-3.0) == 2.0 ** -6
+    assert ulp_bf16(0.0) == 2.0 ** -133
+
+
+def test_tiny_case_all_recipes_gemm_close_to_bf16_product():
+    a, w = W.tiny_current_case(0)
+    x = a                         # [256, 512]
+    dy = W.grads(256, 256, seed=3)
+    exact = {p: None for p in ("fprop",)}
+    ta = bf16_to_f32(a).astype(np.float64)
+    tw = bf16_to_f32(w).astype(np.float64)
+    ref = ta @ tw.T
+    errs = {}
+    for rec in RECIPES:
+        st = None
+        if rec == "fp8_delayed":
+            st = {"x": R.DelayedScaling("e4m3"), "w": R.DelayedScaling("e4m3")}
+            st["x"].update(R.amax(x))
+            st["w"].update(R.amax(w))
+        A, B = pass_operands(rec, "fprop", x=x, w=w, dy=dy, delayed_states=st)
+        c, _ = gemm_ref(A.dequant(), B.dequant())
+        errs[rec] = np.abs(c - ref).max() / np.abs(ref).max()
+    assert errs["bf16"] == 0.0
+    # finer granularity tracks the bf16 product more closely
+    assert errs["fp8_block128"] <= errs["fp8_current"] * 1.05
+    assert errs["mxfp8"] < 0.1 and errs["nvfp4"] < 0.3
+    for rec in ("fp8_current", "fp8_delayed", "fp8_block128", "mxfp8"):
+        assert errs[rec] < 0.1, (rec, errs[rec])
+
+
+# ---------------------------------------------------------------------------
+# shapes and inputs
+# ---------------------------------------------------------------------------
+def test_codonfm_shapes_match_page():
+    g = GOLDEN["codonfm_5b"]
+    c = W.CODONFM_5B
+    assert c["micro_batch"] * c["seq_len"] == g["tokens_M"] == 15872
+    shapes = W.codonfm_shapes()
+    assert len(shapes) == g["n_gemm_shapes"] == 12
+    assert len({(s.layer, s.pass_) for s in shapes}) == 12
+    d = {(s.layer, s.pass_): (s.m, s.k, s.n) for s in shapes}
+    assert d[("qkv", "fprop")] == (15872, 4096, 12288)
+    assert d[("qkv", "dgrad")] == (15872, 12288, 4096)     # K and N swapped
+    assert d[("attn_out", "fprop")] == (15872, 4096, 4096)
+    assert d[("mlp_up", "fprop")] == (15872, 4096, 16384)
+    assert d[("mlp_down", "fprop")] == (15872, 16384, 4096)
+    assert d[("mlp_down", "wgrad")] == (16384, 15872, 4096)
+    total = sum(s.flop for s in shapes)
+    assert abs(total / 1e12 - 19.173) < 1e-3
+    assert len(W.codonfm_shapes(tokens=32 * 1024)) == 12
+    ll = W.gemm_shapes(**{k: v for k, v in W.LLAMA3_8B_LAYER.items()})
+    dl = {(s.layer, s.pass_): (s.m, s.k, s.n) for s in ll}
+    assert dl[("qkv", "fprop")] == (8192, 4096, 6144)
+    assert dl[("mlp_up", "fprop")] == (8192, 4096, 28672)
+    assert dl[("mlp_down", "fprop")] == (8192, 14336, 4096)
+
+
+def test_inputs_deterministic_and_rne():
+    import torch
+    a1 = W.activations(600, 64, seed=1)
+    a2 = W.activations(600, 64, seed=1)
+    assert (a1 == a2).all()
+    assert not (W.activations(600, 64, seed=2) == a1).all()
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 77
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (W.f32_to_bf16_bits(x) == ref).all()
+    t = bf16_to_f32(W.activations(512, 1024, seed=1))
+    big = np.abs(t).max(axis=0) > 50
+    assert big.sum() == 8
+    g = bf16_to_f32(W.grads(256, 256))
+    assert abs(np.median(np.abs(g)) - 0.765e-3) < 0.1e-3     # median |t_3| = 0.765
+
+
+# ---------------------------------------------------------------------------
+# NVFP4: exact worked examples and element-wise brute force
+# ---------------------------------------------------------------------------
+def _frac_nearest_e2m1(v):
+    a = abs(Fraction(float(v)))
+    mags = [Fraction(float(m)) for m in E2M1.magnitudes]
+    if a > 6:
+        c = 7
+    else:
+        best = min(range(8), key=lambda i: (abs(a - mags[i]), i % 2))
+        c = best
+    return c | (8 if np.signbit(v) else 0)
+
+
+def test_nvfp4_ties_worked_example():
+    # global amax 21 -> S_enc = 2688 / 21 = 128 exactly; a block whose max is 6
+    # gets d = E4M3(6 / 6 * 128) = 128 and e_b = 128 / 128 = 1, so every
+    # element is encoded as itself: E2M1 midpoints must go to the even code.
+    blk = np.array([6.0, 2.5, 0.25, 0.75, 1.25, 1.75, 3.5, 5.0,
+                    -2.5, -0.25, -5.0, 0.0, 21.0 / 64, 4.0, 1.0, -6.0], dtype=np.float32)
+    t = np.stack([blk, np.r_[np.full(15, 1.0), 21.0].astype(np.float32)])
+    S_enc, S_dec = R.nvfp4_tensor_scales(R.amax(t))
+    assert S_enc == 128.0
+    packed, d = R.quantize_nvfp4(t, S_enc)
+    assert d[0, 0] == E4M3.encode(np.float32(128.0))
+    codes = R.unpack_e2m1(packed)[0]
+    want = [6.0, 2.0, 0.0, 1.0, 1.0, 2.0, 4.0, 4.0, -2.0, -0.0, -4.0, 0.0, 0.5, 4.0, 1.0, -6.0]
+    got = E2M1.decode(codes)
+    assert list(got) == want
+    assert np.signbit(got[9])
+
+
+def test_nvfp4_block_scale_rounding_order():
+    # d = enc_E4M3(fp32(fp32(a_b / 6) * S_enc)): the division by 6 rounds
+    # first.  Search pairs (a_b, S) where doing the product first would give
+    # another E4M3 code, and check the oracle follows the stated order.
+    mids = (E4M3.magnitudes[:-1] + E4M3.magnitudes[1:]) / 2
+    found = []
+    bf = bf16_to_f32(np.arange(0x3F80, 0x4000, dtype=np.uint16))       # a_b in [1, 2)
+    for M in mids[(mids > 1) & (mids < 400)][::3]:
+        for a in bf:
+            S = np.float32(6 * M / float(a))
+            stated = frac_to_f32(Fraction(frac_to_f32(Fraction(float(a)) / 6)) * Fraction(float(S)))
+            other = frac_to_f32(Fraction(frac_to_f32(Fraction(float(a)) * Fraction(float(S)))) / 6)
+            cs = _brute_e4m3(np.array([stated], np.float32))[0]
+            co = _brute_e4m3(np.array([other], np.float32))[0]
+            if cs != co:
+                found.append((a, S, cs))
+        if len(found) >= 12:
+            break
+    assert len(found) >= 4
+    for a, S, cs in found:
+        t = np.zeros((1, 16), np.float32)
+        t[0, 3] = a
+        _, d = R.quantize_nvfp4(t, S)
+        assert d[0, 0] == cs
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_nvfp4_elements_bruteforce(seed):
+    # bf16 magnitudes 2**-21 .. 16 in shuffled 16-blocks, both signs
+    b = np.arange(0x3500, 0x4180, dtype=np.uint16)
+    b = np.concatenate([b, b | 0x8000])
+    rng = np.random.default_rng(seed)
+    b = b[rng.permutation(len(b))][: (len(b) // 16) * 16].reshape(-1, 16)
+    t = bf16_to_f32(b)
+    S_enc, _ = R.nvfp4_tensor_scales(R.amax(t))
+    r = philox_word0_for_index(np.arange(t.size), 42).reshape(t.shape)
+    for sr in (False, True):
+        packed, d = R.quantize_nvfp4(t, S_enc, sr_random=r if sr else None)
+        codes = R.unpack_e2m1(packed)
+        for i in range(0, t.shape[0], 3):
+            a_b = max(abs(Fraction(float(z))) for z in t[i])
+            dv = frac_to_f32(Fraction(frac_to_f32(a_b / 6)) * Fraction(float(S_enc)))
+            dc = int(_brute_e4m3(np.array([dv], np.float32))[0])
+            assert d[i, 0] == dc
+            dval = float(E4M3.decode(dc))
+            for j in range(16):
+                if dval == 0:
+                    want = 8 if np.signbit(t[i, j]) else 0
+                else:
+                    eb = frac_to_f32(Fraction(float(S_enc)) / Fraction(dval))
+                    eb = FLT_MAX if eb == math.inf else eb
+                    v = np.float32(frac_to_f32(Fraction(float(t[i, j])) * Fraction(eb)))
+                    if np.signbit(t[i, j]) and v == 0:
+                        v = np.float32(-0.0)
+                    if not sr:
+                        want = _frac_nearest_e2m1(v)
+                    else:
+                        av = abs(Fraction(float(v)))
+                        mags = [Fraction(float(m)) for m in E2M1.magnitudes]
+                        if av >= 6:
+                            c = 7
+                        else:
+                            lo = max(k for k in range(8) if mags[k] <= av)
+                            P = (av - mags[lo]) / (mags[lo + 1] - mags[lo])
+                            c = lo + 1 if int(r[i, j]) < P * 2 ** 32 else lo
+                        want = c | (8 if np.signbit(v) else 0)
+                assert codes[i, j] == want, (i, j, sr)
