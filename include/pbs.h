@@ -1,0 +1,241 @@
+/*
+ * pbs.h -- block-scaled quantize-then-GEMM for the linear layers of a
+ * Transformer, on AMD Instinct MI355X (gfx950).  C ABI of libpbs.so.
+ *
+ * What the library computes follows these pages:
+ *  [LP]  "How to optimize Transformer-based models for low-precision
+ *        training" (NVIDIA technical blog).
+ *  [NEMO] "Faster training throughput in FP8 precision with NVIDIA NeMo"
+ *        (NVIDIA technical blog).
+ *  [OPT] "Optimizing Transformer models for low-precision training"
+ *        (setupai.cc digest of an NVIDIA blog post).
+ *  [FP4] "Accelerate LLM training with NVFP4 on Blackwell" (setupai.cc
+ *        digest of an NVIDIA blog post).
+ * Each entry point names the section it implements.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers are DEVICE pointers unless marked [host].  The caller owns
+ *    every buffer; the library never allocates or frees device memory and
+ *    keeps no device state between calls.
+ *  - Every call only enqueues work on `stream` (a hipStream_t; 0 = the
+ *    null stream) and returns without synchronising.  Outputs are valid
+ *    once the stream reaches that point.
+ *  - Arguments are validated on the host before anything is enqueued; on
+ *    a validation error nothing is enqueued.  A failed kernel launch
+ *    returns PBS_ERR_HIP.  pbs_last_error() gives a text message for the
+ *    calling thread's last failure.  No C++ exception crosses the ABI.
+ *  - There is no silent fallback ([LP], "Interpreting results for a real
+ *    model", warns that an unsupported layer can fall back to a wider
+ *    format unnoticed): a combination without a kernel returns
+ *    PBS_ERR_UNSUPPORTED.  Setting the environment variable
+ *    PBS_LOG_LEVEL=1 prints one line per dispatched kernel to stderr.
+ *  - Tensors are row-major.  bf16 inputs are raw bf16 bit patterns.
+ *  - Identical inputs give identical output bytes (amax reductions use an
+ *    order-independent maximum).
+ *  - Shapes: every dimension that a block or a GEMM tile runs along must
+ *    be a multiple of that block (16, 32 or 128) or of the GEMM's tile
+ *    multiple (128); otherwise PBS_ERR_SHAPE.
+ */
+#ifndef PBS_H
+#define PBS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PBS_VERSION 1
+
+typedef enum {
+  PBS_OK = 0,
+  PBS_ERR_INVALID_ARG = 1, /* null pointer, unknown enum, bad flag         */
+  PBS_ERR_SHAPE = 2,       /* dimension not a multiple of block / tile     */
+  PBS_ERR_UNSUPPORTED = 3, /* recipe / format / layout with no kernel      */
+  PBS_ERR_HIP = 4          /* a HIP launch or runtime call failed          */
+} pbs_status;
+
+/* Element formats.  E4M3 is the OCP "FN" variant (max 448, no Inf); E5M2
+ * max 57344; E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 ([OPT] "Technical
+ * deep-dive"; [FP4] "Technical deep-dive"). */
+typedef enum {
+  PBS_FMT_BF16 = 0,
+  PBS_FMT_E4M3 = 1,
+  PBS_FMT_E5M2 = 2,
+  PBS_FMT_E2M1 = 3,
+  PBS_FMT_F32 = 4
+} pbs_format;
+
+/* Scaling recipes ([NEMO] "What are the strengths and trade-offs of the
+ * FP8 scaling recipes?"; [FP4] "Technical deep-dive"). */
+typedef enum {
+  PBS_RECIPE_BF16 = 0,         /* no quantization: bf16 operands            */
+  PBS_RECIPE_FP8_CURRENT = 1,  /* per-tensor scale from this tensor's amax  */
+  PBS_RECIPE_FP8_DELAYED = 2,  /* per-tensor scale from an amax history     */
+  PBS_RECIPE_FP8_BLOCK128 = 3, /* fp32 scale per 1x128 (act/grad) or
+                                  128x128 (weight) block, E4M3 values       */
+  PBS_RECIPE_MXFP8 = 4,        /* E8M0 scale per 32 values, E4M3 values     */
+  PBS_RECIPE_NVFP4 = 5         /* E2M1 values, E4M3 scale per 16 values (1x16
+                                  act/grad, 16x16 weight), fp32 per tensor  */
+} pbs_recipe;
+
+/* The three GEMMs of a linear layer ([LP] "Using autocast mode vs
+ * pre-quantized mode": Fprop, Dgrad and Wgrad are timed separately).
+ * With X [M_tok, K_in], W stored [N_out, K_in], dY [M_tok, N_out]:
+ *   FPROP  Y  [M_tok, N_out] = X  . W^T   contraction K_in
+ *   DGRAD  dX [M_tok, K_in]  = dY . W     contraction N_out
+ *   WGRAD  dW [K_in, N_out]  = X^T . dY   contraction M_tok              */
+typedef enum { PBS_FPROP = 0, PBS_DGRAD = 1, PBS_WGRAD = 2 } pbs_layout;
+
+/* Orientation of a quantized copy.  ROW: blocks run along the stored
+ * columns, output has the input's shape [rows, cols].  COL: blocks run
+ * along the stored rows and the output is written transposed,
+ * [cols, rows], so that in both cases the blocks run along the output's
+ * contiguous axis (the GEMM contraction axis). */
+#define PBS_ROW 1
+#define PBS_COL 2
+
+/* Cast / amax flags. */
+#define PBS_FLAG_RHT16 1   /* apply the 16x16 random Hadamard transform along
+                              the rows first (NVFP4 Wgrad operands)         */
+#define PBS_FLAG_SR 2      /* stochastic rounding of the E2M1 values
+                              (NVFP4 gradients)                             */
+
+/* ---------------------------------------------------------------------
+ * pbs_amax: amax_out[0] = max |x| over a bf16 tensor [rows, cols].
+ * [OPT] "Technical deep-dive" (per-tensor dynamic scaling from the max
+ * absolute value); [LP] "Interpreting results for a real model" (NVFP4's
+ * extra per-tensor amax pass).  With PBS_FLAG_RHT16 the maximum is taken
+ * over the float32 result of the random Hadamard transform applied along
+ * the rows (rows % 16 == 0), sign seed `seed`.  The result is exact.
+ * amax_out: 1 float, overwritten (no need to clear it first).
+ * ------------------------------------------------------------------- */
+pbs_status pbs_amax(const void* x_bf16, int64_t rows, int64_t cols, int flags,
+                    uint64_t seed, float* amax_out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * pbs_scale_from_amax: scale[0] = fp32(fmax / amax[0]), scale_inv[0] =
+ * fp32(1 / scale[0]); amax 0 gives scale 1, an overflowing division gives
+ * FLT_MAX.  fmax = 448 (E4M3), 57344 (E5M2), or 2688 (= 6 * 448, the NVFP4
+ * per-tensor encode scale S_enc; scale_inv is then S_dec).
+ * [NEMO] per-tensor current scaling item; [FP4] two-level scaling.
+ * Any of scale / scale_inv may be NULL.
+ * ------------------------------------------------------------------- */
+pbs_status pbs_scale_from_amax(const float* amax, float fmax, float* scale,
+                               float* scale_inv, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * Delayed scaling state ([OPT] "Technical deep-dive": a rolling amax
+ * history, scale from earlier iterations; [NEMO] per-tensor delayed
+ * scaling item).  The state is a caller-owned device buffer of
+ * pbs_delayed_state_bytes() bytes; checkpointing it is a plain copy.
+ * Layout: float scale; float scale_inv; int32 pos; int32 len;
+ *         float history[len].
+ *  init:   history = 0, pos = 0, scale = scale_inv = 1.
+ *  A step: pbs_cast(PBS_RECIPE_FP8_DELAYED, scale = pbs_delayed_scale(st),
+ *          amax_out = a) casts with the current scale and measures the
+ *          tensor's amax in the same pass; the GEMM of the step reads
+ *          pbs_delayed_scale_inv(st); then
+ *  update: history[pos] = a[0]; pos = (pos + 1) % len;
+ *          scale = fp32(fmax / max(history)) (1 if 0, FLT_MAX on overflow);
+ *          scale_inv = fp32(1 / scale).
+ * Enqueue the GEMM that consumes a delayed cast before the update.
+ * ------------------------------------------------------------------- */
+pbs_status pbs_delayed_state_bytes(int hist_len, size_t* bytes /* [host] */);
+pbs_status pbs_delayed_init(void* state, int hist_len, hipStream_t stream);
+pbs_status pbs_delayed_update(void* state, const float* amax, float fmax,
+                              hipStream_t stream);
+float* pbs_delayed_scale(void* state);     /* device address of `scale`     */
+float* pbs_delayed_scale_inv(void* state); /* device address of `scale_inv` */
+
+/* ---------------------------------------------------------------------
+ * pbs_cast: quantize a bf16 tensor x [rows, cols] into a row copy, a col
+ * copy, or both from one read (orient_mask = PBS_ROW | PBS_COL).
+ *
+ *  recipe FP8_CURRENT / FP8_DELAYED ([NEMO] per-tensor items):
+ *    fmt E4M3 or E5M2; scale = device fp32 scalar s; codes =
+ *    enc(fp32(x * s)), round-to-nearest-even, saturating.  No block
+ *    scales (row_scales / col_scales ignored).  amax_out (optional, may be
+ *    NULL): receives max |x|, measured in the same pass (delayed scaling).
+ *  recipe FP8_BLOCK128 ([NEMO] "Scaling recipe granularity"): fmt E4M3;
+ *    weight_2d = 0: one scale per 1x128 block along the contraction axis,
+ *    scales [rows, cols/128] (row copy) / [cols, rows/128] (col copy);
+ *    weight_2d = 1: one scale per 128x128 tile, [rows/128, cols/128] /
+ *    [cols/128, rows/128].  Stored scale = fp32(1 / s_b), s_b =
+ *    fp32(448 / amax_b).  `scale` unused.
+ *  recipe MXFP8 ([NEMO] MXFP8 item): fmt E4M3, 32-value blocks along the
+ *    contraction axis, E8M0 scale bytes [rows, cols/32] / [cols, rows/32];
+ *    the exponent is the smallest e with amax_b <= 448 * 2^e.
+ *  recipe NVFP4 ([FP4] "Technical deep-dive"; [LP] "Interpreting results
+ *    for a real model"): fmt E2M1, codes packed two per byte along the
+ *    contiguous axis, even element in the low nibble: [rows, cols/2] /
+ *    [cols, rows/2].  E4M3 block scale bytes per 1x16 (weight_2d = 0) or
+ *    16x16 (weight_2d = 1) block, laid out like FP8_BLOCK128's with 16 for
+ *    128.  scale = device fp32 S_enc (pbs_scale_from_amax with fmax 2688 of
+ *    this tensor's amax, taken after the RHT when it is used).
+ *    flags: PBS_FLAG_RHT16 (col copy only, rows % 16 == 0; sign seed
+ *    `seed`), PBS_FLAG_SR (stochastic rounding with Philox4x32-10, key =
+ *    `seed`, counter = logical element index r * cols + c of x).
+ *  Outputs for an orientation not in orient_mask may be NULL.
+ * ------------------------------------------------------------------- */
+pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t cols,
+                    pbs_format fmt, int orient_mask, int weight_2d, int flags,
+                    uint64_t seed, const float* scale, float* amax_out,
+                    void* row_codes, void* row_scales, void* col_codes,
+                    void* col_scales, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * pbs_gemm: C[M, N] = sum_k A[m, k] * B[n, k] with fp32 accumulation, in
+ * the GEMM of `layout` ([LP] "Model configuration and training inputs":
+ * every linear layer is an M x K x N product; "Using autocast mode vs
+ * pre-quantized mode": Fprop / Dgrad / Wgrad).  M, N, K are the GEMM's own
+ * dims (output rows, output cols, contraction).
+ *
+ * Quantized recipes: A is [M, K] and B is [N, K], both contraction-
+ * contiguous, i.e. the copies pbs_cast produces:
+ *   FPROP: A = X row copy,  B = W row copy
+ *   DGRAD: A = dY row copy, B = W col copy
+ *   WGRAD: A = X col copy,  B = dY col copy
+ *  - FP8_CURRENT / FP8_DELAYED: a_fmt, b_fmt in {E4M3, E5M2};
+ *    a_tensor_scale / b_tensor_scale = device fp32 scale_inv of each
+ *    operand; C = acc * fp32(sa_inv * sb_inv).
+ *  - FP8_BLOCK128: a_scale = fp32 [M, K/128]; b_scale = fp32 [N/128, K/128]
+ *    for FPROP / DGRAD (weights, 2D) or [N, K/128] for WGRAD; each 128-long
+ *    slice of the contraction is accumulated apart and added in with the
+ *    product of its two scales.
+ *  - MXFP8: a_scale = E8M0 [M, K/32], b_scale = E8M0 [N, K/32].
+ *  - NVFP4: A, B packed E2M1 [M, K/2], [N, K/2]; a_scale = E4M3 [M, K/16];
+ *    b_scale = E4M3 [N/16, K/16] for FPROP / DGRAD (weights, 2D) or
+ *    [N, K/16] for WGRAD; a_tensor_scale / b_tensor_scale = S_dec of each.
+ * BF16 recipe: operands in their natural storage -- FPROP: A = X [M, K],
+ *    B = W [N, K]; DGRAD: A = dY [M, K], B = W stored [K, N]; WGRAD:
+ *    A = X stored [K, M], B = dY stored [K, N].
+ * c_fmt: PBS_FMT_F32 or PBS_FMT_BF16 (round-to-nearest-even).
+ * Shapes: M, N multiples of 128; K a multiple of 128 (256 for NVFP4).
+ * ------------------------------------------------------------------- */
+pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, int64_t N, int64_t K,
+                    const void* A, pbs_format a_fmt, const void* a_scale,
+                    const float* a_tensor_scale, const void* B, pbs_format b_fmt,
+                    const void* b_scale, const float* b_tensor_scale, void* C,
+                    pbs_format c_fmt, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * pbs_quantized_bytes [host]: bytes of the codes and of the block scales
+ * of one quantized copy of a [rows, cols] tensor (not counting per-tensor
+ * fp32 scalars).  For NVFP4 with 1x16 blocks this is n/2 + n/16 bytes,
+ * about 4.5 bits per value with the fp32 tensor scale ([FP4] "Technical
+ * deep-dive").
+ * ------------------------------------------------------------------- */
+pbs_status pbs_quantized_bytes(pbs_recipe recipe, int64_t rows, int64_t cols, int weight_2d,
+                               size_t* code_bytes, size_t* scale_bytes);
+
+const char* pbs_last_error(void);
+int pbs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PBS_H */

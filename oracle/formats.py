@@ -77,15 +77,17 @@ class MiniFloat:
 
     # -- encode ---------------------------------------------------------
     def encode(self, v):
-        """Round-to-nearest-even, saturating encode of finite values ``v``.
+        """Round-to-nearest-even, saturating encode of the values ``v``.
 
         ``v`` is any float array (float32 values are represented exactly in
-        float64).  Returns uint8 codes.
+        float64).  An infinite value -- a scaled fp32 product that overflowed,
+        whose exact magnitude is above every finite code -- saturates like
+        any other value above the maximum.  Returns uint8 codes.
         """
         v = np.asarray(v)
-        if not np.all(np.isfinite(v)):
-            raise ValueError("non-finite input is outside the encoder's contract")
-        v64 = v.astype(np.float64)
+        if np.any(np.isnan(v)):
+            raise ValueError("NaN input is outside the encoder's contract")
+        v64 = v.astype(np.float64)     # +-Inf (a scaled value that overflowed fp32) saturates
         neg = np.signbit(v64)
         a = np.abs(v64)
         mags = self.magnitudes

@@ -1,0 +1,466 @@
+// Quantize (cast) kernels for every recipe.
+//
+// One kernel template covers all recipes.  A workgroup of 128 threads
+// stages a 128 x 128 tile of the bf16 input in LDS (one coalesced HBM read),
+// then
+//   * the row copy: thread t quantizes row t of the tile (blocks along the
+//     columns) and writes it in place, and/or
+//   * the col copy: thread t quantizes column t of the tile (blocks along
+//     the rows) and writes it as row t of the transposed output,
+// so both copies come from one read of the input, and every 1D block (16,
+// 32 or 128 long) lies inside one thread's strip: block maxima need no
+// cross-thread reduction.  2D weight blocks (16x16 NVFP4) reduce across 16
+// neighbouring lanes; 128x128 tiles use the tile maximum.
+//
+// Recipes:
+//  per-tensor FP8 -- "Faster training throughput in FP8 precision with NVIDIA
+//    NeMo", strengths and trade-offs (per-tensor current / delayed items);
+//    codes = enc(fp32(x * s)).
+//  sub-channel FP8 -- same page, "Scaling recipe granularity": 1x128 blocks
+//    for activations and gradients, 128x128 for weights; s_b = fp32(448 /
+//    amax_b), stored as fp32(1 / s_b).
+//  MXFP8 -- same page, MXFP8 item: 32-value blocks, E8M0 power-of-two scale,
+//    the smallest exponent that brings the block maximum within 448.
+//  NVFP4 -- "Accelerate LLM training with NVFP4 on Blackwell", "Technical
+//    deep-dive": E2M1 values, E4M3 scale per 16 values, fp32 per tensor;
+//    "How to optimize Transformer-based models for low-precision training",
+//    "Interpreting results for a real model": 2D block scales for weights,
+//    random Hadamard transform on the Wgrad inputs, stochastic rounding of
+//    gradients.  d = enc_E4M3(fp32(fp32(amax_b / 6) * S_enc)), e_b =
+//    fp32(S_enc / d), codes = enc_E2M1(fp32(x * e_b)) or its stochastic
+//    rounding with Philox4x32-10 (counter = logical element index).
+#include "device.hpp"
+#include "host.hpp"
+
+namespace pbs {
+
+enum { R_TENSOR = 0, R_BLOCK128 = 1, R_MX = 2, R_NV = 3 };
+enum { F_E4M3 = 0, F_E5M2 = 1 };
+
+constexpr int TILE = 128;
+constexpr int LDS_STRIDE = TILE + 8;   // bf16 per LDS row: 272 B, offsets rows by 4 banks
+
+struct CastArgs {
+  const bf16_t* x;
+  int64_t R, C;
+  const float* scale;      // per-tensor s, or NVFP4 S_enc
+  uint32_t* amax_out;      // fused amax (per-tensor recipes), may be null
+  uint8_t* row_codes;
+  void* row_scales;
+  uint8_t* col_codes;
+  void* col_scales;
+  uint64_t seed;
+};
+
+template <int FMT>
+__device__ __forceinline__ uint32_t enc_fp8(float v) {
+  return FMT == F_E4M3 ? enc_e4m3(v) : enc_e5m2(v);
+}
+
+__device__ __forceinline__ uint32_t lds_bits(const bf16_t* tile, int r, int c) {
+  return (uint32_t)tile[r * LDS_STRIDE + c];
+}
+
+// 16 consecutive values of a strip: along a row (ROWDIR) or down a column.
+template <bool ROWDIR>
+__device__ __forceinline__ void read16(const bf16_t* tile, int strip, int off, uint32_t* b) {
+  if (ROWDIR) {
+    const uint4 v0 = *(const uint4*)&tile[strip * LDS_STRIDE + off];
+    const uint4 v1 = *(const uint4*)&tile[strip * LDS_STRIDE + off + 8];
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      b[2 * i] = w[i] & 0xFFFFu;
+      b[2 * i + 1] = w[i] >> 16;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) b[i] = lds_bits(tile, off + i, strip);
+  }
+}
+
+__device__ __forceinline__ uint32_t max_abs_bits16(const uint32_t* b) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t a = b[i] & 0x7FFFu;
+    m = m > a ? m : a;
+  }
+  return m;
+}
+
+__device__ __forceinline__ void store16(uint8_t* dst, const uint32_t* code) {
+  uint4 w;
+  w.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+  w.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+  w.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
+  w.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
+  *(uint4*)dst = w;
+}
+
+__device__ __forceinline__ uint2 pack_e2m1_16(const uint32_t* q) {
+  uint2 w;
+  w.x = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12) | (q[4] << 16) | (q[5] << 20) |
+        (q[6] << 24) | (q[7] << 28);
+  w.y = q[8] | (q[9] << 4) | (q[10] << 8) | (q[11] << 12) | (q[12] << 16) | (q[13] << 20) |
+        (q[14] << 24) | (q[15] << 28);
+  return w;
+}
+
+// Max over the 16 lanes that share bits 4..5 of the lane id.
+__device__ __forceinline__ uint32_t max16lanes(uint32_t v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    uint32_t w = (uint32_t)__shfl_xor((int)v, o, 64);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+// NVFP4 block: codes for 16 fp32 values with block max bits `abits`
+// (of |value|), global encode scale S.  Returns the E4M3 block scale code.
+template <bool SR>
+__device__ __forceinline__ uint32_t nvfp4_block(const float* v, uint32_t abits, float S,
+                                                const uint32_t* rnd, uint32_t* q) {
+  const float a_b = __uint_as_float(abits);
+  const float d_val = (a_b / 6.0f) * S;
+  const uint32_t d_code = enc_e4m3(d_val);              // non-negative input: no sign bit
+  const float d = dec_e4m3_pos(d_code);
+  if (d == 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = (__float_as_uint(v[i]) >> 28) & 0x8u;
+  } else {
+    float e_b = S / d;
+    if (__float_as_uint(e_b) == 0x7F800000u) e_b = 3.40282346638528859812e+38f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float s = v[i] * e_b;
+      q[i] = SR ? sr_e2m1(s, rnd[i]) : enc_e2m1(s);
+    }
+  }
+  return d_code;
+}
+
+// Quantize one strip (a tile row if ROWDIR, else a tile column) of `len`
+// valid values (multiple of 16) and write it.
+//  strip: index of the strip in the tile (= thread id)
+//  out_codes: start of this strip's output row segment
+//  g_row/g_col of element 0 of the strip (for the SR counter)
+template <int RECIPE, int FMT, bool ROWDIR, bool W2D, bool RHT, bool SR>
+__device__ __forceinline__ void quantize_strip(const bf16_t* tile, int strip, int len,
+                                               const CastArgs& a, float tile_scale,
+                                               uint8_t* out_codes, uint8_t* out_scales8,
+                                               float* out_scales32, int64_t g_row0, int64_t g_col0,
+                                               uint32_t rht_mask, bool scale_writer) {
+  if (RECIPE == R_TENSOR) {
+    const float s = tile_scale;
+    for (int j = 0; j < len; j += 16) {
+      uint32_t b[16], code[16];
+      read16<ROWDIR>(tile, strip, j, b);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) code[i] = enc_fp8<FMT>(bf16_to_float(b[i]) * s);
+      store16(out_codes + j, code);
+    }
+  } else if (RECIPE == R_BLOCK128) {
+    float s = tile_scale;
+    if (!W2D) {                 // one 1x128 block = the whole strip
+      uint32_t m = 0;
+      for (int j = 0; j < TILE; j += 16) {
+        uint32_t b[16];
+        read16<ROWDIR>(tile, strip, j, b);
+        uint32_t mm = max_abs_bits16(b);
+        m = m > mm ? m : mm;
+      }
+      s = scale_from_amax(bf16_to_float(m), 448.0f);
+      out_scales32[0] = 1.0f / s;
+    } else if (scale_writer) {
+      out_scales32[0] = 1.0f / s;
+    }
+    for (int j = 0; j < TILE; j += 16) {
+      uint32_t b[16], code[16];
+      read16<ROWDIR>(tile, strip, j, b);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) code[i] = enc_e4m3(bf16_to_float(b[i]) * s);
+      store16(out_codes + j, code);
+    }
+  } else if (RECIPE == R_MX) {
+    for (int j = 0; j < len; j += 32) {
+      uint32_t b0[16], b1[16], code[16];
+      read16<ROWDIR>(tile, strip, j, b0);
+      read16<ROWDIR>(tile, strip, j + 16, b1);
+      uint32_t m0 = max_abs_bits16(b0), m1 = max_abs_bits16(b1);
+      const uint32_t c = mx_e8m0_from_bf16_amax(m0 > m1 ? m0 : m1);
+      const float inv = mx_inv_scale(c);
+      out_scales8[j / 32] = (uint8_t)c;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) code[i] = enc_e4m3(bf16_to_float(b0[i]) * inv);
+      store16(out_codes + j, code);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) code[i] = enc_e4m3(bf16_to_float(b1[i]) * inv);
+      store16(out_codes + j + 16, code);
+    }
+  } else {  // R_NV
+    const float S = tile_scale;
+    for (int j = 0; j < len; j += 16) {
+      uint32_t b[16], q[16], rnd[16];
+      float v[16];
+      read16<ROWDIR>(tile, strip, j, b);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = bf16_to_float(b[i]);
+      if (RHT) rht16(v, rht_mask);
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint32_t x = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+        m = m > x ? m : x;
+      }
+      if (W2D) m = max16lanes(m);
+      if (SR) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          // element i of this segment sits at logical (row, col) of x
+          const int64_t gr = ROWDIR ? g_row0 : g_row0 + j + i;
+          const int64_t gc = ROWDIR ? g_col0 + j + i : g_col0;
+          const uint64_t idx = (uint64_t)(gr * a.C + gc);
+          rnd[i] = philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
+                                (uint32_t)(a.seed >> 32));
+        }
+      }
+      const uint32_t dcode = nvfp4_block<SR>(v, m, S, rnd, q);
+      const uint2 w = pack_e2m1_16(q);
+      *(uint2*)(out_codes + j / 2) = w;
+      if (!W2D || scale_writer) out_scales8[j / 16] = (uint8_t)dcode;
+    }
+  }
+}
+
+template <int RECIPE, int FMT, bool ROW, bool COL, bool W2D, bool RHT, bool SR, bool AMAX>
+__global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
+  __shared__ __align__(16) bf16_t tile[TILE * LDS_STRIDE];
+  __shared__ uint32_t s_part[2];
+  __shared__ uint32_t s_rht_mask;
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * TILE, c0 = (int64_t)blockIdx.x * TILE;
+  const int rlim = (int)min((int64_t)TILE, a.R - r0);
+  const int clim = (int)min((int64_t)TILE, a.C - c0);
+
+  // Stage the tile: 16 threads per 256-byte row, 8 rows per pass.
+  uint32_t mx = 0;
+  {
+    const int ch = t & 15;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int row = (t >> 4) + 8 * i;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < rlim && ch * 8 < clim)
+        v = ld_nt16(a.x + (r0 + row) * a.C + c0 + ch * 8);
+      *(uint4*)&tile[row * LDS_STRIDE + ch * 8] = v;
+      if (AMAX || (RECIPE == R_BLOCK128 && W2D)) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t lo = w[k] & 0x7FFFu, hi = (w[k] >> 16) & 0x7FFFu;
+          mx = mx > lo ? mx : lo;
+          mx = mx > hi ? mx : hi;
+        }
+      }
+    }
+  }
+  if (RHT && t < 64) {
+    uint32_t bit = 0;
+    if (t < 16) bit = philox_word0(t, 0u, 1u, 0u, (uint32_t)a.seed, (uint32_t)(a.seed >> 32)) & 1u;
+    const uint64_t bal = __ballot(bit);
+    if (t == 0) s_rht_mask = (uint32_t)bal;
+  }
+  if (AMAX || (RECIPE == R_BLOCK128 && W2D)) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      uint32_t w = (uint32_t)__shfl_xor((int)mx, o, 64);
+      mx = mx > w ? mx : w;
+    }
+    if ((t & 63) == 0) s_part[t >> 6] = mx;
+  }
+  __syncthreads();
+  uint32_t tile_max_bits = 0;
+  if (AMAX || (RECIPE == R_BLOCK128 && W2D)) {
+    tile_max_bits = s_part[0] > s_part[1] ? s_part[0] : s_part[1];
+    if (AMAX && t == 0) atomicMax(a.amax_out, tile_max_bits << 16);
+  }
+  const uint32_t rht_mask = RHT ? s_rht_mask : 0u;
+
+  float tile_scale = 0.0f;
+  if (RECIPE == R_TENSOR || RECIPE == R_NV) tile_scale = *a.scale;
+  if (RECIPE == R_BLOCK128 && W2D) tile_scale = scale_from_amax(bf16_to_float(tile_max_bits), 448.0f);
+
+  if (ROW && t < rlim) {
+    const int64_t gr = r0 + t;
+    uint8_t* codes = (RECIPE == R_NV) ? a.row_codes + gr * (a.C / 2) + c0 / 2 : a.row_codes + gr * a.C + c0;
+    uint8_t* sc8 = nullptr;
+    float* sc32 = nullptr;
+    bool writer = true;
+    if (RECIPE == R_BLOCK128)
+      sc32 = W2D ? (float*)a.row_scales + (r0 / 128) * (a.C / 128) + c0 / 128
+                 : (float*)a.row_scales + gr * (a.C / 128) + c0 / 128;
+    if (RECIPE == R_BLOCK128 && W2D) writer = (t == 0);
+    if (RECIPE == R_MX) sc8 = (uint8_t*)a.row_scales + gr * (a.C / 32) + c0 / 32;
+    if (RECIPE == R_NV) {
+      sc8 = W2D ? (uint8_t*)a.row_scales + (gr / 16) * (a.C / 16) + c0 / 16
+                : (uint8_t*)a.row_scales + gr * (a.C / 16) + c0 / 16;
+      if (W2D) writer = (t & 15) == 0;
+    }
+    quantize_strip<RECIPE, FMT, true, W2D, false, SR>(tile, t, clim, a, tile_scale, codes, sc8, sc32,
+                                                      gr, c0, 0u, writer);
+  }
+  if (COL && t < clim) {
+    const int64_t gc = c0 + t;
+    uint8_t* codes = (RECIPE == R_NV) ? a.col_codes + gc * (a.R / 2) + r0 / 2 : a.col_codes + gc * a.R + r0;
+    uint8_t* sc8 = nullptr;
+    float* sc32 = nullptr;
+    bool writer = true;
+    if (RECIPE == R_BLOCK128)
+      sc32 = W2D ? (float*)a.col_scales + (c0 / 128) * (a.R / 128) + r0 / 128
+                 : (float*)a.col_scales + gc * (a.R / 128) + r0 / 128;
+    if (RECIPE == R_BLOCK128 && W2D) writer = (t == 0);
+    if (RECIPE == R_MX) sc8 = (uint8_t*)a.col_scales + gc * (a.R / 32) + r0 / 32;
+    if (RECIPE == R_NV) {
+      sc8 = W2D ? (uint8_t*)a.col_scales + (gc / 16) * (a.R / 16) + r0 / 16
+                : (uint8_t*)a.col_scales + gc * (a.R / 16) + r0 / 16;
+      if (W2D) writer = (t & 15) == 0;
+    }
+    quantize_strip<RECIPE, FMT, false, W2D, RHT, SR>(tile, t, rlim, a, tile_scale, codes, sc8, sc32,
+                                                     r0, gc, rht_mask, writer);
+  }
+}
+
+__global__ void zero_u32_kernel(uint32_t* p) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0u;
+}
+
+typedef void (*cast_fn)(CastArgs);
+
+template <int RECIPE, int FMT, bool W2D, bool RHT, bool SR, bool AMAX>
+static cast_fn pick_orient(int mask) {
+  if (mask == PBS_ROW) return cast_tile_kernel<RECIPE, FMT, true, false, W2D, false, SR, AMAX>;
+  if (mask == PBS_COL) return cast_tile_kernel<RECIPE, FMT, false, true, W2D, RHT, SR, AMAX>;
+  return cast_tile_kernel<RECIPE, FMT, true, true, W2D, false, SR, AMAX>;
+}
+
+}  // namespace pbs
+
+using namespace pbs;
+
+extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t cols,
+                               pbs_format fmt, int orient_mask, int weight_2d, int flags,
+                               uint64_t seed, const float* scale, float* amax_out, void* row_codes,
+                               void* row_scales, void* col_codes, void* col_scales,
+                               hipStream_t stream) {
+  PBS_REQUIRE(orient_mask >= 1 && orient_mask <= 3, PBS_ERR_INVALID_ARG,
+              "pbs_cast: orient_mask must be PBS_ROW, PBS_COL or both");
+  PBS_REQUIRE((flags & ~(PBS_FLAG_RHT16 | PBS_FLAG_SR)) == 0, PBS_ERR_INVALID_ARG,
+              "pbs_cast: unknown flags %d", flags);
+  PBS_REQUIRE(rows >= 0 && cols >= 0, PBS_ERR_SHAPE, "pbs_cast: negative shape");
+  PBS_REQUIRE(rows % 16 == 0 && cols % 16 == 0, PBS_ERR_SHAPE,
+              "pbs_cast: rows and cols must be multiples of 16 (got %lld x %lld)", (long long)rows,
+              (long long)cols);
+  const bool row = orient_mask & PBS_ROW, col = orient_mask & PBS_COL;
+  const bool rht = flags & PBS_FLAG_RHT16, sr = flags & PBS_FLAG_SR;
+  const bool w2d = weight_2d != 0;
+  PBS_REQUIRE(rows * cols == 0 || x_bf16, PBS_ERR_INVALID_ARG, "pbs_cast: x is null");
+  PBS_REQUIRE(((uintptr_t)x_bf16 & 15) == 0, PBS_ERR_INVALID_ARG, "pbs_cast: x not 16-byte aligned");
+  PBS_REQUIRE(!row || row_codes, PBS_ERR_INVALID_ARG, "pbs_cast: row_codes is null");
+  PBS_REQUIRE(!col || col_codes, PBS_ERR_INVALID_ARG, "pbs_cast: col_codes is null");
+  PBS_REQUIRE(!row || ((uintptr_t)row_codes & 15) == 0, PBS_ERR_INVALID_ARG, "pbs_cast: row_codes not 16-byte aligned");
+  PBS_REQUIRE(!col || ((uintptr_t)col_codes & 15) == 0, PBS_ERR_INVALID_ARG, "pbs_cast: col_codes not 16-byte aligned");
+  PBS_REQUIRE(!rht && !sr || recipe == PBS_RECIPE_NVFP4, PBS_ERR_UNSUPPORTED,
+              "pbs_cast: RHT16 / SR flags apply to the NVFP4 recipe only");
+  PBS_REQUIRE(!rht || orient_mask == PBS_COL, PBS_ERR_UNSUPPORTED,
+              "pbs_cast: RHT16 runs along the rows and produces the col copy only");
+  PBS_REQUIRE(!w2d || recipe == PBS_RECIPE_FP8_BLOCK128 || recipe == PBS_RECIPE_NVFP4,
+              PBS_ERR_UNSUPPORTED, "pbs_cast: 2D blocks exist for FP8_BLOCK128 and NVFP4 only");
+  PBS_REQUIRE(!(w2d && (rht || sr)), PBS_ERR_UNSUPPORTED,
+              "pbs_cast: 2D weight blocks take neither RHT16 nor SR");
+  PBS_REQUIRE(amax_out == nullptr || recipe == PBS_RECIPE_FP8_CURRENT || recipe == PBS_RECIPE_FP8_DELAYED,
+              PBS_ERR_UNSUPPORTED, "pbs_cast: fused amax is for the per-tensor recipes");
+
+  CastArgs a;
+  a.x = (const bf16_t*)x_bf16;
+  a.R = rows;
+  a.C = cols;
+  a.scale = scale;
+  a.amax_out = (uint32_t*)amax_out;
+  a.row_codes = (uint8_t*)row_codes;
+  a.row_scales = row_scales;
+  a.col_codes = (uint8_t*)col_codes;
+  a.col_scales = col_scales;
+  a.seed = seed;
+
+  cast_fn fn = nullptr;
+  const char* name = "";
+  switch (recipe) {
+    case PBS_RECIPE_FP8_CURRENT:
+    case PBS_RECIPE_FP8_DELAYED: {
+      PBS_REQUIRE(fmt == PBS_FMT_E4M3 || fmt == PBS_FMT_E5M2, PBS_ERR_UNSUPPORTED,
+                  "pbs_cast: per-tensor FP8 takes E4M3 or E5M2");
+      PBS_REQUIRE(scale, PBS_ERR_INVALID_ARG, "pbs_cast: per-tensor FP8 needs the device scale");
+      const bool am = amax_out != nullptr;
+      if (fmt == PBS_FMT_E4M3)
+        fn = am ? pick_orient<R_TENSOR, F_E4M3, false, false, false, true>(orient_mask)
+                : pick_orient<R_TENSOR, F_E4M3, false, false, false, false>(orient_mask);
+      else
+        fn = am ? pick_orient<R_TENSOR, F_E5M2, false, false, false, true>(orient_mask)
+                : pick_orient<R_TENSOR, F_E5M2, false, false, false, false>(orient_mask);
+      name = "cast_tensor_fp8";
+      break;
+    }
+    case PBS_RECIPE_FP8_BLOCK128: {
+      PBS_REQUIRE(fmt == PBS_FMT_E4M3, PBS_ERR_UNSUPPORTED, "pbs_cast: FP8_BLOCK128 takes E4M3");
+      PBS_REQUIRE((!row || cols % 128 == 0) && (!col || rows % 128 == 0) &&
+                      (!w2d || (rows % 128 == 0 && cols % 128 == 0)),
+                  PBS_ERR_SHAPE, "pbs_cast: FP8_BLOCK128 needs the blocked dims to be multiples of 128");
+      PBS_REQUIRE((!row || row_scales) && (!col || col_scales), PBS_ERR_INVALID_ARG,
+                  "pbs_cast: block scales output is null");
+      fn = w2d ? pick_orient<R_BLOCK128, F_E4M3, true, false, false, false>(orient_mask)
+               : pick_orient<R_BLOCK128, F_E4M3, false, false, false, false>(orient_mask);
+      name = "cast_block128";
+      break;
+    }
+    case PBS_RECIPE_MXFP8: {
+      PBS_REQUIRE(fmt == PBS_FMT_E4M3, PBS_ERR_UNSUPPORTED, "pbs_cast: MXFP8 takes E4M3");
+      PBS_REQUIRE((!row || cols % 32 == 0) && (!col || rows % 32 == 0), PBS_ERR_SHAPE,
+                  "pbs_cast: MXFP8 needs the blocked dim to be a multiple of 32");
+      PBS_REQUIRE((!row || row_scales) && (!col || col_scales), PBS_ERR_INVALID_ARG,
+                  "pbs_cast: block scales output is null");
+      fn = pick_orient<R_MX, F_E4M3, false, false, false, false>(orient_mask);
+      name = "cast_mxfp8";
+      break;
+    }
+    case PBS_RECIPE_NVFP4: {
+      PBS_REQUIRE(fmt == PBS_FMT_E2M1, PBS_ERR_UNSUPPORTED, "pbs_cast: NVFP4 takes E2M1");
+      PBS_REQUIRE(scale, PBS_ERR_INVALID_ARG, "pbs_cast: NVFP4 needs the device S_enc");
+      PBS_REQUIRE((!row || row_scales) && (!col || col_scales), PBS_ERR_INVALID_ARG,
+                  "pbs_cast: block scales output is null");
+      if (rht)
+        fn = sr ? pick_orient<R_NV, F_E4M3, false, true, true, false>(orient_mask)
+                : pick_orient<R_NV, F_E4M3, false, true, false, false>(orient_mask);
+      else if (w2d)
+        fn = pick_orient<R_NV, F_E4M3, true, false, false, false>(orient_mask);
+      else
+        fn = sr ? pick_orient<R_NV, F_E4M3, false, false, true, false>(orient_mask)
+                : pick_orient<R_NV, F_E4M3, false, false, false, false>(orient_mask);
+      name = "cast_nvfp4";
+      break;
+    }
+    case PBS_RECIPE_BF16:
+      return set_error(PBS_ERR_UNSUPPORTED, "pbs_cast: the BF16 recipe has no cast");
+    default:
+      return set_error(PBS_ERR_INVALID_ARG, "pbs_cast: unknown recipe %d", (int)recipe);
+  }
+  if (amax_out) hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)amax_out);
+  if (rows == 0 || cols == 0) return check_launch("pbs_cast");
+  dim3 grid((unsigned)ceil_div(cols, TILE), (unsigned)ceil_div(rows, TILE));
+  log_dispatch("%s recipe=%d fmt=%d orient=%d w2d=%d flags=%d rows=%lld cols=%lld grid=%ux%u", name,
+               (int)recipe, (int)fmt, orient_mask, (int)w2d, flags, (long long)rows, (long long)cols,
+               grid.x, grid.y);
+  hipLaunchKernelGGL(fn, grid, dim3(128), 0, stream, a);
+  return check_launch("pbs_cast");
+}

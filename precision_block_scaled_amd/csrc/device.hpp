@@ -1,0 +1,231 @@
+// Device helpers for the gfx950 kernels: bf16 access, bit-level encoders
+// for E4M3 / E5M2 / E2M1, E8M0 exponent selection, Philox4x32-10,
+// stochastic rounding and the 16-point random Hadamard transform.
+//
+// Every encoder here works on the bits of an IEEE binary32 value: the
+// rounding of the value into the narrow format is a round-to-nearest-even
+// right shift of (exponent | mantissa), which carries into the exponent by
+// itself.  Saturation is a compare against the bit pattern of the largest
+// finite value.  Formats: "Optimizing Transformer models for low-precision
+// training", "Technical deep-dive" (E4M3 / E5M2 bit splits); "Accelerate LLM
+// training with NVFP4 on Blackwell", "Technical deep-dive" (E2M1, values in
+// -6..6).  Rounding rule where the pages are silent: nearest, ties to even,
+// saturating, sign of zero kept.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pbs {
+
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal: the data is read once).
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Round-to-nearest-even right shift of x by s (1 <= s <= 31).
+__device__ __forceinline__ uint32_t rne_shr(uint32_t x, uint32_t s) {
+  uint32_t q = x >> s;
+  uint32_t r = x & ((1u << s) - 1u);
+  uint32_t h = 1u << (s - 1u);
+  return q + (uint32_t)((r > h) | ((r == h) & (q & 1u)));
+}
+
+// E4M3 (bias 7, max 448 = 0x7E).  Normal results: fp32 biased exponent
+// e >= 121 (2^-6); the E4M3 code is (e - 120) << 3 | top 3 mantissa bits,
+// i.e. (a - (120 << 23)) >> 20 rounded.  Subnormal results: a / 2^-9
+// rounded, = m24 >> (141 - e).
+__device__ __forceinline__ uint32_t enc_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x43E00000u) {                 // > 448
+    code = 0x7Eu;
+  } else {
+    uint32_t e = a >> 23;
+    if (e >= 121u) {
+      code = rne_shr(a - (120u << 23), 20u);
+    } else {
+      uint32_t m = (a & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+      uint32_t s = 141u - (e ? e : 1u);
+      code = (s > 25u) ? 0u : rne_shr(m, s);
+    }
+  }
+  return sign | code;
+}
+
+// E5M2 (bias 15, max 57344 = 0x7B).  Normal: e >= 113, code =
+// (a - (112 << 23)) >> 21 rounded.  Subnormal: a / 2^-16 = m24 >> (134 - e).
+__device__ __forceinline__ uint32_t enc_e5m2(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x47600000u) {                 // > 57344
+    code = 0x7Bu;
+  } else {
+    uint32_t e = a >> 23;
+    if (e >= 113u) {
+      code = rne_shr(a - (112u << 23), 21u);
+    } else {
+      uint32_t m = (a & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+      uint32_t s = 134u - (e ? e : 1u);
+      code = (s > 25u) ? 0u : rne_shr(m, s);
+    }
+  }
+  return sign | code;
+}
+
+// E2M1 (bias 1, max 6 = 0x7), 4-bit code with the sign in bit 3.
+// Normal: e >= 127 (1.0), code = (a - (126 << 23)) >> 22 rounded.
+// Subnormal (0.5 = code 1): a / 0.5 = m24 >> (149 - e).
+__device__ __forceinline__ uint32_t enc_e2m1(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 28) & 0x8u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x40C00000u) {                 // > 6
+    code = 0x7u;
+  } else {
+    uint32_t e = a >> 23;
+    if (e >= 127u) {
+      code = rne_shr(a - (126u << 23), 22u);
+    } else {
+      uint32_t m = (a & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+      uint32_t s = 149u - (e ? e : 1u);
+      code = (s > 25u) ? 0u : rne_shr(m, s);
+    }
+  }
+  return sign | code;
+}
+
+// Exact value of a non-negative E4M3 code (0..0x7E) as float.
+__device__ __forceinline__ float dec_e4m3_pos(uint32_t c) {
+  uint32_t e = c >> 3, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;             // m * 2^-9, exact
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Magnitude of an E2M1 code's low 3 bits as float (0, .5, 1, 1.5, 2, 3, 4, 6).
+__device__ __forceinline__ float dec_e2m1_mag(uint32_t c) {
+  uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  if (e == 0) return m ? 0.5f : 0.0f;
+  return __uint_as_float(((e + 126u) << 23) | (m << 22));
+}
+
+// MXFP8 block exponent: E8M0 code of the smallest e in [-127, 127] with
+// amax <= 448 * 2^e, from the bf16 bits of a non-negative block maximum.
+// amax = 1.f * 2^(E-127): e = E - 135 if f <= 0.75, else E - 134.
+// Zero, bf16 subnormals and anything below 448 * 2^-127 give code 0.
+__device__ __forceinline__ uint32_t mx_e8m0_from_bf16_amax(uint32_t abits) {
+  int E = (int)((abits >> 7) & 0xFFu);
+  if (E == 0) return 0u;
+  int c = E - 8 + (((abits & 0x7Fu) > 0x60u) ? 1 : 0);
+  c = c < 0 ? 0 : (c > 254 ? 254 : c);
+  return (uint32_t)c;
+}
+
+// 2^(127 - c) as float for an E8M0 code c in [0, 254]: the factor that
+// divides a block by its scale.  Normal for every c that can occur (c <= 247).
+__device__ __forceinline__ float mx_inv_scale(uint32_t c) {
+  return __uint_as_float((254u - c) << 23);
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC'11): ten rounds of two 32x32->64 products and a
+// word permutation, key bumped by the Weyl constants between rounds.
+// Only word 0 of the output is used.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    uint32_t lo0 = 0xD2511F53u * c0;
+    uint32_t hi0 = __umulhi(0xD2511F53u, c0);
+    uint32_t lo1 = 0xCD9E8D57u * c2;
+    uint32_t hi1 = __umulhi(0xCD9E8D57u, c2);
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c0;
+}
+
+// Stochastic rounding of v to E2M1 with the 32-bit random r: |v| >= 6 gives
+// 6; otherwise with lo <= |v| < hi adjacent E2M1 magnitudes, round up iff
+// r < ceil((|v| - lo) / (hi - lo) * 2^32).  |v| - lo is exact (Sterbenz or
+// lo = 0) and the scaling by 2^32 / (hi - lo) is a power of two, so the
+// threshold is computed exactly.
+__device__ __forceinline__ uint32_t sr_e2m1(float v, uint32_t r) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 28) & 0x8u;
+  float a = __uint_as_float(u & 0x7FFFFFFFu);
+  uint32_t code;
+  if (a >= 6.0f) {
+    code = 7u;
+  } else {
+    uint32_t lo_code;
+    float lo, scale;                                   // scale = 2^32 / (hi - lo)
+    if (a < 0.5f)      { lo_code = 0; lo = 0.0f; scale = 8589934592.0f; }
+    else if (a < 2.0f) { lo_code = (uint32_t)((a - 0.5f) * 2.0f) + 1u;   // 1,2,3 (exact floor)
+                         lo = 0.5f * (float)lo_code; scale = 8589934592.0f; }
+    else if (a < 4.0f) { lo_code = (a < 3.0f) ? 4u : 5u; lo = (a < 3.0f) ? 2.0f : 3.0f;
+                         scale = 4294967296.0f; }
+    else               { lo_code = 6u; lo = 4.0f; scale = 2147483648.0f; }
+    float x = (a - lo) * scale;
+    uint64_t T = (uint64_t)ceilf(x);
+    code = lo_code + (((uint64_t)r < T) ? 1u : 0u);
+  }
+  return sign | code;
+}
+
+// 16-point random Hadamard transform of u[0..15] (in place):
+// y = 1/4 * H16 * D * x with D = diag(sign bits), Sylvester-ordered H16,
+// butterfly stages h = 1, 2, 4, 8, each an fp32 add and subtract, then an
+// exact multiply by 0.25.  sign_mask bit j set means sigma_j = -1.
+__device__ __forceinline__ void rht16(float* u, uint32_t sign_mask) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if ((sign_mask >> j) & 1u) u[j] = -u[j];
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        float a = u[i], b = u[i + h];
+        u[i] = a + b;
+        u[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) u[j] = u[j] * 0.25f;
+}
+
+// Sign mask of the RHT: bit j = bit 0 of word 0 of Philox(key = seed,
+// counter = (j, 0, 1, 0)).
+__device__ __forceinline__ uint32_t rht_sign_mask(uint64_t seed) {
+  uint32_t m = 0;
+  for (uint32_t j = 0; j < 16; ++j)
+    m |= (philox_word0(j, 0u, 1u, 0u, (uint32_t)seed, (uint32_t)(seed >> 32)) & 1u) << j;
+  return m;
+}
+
+// fp32 scale = fmax / a with the corner rules: a == 0 -> 1, overflow -> FLT_MAX.
+__device__ __forceinline__ float scale_from_amax(float a, float fmax) {
+  if (a == 0.0f) return 1.0f;
+  float s = fmax / a;
+  return (__float_as_uint(s) == 0x7F800000u) ? 3.40282346638528859812e+38f : s;
+}
+
+}  // namespace pbs
