@@ -1,0 +1,407 @@
+"""Benchmark: quantize-then-GEMM over the 12 GEMMs of a CodonFM-5B layer.
+
+Workload ("How to optimize Transformer-based models for low-precision
+training", "Model configuration and training inputs" and "Using autocast
+mode vs pre-quantized mode"): hidden 4096, intermediate 16384, 32 heads,
+micro-batch 31 x sequence 512 = 15872 tokens; QKV, attention-out, MLP-up and
+MLP-down in Fprop, Dgrad and Wgrad = 12 GEMMs.
+
+One step = every recipe (BF16, FP8 current, FP8 delayed, FP8 1x128/128x128,
+MXFP8, NVFP4) over the 12 GEMMs in autocast mode: each GEMM quantizes both
+of its operands from bf16 (amax, scale, cast, RHT, SR as the recipe needs)
+and then runs the GEMM, bf16 output.  Inputs are seeded synthetic tensors
+resident in HBM before timing starts; each layer has its own X, W and dY.
+
+Printed: one JSON line.  ``value`` = total GEMM FLOP of the step / step time
+(TFLOP/s), plus per-recipe ms/layer and TFLOP/s in autocast and pre-quantized
+modes, quantize-pass GB/s, the roofline of the dominant kernel (timed with
+HIP events on the stream it runs on), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+RECIPES = ["bf16", "fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "nvfp4"]
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2, "fp4": 10066.3}
+HBM_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_key(recipe, pass_):
+    """The GEMM kernel instantiation a (recipe, pass) launches, and its MFMA dtype."""
+    if recipe == "bf16":
+        return f"gemm_bf16_{pass_}", "bf16"
+    if recipe in ("fp8_current", "fp8_delayed"):
+        fmts = {"fprop": "e4m3xe4m3", "dgrad": "e5m2xe4m3", "wgrad": "e4m3xe5m2"}[pass_]
+        return f"gemm_fp8_tensor_{fmts}", "fp8"
+    if recipe == "fp8_block128":
+        return ("gemm_fp8_block128_w2d" if pass_ != "wgrad" else "gemm_fp8_block128_1d"), "fp8"
+    if recipe == "mxfp8":
+        return "gemm_mxfp8", "fp8"
+    return ("gemm_nvfp4_w2d" if pass_ != "wgrad" else "gemm_nvfp4_1d"), "fp16"
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "precision_block_scaled_amd", "csrc"))):
+        with open(os.path.join(ROOT, "precision_block_scaled_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def upload_bf16(bits, dev):
+    import torch
+    a = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def build_layer_tensors(tokens, dev):
+    import workloads as W
+    layers = {}
+    for i, ls in enumerate(W.layer_shapes(4096, 16384, 32)):
+        x = upload_bf16(W.activations(tokens, ls.k_in, seed=10 + i), dev)
+        w = upload_bf16(W.weights(ls.n_out, ls.k_in, seed=20 + i), dev)
+        dy = upload_bf16(W.grads(tokens, ls.n_out, seed=30 + i), dev)
+        layers[ls.name] = (x, w, dy, ls)
+    return layers
+
+
+class Runner:
+    """Holds pre-allocated quantized operands and outputs for every (recipe, GEMM)."""
+
+    def __init__(self, layers, tokens, dev):
+        import torch
+        from precision_block_scaled_amd import pipeline as PL
+        import precision_block_scaled_amd as P
+        self.torch, self.PL, self.P = torch, PL, P
+        self.layers = layers
+        self.tokens = tokens
+        self.dev = dev
+        self.gemms = []          # (layer, pass, M, N, K)
+        for name, (x, w, dy, ls) in layers.items():
+            for p in ("fprop", "dgrad", "wgrad"):
+                M, N, K = PL.pass_dims(p, tokens, ls.k_in, ls.n_out)
+                self.gemms.append((name, p, M, N, K))
+        self.C = {}
+        for (name, p, M, N, K) in self.gemms:
+            self.C[(name, p)] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.q = {}              # (recipe, layer, pass) -> (A, B)
+        self.states = {}         # delayed states per (layer, src)
+        for name, (x, w, dy, ls) in layers.items():
+            for src, fmt in (("x", P.PBS_FMT_E4M3), ("w", P.PBS_FMT_E4M3), ("dy", P.PBS_FMT_E5M2)):
+                self.states[(name, src)] = PL.DelayedState(fmt, dev)
+
+    def operands(self, recipe, name, p):
+        PL = self.PL
+        x, w, dy, ls = self.layers[name]
+        src = {"x": x, "w": w, "dy": dy}
+        (sa, oa), (sb, ob) = PL.ROLES[p]
+        if recipe == "bf16":
+            return src[sa], src[sb], None
+        st = {k: self.states[(name, k)] for k in ("x", "w", "dy")} if recipe == "fp8_delayed" else {}
+        prev = self.q.get((recipe, name, p))
+        A = PL.quantize(recipe, src[sa], sa, oa, p, st.get(sa), prev[0] if prev else None)
+        B = PL.quantize(recipe, src[sb], sb, ob, p, st.get(sb), prev[1] if prev else None)
+        self.q[(recipe, name, p)] = (A, B)
+        return A, B, (st.get(sa), st.get(sb))
+
+    def run_gemm(self, recipe, name, p, A, B, M, N, K):
+        self.PL.gemm(recipe, p, A, B, M, N, K, C=self.C[(name, p)])
+
+    def step(self, recipes, events=None):
+        """One autocast pass over all recipes x 12 GEMMs.  events: list to append timing."""
+        torch = self.torch
+        for r in recipes:
+            for (name, p, M, N, K) in self.gemms:
+                if events is not None:
+                    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                    e0.record()
+                A, B, st = self.operands(r, name, p)
+                if events is not None:
+                    e1.record()
+                self.run_gemm(r, name, p, A, B, M, N, K)
+                if events is not None:
+                    e2.record()
+                    events.append((r, name, p, M, N, K, e0, e1, e2))
+                if r == "fp8_delayed":
+                    for s in st:
+                        s.update()
+
+    def prequant_pass(self, recipes, iters):
+        """GEMM-only timing with operands quantized once beforehand."""
+        torch = self.torch
+        out = {}
+        for r in recipes:
+            for (name, p, M, N, K) in self.gemms:
+                if r == "bf16":
+                    A, B, _ = self.operands(r, name, p)
+                else:
+                    A, B = self.q[(r, name, p)]
+                ts = []
+                for _ in range(iters):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    self.run_gemm(r, name, p, A, B, M, N, K)
+                    e1.record()
+                    ts.append((e0, e1))
+                out[(r, name, p)] = ts
+        torch.cuda.synchronize()
+        return {k: float(np.median([a.elapsed_time(b) for a, b in v])) for k, v in out.items()}
+
+
+def quant_bandwidth(runner, iters=5):
+    """GB/s of single cast passes on full-size operands (algorithmic bytes)."""
+    torch, PL = runner.torch, runner.PL
+    # X of MLP-down and dY of MLP-up: [15872, 16384] each, 520 MB, twice the
+    # 256 MB last-level cache, so repeated casts still stream from HBM
+    x = runner.layers["mlp_down"][0]
+    dy = runner.layers["mlp_up"][2]
+    n = x.numel()
+    cases = [  # (label, recipe, src, orient, pass, algorithmic bytes per element)
+        ("fp8_tensor_cast_row", "fp8_current", "x", "row", "fprop", 3.0),
+        ("fp8_block128_cast_row", "fp8_block128", "x", "row", "fprop", 2 + 1 + 4 / 128),
+        ("mxfp8_cast_row", "mxfp8", "x", "row", "fprop", 2 + 1 + 1 / 32),
+        ("mxfp8_cast_col", "mxfp8", "x", "col", "wgrad", 2 + 1 + 1 / 32),
+        ("nvfp4_cast_row", "nvfp4", "x", "row", "fprop", 2 + 0.5 + 1 / 16),
+        ("nvfp4_rht_sr_cast_col", "nvfp4", "dy", "col", "wgrad", 2 + 0.5 + 1 / 16),
+    ]
+    res = {}
+    P = runner.P
+    amax = torch.zeros(4, device=runner.dev)
+    # amax pass
+    ts = []
+    for _ in range(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        P.pbs_amax(x, x.shape[0], x.shape[1], 0, 0, amax[0:1])
+        e1.record()
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
+    res["amax"] = {"ms": round(ms, 4), "GBps": round(2.0 * n / ms / 1e6, 1)}
+    for label, r, src, orient, p, bpe in cases:
+        t = {"x": x, "dy": dy}[src]
+        out = PL.quantize(r, t, src, orient, p)    # allocate + warm
+        rows, cols = t.shape
+        ts = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rec = PL.RECIPES[r]
+            rmask = P.PBS_ROW if orient == "row" else P.PBS_COL
+            rc, rs, cc, cs = ((out.codes, out.scales, None, None) if orient == "row"
+                              else (None, None, out.codes, out.scales))
+            flags = 0
+            scale = None
+            if r == "nvfp4":
+                flags = (P.PBS_FLAG_RHT16 if p == "wgrad" else 0) | (P.PBS_FLAG_SR if src == "dy" else 0)
+                scale = out._scal[1:2]
+            elif r == "fp8_current":
+                scale = out._scal[1:2]
+            P.pbs_cast(rec, t, rows, cols, PL.fmt_for(r, src), rmask, 0, flags, 42, scale, None,
+                       rc, rs, cc, cs)
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
+        res[label] = {"ms": round(ms, 4), "GBps": round(bpe * t.numel() / ms / 1e6, 1)}
+    return res
+
+
+def cpu_baseline(seconds_target=20.0):
+    """The CPU oracle on a bounded sample of the workload: autocast Fprop of the
+    attention-out layer (W [4096, 4096]) for the first `rows` tokens, every
+    recipe (quantize X and W, fp64 GEMM over the dequantized operands)."""
+    import workloads as W
+    from oracle import recipes as R
+    from oracle.passes import pass_operands
+    from oracle.gemm_ref import gemm_ref
+    rows = 256
+    x = W.activations(rows, 4096, seed=11)
+    w = W.weights(4096, 4096, seed=21)
+    dy = W.grads(rows, 4096, seed=31)
+    flop = 0.0
+    t0 = time.perf_counter()
+    for r in RECIPES:
+        st = None
+        if r == "fp8_delayed":
+            st = {"x": R.DelayedScaling("e4m3"), "w": R.DelayedScaling("e4m3")}
+            st["x"].update(R.amax(x))
+            st["w"].update(R.amax(w))
+        A, B = pass_operands(r, "fprop", x=x, w=w, dy=dy, delayed_states=st)
+        gemm_ref(A.dequant(), B.dequant())
+        flop += 2.0 * rows * 4096 * 4096
+    dt = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas_threads = max((i.get("num_threads", 1) for i in info), default=1)
+    except Exception:
+        blas_threads = None
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads or cores,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"autocast Fprop of attn-out (W 4096x4096) for {rows} tokens, all 6 recipes: "
+                      "oracle quantize of X and W + fp64 GEMM"}
+
+
+def load_traffic(kernel_name):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    rec = d.get(kernel_name)
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--tokens", type=int, default=15872)
+    ap.add_argument("--recipes", default=",".join(RECIPES))
+    ap.add_argument("--prequant-iters", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip pre-quant and GB/s passes")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    if a.calib_copy:
+        n = 1 << 28                       # 256 Mi float32 = 1 GiB each way
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_each_way": n * 4}))
+        return
+
+    import precision_block_scaled_amd as P
+    P.lib()
+    recipes = [r for r in a.recipes.split(",") if r]
+    log("generating inputs")
+    layers = build_layer_tensors(a.tokens, dev)
+    runner = Runner(layers, a.tokens, dev)
+    total_flop = sum(2.0 * M * N * K for (_, _, M, N, K) in runner.gemms) * len(recipes)
+
+    log(f"warmup {a.warmup} steps")
+    for _ in range(a.warmup):
+        runner.step(recipes)
+    torch.cuda.synchronize()
+
+    log(f"timing {a.steps} steps")
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        runner.step(recipes, events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / a.steps
+
+    # per-GEMM autocast and GEMM-only (in-step) times
+    per = {}
+    for (r, name, p, M, N, K, e0, e1, e2) in events:
+        d = per.setdefault((r, name, p), {"auto": [], "gemm": [], "flop": 2.0 * M * N * K})
+        d["auto"].append(e0.elapsed_time(e2))
+        d["gemm"].append(e1.elapsed_time(e2))
+    kern = {}
+    for (r, name, p), d in per.items():
+        key, dt = kernel_key(r, p)
+        k = kern.setdefault(key, {"ms": 0.0, "flop": 0.0, "launches": 0, "dtype": dt})
+        k["ms"] += float(np.sum(d["gemm"]))
+        k["flop"] += d["flop"] * len(d["gemm"])
+        k["launches"] += len(d["gemm"])
+    dom = max(kern.items(), key=lambda kv: kv[1]["ms"])
+    dom_name, dk = dom
+    avg_ms = dk["ms"] / dk["launches"]
+    achieved = dk["flop"] / (dk["ms"] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dk["dtype"]]
+    traffic = load_traffic(dom_name)
+
+    pre = {}
+    if not a.no_extras:
+        log("pre-quantized GEMM timing")
+        pre = runner.prequant_pass(recipes, a.prequant_iters)
+    per_recipe = {}
+    layer_flop = sum(2.0 * M * N * K for (_, _, M, N, K) in runner.gemms)
+    for r in recipes:
+        auto_ms = sum(float(np.median(per[(r, n, p)]["auto"])) for (n, p, *_) in runner.gemms)
+        ent = {"autocast_ms_per_layer": round(auto_ms, 3),
+               "autocast_TFLOPs": round(layer_flop / (auto_ms * 1e-3) / 1e12, 1)}
+        if pre:
+            pre_ms = sum(pre[(r, n, p)] for (n, p, *_) in runner.gemms)
+            ent["prequant_ms_per_layer"] = round(pre_ms, 3)
+            ent["prequant_TFLOPs"] = round(layer_flop / (pre_ms * 1e-3) / 1e12, 1)
+            ent["ms_per_gemm_prequant"] = {f"{n}.{p}": round(pre[(r, n, p)], 4) for (n, p, *_) in runner.gemms}
+        per_recipe[r] = ent
+    qbw = {}
+    if not a.no_extras:
+        log("quantize-pass bandwidth")
+        qbw = quant_bandwidth(runner)
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": "TFLOPS & ms/GEMM over 12 layer shapes (M=15872) per recipe; quant GB/s",
+        "value": round(total_flop / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mixed: bf16 | fp8 (e4m3/e5m2) | nvfp4 decoded to fp16",
+        "data": "synthetic (seeded N(0,1)+8 outlier channels x100, N(0,0.02^2), Student-t(3)x1e-3)",
+        "config": {"workload": "CodonFM-5B layer, 12 GEMMs (QKV/attn-out/MLP-up/MLP-down x "
+                               "Fprop/Dgrad/Wgrad), autocast, every recipe",
+                   "tokens": a.tokens, "hidden": 4096, "intermediate": 16384,
+                   "recipes": recipes, "gemm_out": "bf16", "parallelism": "single GPU"},
+        "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "avg_launch_ms": round(avg_ms, 4), "launches": dk["launches"],
+                     "traffic": traffic},
+        "per_recipe": per_recipe,
+        "quant_GBps": qbw,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

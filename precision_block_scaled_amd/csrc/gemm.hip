@@ -10,7 +10,7 @@
 //  BF16        v_mfma_f32_32x32x16_bf16.  Operands may be stored
 //              contraction-contiguous or, for the Dgrad / Wgrad products of
 //              natural-layout tensors, MN-contiguous; MN-contiguous tiles are
-//              transposed in registers (4x8 bf16 blocks) on their way into
+//              transposed in registers (8x8 bf16 blocks) on their way into
 //              LDS, so the MFMA always reads contraction-contiguous rows.
 //  FP8 per-tensor  v_mfma_f32_32x32x64_f8f6f4 (format per operand: E4M3 or
 //              E5M2), scales applied once in the epilogue.
@@ -31,11 +31,17 @@
 //              and the product runs on v_mfma_f32_32x32x16_f16.  The two
 //              fp32 tensor scales are applied in the epilogue.
 //
-// Tiling: 128 x 128 output tile per workgroup of 256 threads (4 waves in a
-// 2 x 2 grid, 64 x 64 per wave, 2 x 2 MFMA 32x32 tiles per wave).  Each
-// K stage moves 128 bytes per operand row (64 bf16 / fp16, 128 fp8) through
-// a double-buffered LDS tile whose 16-byte chunks are XOR-swizzled by row
-// so that the MFMA fragment reads (ds_read_b128) are conflict-free.
+// Tiling: 256 x 256 output tile per workgroup of 256 threads (4 waves in a
+// 2 x 2 grid, 128 x 128 per wave = 4 x 4 MFMA 32x32 tiles, 256 fp32
+// accumulators per lane).  Each K stage moves 128 bytes per operand row
+// (64 bf16 / fp16, 128 fp8): 32 KB per operand, double-buffered in LDS
+// (128 KB).  Contraction-contiguous operands go global -> LDS directly
+// (global_load_lds_dwordx4, no registers), each lane fetching the 16-byte
+// chunk whose XOR-swizzled LDS slot it owns, so the MFMA fragment reads
+// (ds_read_b128) are bank-conflict-free.  Operands that must be transformed
+// (MN-major bf16, NVFP4) are staged through registers.  Workgroups are
+// mapped to tiles so that each of the 8 XCDs (each with its own L2) works on
+// a contiguous, row-grouped range of tiles.
 #include "device.hpp"
 #include "host.hpp"
 
@@ -46,14 +52,17 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 enum { OP_BF16 = 0, OP_F16 = 1, OP_FP8 = 2 };                 // what the MFMA consumes
 enum { LD_KMAJOR = 0, LD_MNMAJOR = 1, LD_NVFP4 = 2 };         // how a tile reaches LDS
 enum { SC_NONE = 0, SC_TENSOR = 1, SC_MX = 2, SC_BLK = 3, SC_NV = 4 };
 
-constexpr int BM = 128, BN = 128, NTHR = 256;
+constexpr int BM = 256, BN = 256, NTHR = 256;
 constexpr int ROWB = 128;               // bytes per LDS row per K stage
-constexpr int TILEB = BM * ROWB;        // 16 KB per operand per stage
+constexpr int TILEB = BM * ROWB;        // 32 KB per operand per stage
+constexpr int GROUP_M = 8;              // tile rows walked together (L2 reuse)
+constexpr int NXCD = 8;
 
 struct GemmArgs {
   const uint8_t* A;
@@ -66,90 +75,117 @@ struct GemmArgs {
   int M, N, K;            // GEMM dims, K in elements
   int64_t lda, ldb;       // bytes between stored rows of A / B
   int ldc;                // elements between rows of C
+  int tiles_m, tiles_n;
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ (row & 7)) << 4); }
 
-// ---------------------------------------------------------------------------
-// Global -> register -> LDS staging, one operand.
-//   rows0: first tile row (M or N index), nrows: valid rows (M or N)
-// ---------------------------------------------------------------------------
-template <int LD, bool SCALE2D>
-struct Stage {
-  uint4 v[4];
-  uint32_t s;             // NVFP4 block scale bytes (2)
-};
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// K-major: tile row r, 16-byte chunk c: thread t loads chunks t + 256 i.
-template <int LD, bool SCALE2D>
-__device__ __forceinline__ void load_stage(Stage<LD, SCALE2D>& st, const uint8_t* base, int64_t ld,
-                                           int rows0, int nrows, int kt, int K,
-                                           const uint8_t* scale) {
-  const int t = threadIdx.x;
-  if (LD == LD_KMAJOR) {
+// ---------------------------------------------------------------------------
+// Operand staging.  Every variant fills one [256 rows][128 B] swizzled LDS
+// tile for K stage kt.  rows0 / nrows: first tile row and valid rows.
+// ---------------------------------------------------------------------------
+
+// K-major, direct to LDS: instruction q (of 32) writes LDS rows 8q..8q+7;
+// lane l owns row 8q + l/8, physical chunk l%8, i.e. logical chunk
+// (l % 8) ^ (l / 8).
+__device__ __forceinline__ void load_direct(const uint8_t* base, int64_t ld, int rows0, int nrows,
+                                            int kt, uint8_t* lds) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane >> 3, lc = (lane & 7) ^ lr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = t + NTHR * i;
-      int row = rows0 + (q >> 3);
-      row = row < nrows ? row : nrows - 1;
-      st.v[i] = *(const uint4*)(base + (int64_t)row * ld + (int64_t)kt * ROWB + ((q & 7) << 4));
-    }
-  } else if (LD == LD_MNMAJOR) {
-    // stored [K][MN], ld = bytes per k row; this thread: k rows 4*kq..+3, mn 8*mq..+7
-    const int kq = t >> 4, mq = t & 15;
-    int mn = rows0 + 8 * mq;
-    mn = mn < nrows ? mn : nrows - 8;
-    const int64_t k = (int64_t)kt * 64 + 4 * kq;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st.v[i] = *(const uint4*)(base + (k + i) * ld + (int64_t)mn * 2);
-  } else {  // LD_NVFP4: row t/2, 32 values (16 bytes) at K offset 64 kt + 32 (t & 1)
-    const int r = t >> 1, half = t & 1;
-    int row = rows0 + r;
+  for (int i = 0; i < 8; ++i) {
+    const int q = w * 8 + i;
+    int row = rows0 + 8 * q + lr;
     row = row < nrows ? row : nrows - 1;
-    st.v[0] = *(const uint4*)(base + (int64_t)row * ld + (int64_t)kt * 32 + half * 16);
-    const int64_t kb = ((int64_t)kt * 64 + 32 * half) / 16;          // first of two blocks
-    const int64_t srow = SCALE2D ? row / 16 : row;
-    st.s = *(const uint16_t*)(scale + srow * (K / 16) + kb);
+    const uint8_t* g = base + (int64_t)row * ld + (int64_t)kt * ROWB + (lc << 4);
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds + q * 1024), 16, 0, 0);
   }
 }
 
-template <int LD, bool SCALE2D>
-__device__ __forceinline__ void store_stage(const Stage<LD, SCALE2D>& st, uint8_t* lds) {
-  const int t = threadIdx.x;
-  if (LD == LD_KMAJOR) {
+// Per-row dword (MX scales / block-128 scales) for this stage, direct to LDS:
+// wave w loads rows 64 w .. 64 w + 63.
+__device__ __forceinline__ void load_row_dwords(const uint8_t* p, int64_t row_stride, int rows0, int nrows,
+                                                int div_rows, uint32_t* lds) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int row = rows0 + 64 * w + lane;
+  row = row < nrows ? row : nrows - 1;
+  const uint8_t* g = p + (int64_t)(row / div_rows) * row_stride;
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds + 64 * w), 4, 0, 0);
+}
+
+// Register-staged operands.
+struct RegStage {
+  uint4 v[8];
+  uint32_t s[2];
+};
+
+// MN-major bf16: stored [K][MN]; thread: k rows 8 kq .. 8 kq + 7, mn 8 mq .. 8 mq + 7.
+__device__ __forceinline__ void load_mn(RegStage& st, const uint8_t* base, int64_t ld, int rows0,
+                                        int nrows, int kt) {
+  const int t = threadIdx.x, kq = t >> 5, mq = t & 31;
+  int mn = rows0 + 8 * mq;
+  mn = mn < nrows ? mn : nrows - 8;
+  const int64_t k = (int64_t)kt * 64 + 8 * kq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = t + NTHR * i;
-      *(uint4*)(lds + swz(q >> 3, q & 7)) = st.v[i];
-    }
-  } else if (LD == LD_MNMAJOR) {
-    const int kq = t >> 4, mq = t & 15;
-    const uint32_t w0[4] = {st.v[0].x, st.v[0].y, st.v[0].z, st.v[0].w};
-    const uint32_t w1[4] = {st.v[1].x, st.v[1].y, st.v[1].z, st.v[1].w};
-    const uint32_t w2[4] = {st.v[2].x, st.v[2].y, st.v[2].z, st.v[2].w};
-    const uint32_t w3[4] = {st.v[3].x, st.v[3].y, st.v[3].z, st.v[3].w};
+  for (int i = 0; i < 8; ++i) st.v[i] = *(const uint4*)(base + (k + i) * ld + (int64_t)mn * 2);
+}
+
+__device__ __forceinline__ void store_mn(const RegStage& st, uint8_t* lds) {
+  const int t = threadIdx.x, kq = t >> 5, mq = t & 31;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // mn row 8 mq + i gets (k 4kq .. 4kq+3) = element i of each loaded row
-      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-      uint2 o;
-      o.x = __builtin_amdgcn_perm(w1[i >> 1], w0[i >> 1], sel);
-      o.y = __builtin_amdgcn_perm(w3[i >> 1], w2[i >> 1], sel);
-      const int row = 8 * mq + i;
-      *(uint2*)(lds + swz(row, kq >> 1) + ((kq & 1) << 3)) = o;
+  for (int i = 0; i < 8; ++i) {
+    // mn row 8 mq + i receives element i of each of the 8 loaded k rows
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t w_[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint4 v = st.v[r];
+      const int j = i >> 1;
+      w_[r] = j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
     }
-  } else {  // LD_NVFP4: decode 32 E2M1 values to fp16 times their block scale
-    const int r = t >> 1, half = t & 1;
-    const uint32_t w[4] = {st.v[0].x, st.v[0].y, st.v[0].z, st.v[0].w};
+    uint4 o;
+    o.x = __builtin_amdgcn_perm(w_[1], w_[0], sel);
+    o.y = __builtin_amdgcn_perm(w_[3], w_[2], sel);
+    o.z = __builtin_amdgcn_perm(w_[5], w_[4], sel);
+    o.w = __builtin_amdgcn_perm(w_[7], w_[6], sel);
+    *(uint4*)(lds + swz(8 * mq + i, kq)) = o;
+  }
+}
+
+// NVFP4: thread handles rows r = t / 2 and r + 128; 32 values (16 bytes) at
+// K offset 64 kt + 32 (t & 1); two E4M3 block-scale bytes for each.
+template <bool SCALE2D>
+__device__ __forceinline__ void load_nv(RegStage& st, const uint8_t* base, int64_t ld, int rows0,
+                                        int nrows, int kt, int K, const uint8_t* scale) {
+  const int t = threadIdx.x, half = t & 1;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int row = rows0 + (t >> 1) + 128 * h;
+    row = row < nrows ? row : nrows - 1;
+    st.v[h] = *(const uint4*)(base + (int64_t)row * ld + (int64_t)kt * 32 + half * 16);
+    const int64_t kb = ((int64_t)kt * 64 + 32 * half) / 16;
+    const int64_t srow = SCALE2D ? row / 16 : row;
+    st.s[h] = *(const uint16_t*)(scale + srow * (K / 16) + kb);
+  }
+}
+
+__device__ __forceinline__ void store_nv(const RegStage& st, uint8_t* lds) {
+  const int t = threadIdx.x, half = t & 1;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = (t >> 1) + 128 * h;
+    const uint32_t w[4] = {st.v[h].x, st.v[h].y, st.v[h].z, st.v[h].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t dcode = (st.s >> (8 * (j >> 1))) & 0x7Fu;   // words 0,1: block 0; 2,3: block 1
-      const _Float16 dh = (_Float16)dec_e4m3_pos(dcode);           // exact: E4M3 fits fp16
+      const uint32_t dcode = (st.s[h] >> (8 * (j >> 1))) & 0x7Fu;   // words 0,1: block 0; 2,3: block 1
+      const _Float16 dh = (_Float16)dec_e4m3_pos(dcode);              // exact: E4M3 fits fp16
       const f16x2 dd = {dh, dh};
-      f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 0) * dd;
-      f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 1) * dd;
-      f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 2) * dd;
-      f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 3) * dd;
+      const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 0) * dd;
+      const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 1) * dd;
+      const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 2) * dd;
+      const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 3) * dd;
       uint4 o;
       o.x = __builtin_bit_cast(uint32_t, h0);
       o.y = __builtin_bit_cast(uint32_t, h1);
@@ -166,94 +202,96 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a
+// contiguous range of logical tiles, then walk tiles GROUP_M rows at a time.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int q = T / NXCD, r = T % NXCD;
+  const int x = b % NXCD, idx = b / NXCD;
+  const int id = x * q + (x < r ? x : r) + idx;
+  const int per_group = GROUP_M * tiles_n;
+  const int g = id / per_group;
+  const int first_m = g * GROUP_M;
+  const int gm = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+  const int in = id - g * per_group;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
 template <int OP, int LDA, int LDB, int SC, int AFMT, int BFMT, bool B2D, bool OUT_BF16>
-__global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   __shared__ __align__(16) uint8_t lds[2][2][TILEB];     // [stage][A/B]
-  __shared__ __align__(16) uint32_t lds_sc[2][2][BM];    // [stage][A/B][row] MX dwords / block fp32
+  __shared__ __align__(16) uint32_t lds_sc[2][2][BM];    // [stage][A/B][row]
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int KST = (OP == OP_FP8) ? 128 : 64;              // K elements per stage
+  int tm, tn;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  constexpr int KST = (OP == OP_FP8) ? 128 : 64;         // K elements per stage
   const int nk = g.K / KST;
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  Stage<LDA, false> sa;
-  Stage<LDB, B2D> sb;
-  uint32_t sca = 0, scb = 0;
+  RegStage ra, rb;
 
-  auto load_scales = [&](int kt) {
+  auto issue = [&](int kt, int buf) {
+    if (LDA == LD_KMAJOR) load_direct(g.A, g.lda, m0, g.M, kt, lds[buf][0]);
+    else if (LDA == LD_MNMAJOR) load_mn(ra, g.A, g.lda, m0, g.M, kt);
+    else load_nv<false>(ra, g.A, g.lda, m0, g.M, kt, g.K, g.a_scale);
+    if (LDB == LD_KMAJOR) load_direct(g.B, g.ldb, n0, g.N, kt, lds[buf][1]);
+    else if (LDB == LD_MNMAJOR) load_mn(rb, g.B, g.ldb, n0, g.N, kt);
+    else load_nv<B2D>(rb, g.B, g.ldb, n0, g.N, kt, g.K, g.b_scale);
     if (SC == SC_MX) {
-      const int r = t & 127;
-      if (t < 128) {
-        int row = m0 + r; row = row < g.M ? row : g.M - 1;
-        sca = *(const uint32_t*)(g.a_scale + (int64_t)row * (g.K / 32) + kt * 4);
-      } else {
-        int row = n0 + r; row = row < g.N ? row : g.N - 1;
-        scb = *(const uint32_t*)(g.b_scale + (int64_t)row * (g.K / 32) + kt * 4);
-      }
+      load_row_dwords(g.a_scale + (int64_t)kt * 4, g.K / 32, m0, g.M, 1, lds_sc[buf][0]);
+      load_row_dwords(g.b_scale + (int64_t)kt * 4, g.K / 32, n0, g.N, 1, lds_sc[buf][1]);
     } else if (SC == SC_BLK) {
-      const int r = t & 127;
-      const float* as = (const float*)g.a_scale;
-      const float* bs = (const float*)g.b_scale;
-      if (t < 128) {
-        int row = m0 + r; row = row < g.M ? row : g.M - 1;
-        sca = __float_as_uint(as[(int64_t)row * (g.K / 128) + kt]);
-      } else {
-        int row = n0 + r; row = row < g.N ? row : g.N - 1;
-        scb = __float_as_uint(B2D ? bs[(int64_t)(row / 128) * (g.K / 128) + kt]
-                                  : bs[(int64_t)row * (g.K / 128) + kt]);
-      }
+      load_row_dwords(g.a_scale + (int64_t)kt * 4, (g.K / 128) * 4, m0, g.M, 1, lds_sc[buf][0]);
+      load_row_dwords(g.b_scale + (int64_t)kt * 4, (g.K / 128) * 4, n0, g.N, B2D ? 128 : 1,
+                      lds_sc[buf][1]);
     }
   };
-  auto store_scales = [&](int buf) {
-    if (SC == SC_MX || SC == SC_BLK) {
-      if (t < 128) lds_sc[buf][0][t] = sca;
-      else lds_sc[buf][1][t - 128] = scb;
-    }
+  auto commit = [&](int buf) {       // register-staged operands -> LDS
+    if (LDA == LD_MNMAJOR) store_mn(ra, lds[buf][0]);
+    if (LDA == LD_NVFP4) store_nv(ra, lds[buf][0]);
+    if (LDB == LD_MNMAJOR) store_mn(rb, lds[buf][1]);
+    if (LDB == LD_NVFP4) store_nv(rb, lds[buf][1]);
   };
 
-  load_stage<LDA, false>(sa, g.A, g.lda, m0, g.M, 0, g.K, g.a_scale);
-  load_stage<LDB, B2D>(sb, g.B, g.ldb, n0, g.N, 0, g.K, g.b_scale);
-  load_scales(0);
-  store_stage<LDA, false>(sa, lds[0][0]);
-  store_stage<LDB, B2D>(sb, lds[0][1]);
-  store_scales(0);
+  issue(0, 0);
+  commit(0);
+  wait_vm0();
   __syncthreads();
 
   const int lr = lane & 31, lg = lane >> 5;     // row within a 32-tile, K group
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      load_stage<LDA, false>(sa, g.A, g.lda, m0, g.M, kt + 1, g.K, g.a_scale);
-      load_stage<LDB, B2D>(sb, g.B, g.ldb, n0, g.N, kt + 1, g.K, g.b_scale);
-      load_scales(kt + 1);
-    }
+    const bool more = kt + 1 < nk;
+    if (more) issue(kt + 1, buf ^ 1);
     const uint8_t* la = lds[buf][0];
     const uint8_t* lb = lds[buf][1];
 
     if (OP == OP_BF16 || OP == OP_F16) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        uint4 fa[2], fb[2];
+        uint4 fa[4], fb[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) fa[i] = *(const uint4*)(la + swz(wm * 64 + 32 * i + lr, 2 * s + lg));
+        for (int i = 0; i < 4; ++i) fa[i] = *(const uint4*)(la + swz(wm * 128 + 32 * i + lr, 2 * s + lg));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fb[j] = *(const uint4*)(lb + swz(wn * 64 + 32 * j + lr, 2 * s + lg));
+        for (int j = 0; j < 4; ++j) fb[j] = *(const uint4*)(lb + swz(wn * 128 + 32 * j + lr, 2 * s + lg));
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
+          for (int j = 0; j < 4; ++j) {
             if (OP == OP_BF16)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                   __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
@@ -270,101 +308,129 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs g) {
       // l supplies applies to K block g (K 32 g .. 32 g + 31) of its row.
       // So lane group g reads 16-byte chunks g and 2 + g of each 64-byte step,
       // and supplies the scale of MX block 2 s + g of the stage.
-      f32x16 part[2][2];
-      if (SC == SC_BLK) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
-      }
-      uint32_t mxa[2] = {0, 0}, mxb[2] = {0, 0};
+      uint32_t mxa[4] = {0, 0, 0, 0}, mxb[4] = {0, 0, 0, 0};
       if (SC == SC_MX) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) mxa[i] = lds_sc[buf][0][wm * 64 + 32 * i + lr];
+        for (int i = 0; i < 4; ++i) mxa[i] = lds_sc[buf][0][wm * 128 + 32 * i + lr];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mxb[j] = lds_sc[buf][1][wn * 64 + 32 * j + lr];
+        for (int j = 0; j < 4; ++j) mxb[j] = lds_sc[buf][1][wn * 128 + 32 * j + lr];
       }
+      if (SC != SC_BLK) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        i32x8 fa[2], fb[2];
+        for (int s = 0; s < 2; ++s) {
+          i32x8 fa[4], fb[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int row = wm * 64 + 32 * i + lr;
-          const uint4 lo = *(const uint4*)(la + swz(row, 4 * s + lg));
-          const uint4 hi = *(const uint4*)(la + swz(row, 4 * s + 2 + lg));
-          fa[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int row = wn * 64 + 32 * j + lr;
-          const uint4 lo = *(const uint4*)(lb + swz(row, 4 * s + lg));
-          const uint4 hi = *(const uint4*)(lb + swz(row, 4 * s + 2 + lg));
-          fb[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            if (SC == SC_MX) {
-              // this lane's block within the stage: 2 s + lg (byte of the row's dword)
-              const int sa_ = (int)((mxa[i] >> (8 * (2 * s + lg))) & 0xFFu);
-              const int sb_ = (int)((mxb[j] >> (8 * (2 * s + lg))) & 0xFFu);
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AFMT,
-                                                                           BFMT, 0, sa_, 0, sb_);
-            } else if (SC == SC_BLK) {
-              part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], part[i][j], AFMT,
-                                                                            BFMT, 0, 0, 0, 0);
-            } else {
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AFMT,
-                                                                           BFMT, 0, 0, 0, 0);
-            }
+          for (int i = 0; i < 4; ++i) {
+            const int row = wm * 128 + 32 * i + lr;
+            const uint4 lo = *(const uint4*)(la + swz(row, 4 * s + lg));
+            const uint4 hi = *(const uint4*)(la + swz(row, 4 * s + 2 + lg));
+            fa[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
           }
-      }
-      if (SC == SC_BLK) {
-        // acc += part * (a_scale[row] * b_scale[col]) for this 128-long K block
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float sbv = __uint_as_float(lds_sc[buf][1][wn * 64 + 32 * j + lr]);
+          for (int j = 0; j < 4; ++j) {
+            const int row = wn * 128 + 32 * j + lr;
+            const uint4 lo = *(const uint4*)(lb + swz(row, 4 * s + lg));
+            const uint4 hi = *(const uint4*)(lb + swz(row, 4 * s + 2 + lg));
+            fb[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          }
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = wm * 64 + 32 * i + (r >> 2) * 8 + lg * 4 + (r & 3);
-              const float f = __uint_as_float(lds_sc[buf][0][row]) * sbv;
-              acc[i][j][r] = __builtin_fmaf(part[i][j][r], f, acc[i][j][r]);
+            for (int j = 0; j < 4; ++j) {
+              if (SC == SC_MX) {
+                const int sa_ = (int)((mxa[i] >> (8 * (2 * s + lg))) & 0xFFu);
+                const int sb_ = (int)((mxb[j] >> (8 * (2 * s + lg))) & 0xFFu);
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AFMT,
+                                                                             BFMT, 0, sa_, 0, sb_);
+              } else {
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AFMT,
+                                                                             BFMT, 0, 0, 0, 0);
+              }
             }
+        }
+      } else {
+        // Block-128: per output 32x32 tile, the 128-long K block accumulates
+        // into fresh registers (two K=64 steps), then is added in with
+        // a_scale[row] * b_scale[col].
+        i32x8 fa[2][4], fb[2][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = wm * 128 + 32 * i + lr;
+            const uint4 lo = *(const uint4*)(la + swz(row, 4 * s + lg));
+            const uint4 hi = *(const uint4*)(la + swz(row, 4 * s + 2 + lg));
+            fa[s][i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = wn * 128 + 32 * j + lr;
+            const uint4 lo = *(const uint4*)(lb + swz(row, 4 * s + lg));
+            const uint4 hi = *(const uint4*)(lb + swz(row, 4 * s + 2 + lg));
+            fb[s][j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          }
+        }
+        float sbv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sbv[j] = __uint_as_float(lds_sc[buf][1][wn * 128 + 32 * j + lr]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float sav[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sav[r] = __uint_as_float(lds_sc[buf][0][wm * 128 + 32 * i + (r >> 2) * 8 + lg * 4 + (r & 3)]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f32x16 part;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) part[r] = 0.0f;
+            part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0][i], fb[0][j], part, 0, 0, 0, 0, 0, 0);
+            part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[1][i], fb[1][j], part, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[r], sav[r] * sbv[j], acc[i][j][r]);
+          }
         }
       }
     }
 
-    if (kt + 1 < nk) {
-      store_stage<LDA, false>(sa, lds[buf ^ 1][0]);
-      store_stage<LDB, B2D>(sb, lds[buf ^ 1][1]);
-      store_scales(buf ^ 1);
-    }
+    if (more) commit(buf ^ 1);
+    wait_vm0();
     __syncthreads();
   }
 
-  // Epilogue.
+  // Epilogue.  Lane (lr, lg) of tile (i, j) holds column 32 j + lr and rows
+  // 32 i + 8 (r / 4) + 4 lg + r % 4, r = 0..15.
   float post = 1.0f;
   if (SC == SC_TENSOR || SC == SC_NV) post = (*g.a_ts) * (*g.b_ts);
+  int roff[16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int r = 0; r < 16; ++r) roff[r] = ((r >> 2) * 8 + lg * 4 + (r & 3)) * g.ldc;
+  const bool full = (m0 + BM <= g.M) && (n0 + BN <= g.N);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + 32 * j + lr;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + 32 * i + (r >> 2) * 8 + lg * 4 + (r & 3);
-        if (row < g.M && col < g.N) {
-          float v = acc[i][j][r];
-          if (SC == SC_TENSOR || SC == SC_NV) v *= post;
-          if (OUT_BF16)
-            ((uint16_t*)g.C)[(int64_t)row * g.ldc + col] = (uint16_t)f32_to_bf16_rne(v);
-          else
-            ((float*)g.C)[(int64_t)row * g.ldc + col] = v;
+    for (int j = 0; j < 4; ++j) {
+      const int row0 = m0 + wm * 128 + 32 * i;
+      const int col = n0 + wn * 128 + 32 * j + lr;
+      const int64_t base = (int64_t)row0 * g.ldc + col;
+      f32x16 v = acc[i][j];
+      if (SC == SC_TENSOR || SC == SC_NV) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] *= post;
+      }
+      if (OUT_BF16) {
+        uint16_t* cp = (uint16_t*)g.C + base;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + (r >> 2) * 8 + lg * 4 + (r & 3);
+          if (full || (row < g.M && col < g.N)) cp[roff[r]] = (uint16_t)f32_to_bf16_rne(v[r]);
+        }
+      } else {
+        float* cp = (float*)g.C + base;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + (r >> 2) * 8 + lg * 4 + (r & 3);
+          if (full || (row < g.M && col < g.N)) cp[roff[r]] = v[r];
         }
       }
     }
@@ -432,6 +498,8 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
   g.N = (int)N;
   g.K = (int)K;
   g.ldc = (int)N;
+  g.tiles_m = (int)ceil_div(M, BM);
+  g.tiles_n = (int)ceil_div(N, BN);
 
   gemm_fn fn = nullptr;
   const char* name = "";
@@ -484,6 +552,8 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
                   "pbs_gemm: MXFP8 takes E4M3 operands");
       PBS_REQUIRE(a_scale && b_scale, PBS_ERR_INVALID_ARG, "pbs_gemm: block scales are null");
       PBS_REQUIRE(K % 128 == 0, PBS_ERR_SHAPE, "pbs_gemm: MXFP8 needs K %% 128 == 0");
+      PBS_REQUIRE(((uintptr_t)a_scale & 3) == 0 && ((uintptr_t)b_scale & 3) == 0, PBS_ERR_INVALID_ARG,
+                  "pbs_gemm: MXFP8 block scales must be 4-byte aligned");
       g.lda = K; g.ldb = K;
       fn = pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_MX, 0, 0, false>(bf16_out);
       name = "gemm_mxfp8";
@@ -506,9 +576,9 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
     default:
       return set_error(PBS_ERR_INVALID_ARG, "pbs_gemm: unknown recipe %d", (int)recipe);
   }
-  dim3 grid((unsigned)ceil_div(N, BN), (unsigned)ceil_div(M, BM));
-  log_dispatch("%s layout=%d M=%lld N=%lld K=%lld out=%s grid=%ux%u", name, (int)layout, (long long)M,
-               (long long)N, (long long)K, bf16_out ? "bf16" : "f32", grid.x, grid.y);
-  hipLaunchKernelGGL(fn, grid, dim3(NTHR), 0, stream, g);
+  const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n);
+  log_dispatch("%s layout=%d M=%lld N=%lld K=%lld out=%s tiles=%dx%d", name, (int)layout, (long long)M,
+               (long long)N, (long long)K, bf16_out ? "bf16" : "f32", g.tiles_m, g.tiles_n);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(NTHR), 0, stream, g);
   return check_launch("pbs_gemm");
 }
