@@ -8,6 +8,9 @@ Every source is compiled by hipcc for gfx950 only.  Flags:
                          single fp32 operations; no multiply-add fusion
   -Xclang -target-feature -Xclang -packed-fp32-ops
                          no packed-fp32 VALU instructions
+  -mllvm -disable-promote-alloca-to-lds
+                         keep private arrays in registers (the GEMM's LDS
+                         budget is spoken for)
 fp32 division stays IEEE correctly rounded (hipcc's default) and fp32
 denormals are kept (no flush-to-zero), which the bit-exact casts rely on.
 """
@@ -38,6 +41,7 @@ def hipcc():
 def compile_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
             "-fno-gpu-flush-denormals-to-zero",
+            "-mllvm", "-disable-promote-alloca-to-lds",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(HERE, "..", "include")]
 

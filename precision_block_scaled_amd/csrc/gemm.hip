@@ -218,13 +218,93 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
   tn = in / gm;
 }
 
+// Fragments of one half K-stage (64 of the 128 bytes of every LDS row): for
+// each of the wave's 4 row tiles (A) and 4 column tiles (B), lane (lr, lg)
+// holds 16-byte chunks 4h + lg (elements 0-3) and 4h + 2 + lg (elements
+// 4-7) of its row.  For 8-bit operands the 8 dwords are one K=64 MFMA
+// operand (see the layout note in the kernel); for 16-bit operands the two
+// halves are the operands of two K=16 steps (chunks 2s + lg, s = 2h, 2h + 1).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+struct Frags {
+  i32x8 a[4], b[4];
+};
+
+__device__ __forceinline__ i32x8 read2(const uint8_t* l, int row, int c_lo, int c_hi) {
+  const i32x4 lo = *(const i32x4*)(l + swz(row, c_lo));
+  const i32x4 hi = *(const i32x4*)(l + swz(row, c_hi));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* la, const uint8_t* lb, int wm, int wn,
+                                           int lr, int lg, int h) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = read2(la, wm * 128 + 32 * i + lr, 4 * h + lg, 4 * h + 2 + lg);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.b[j] = read2(lb, wn * 128 + 32 * j + lr, 4 * h + lg, 4 * h + 2 + lg);
+}
+
+// MFMAs of one half stage on all 16 tiles (every recipe but block-128).
+template <int OP, int SC, int AFMT, int BFMT>
+__device__ __forceinline__ void mfma_half(f32x16 (&acc)[4][4], const Frags& f, const uint32_t* mxa,
+                                          const uint32_t* mxb, int h, int lg) {
+  if (OP == OP_FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (SC == SC_MX) {
+          // the lane supplies the scale of MX block 2 h + lg of this stage
+          const int sa_ = (int)((mxa[i] >> (8 * (2 * h + lg))) & 0xFFu);
+          const int sb_ = (int)((mxb[j] >> (8 * (2 * h + lg))) & 0xFFu);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], AFMT, BFMT, 0,
+                                                                       sa_, 0, sb_);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], AFMT, BFMT, 0, 0,
+                                                                       0, 0);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const i32x4 a = s ? __builtin_shufflevector(f.a[i], f.a[i], 4, 5, 6, 7)
+                            : __builtin_shufflevector(f.a[i], f.a[i], 0, 1, 2, 3);
+          const i32x4 b = s ? __builtin_shufflevector(f.b[j], f.b[j], 4, 5, 6, 7)
+                            : __builtin_shufflevector(f.b[j], f.b[j], 0, 1, 2, 3);
+          if (OP == OP_BF16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                __builtin_bit_cast(bf16x8, b), acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                               __builtin_bit_cast(f16x8, b), acc[i][j], 0, 0, 0);
+        }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The kernel.
+//
+// Schedule of K stage kt (LDS buffer b = kt & 1; f0 = fragments of its first
+// half, already in registers):
+//   f1 <- LDS b, second half
+//   MFMA(f0)
+//   wait for the loads of stage kt+1; write register-staged operands of
+//   stage kt+1 into LDS b^1; barrier (b^1 complete, nobody reads b any more)
+//   issue the loads of stage kt+2 into b
+//   f0 <- LDS b^1, first half        (the next stage's first half)
+//   MFMA(f1)
+// so LDS reads overlap MFMAs and global loads get ~1.5 stages of lead.  Scale
+// rows use a 3-deep LDS ring so stage kt+2's scales never overwrite stage kt's.
+// Block-128 keeps a plain double-buffered loop (see below).
 // ---------------------------------------------------------------------------
 template <int OP, int LDA, int LDB, int SC, int AFMT, int BFMT, bool B2D, bool OUT_BF16>
 __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   __shared__ __align__(16) uint8_t lds[2][2][TILEB];     // [stage][A/B]
-  __shared__ __align__(16) uint32_t lds_sc[2][2][BM];    // [stage][A/B][row]
+  __shared__ __align__(16) uint32_t lds_sc[3][2][BM];    // [stage % 3][A/B][row]
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -244,7 +324,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
 
   RegStage ra, rb;
 
-  auto issue = [&](int kt, int buf) {
+  auto issue = [&](int kt) {
+    const int buf = kt & 1, sbuf = kt % 3;
     if (LDA == LD_KMAJOR) load_direct(g.A, g.lda, m0, g.M, kt, lds[buf][0]);
     else if (LDA == LD_MNMAJOR) load_mn(ra, g.A, g.lda, m0, g.M, kt);
     else load_nv<false>(ra, g.A, g.lda, m0, g.M, kt, g.K, g.a_scale);
@@ -252,150 +333,101 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
     else if (LDB == LD_MNMAJOR) load_mn(rb, g.B, g.ldb, n0, g.N, kt);
     else load_nv<B2D>(rb, g.B, g.ldb, n0, g.N, kt, g.K, g.b_scale);
     if (SC == SC_MX) {
-      load_row_dwords(g.a_scale + (int64_t)kt * 4, g.K / 32, m0, g.M, 1, lds_sc[buf][0]);
-      load_row_dwords(g.b_scale + (int64_t)kt * 4, g.K / 32, n0, g.N, 1, lds_sc[buf][1]);
+      load_row_dwords(g.a_scale + (int64_t)kt * 4, g.K / 32, m0, g.M, 1, lds_sc[sbuf][0]);
+      load_row_dwords(g.b_scale + (int64_t)kt * 4, g.K / 32, n0, g.N, 1, lds_sc[sbuf][1]);
     } else if (SC == SC_BLK) {
-      load_row_dwords(g.a_scale + (int64_t)kt * 4, (g.K / 128) * 4, m0, g.M, 1, lds_sc[buf][0]);
+      load_row_dwords(g.a_scale + (int64_t)kt * 4, (g.K / 128) * 4, m0, g.M, 1, lds_sc[sbuf][0]);
       load_row_dwords(g.b_scale + (int64_t)kt * 4, (g.K / 128) * 4, n0, g.N, B2D ? 128 : 1,
-                      lds_sc[buf][1]);
+                      lds_sc[sbuf][1]);
     }
   };
-  auto commit = [&](int buf) {       // register-staged operands -> LDS
+  auto commit = [&](int kt) {        // register-staged operands of stage kt -> LDS
+    const int buf = kt & 1;
     if (LDA == LD_MNMAJOR) store_mn(ra, lds[buf][0]);
     if (LDA == LD_NVFP4) store_nv(ra, lds[buf][0]);
     if (LDB == LD_MNMAJOR) store_mn(rb, lds[buf][1]);
     if (LDB == LD_NVFP4) store_nv(rb, lds[buf][1]);
   };
 
-  issue(0, 0);
-  commit(0);
-  wait_vm0();
-  __syncthreads();
-
   const int lr = lane & 31, lg = lane >> 5;     // row within a 32-tile, K group
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) issue(kt + 1, buf ^ 1);
-    const uint8_t* la = lds[buf][0];
-    const uint8_t* lb = lds[buf][1];
 
-    if (OP == OP_BF16 || OP == OP_F16) {
+  if constexpr (SC == SC_BLK) {
+    // Block-128: the VALU fold needs both halves of a stage per tile, so this
+    // recipe keeps the plain double-buffered loop (loads of stage kt+1 issued
+    // at the top of stage kt, one barrier at its end).
+    issue(0);
+    wait_vm0();
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1, sbuf = kt % 3;
+      if (kt + 1 < nk) issue(kt + 1);
+      const uint8_t* la = lds[buf][0];
+      const uint8_t* lb = lds[buf][1];
+      i32x8 fa[2][4], fb[2][4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        uint4 fa[4], fb[4];
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = *(const uint4*)(la + swz(wm * 128 + 32 * i + lr, 2 * s + lg));
+        for (int i = 0; i < 4; ++i) {
+          fa[h][i] = read2(la, wm * 128 + 32 * i + lr, 4 * h + lg, 4 * h + 2 + lg);
+          fb[h][i] = read2(lb, wn * 128 + 32 * i + lr, 4 * h + lg, 4 * h + 2 + lg);
+        }
+      float sbv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[j] = *(const uint4*)(lb + swz(wn * 128 + 32 * j + lr, 2 * s + lg));
+      for (int j = 0; j < 4; ++j) sbv[j] = __uint_as_float(lds_sc[sbuf][1][wn * 128 + 32 * j + lr]);
+      // the whole 128-long K block of each 32x32 tile accumulates into fresh
+      // registers, then acc += part * a_scale[row] * b_scale[col]
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        float sav[16];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (OP == OP_BF16)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
-            else
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                  __builtin_bit_cast(f16x8, fa[i]), __builtin_bit_cast(f16x8, fb[j]), acc[i][j], 0, 0, 0);
-          }
+        for (int r = 0; r < 16; ++r)
+          sav[r] = __uint_as_float(lds_sc[sbuf][0][wm * 128 + 32 * i + (r >> 2) * 8 + lg * 4 + (r & 3)]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x16 part;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) part[r] = 0.0f;
+          part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0][i], fb[0][j], part, 0, 0, 0, 0, 0, 0);
+          part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[1][i], fb[1][j], part, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[r], sav[r] * sbv[j], acc[i][j][r]);
+        }
       }
-    } else {
-      // OP_FP8: two K=64 steps per stage.  Operand layout of the 32x32x64
-      // f8f6f4 instruction (8-bit formats): lane l holds row (or column)
-      // l % 32; its bytes 0-15 are K 16 g .. 16 g + 15 and bytes 16-31 are
-      // K 32 + 16 g .. 32 + 16 g + 15, g = l / 32.  The E8M0 scale that lane
-      // l supplies applies to K block g (K 32 g .. 32 g + 31) of its row.
-      // So lane group g reads 16-byte chunks g and 2 + g of each 64-byte step,
-      // and supplies the scale of MX block 2 s + g of the stage.
+      wait_vm0();
+      __syncthreads();
+    }
+  } else {
+    Frags f0, f1;
+    issue(0);
+    wait_vm0();
+    commit(0);
+    __syncthreads();
+    if (nk > 1) issue(1);
+    read_frags(f0, lds[0][0], lds[0][1], wm, wn, lr, lg, 0);
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1, sbuf = kt % 3;
+      const bool next = kt + 1 < nk;
+      read_frags(f1, lds[buf][0], lds[buf][1], wm, wn, lr, lg, 1);
       uint32_t mxa[4] = {0, 0, 0, 0}, mxb[4] = {0, 0, 0, 0};
       if (SC == SC_MX) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mxa[i] = lds_sc[buf][0][wm * 128 + 32 * i + lr];
+        for (int i = 0; i < 4; ++i) mxa[i] = lds_sc[sbuf][0][wm * 128 + 32 * i + lr];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mxb[j] = lds_sc[buf][1][wn * 128 + 32 * j + lr];
+        for (int j = 0; j < 4; ++j) mxb[j] = lds_sc[sbuf][1][wn * 128 + 32 * j + lr];
       }
-      if (SC != SC_BLK) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          i32x8 fa[4], fb[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = wm * 128 + 32 * i + lr;
-            const uint4 lo = *(const uint4*)(la + swz(row, 4 * s + lg));
-            const uint4 hi = *(const uint4*)(la + swz(row, 4 * s + 2 + lg));
-            fa[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = wn * 128 + 32 * j + lr;
-            const uint4 lo = *(const uint4*)(lb + swz(row, 4 * s + lg));
-            const uint4 hi = *(const uint4*)(lb + swz(row, 4 * s + 2 + lg));
-            fb[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if (SC == SC_MX) {
-                const int sa_ = (int)((mxa[i] >> (8 * (2 * s + lg))) & 0xFFu);
-                const int sb_ = (int)((mxb[j] >> (8 * (2 * s + lg))) & 0xFFu);
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AFMT,
-                                                                             BFMT, 0, sa_, 0, sb_);
-              } else {
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AFMT,
-                                                                             BFMT, 0, 0, 0, 0);
-              }
-            }
-        }
-      } else {
-        // Block-128: per output 32x32 tile, the 128-long K block accumulates
-        // into fresh registers (two K=64 steps), then is added in with
-        // a_scale[row] * b_scale[col].
-        i32x8 fa[2][4], fb[2][4];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = wm * 128 + 32 * i + lr;
-            const uint4 lo = *(const uint4*)(la + swz(row, 4 * s + lg));
-            const uint4 hi = *(const uint4*)(la + swz(row, 4 * s + 2 + lg));
-            fa[s][i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = wn * 128 + 32 * j + lr;
-            const uint4 lo = *(const uint4*)(lb + swz(row, 4 * s + lg));
-            const uint4 hi = *(const uint4*)(lb + swz(row, 4 * s + 2 + lg));
-            fb[s][j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          }
-        }
-        float sbv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sbv[j] = __uint_as_float(lds_sc[buf][1][wn * 128 + 32 * j + lr]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sav[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sav[r] = __uint_as_float(lds_sc[buf][0][wm * 128 + 32 * i + (r >> 2) * 8 + lg * 4 + (r & 3)]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            f32x16 part;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) part[r] = 0.0f;
-            part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0][i], fb[0][j], part, 0, 0, 0, 0, 0, 0);
-            part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[1][i], fb[1][j], part, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[r], sav[r] * sbv[j], acc[i][j][r]);
-          }
-        }
+      mfma_half<OP, SC, AFMT, BFMT>(acc, f0, mxa, mxb, 0, lg);
+      if (next) {
+        wait_vm0();
+        commit(kt + 1);
       }
+      __syncthreads();
+      if (kt + 2 < nk) issue(kt + 2);
+      // the next stage's first half (on the last stage this re-reads a settled
+      // buffer and is discarded)
+      read_frags(f0, lds[buf ^ 1][0], lds[buf ^ 1][1], wm, wn, lr, lg, 0);
+      mfma_half<OP, SC, AFMT, BFMT>(acc, f1, mxa, mxb, 1, lg);
     }
-
-    if (more) commit(buf ^ 1);
-    wait_vm0();
-    __syncthreads();
   }
 
   // Epilogue.  Lane (lr, lg) of tile (i, j) holds column 32 j + lr and rows
