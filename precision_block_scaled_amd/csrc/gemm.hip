@@ -37,8 +37,8 @@
 // (64 bf16 / fp16, 128 fp8): 32 KB per operand, double-buffered in LDS
 // (128 KB).  Contraction-contiguous operands go global -> LDS directly
 // (global_load_lds_dwordx4, no registers), each lane fetching the 16-byte
-// chunk whose XOR-swizzled LDS slot it owns, so the MFMA fragment reads
-// (ds_read_b128) are bank-conflict-free.  Operands that must be transformed
+// chunk whose XOR-swizzled LDS slot it owns; the swizzle makes the MFMA
+// fragment reads (ds_read_b128) bank-conflict-free.  Operands that must be transformed
 // (MN-major bf16, NVFP4) are staged through registers.  Workgroups are
 // mapped to tiles so that each of the 8 XCDs (each with its own L2) works on
 // a contiguous, row-grouped range of tiles.
@@ -78,7 +78,15 @@ struct GemmArgs {
   int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ (row & 7)) << 4); }
+// LDS tile layout: row r, 16-byte chunk c lives at r * 128 + ((c ^ f(r)) << 4).
+// gfx950's LDS serves a 16-byte-per-lane access 16 lanes (256 bytes, 64
+// banks) at a time; f(r) = (r ^ r >> 1 ^ r >> 4) & 7 makes the MFMA fragment
+// reads (16 consecutive rows, one chunk) and the NVFP4 decode stores
+// conflict-free, and the MN-major bf16 stores at most 2-way (a plain
+// r & 7 leaves every fragment read 2-way conflicted).
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * ROWB + ((chunk ^ ((row ^ (row >> 1) ^ (row >> 4)) & 7)) << 4);
+}
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -88,16 +96,18 @@ __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" :
 // ---------------------------------------------------------------------------
 
 // K-major, direct to LDS: instruction q (of 32) writes LDS rows 8q..8q+7;
-// lane l owns row 8q + l/8, physical chunk l%8, i.e. logical chunk
-// (l % 8) ^ (l / 8).
+// lane l owns row 8q + l/8, physical chunk l%8, i.e. the logical chunk that
+// the swizzle places there.
 __device__ __forceinline__ void load_direct(const uint8_t* base, int64_t ld, int rows0, int nrows,
                                             int kt, uint8_t* lds) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+  const int lr = lane >> 3;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int q = w * 8 + i;
-    int row = rows0 + 8 * q + lr;
+    const int trow = 8 * q + lr;
+    const int lc = (lane & 7) ^ ((trow ^ (trow >> 1) ^ (trow >> 4)) & 7);
+    int row = rows0 + trow;
     row = row < nrows ? row : nrows - 1;
     const uint8_t* g = base + (int64_t)row * ld + (int64_t)kt * ROWB + (lc << 4);
     __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds + q * 1024), 16, 0, 0);
