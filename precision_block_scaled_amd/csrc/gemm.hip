@@ -45,6 +45,8 @@
 #include "device.hpp"
 #include "host.hpp"
 
+#include <type_traits>
+
 namespace pbs {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -52,6 +54,8 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 enum { OP_BF16 = 0, OP_F16 = 1, OP_FP8 = 2 };                 // what the MFMA consumes
@@ -61,8 +65,18 @@ enum { SC_NONE = 0, SC_TENSOR = 1, SC_MX = 2, SC_BLK = 3, SC_NV = 4 };
 constexpr int BM = 256, BN = 256, NTHR = 256;
 constexpr int ROWB = 128;               // bytes per LDS row per K stage
 constexpr int TILEB = BM * ROWB;        // 32 KB per operand per stage
+constexpr int SC_OFF = 4 * TILEB;       // scale-row ring after 2 stages x 2 operands
+constexpr int SC_RING = 3;
+constexpr int STG_BF16 = 544;           // epilogue staging row pitch, bf16 output (256 rows)
+constexpr int STG_F32 = 1056;           // epilogue staging row pitch, fp32 output (128 rows a pass)
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int SMEM = cmax(SC_OFF + SC_RING * 2 * BM * 4, cmax(256 * STG_BF16, 128 * STG_F32));
 constexpr int GROUP_M = 8;              // tile rows walked together (L2 reuse)
 constexpr int NXCD = 8;
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM = 0x010, SG_DSR = 0x100, SG_DSW = 0x200 };
+#define PBS_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 struct GemmArgs {
   const uint8_t* A;
@@ -78,51 +92,75 @@ struct GemmArgs {
   int tiles_m, tiles_n;
 };
 
-// LDS tile layout: row r, 16-byte chunk c lives at r * 128 + ((c ^ f(r)) << 4).
+// LDS tile layout: row r, 16-byte chunk c lives at r * 128 + ((c ^ key(r)) << 4).
 // gfx950's LDS serves a 16-byte-per-lane access 16 lanes (256 bytes, 64
-// banks) at a time; f(r) = (r ^ r >> 1 ^ r >> 4) & 7 makes the MFMA fragment
-// reads (16 consecutive rows, one chunk) and the NVFP4 decode stores
-// conflict-free, and the MN-major bf16 stores at most 2-way (a plain
+// banks) at a time; key(r) = (r ^ r >> 1 ^ r >> 4) & 7 makes the MFMA
+// fragment reads (16 consecutive rows, one chunk) and the NVFP4 decode
+// stores conflict-free, and the MN-major bf16 stores at most 2-way (a plain
 // r & 7 leaves every fragment read 2-way conflicted).
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * ROWB + ((chunk ^ ((row ^ (row >> 1) ^ (row >> 4)) & 7)) << 4);
-}
+__device__ __forceinline__ int swz_key(int row) { return (row ^ (row >> 1) ^ (row >> 4)) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ swz_key(row)) << 4); }
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // Operand staging.  Every variant fills one [256 rows][128 B] swizzled LDS
-// tile for K stage kt.  rows0 / nrows: first tile row and valid rows.
+// tile for K stage kt.  rows0 / nrows: first tile row and valid rows (rows
+// past the end re-read the last valid row; their results are never stored).
 // ---------------------------------------------------------------------------
 
-// K-major, direct to LDS: instruction q (of 32) writes LDS rows 8q..8q+7;
-// lane l owns row 8q + l/8, physical chunk l%8, i.e. the logical chunk that
-// the swizzle places there.
-__device__ __forceinline__ void load_direct(const uint8_t* base, int64_t ld, int rows0, int nrows,
-                                            int kt, uint8_t* lds) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int lr = lane >> 3;
+// K-major, direct to LDS (global_load_lds_dwordx4, no registers): load i (of
+// 8) of wave w fills LDS rows 64 w + 8 i .. + 7; lane l owns row
+// 64 w + 8 i + l / 8, physical chunk l % 8, i.e. the logical chunk that the
+// swizzle places there.  The tile's row base is wave-uniform; each lane keeps
+// eight 32-bit offsets (row * ld < 2^32 is checked on the host).
+struct Direct {
+  const uint8_t* base;
+  uint32_t off[8];
+};
+
+__device__ __forceinline__ void direct_init(Direct& d, const uint8_t* p, int64_t ld, int rows0, int nrows,
+                                            int w) {
+  const int lane = threadIdx.x & 63;
+  d.base = p + (int64_t)rows0 * ld;
+  const int lim = nrows - rows0 - 1;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int q = w * 8 + i;
-    const int trow = 8 * q + lr;
-    const int lc = (lane & 7) ^ ((trow ^ (trow >> 1) ^ (trow >> 4)) & 7);
-    int row = rows0 + trow;
-    row = row < nrows ? row : nrows - 1;
-    const uint8_t* g = base + (int64_t)row * ld + (int64_t)kt * ROWB + (lc << 4);
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds + q * 1024), 16, 0, 0);
+    const int trow = 64 * w + 8 * i + (lane >> 3);
+    const int lc = (lane & 7) ^ swz_key(trow);
+    const int r = trow < lim ? trow : lim;
+    d.off[i] = (uint32_t)r * (uint32_t)ld + (uint32_t)(lc << 4);
   }
 }
 
-// Per-row dword (MX scales / block-128 scales) for this stage, direct to LDS:
-// wave w loads rows 64 w .. 64 w + 63.
-__device__ __forceinline__ void load_row_dwords(const uint8_t* p, int64_t row_stride, int rows0, int nrows,
-                                                int div_rows, uint32_t* lds) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ void direct_issue(const Direct& d, int kt, uint8_t* tile, int w) {
+  const uint8_t* g = d.base + (int64_t)kt * ROWB;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_global_load_lds(g + d.off[i], (lds_ptr_t)(tile + (w * 8 + i) * 1024), 16, 0, 0);
+}
+
+__device__ __forceinline__ void direct_item(const Direct& d, int kt, uint8_t* tile, int w, int i) {
+  const uint8_t* g = d.base + (int64_t)kt * ROWB;
+  __builtin_amdgcn_global_load_lds(g + d.off[i], (lds_ptr_t)(tile + (w * 8 + i) * 1024), 16, 0, 0);
+}
+
+// One dword per tile row per stage (MX scales: 4 E8M0 bytes; block-128: one
+// fp32 scale), direct to LDS: wave w loads rows 64 w .. 64 w + 63.
+struct RowDword {
+  const uint8_t* p;        // this lane's row of the scale array
+};
+
+__device__ __forceinline__ void rowdw_init(RowDword& d, const uint8_t* scale, int64_t row_stride, int rows0,
+                                           int nrows, int div_rows, int w) {
+  const int lane = threadIdx.x & 63;
   int row = rows0 + 64 * w + lane;
   row = row < nrows ? row : nrows - 1;
-  const uint8_t* g = p + (int64_t)(row / div_rows) * row_stride;
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds + 64 * w), 4, 0, 0);
+  d.p = scale + (int64_t)(row / div_rows) * row_stride;
+}
+
+__device__ __forceinline__ void rowdw_issue(const RowDword& d, int kt, uint32_t* ring_slot, int w) {
+  __builtin_amdgcn_global_load_lds(d.p + (int64_t)kt * 4, (lds_ptr_t)(ring_slot + 64 * w), 4, 0, 0);
 }
 
 // Register-staged operands.
@@ -140,6 +178,15 @@ __device__ __forceinline__ void load_mn(RegStage& st, const uint8_t* base, int64
   const int64_t k = (int64_t)kt * 64 + 8 * kq;
 #pragma unroll
   for (int i = 0; i < 8; ++i) st.v[i] = *(const uint4*)(base + (k + i) * ld + (int64_t)mn * 2);
+}
+
+__device__ __forceinline__ void load_mn_item(RegStage& st, const uint8_t* base, int64_t ld, int rows0,
+                                             int nrows, int kt, int i) {
+  const int t = threadIdx.x, kq = t >> 5, mq = t & 31;
+  int mn = rows0 + 8 * mq;
+  mn = mn < nrows ? mn : nrows - 8;
+  const int64_t k = (int64_t)kt * 64 + 8 * kq;
+  st.v[i] = *(const uint4*)(base + (k + i) * ld + (int64_t)mn * 2);
 }
 
 __device__ __forceinline__ void store_mn(const RegStage& st, uint8_t* lds) {
@@ -181,6 +228,22 @@ __device__ __forceinline__ void load_nv(RegStage& st, const uint8_t* base, int64
   }
 }
 
+// item it of 4: it / 2 = row half h, it % 2 = 0: 16 data bytes, 1: scale bytes
+template <bool SCALE2D>
+__device__ __forceinline__ void load_nv_item(RegStage& st, const uint8_t* base, int64_t ld, int rows0,
+                                             int nrows, int kt, int K, const uint8_t* scale, int it) {
+  const int t = threadIdx.x, half = t & 1, h = it >> 1;
+  int row = rows0 + (t >> 1) + 128 * h;
+  row = row < nrows ? row : nrows - 1;
+  if ((it & 1) == 0) {
+    st.v[h] = *(const uint4*)(base + (int64_t)row * ld + (int64_t)kt * 32 + half * 16);
+  } else {
+    const int64_t kb = ((int64_t)kt * 64 + 32 * half) / 16;
+    const int64_t srow = SCALE2D ? row / 16 : row;
+    st.s[h] = *(const uint16_t*)(scale + srow * (K / 16) + kb);
+  }
+}
+
 __device__ __forceinline__ void store_nv(const RegStage& st, uint8_t* lds) {
   const int t = threadIdx.x, half = t & 1;
 #pragma unroll
@@ -206,12 +269,6 @@ __device__ __forceinline__ void store_nv(const RegStage& st, uint8_t* lds) {
   }
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 // XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a
 // contiguous range of logical tiles, then walk tiles GROUP_M rows at a time.
 __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -234,65 +291,78 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
 // 4-7) of its row.  For 8-bit operands the 8 dwords are one K=64 MFMA
 // operand (see the layout note in the kernel); for 16-bit operands the two
 // halves are the operands of two K=16 steps (chunks 2s + lg, s = 2h, 2h + 1).
+//
+// Address: row = 128 wm + 32 i + lr has key(row) = key(lr) ^ 2 i, so the
+// physical chunk is (lg ^ key(lr)) ^ 4 h ^ 2 i (^ 2 for the upper half): one
+// per-lane constant lb = 128 lr + ((lg ^ key(lr)) << 4), XOR-ed with a
+// compile-time pattern.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 struct Frags {
-  i32x8 a[4], b[4];
+  i32x4 a[4][2], b[4][2];     // [tile][lower / upper 16 bytes]
 };
 
-__device__ __forceinline__ i32x8 read2(const uint8_t* l, int row, int c_lo, int c_hi) {
-  const i32x4 lo = *(const i32x4*)(l + swz(row, c_lo));
-  const i32x4 hi = *(const i32x4*)(l + swz(row, c_hi));
+// LDS read d (of 16) of a half stage: operand d / 8, tile (d / 2) % 4, part d % 2.
+template <int H>
+__device__ __forceinline__ void frag_read(Frags& f, int d, const uint8_t* la, const uint8_t* lbp, uint32_t lb) {
+  const int op = d >> 3, tile = (d >> 1) & 3, part = d & 1;
+  const uint32_t x = (uint32_t)((((4 * H) ^ (2 * tile)) << 4) ^ (part << 5));
+  const uint8_t* base = (op == 0 ? la : lbp) + tile * 4096;
+  const i32x4 v = *(const i32x4*)(base + (lb ^ x));
+  if (op == 0) f.a[tile][part] = v;
+  else f.b[tile][part] = v;
+}
+
+__device__ __forceinline__ i32x8 read2(const uint8_t* tile_row0, uint32_t lb, uint32_t x) {
+  const i32x4 lo = *(const i32x4*)(tile_row0 + (lb ^ x));
+  const i32x4 hi = *(const i32x4*)(tile_row0 + (lb ^ x ^ 32u));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* la, const uint8_t* lb, int wm, int wn,
-                                           int lr, int lg, int h) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = read2(la, wm * 128 + 32 * i + lr, 4 * h + lg, 4 * h + 2 + lg);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = read2(lb, wn * 128 + 32 * j + lr, 4 * h + lg, 4 * h + 2 + lg);
+__device__ __forceinline__ i32x8 cat(const i32x4 (&p)[2]) {
+  return __builtin_shufflevector(p[0], p[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// MFMAs of one half stage on all 16 tiles (every recipe but block-128).
+// MFMA m of one half stage (every recipe but block-128): 8-bit operands
+// issue 16 (tile i = m / 4, j = m % 4, one K=64 step), 16-bit operands 32
+// (K=16 step s = m / 16 of the half, then i, j).
 template <int OP, int SC, int AFMT, int BFMT>
-__device__ __forceinline__ void mfma_half(f32x16 (&acc)[4][4], const Frags& f, const uint32_t* mxa,
-                                          const uint32_t* mxb, int h, int lg) {
+__device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const Frags& f, const uint32_t* mxa,
+                                         const uint32_t* mxb, int h, int lg, int m) {
   if (OP == OP_FP8) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (SC == SC_MX) {
-          // the lane supplies the scale of MX block 2 h + lg of this stage
-          const int sa_ = (int)((mxa[i] >> (8 * (2 * h + lg))) & 0xFFu);
-          const int sb_ = (int)((mxb[j] >> (8 * (2 * h + lg))) & 0xFFu);
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], AFMT, BFMT, 0,
-                                                                       sa_, 0, sb_);
-        } else {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], AFMT, BFMT, 0, 0,
-                                                                       0, 0);
-        }
-      }
+    const int i = m >> 2, j = m & 3;
+    if (SC == SC_MX) {
+      // the lane supplies the scale of MX block 2 h + lg of this stage
+      const int sa_ = (int)((mxa[i] >> (8 * (2 * h + lg))) & 0xFFu);
+      const int sb_ = (int)((mxb[j] >> (8 * (2 * h + lg))) & 0xFFu);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(f.a[i]), cat(f.b[j]), acc[i][j], AFMT, BFMT,
+                                                                   0, sa_, 0, sb_);
+    } else {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(f.a[i]), cat(f.b[j]), acc[i][j], AFMT, BFMT,
+                                                                   0, 0, 0, 0);
+    }
   } else {
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const i32x4 a = s ? __builtin_shufflevector(f.a[i], f.a[i], 4, 5, 6, 7)
-                            : __builtin_shufflevector(f.a[i], f.a[i], 0, 1, 2, 3);
-          const i32x4 b = s ? __builtin_shufflevector(f.b[j], f.b[j], 4, 5, 6, 7)
-                            : __builtin_shufflevector(f.b[j], f.b[j], 0, 1, 2, 3);
-          if (OP == OP_BF16)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                __builtin_bit_cast(bf16x8, b), acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                               __builtin_bit_cast(f16x8, b), acc[i][j], 0, 0, 0);
-        }
+    const int s = m >> 4, i = (m >> 2) & 3, j = m & 3;
+    const i32x4 a = f.a[i][s], b = f.b[j][s];
+    if (OP == OP_BF16)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                          acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                         acc[i][j], 0, 0, 0);
   }
+}
+
+// Share of n items that goes with MFMA m when n items are spread evenly over
+// the first `over` MFMAs: items [n m / over, n (m + 1) / over).
+__device__ __forceinline__ constexpr int share_lo(int n, int over, int m) { return m < over ? n * m / over : n; }
+__device__ __forceinline__ constexpr int share_hi(int n, int over, int m) {
+  return m < over ? n * (m + 1) / over : n;
+}
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // ---------------------------------------------------------------------------
@@ -300,29 +370,36 @@ __device__ __forceinline__ void mfma_half(f32x16 (&acc)[4][4], const Frags& f, c
 //
 // Schedule of K stage kt (LDS buffer b = kt & 1; f0 = fragments of its first
 // half, already in registers):
-//   f1 <- LDS b, second half
-//   MFMA(f0)
-//   wait for the loads of stage kt+1; write register-staged operands of
-//   stage kt+1 into LDS b^1; barrier (b^1 complete, nobody reads b any more)
-//   issue the loads of stage kt+2 into b
-//   f0 <- LDS b^1, first half        (the next stage's first half)
-//   MFMA(f1)
-// so LDS reads overlap MFMAs and global loads get ~1.5 stages of lead.  Scale
-// rows use a 3-deep LDS ring so stage kt+2's scales never overwrite stage kt's.
-// Block-128 keeps a plain double-buffered loop (see below).
+//   phase A: MFMA(f0), interleaved with the reads f1 <- LDS b, second half
+//   phase B: (register-staged operands) wait for stage kt+1's loads and write
+//            them into LDS b^1; barrier: b^1 complete, nobody reads b any more
+//   phase C: MFMA(f1), interleaved with the loads of stage kt+2 into b and
+//            the reads f0 <- LDS b^1, first half
+// so LDS reads and global loads ride between MFMAs and global loads get
+// about one stage of lead.  The last two stages are peeled (no loads, then
+// no reads), so every phase is straight-line code.  Scale rows use a 3-deep
+// LDS ring.  Block-128 keeps a plain double-buffered loop (see below).
+//
+// Epilogue: the accumulators go through LDS (bf16: adjacent lanes swap
+// halves so each lane writes two 4-byte column pairs; fp32: 128 rows per
+// pass), then every lane stores 16 contiguous bytes of C.
 // ---------------------------------------------------------------------------
 template <int OP, int LDA, int LDB, int SC, int AFMT, int BFMT, bool B2D, bool OUT_BF16>
 __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
-  __shared__ __align__(16) uint8_t lds[2][2][TILEB];     // [stage][A/B]
-  __shared__ __align__(16) uint32_t lds_sc[3][2][BM];    // [stage % 3][A/B][row]
+  __shared__ __align__(16) uint8_t smem[SMEM];
 
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w >> 1, wn = w & 1;
   int tm, tn;
   tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   constexpr int KST = (OP == OP_FP8) ? 128 : 64;         // K elements per stage
   const int nk = g.K / KST;
+
+  auto tileA = [&](int buf) { return smem + (buf * 2 + 0) * TILEB; };
+  auto tileB = [&](int buf) { return smem + (buf * 2 + 1) * TILEB; };
+  auto ring = [&](int slot, int o) { return (uint32_t*)(smem + SC_OFF + (slot * 2 + o) * BM * 4); };
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -332,34 +409,44 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  Direct da, db;
+  RowDword sa, sb;
   RegStage ra, rb;
+  if (LDA == LD_KMAJOR) direct_init(da, g.A, g.lda, m0, g.M, w);
+  if (LDB == LD_KMAJOR) direct_init(db, g.B, g.ldb, n0, g.N, w);
+  if (SC == SC_MX) {
+    rowdw_init(sa, g.a_scale, g.K / 32, m0, g.M, 1, w);
+    rowdw_init(sb, g.b_scale, g.K / 32, n0, g.N, 1, w);
+  } else if (SC == SC_BLK) {
+    rowdw_init(sa, g.a_scale, (g.K / 128) * 4, m0, g.M, 1, w);
+    rowdw_init(sb, g.b_scale, (g.K / 128) * 4, n0, g.N, B2D ? 128 : 1, w);
+  }
 
   auto issue = [&](int kt) {
-    const int buf = kt & 1, sbuf = kt % 3;
-    if (LDA == LD_KMAJOR) load_direct(g.A, g.lda, m0, g.M, kt, lds[buf][0]);
+    const int buf = kt & 1;
+    if (LDA == LD_KMAJOR) direct_issue(da, kt, tileA(buf), w);
     else if (LDA == LD_MNMAJOR) load_mn(ra, g.A, g.lda, m0, g.M, kt);
     else load_nv<false>(ra, g.A, g.lda, m0, g.M, kt, g.K, g.a_scale);
-    if (LDB == LD_KMAJOR) load_direct(g.B, g.ldb, n0, g.N, kt, lds[buf][1]);
+    if (LDB == LD_KMAJOR) direct_issue(db, kt, tileB(buf), w);
     else if (LDB == LD_MNMAJOR) load_mn(rb, g.B, g.ldb, n0, g.N, kt);
     else load_nv<B2D>(rb, g.B, g.ldb, n0, g.N, kt, g.K, g.b_scale);
-    if (SC == SC_MX) {
-      load_row_dwords(g.a_scale + (int64_t)kt * 4, g.K / 32, m0, g.M, 1, lds_sc[sbuf][0]);
-      load_row_dwords(g.b_scale + (int64_t)kt * 4, g.K / 32, n0, g.N, 1, lds_sc[sbuf][1]);
-    } else if (SC == SC_BLK) {
-      load_row_dwords(g.a_scale + (int64_t)kt * 4, (g.K / 128) * 4, m0, g.M, 1, lds_sc[sbuf][0]);
-      load_row_dwords(g.b_scale + (int64_t)kt * 4, (g.K / 128) * 4, n0, g.N, B2D ? 128 : 1,
-                      lds_sc[sbuf][1]);
+    if (SC == SC_MX || SC == SC_BLK) {
+      const int slot = kt % SC_RING;
+      rowdw_issue(sa, kt, ring(slot, 0), w);
+      rowdw_issue(sb, kt, ring(slot, 1), w);
     }
   };
   auto commit = [&](int kt) {        // register-staged operands of stage kt -> LDS
     const int buf = kt & 1;
-    if (LDA == LD_MNMAJOR) store_mn(ra, lds[buf][0]);
-    if (LDA == LD_NVFP4) store_nv(ra, lds[buf][0]);
-    if (LDB == LD_MNMAJOR) store_mn(rb, lds[buf][1]);
-    if (LDB == LD_NVFP4) store_nv(rb, lds[buf][1]);
+    if (LDA == LD_MNMAJOR) store_mn(ra, tileA(buf));
+    if (LDA == LD_NVFP4) store_nv(ra, tileA(buf));
+    if (LDB == LD_MNMAJOR) store_mn(rb, tileB(buf));
+    if (LDB == LD_NVFP4) store_nv(rb, tileB(buf));
   };
 
   const int lr = lane & 31, lg = lane >> 5;     // row within a 32-tile, K group
+  const uint32_t lb = (uint32_t)(lr * 128 + ((lg ^ swz_key(lr)) << 4));
+  const int offA = wm * 16384, offB = wn * 16384;   // the wave's 128 rows within a tile
 
   if constexpr (SC == SC_BLK) {
     // Block-128: the VALU fold needs both halves of a stage per tile, so this
@@ -369,21 +456,23 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
     wait_vm0();
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1, sbuf = kt % 3;
+      const int buf = kt & 1, slot = kt % SC_RING;
       if (kt + 1 < nk) issue(kt + 1);
-      const uint8_t* la = lds[buf][0];
-      const uint8_t* lb = lds[buf][1];
+      const uint8_t* la = tileA(buf) + offA;
+      const uint8_t* lbp = tileB(buf) + offB;
       i32x8 fa[2][4], fb[2][4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          fa[h][i] = read2(la, wm * 128 + 32 * i + lr, 4 * h + lg, 4 * h + 2 + lg);
-          fb[h][i] = read2(lb, wn * 128 + 32 * i + lr, 4 * h + lg, 4 * h + 2 + lg);
-        }
+      for (int i = 0; i < 4; ++i) {
+        fa[0][i] = read2(la + i * 4096, lb, (uint32_t)((2 * i) << 4));
+        fa[1][i] = read2(la + i * 4096, lb, (uint32_t)((4 ^ (2 * i)) << 4));
+        fb[0][i] = read2(lbp + i * 4096, lb, (uint32_t)((2 * i) << 4));
+        fb[1][i] = read2(lbp + i * 4096, lb, (uint32_t)((4 ^ (2 * i)) << 4));
+      }
+      const uint32_t* sca = ring(slot, 0);
+      const uint32_t* scb = ring(slot, 1);
       float sbv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sbv[j] = __uint_as_float(lds_sc[sbuf][1][wn * 128 + 32 * j + lr]);
+      for (int j = 0; j < 4; ++j) sbv[j] = __uint_as_float(scb[wn * 128 + 32 * j + lr]);
       // the whole 128-long K block of each 32x32 tile accumulates into fresh
       // registers, then acc += part * a_scale[row] * b_scale[col]
 #pragma unroll
@@ -391,7 +480,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
         float sav[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          sav[r] = __uint_as_float(lds_sc[sbuf][0][wm * 128 + 32 * i + (r >> 2) * 8 + lg * 4 + (r & 3)]);
+          sav[r] = __uint_as_float(sca[wm * 128 + 32 * i + (r >> 2) * 8 + lg * 4 + (r & 3)]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           f32x16 part;
@@ -407,75 +496,173 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
       __syncthreads();
     }
   } else {
+    constexpr bool REG_A = LDA != LD_KMAJOR, REG_B = LDB != LD_KMAJOR;
+    constexpr int NMFMA = (OP == OP_FP8) ? 16 : 32;                // per half stage
+    constexpr int VM_A = LDA == LD_KMAJOR ? 8 : LDA == LD_MNMAJOR ? 8 : 4;
+    constexpr int VM_B = LDB == LD_KMAJOR ? 8 : LDB == LD_MNMAJOR ? 8 : 4;
+    constexpr int VM_STAGE = VM_A + VM_B + (SC == SC_MX ? 2 : 0);
+    constexpr int DS_NEXT = 16 + (SC == SC_MX ? 8 : 0);
+
     Frags f0, f1;
+    uint32_t mxa[4] = {0, 0, 0, 0}, mxb[4] = {0, 0, 0, 0};
+    constexpr int HALF = NMFMA / 2;
+
+    // global load v (of VM_STAGE) of stage kt
+    auto issue_item = [&](int kt, int v) {
+      const int buf = kt & 1;
+      if (v < VM_A) {
+        if (LDA == LD_KMAJOR) direct_item(da, kt, tileA(buf), w, v);
+        else if (LDA == LD_MNMAJOR) load_mn_item(ra, g.A, g.lda, m0, g.M, kt, v);
+        else load_nv_item<false>(ra, g.A, g.lda, m0, g.M, kt, g.K, g.a_scale, v);
+      } else if (v < VM_A + VM_B) {
+        const int u = v - VM_A;
+        if (LDB == LD_KMAJOR) direct_item(db, kt, tileB(buf), w, u);
+        else if (LDB == LD_MNMAJOR) load_mn_item(rb, g.B, g.ldb, n0, g.N, kt, u);
+        else load_nv_item<B2D>(rb, g.B, g.ldb, n0, g.N, kt, g.K, g.b_scale, u);
+      } else {
+        const int slot = kt % SC_RING;
+        if (v == VM_A + VM_B) rowdw_issue(sa, kt, ring(slot, 0), w);
+        else rowdw_issue(sb, kt, ring(slot, 1), w);
+      }
+    };
+    // LDS read e (of 8) of the MX scale words of stage kt
+    auto mx_item = [&](uint32_t* xa, uint32_t* xb, int kt, int e) {
+      const int slot = kt % SC_RING;
+      if (e < 4) xa[e] = ring(slot, 0)[wm * 128 + 32 * e + lr];
+      else xb[e - 4] = ring(slot, 1)[wn * 128 + 32 * (e - 4) + lr];
+    };
+
     issue(0);
     wait_vm0();
     commit(0);
     __syncthreads();
     if (nk > 1) issue(1);
-    read_frags(f0, lds[0][0], lds[0][1], wm, wn, lr, lg, 0);
+#pragma unroll
+    for (int d = 0; d < 16; ++d) frag_read<0>(f0, d, tileA(0) + offA, tileB(0) + offB, lb);
+    if (SC == SC_MX) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx_item(mxa, mxb, 0, e);
+    }
 
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1, sbuf = kt % 3;
-      const bool next = kt + 1 < nk;
-      read_frags(f1, lds[buf][0], lds[buf][1], wm, wn, lr, lg, 1);
-      uint32_t mxa[4] = {0, 0, 0, 0}, mxb[4] = {0, 0, 0, 0};
-      if (SC == SC_MX) {
+    auto body = [&](int kt, auto issue_c, auto next_c) {
+      constexpr bool ISSUE = decltype(issue_c)::value;
+      constexpr bool NEXT = decltype(next_c)::value;
+      const int buf = kt & 1;
+      const uint8_t* curA = tileA(buf) + offA;
+      const uint8_t* curB = tileB(buf) + offB;
+      const uint8_t* nxtA = tileA(buf ^ 1) + offA;
+      const uint8_t* nxtB = tileB(buf ^ 1) + offB;
+      // phase A: MFMA(f0); the 16 reads of f1 ride on the first half of the MFMAs
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mxa[i] = lds_sc[sbuf][0][wm * 128 + 32 * i + lr];
+      for (int m = 0; m < NMFMA; ++m) {
+        mfma_one<OP, SC, AFMT, BFMT>(acc, f0, mxa, mxb, 0, lg, m);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mxb[j] = lds_sc[sbuf][1][wn * 128 + 32 * j + lr];
+        for (int d = share_lo(16, HALF, m); d < share_hi(16, HALF, m); ++d) frag_read<1>(f1, d, curA, curB, lb);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      mfma_half<OP, SC, AFMT, BFMT>(acc, f0, mxa, mxb, 0, lg);
-      if (next) {
+      // phase B
+      if constexpr (NEXT && (REG_A || REG_B)) {
         wait_vm0();
         commit(kt + 1);
       }
       __syncthreads();
-      if (kt + 2 < nk) issue(kt + 2);
-      // the next stage's first half (on the last stage this re-reads a settled
-      // buffer and is discarded)
-      read_frags(f0, lds[buf ^ 1][0], lds[buf ^ 1][1], wm, wn, lr, lg, 0);
-      mfma_half<OP, SC, AFMT, BFMT>(acc, f1, mxa, mxb, 1, lg);
-    }
+      __builtin_amdgcn_sched_barrier(0);
+      // phase C: MFMA(f1); reads of the next f0 (and MX words) on the first
+      // half of the MFMAs, the loads of stage kt+2 spread over all of them
+      uint32_t nxa[4] = {0, 0, 0, 0}, nxb[4] = {0, 0, 0, 0};
+      constexpr int NDS = NEXT ? DS_NEXT : 0;
+      constexpr int NVM = ISSUE ? VM_STAGE : 0;
+#pragma unroll
+      for (int m = 0; m < NMFMA; ++m) {
+        mfma_one<OP, SC, AFMT, BFMT>(acc, f1, mxa, mxb, 1, lg, m);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = share_lo(NDS, HALF, m); d < share_hi(NDS, HALF, m); ++d) {
+          if (d < 16) frag_read<0>(f0, d, nxtA, nxtB, lb);
+          else mx_item(nxa, nxb, kt + 1, d - 16);
+        }
+#pragma unroll
+        for (int v = share_lo(NVM, NMFMA, m); v < share_hi(NVM, NMFMA, m); ++v) issue_item(kt + 2, v);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (NEXT && SC == SC_MX) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          mxa[i] = nxa[i];
+          mxb[i] = nxb[i];
+        }
+      }
+    };
+    using T_ = std::integral_constant<bool, true>;
+    using F_ = std::integral_constant<bool, false>;
+    for (int kt = 0; kt < nk - 2; ++kt) body(kt, T_{}, T_{});
+    if (nk >= 2) body(nk - 2, F_{}, T_{});
+    body(nk - 1, F_{}, F_{});
   }
 
   // Epilogue.  Lane (lr, lg) of tile (i, j) holds column 32 j + lr and rows
-  // 32 i + 8 (r / 4) + 4 lg + r % 4, r = 0..15.
+  // 32 i + 8 (r / 4) + 4 lg + r % 4, r = 0..15.  Every LDS read of the main
+  // loop finished before its last barrier and no load is in flight, so the
+  // staging area may overwrite the tiles and the scale ring.
   float post = 1.0f;
   if (SC == SC_TENSOR || SC == SC_NV) post = (*g.a_ts) * (*g.b_ts);
-  int roff[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) roff[r] = ((r >> 2) * 8 + lg * 4 + (r & 3)) * g.ldc;
   const bool full = (m0 + BM <= g.M) && (n0 + BN <= g.N);
+  if constexpr (OUT_BF16) {
+    // Lanes lr and lr ^ 1 swap half their values so that the even lane owns
+    // rows R, R+1 and the odd lane rows R+2, R+3 of the column pair.
+    const int par = lr & 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row0 = m0 + wm * 128 + 32 * i;
-      const int col = n0 + wn * 128 + 32 * j + lr;
-      const int64_t base = (int64_t)row0 * g.ldc + col;
-      f32x16 v = acc[i][j];
-      if (SC == SC_TENSOR || SC == SC_NV) {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] *= post;
-      }
-      if (OUT_BF16) {
-        uint16_t* cp = (uint16_t*)g.C + base;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row0 + (r >> 2) * 8 + lg * 4 + (r & 3);
-          if (full || (row < g.M && col < g.N)) cp[roff[r]] = (uint16_t)f32_to_bf16_rne(v[r]);
+        for (int q = 0; q < 4; ++q) {
+          const float v0 = acc[i][j][4 * q] * post, v1 = acc[i][j][4 * q + 1] * post;
+          const float v2 = acc[i][j][4 * q + 2] * post, v3 = acc[i][j][4 * q + 3] * post;
+          const uint32_t own = par ? pk_bf16(v2, v3) : pk_bf16(v0, v1);
+          const uint32_t snd = par ? pk_bf16(v0, v1) : pk_bf16(v2, v3);
+          const uint32_t rcv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0xB1, 0xF, 0xF, false);
+          const uint32_t lo = par ? rcv : own, hi = par ? own : rcv;
+          const int row = wm * 128 + 32 * i + 8 * q + 4 * lg + 2 * par;
+          const int colb = (wn * 128 + 32 * j + (lr & ~1)) * 2;
+          *(uint32_t*)(smem + row * STG_BF16 + colb) = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          *(uint32_t*)(smem + (row + 1) * STG_BF16 + colb) = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
         }
-      } else {
-        float* cp = (float*)g.C + base;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row0 + (r >> 2) * 8 + lg * 4 + (r & 3);
-          if (full || (row < g.M && col < g.N)) cp[roff[r]] = v[r];
-        }
-      }
+    __syncthreads();
+    const int ch = lane & 31;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int s = 64 * w + 2 * it + (lane >> 5);
+      const uint4 val = *(const uint4*)(smem + s * STG_BF16 + ch * 16);
+      const int grow = m0 + s, gcol = n0 + ch * 8;
+      if (full || (grow < g.M && gcol < g.N))
+        *(uint4*)((uint16_t*)g.C + (int64_t)grow * g.ldc + gcol) = val;
     }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = wm * 64 + 32 * ii + 8 * (r >> 2) + 4 * lg + (r & 3);
+            const int col = wn * 128 + 32 * j + lr;
+            *(float*)(smem + row * STG_F32 + col * 4) = acc[2 * p + ii][j][r] * post;
+          }
+      __syncthreads();
+#pragma unroll 4
+      for (int it = 0; it < 32; ++it) {
+        const int s = 32 * w + it;
+        const uint4 val = *(const uint4*)(smem + s * STG_F32 + lane * 16);
+        const int grow = m0 + (s >> 6) * 128 + 64 * p + (s & 63), gcol = n0 + lane * 4;
+        if (full || (grow < g.M && gcol < g.N)) *(uint4*)((float*)g.C + (int64_t)grow * g.ldc + gcol) = val;
+      }
+      if (p == 0) __syncthreads();
+    }
+  }
 }
 
 __global__ void zero_c_kernel(uint8_t* c, int64_t bytes) {
@@ -527,6 +714,7 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
   PBS_REQUIRE(A && B, PBS_ERR_INVALID_ARG, "pbs_gemm: A or B is null");
   PBS_REQUIRE(((uintptr_t)A & 15) == 0 && ((uintptr_t)B & 15) == 0, PBS_ERR_INVALID_ARG,
               "pbs_gemm: A and B must be 16-byte aligned");
+  PBS_REQUIRE(((uintptr_t)C & 15) == 0, PBS_ERR_INVALID_ARG, "pbs_gemm: C must be 16-byte aligned");
 
   GemmArgs g;
   g.A = (const uint8_t*)A;
@@ -618,6 +806,9 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
     default:
       return set_error(PBS_ERR_INVALID_ARG, "pbs_gemm: unknown recipe %d", (int)recipe);
   }
+  // tiles address their 256 rows with 32-bit offsets: stored rows up to 16 MiB
+  PBS_REQUIRE(g.lda <= (1 << 24) && g.ldb <= (1 << 24), PBS_ERR_SHAPE,
+              "pbs_gemm: stored operand rows longer than 16 MiB are not supported");
   const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n);
   log_dispatch("%s layout=%d M=%lld N=%lld K=%lld out=%s tiles=%dx%d", name, (int)layout, (long long)M,
                (long long)N, (long long)K, bf16_out ? "bf16" : "f32", g.tiles_m, g.tiles_n);
