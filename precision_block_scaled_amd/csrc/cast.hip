@@ -32,6 +32,8 @@
 #include "device.hpp"
 #include "host.hpp"
 
+#include <algorithm>
+
 namespace pbs {
 
 enum { R_TENSOR = 0, R_BLOCK128 = 1, R_MX = 2, R_NV = 3 };
@@ -332,17 +334,359 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Single-orientation casts with 1D blocks: the common case of a cast per
+// GEMM operand.  Both kernels work on 16-value segments (one per lane and
+// step): NVFP4 blocks are one segment, MXFP8 blocks two neighbouring lanes,
+// 1x128 blocks eight, so block maxima reduce with at most three lane swaps.
+//
+// Encoding uses the gfx950 conversion instructions (v_cvt_pk_fp8_f32,
+// v_cvt_pk_bf8_f32, v_cvt_scalef32_pk_fp4_f32 with scale 1): they round to
+// nearest even, and clamping the input to the largest finite code first
+// makes them saturating.  Over every non-NaN fp32 input they return the same
+// codes as enc_e4m3 / enc_e5m2 / enc_e2m1 (checked exhaustively on gfx950).
+// ---------------------------------------------------------------------------
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+template <int FMT>
+__device__ __forceinline__ uint32_t hw_fp8x4(float a, float b, float c, float d) {
+  if (FMT == F_E4M3) {
+    const float L = 448.0f;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -L, L), __builtin_amdgcn_fmed3f(b, -L, L), 0,
+                                            false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, -L, L), __builtin_amdgcn_fmed3f(d, -L, L), w, true);
+    return (uint32_t)w;
+  } else {
+    const float L = 57344.0f;
+    int w = __builtin_amdgcn_cvt_pk_bf8_f32(__builtin_amdgcn_fmed3f(a, -L, L), __builtin_amdgcn_fmed3f(b, -L, L), 0,
+                                            false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(__builtin_amdgcn_fmed3f(c, -L, L), __builtin_amdgcn_fmed3f(d, -L, L), w, true);
+    return (uint32_t)w;
+  }
+}
+
+// 8 values -> 8 E2M1 codes, element 2k in the low nibble of byte k.
+__device__ __forceinline__ uint32_t hw_fp4x8(const float* v) {
+#define PBS_FP4_PAIR(w, k)                                                                         \
+  __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((w), __builtin_amdgcn_fmed3f(v[2 * (k)], -6.0f, 6.0f),    \
+                                           __builtin_amdgcn_fmed3f(v[2 * (k) + 1], -6.0f, 6.0f), 1.0f, (k))
+  uint32_t w = PBS_FP4_PAIR(0u, 0);
+  w = PBS_FP4_PAIR(w, 1);
+  w = PBS_FP4_PAIR(w, 2);
+  w = PBS_FP4_PAIR(w, 3);
+#undef PBS_FP4_PAIR
+  return w;
+}
+
+// Max of the 15-bit magnitudes of 16 bf16 values held as 8 packed words.
+__device__ __forceinline__ uint32_t bf16_absmax16(const uint32_t* w) {
+  u16x2 m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+  return m.x > m.y ? m.x : m.y;
+}
+
+// Max over lane groups of 2 or 8 (xor 1, 2, 4).
+template <int G>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) {
+    const uint32_t u = (uint32_t)__shfl_xor((int)v, o, 64);
+    v = v > u ? v : u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ void bf16x16_to_f32(const uint32_t* w, float* v) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// Quantize one segment.  v: 16 fp32 values; mbits: max |value| bits over the
+// segment (fp32 bits); the group (block) reduction happens here.  Writes the
+// codes to `codes` (16 bytes for FP8, 8 for E2M1) and, from the lane that
+// owns the block's first segment, the block scale.
+//  RECIPE R_TENSOR: s = tensor scale; R_MX: 2-lane blocks; R_BLOCK128:
+//  8-lane blocks; R_NV: one-segment blocks with encode scale S = tscale.
+template <int RECIPE, int FMT, bool SR>
+__device__ __forceinline__ void quantize_segment(const float* v, uint32_t mbits, float tscale, bool valid,
+                                                 uint8_t* codes, uint8_t* sc8, float* sc32, bool writer,
+                                                 const uint32_t* rnd) {
+  if (RECIPE == R_TENSOR || RECIPE == R_MX || RECIPE == R_BLOCK128) {
+    float s = tscale;
+    if (RECIPE == R_MX) {
+      const uint32_t m = group_max<2>(mbits);
+      // the E8M0 rule works on the bf16 bits of the block maximum
+      const uint32_t c = mx_e8m0_from_bf16_amax(m >> 16);
+      s = mx_inv_scale(c);
+      if (valid && writer) *sc8 = (uint8_t)c;
+    } else if (RECIPE == R_BLOCK128) {
+      const uint32_t m = group_max<8>(mbits);
+      s = scale_from_amax(__uint_as_float(m), 448.0f);
+      if (valid && writer) *sc32 = 1.0f / s;
+    }
+    uint4 o;
+    o.x = hw_fp8x4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+    o.y = hw_fp8x4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+    o.z = hw_fp8x4<FMT>(v[8] * s, v[9] * s, v[10] * s, v[11] * s);
+    o.w = hw_fp8x4<FMT>(v[12] * s, v[13] * s, v[14] * s, v[15] * s);
+    if (valid) *(uint4*)codes = o;
+  } else {  // R_NV
+    const float S = tscale;
+    const float a_b = __uint_as_float(mbits);
+    const uint32_t d_code = enc_e4m3((a_b / 6.0f) * S);
+    const float d = dec_e4m3_pos(d_code);
+    uint2 o;
+    if (d == 0.0f) {
+      uint32_t q[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) q[i] = (__float_as_uint(v[i]) >> 28) & 0x8u;
+      o = pack_e2m1_16(q);
+    } else {
+      float e_b = S / d;
+      if (__float_as_uint(e_b) == 0x7F800000u) e_b = 3.40282346638528859812e+38f;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = v[i] * e_b;
+      if (SR) {
+        uint32_t q[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[i] = sr_e2m1(x[i], rnd[i]);
+        o = pack_e2m1_16(q);
+      } else {
+        o.x = hw_fp4x8(x);
+        o.y = hw_fp4x8(x + 8);
+      }
+    }
+    if (valid) {
+      *(uint2*)codes = o;
+      *sc8 = (uint8_t)d_code;
+    }
+  }
+}
+
+// Fold a per-thread |x| maximum (fp32 bits) into *out: wave reduction, one
+// value per workgroup through LDS, then one atomic from thread 0 only when
+// the workgroup maximum exceeds what *out already holds (the running maximum
+// settles early, so most workgroups skip the atomic).
+__device__ __forceinline__ void wg_amax_fold(uint32_t v, uint32_t* out, uint32_t* s_part) {
+  v = group_max<64>(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) s_part[w] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = s_part[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) m = m > s_part[i] ? m : s_part[i];
+    const uint32_t cur = __builtin_nontemporal_load(out);
+    if (m > cur) atomicMax(out, m);
+  }
+}
+
+// Row copy: thread = 16-value segment of a row.  Each lane does U = 2
+// segments per step (the wave covers 128 consecutive segments), both loads
+// issued before any arithmetic.  No LDS.
+template <int RECIPE, int FMT, bool SR, bool AMAX>
+__global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg) {
+  const int lane = threadIdx.x & 63;
+  const int64_t spr = a.C / 16;                         // segments per row
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  const int64_t wave0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  float tscale = 0.0f;
+  if (RECIPE == R_TENSOR || RECIPE == R_NV) tscale = *a.scale;
+  uint32_t amx = 0;
+  constexpr int U = 2;
+  for (int64_t wt = wave0; wt * 64 * U < nseg; wt += waves) {
+    uint32_t w[U][8];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t s = wt * 64 * U + u * 64 + lane;
+      ok[u] = s < nseg;
+      const int64_t sc = ok[u] ? s : 0;
+      const bf16_t* p = a.x + (sc / spr) * a.C + (sc % spr) * 16;
+      const uint4 v0 = ld_nt16(p), v1 = ld_nt16(p + 8);
+      w[u][0] = v0.x; w[u][1] = v0.y; w[u][2] = v0.z; w[u][3] = v0.w;
+      w[u][4] = v1.x; w[u][5] = v1.y; w[u][6] = v1.z; w[u][7] = v1.w;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t s = wt * 64 * U + u * 64 + lane;
+      const int64_t row = s / spr, seg = s % spr;
+      float v[16];
+      bf16x16_to_f32(w[u], v);
+      const uint32_t m16 = bf16_absmax16(w[u]);
+      if (AMAX && ok[u]) amx = amx > m16 ? amx : m16;
+      uint32_t rnd[16];
+      if (SR) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint64_t idx = (uint64_t)(row * a.C + seg * 16 + i);
+          rnd[i] = philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
+                                (uint32_t)(a.seed >> 32));
+        }
+      }
+      uint8_t* codes = (RECIPE == R_NV) ? a.row_codes + row * (a.C / 2) + seg * 8 : a.row_codes + row * a.C + seg * 16;
+      uint8_t* sc8 = nullptr;
+      float* sc32 = nullptr;
+      bool writer = true;
+      if (RECIPE == R_MX) {
+        sc8 = (uint8_t*)a.row_scales + row * (a.C / 32) + seg / 2;
+        writer = (seg & 1) == 0;
+      } else if (RECIPE == R_NV) {
+        sc8 = (uint8_t*)a.row_scales + row * (a.C / 16) + seg;
+      } else if (RECIPE == R_BLOCK128) {
+        sc32 = (float*)a.row_scales + row * (a.C / 128) + seg / 8;
+        writer = (seg & 7) == 0;
+      }
+      quantize_segment<RECIPE, FMT, SR>(v, m16 << 16, tscale, ok[u], codes, sc8, sc32, writer, rnd);
+    }
+  }
+  if (AMAX) {
+    __shared__ uint32_t s_part[4];
+    wg_amax_fold(amx << 16, a.amax_out, s_part);
+  }
+}
+
+// Col copy (the transposed tensor, blocks along x's rows).  A workgroup
+// stages a 256-row x 64-column tile of x in LDS; thread t takes rows
+// 16 (t % 16) .. + 15 of the 4 columns 4 (t / 16) .. + 3, so each of its 4
+// segments is 16 consecutive rows of one column, i.e. 16 consecutive values
+// of an output row.  LDS: row pitch 136 B (34 dwords: rows 16 apart land in
+// opposite bank halves) and the 8-byte column group g of row r stored at
+// g ^ ((r >> 4) & 14): the 64-lane 8-byte column reads are conflict-free.
+constexpr int CT_R = 256, CT_C = 64, CT_PITCH = 136;
+
+template <int RECIPE, int FMT, bool RHT, bool SR, bool AMAX>
+__global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
+  __shared__ __align__(16) uint8_t tile[CT_R * CT_PITCH];
+  const int t = threadIdx.x, lane = t & 63;
+  const int64_t r0 = (int64_t)blockIdx.y * CT_R, c0 = (int64_t)blockIdx.x * CT_C;
+  const int rlim = (int)min((int64_t)CT_R, a.R - r0);
+  const int clim = (int)min((int64_t)CT_C, a.C - c0);
+  // fill: 8 lanes per 128-byte row segment, 32 rows per pass, 8 passes
+  {
+    const int ch = t & 7;
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = (t >> 3) + 32 * i;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (row < rlim && ch * 8 < clim) v[i] = ld_nt16(a.x + (r0 + row) * a.C + c0 + ch * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = (t >> 3) + 32 * i;
+      const int g = (2 * ch) ^ ((row >> 4) & 14);
+      // odd rows start 8 bytes into a 16-byte line: two 8-byte stores
+      *(uint2*)(tile + row * CT_PITCH + g * 8) = make_uint2(v[i].x, v[i].y);
+      *(uint2*)(tile + row * CT_PITCH + g * 8 + 8) = make_uint2(v[i].z, v[i].w);
+    }
+  }
+  uint32_t rht_mask = 0;
+  if (RHT) {
+    // bit j of the mask from lane j (Philox counter (j, 0, 1, 0), bit 0 of word 0)
+    const uint32_t bit = lane < 16 ? (philox_word0((uint32_t)lane, 0u, 1u, 0u, (uint32_t)a.seed,
+                                                   (uint32_t)(a.seed >> 32)) & 1u) : 0u;
+    rht_mask = (uint32_t)__ballot(bit);
+  }
+  float tscale = 0.0f;
+  if (RECIPE == R_TENSOR || RECIPE == R_NV) tscale = *a.scale;
+  __syncthreads();
+
+  const int rs = t & 15, cg = t >> 4;
+  // 16 rows x 4 columns: wv[i] = 4 bf16 of row 16 rs + i
+  uint2 wv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 16 * rs + i;
+    const int g = cg ^ ((row >> 4) & 14);
+    wv[i] = *(const uint2*)(tile + row * CT_PITCH + g * 8);
+  }
+  uint32_t amx = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t word = (c < 2) ? wv[i].x : wv[i].y;
+      v[i] = __uint_as_float((c & 1) ? (word & 0xFFFF0000u) : (word << 16));
+    }
+    const int col = 4 * cg + c;
+    const bool valid = (16 * rs < rlim) && (col < clim);
+    uint32_t mbits = 0;
+    if (RHT) {
+      rht16(v, rht_mask);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t x = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+        mbits = mbits > x ? mbits : x;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t x = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+        mbits = mbits > x ? mbits : x;
+      }
+    }
+    if (AMAX && valid) amx = amx > mbits ? amx : mbits;
+    const int64_t gc = c0 + col, gr = r0 + 16 * rs;
+    uint32_t rnd[16];
+    if (SR) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint64_t idx = (uint64_t)((gr + i) * a.C + gc);
+        rnd[i] = philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
+                              (uint32_t)(a.seed >> 32));
+      }
+    }
+    uint8_t* codes = (RECIPE == R_NV) ? a.col_codes + gc * (a.R / 2) + gr / 2 : a.col_codes + gc * a.R + gr;
+    uint8_t* sc8 = nullptr;
+    float* sc32 = nullptr;
+    bool writer = true;
+    if (RECIPE == R_MX) {
+      sc8 = (uint8_t*)a.col_scales + gc * (a.R / 32) + gr / 32;
+      writer = (rs & 1) == 0;
+    } else if (RECIPE == R_NV) {
+      sc8 = (uint8_t*)a.col_scales + gc * (a.R / 16) + gr / 16;
+    } else if (RECIPE == R_BLOCK128) {
+      sc32 = (float*)a.col_scales + gc * (a.R / 128) + gr / 128;
+      writer = (rs & 7) == 0;
+    }
+    quantize_segment<RECIPE, FMT, SR>(v, mbits, tscale, valid, codes, sc8, sc32, writer, rnd);
+  }
+  if (AMAX) {
+    __shared__ uint32_t s_part[4];
+    wg_amax_fold(amx, a.amax_out, s_part);
+  }
+}
+
 __global__ void zero_u32_kernel(uint32_t* p) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0u;
 }
 
 typedef void (*cast_fn)(CastArgs);
 
+typedef void (*cast_row_fn)(CastArgs, int64_t);
+
+// Kernel choice: single-orientation casts with 1D blocks take the row / col
+// kernels; 2D weight blocks and two-copy casts take the tile kernel.
+struct CastPick {
+  cast_fn tile = nullptr, col = nullptr;
+  cast_row_fn row = nullptr;
+};
+
 template <int RECIPE, int FMT, bool W2D, bool RHT, bool SR, bool AMAX>
-static cast_fn pick_orient(int mask) {
-  if (mask == PBS_ROW) return cast_tile_kernel<RECIPE, FMT, true, false, W2D, false, SR, AMAX>;
-  if (mask == PBS_COL) return cast_tile_kernel<RECIPE, FMT, false, true, W2D, RHT, SR, AMAX>;
-  return cast_tile_kernel<RECIPE, FMT, true, true, W2D, false, SR, AMAX>;
+static CastPick pick_orient(int mask) {
+  CastPick p;
+  if (!W2D && mask == PBS_ROW && !RHT) p.row = cast_row_kernel<RECIPE, FMT, SR, AMAX>;
+  else if (!W2D && mask == PBS_COL) p.col = cast_col_kernel<RECIPE, FMT, RHT, SR, AMAX>;
+  else if (mask == PBS_ROW) p.tile = cast_tile_kernel<RECIPE, FMT, true, false, W2D, false, SR, AMAX>;
+  else if (mask == PBS_COL) p.tile = cast_tile_kernel<RECIPE, FMT, false, true, W2D, RHT, SR, AMAX>;
+  else p.tile = cast_tile_kernel<RECIPE, FMT, true, true, W2D, false, SR, AMAX>;
+  return p;
 }
 
 }  // namespace pbs
@@ -394,7 +738,7 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
   a.col_scales = col_scales;
   a.seed = seed;
 
-  cast_fn fn = nullptr;
+  CastPick fn;
   const char* name = "";
   switch (recipe) {
     case PBS_RECIPE_FP8_CURRENT:
@@ -457,10 +801,24 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
   }
   if (amax_out) hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)amax_out);
   if (rows == 0 || cols == 0) return check_launch("pbs_cast");
-  dim3 grid((unsigned)ceil_div(cols, TILE), (unsigned)ceil_div(rows, TILE));
-  log_dispatch("%s recipe=%d fmt=%d orient=%d w2d=%d flags=%d rows=%lld cols=%lld grid=%ux%u", name,
-               (int)recipe, (int)fmt, orient_mask, (int)w2d, flags, (long long)rows, (long long)cols,
-               grid.x, grid.y);
-  hipLaunchKernelGGL(fn, grid, dim3(128), 0, stream, a);
+  if (fn.row) {
+    const int64_t nseg = rows * cols / 16;
+    // fused amax: fewer, longer-lived workgroups (one atomic at most each)
+    const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(nseg, 512), amax_out ? 2048 : 8192);
+    log_dispatch("%s_row recipe=%d fmt=%d flags=%d rows=%lld cols=%lld grid=%u", name, (int)recipe, (int)fmt,
+                 flags, (long long)rows, (long long)cols, grid);
+    hipLaunchKernelGGL(fn.row, dim3(grid), dim3(256), 0, stream, a, nseg);
+  } else if (fn.col) {
+    dim3 grid((unsigned)ceil_div(cols, CT_C), (unsigned)ceil_div(rows, CT_R));
+    log_dispatch("%s_col recipe=%d fmt=%d flags=%d rows=%lld cols=%lld grid=%ux%u", name, (int)recipe,
+                 (int)fmt, flags, (long long)rows, (long long)cols, grid.x, grid.y);
+    hipLaunchKernelGGL(fn.col, grid, dim3(256), 0, stream, a);
+  } else {
+    dim3 grid((unsigned)ceil_div(cols, TILE), (unsigned)ceil_div(rows, TILE));
+    log_dispatch("%s recipe=%d fmt=%d orient=%d w2d=%d flags=%d rows=%lld cols=%lld grid=%ux%u", name,
+                 (int)recipe, (int)fmt, orient_mask, (int)w2d, flags, (long long)rows, (long long)cols,
+                 grid.x, grid.y);
+    hipLaunchKernelGGL(fn.tile, grid, dim3(128), 0, stream, a);
+  }
   return check_launch("pbs_cast");
 }

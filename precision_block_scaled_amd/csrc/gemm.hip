@@ -365,6 +365,72 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// Epilogue shared by the kernels.  Lane (lr, lg) of tile (i, j) holds column
+// 32 j + lr and rows 32 i + 8 (r / 4) + 4 lg + r % 4, r = 0..15.  Every LDS
+// read of the main loop finished before its last barrier and no load is in
+// flight, so the staging area may overwrite the tiles and the scale ring.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], const GemmArgs& g, uint8_t* smem, int m0, int n0,
+                                           int w, int wm, int wn, int lane, float post) {
+  const int lr = lane & 31, lg = lane >> 5;
+  const bool full = (m0 + BM <= g.M) && (n0 + BN <= g.N);
+  if constexpr (OUT_BF16) {
+    // Lanes lr and lr ^ 1 swap half their values so that the even lane owns
+    // rows R, R+1 and the odd lane rows R+2, R+3 of the column pair.
+    const int par = lr & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float v0 = acc[i][j][4 * q] * post, v1 = acc[i][j][4 * q + 1] * post;
+          const float v2 = acc[i][j][4 * q + 2] * post, v3 = acc[i][j][4 * q + 3] * post;
+          const uint32_t own = par ? pk_bf16(v2, v3) : pk_bf16(v0, v1);
+          const uint32_t snd = par ? pk_bf16(v0, v1) : pk_bf16(v2, v3);
+          const uint32_t rcv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0xB1, 0xF, 0xF, false);
+          const uint32_t lo = par ? rcv : own, hi = par ? own : rcv;
+          const int row = wm * 128 + 32 * i + 8 * q + 4 * lg + 2 * par;
+          const int colb = (wn * 128 + 32 * j + (lr & ~1)) * 2;
+          *(uint32_t*)(smem + row * STG_BF16 + colb) = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          *(uint32_t*)(smem + (row + 1) * STG_BF16 + colb) = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+        }
+    __syncthreads();
+    const int ch = lane & 31;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int s = 64 * w + 2 * it + (lane >> 5);
+      const uint4 val = *(const uint4*)(smem + s * STG_BF16 + ch * 16);
+      const int grow = m0 + s, gcol = n0 + ch * 8;
+      if (full || (grow < g.M && gcol < g.N))
+        *(uint4*)((uint16_t*)g.C + (int64_t)grow * g.ldc + gcol) = val;
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = wm * 64 + 32 * ii + 8 * (r >> 2) + 4 * lg + (r & 3);
+            const int col = wn * 128 + 32 * j + lr;
+            *(float*)(smem + row * STG_F32 + col * 4) = acc[2 * p + ii][j][r] * post;
+          }
+      __syncthreads();
+#pragma unroll 4
+      for (int it = 0; it < 32; ++it) {
+        const int s = 32 * w + it;
+        const uint4 val = *(const uint4*)(smem + s * STG_F32 + lane * 16);
+        const int grow = m0 + (s >> 6) * 128 + 64 * p + (s & 63), gcol = n0 + lane * 4;
+        if (full || (grow < g.M && gcol < g.N)) *(uint4*)((float*)g.C + (int64_t)grow * g.ldc + gcol) = val;
+      }
+      if (p == 0) __syncthreads();
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The kernel.
 //
@@ -601,68 +667,277 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
     body(nk - 1, F_{}, F_{});
   }
 
-  // Epilogue.  Lane (lr, lg) of tile (i, j) holds column 32 j + lr and rows
-  // 32 i + 8 (r / 4) + 4 lg + r % 4, r = 0..15.  Every LDS read of the main
-  // loop finished before its last barrier and no load is in flight, so the
-  // staging area may overwrite the tiles and the scale ring.
   float post = 1.0f;
   if (SC == SC_TENSOR || SC == SC_NV) post = (*g.a_ts) * (*g.b_ts);
-  const bool full = (m0 + BM <= g.M) && (n0 + BN <= g.N);
-  if constexpr (OUT_BF16) {
-    // Lanes lr and lr ^ 1 swap half their values so that the even lane owns
-    // rows R, R+1 and the odd lane rows R+2, R+3 of the column pair.
-    const int par = lr & 1;
+  store_tile<OUT_BF16>(acc, g, smem, m0, n0, w, wm, wn, lane, post);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 kernel: raw E2M1 tiles in LDS, decoded per fragment.
+//
+// A K stage is 128 values = 64 bytes of every operand row, loaded straight
+// into LDS (global_load_lds_dwordx4), with the stage's 8 block-scale bytes
+// per row next to it.  Row r's 16-byte chunk c sits at r * 64 + ((c ^ key)
+// << 4), key = (r >> 2) & 3, which makes the 16-lane fragment reads
+// conflict-free.
+//
+// Lane (lr, lg) of a 32-row tile reads chunk 2 h + lg of its row for half
+// stage h: 32 values, of which dword d (values 8 d .. 8 d + 7 of the chunk)
+// is its operand of K=16 step d of the half.  The contraction index of the
+// stage is thereby permuted (step d of half h takes values 64 h + 8 d + {0..7}
+// from lane group 0 and 64 h + 32 + 8 d + {0..7} from lane group 1), the same
+// way for A and B, which leaves every sum over K unchanged.  Each operand
+// dword decodes exactly into 8 fp16: v_cvt_scalef32_pk_f16_fp4 (scale 1)
+// and a multiply by the E4M3 block scale converted to fp16 (the product has
+// at most 6 significant bits and lies in [2^-10, 2688]).  Values 8 d .. 8 d +
+// 7 of chunk 2 h + lg belong to block 4 h + 2 lg + d / 2 of the stage.
+//
+// Per half stage a wave runs 4 steps x 16 MFMAs (32x32x16 f16) and decodes
+// the next step's 8 operands (4 A and 4 B tiles) between them; the LDS reads
+// of the next half's raw chunks and the next stage's global loads ride on the
+// same MFMAs.  Phases A / B / C and the peeled tail are as in gemm_kernel.
+// ---------------------------------------------------------------------------
+constexpr int NV_ROWB = 64;                   // bytes per row per stage (K = 128)
+constexpr int NV_TILE = BM * NV_ROWB;         // 16 KB per operand per stage
+constexpr int NV_SC = BM * 8;                 // 8 scale bytes per row per stage
+constexpr int NV_SC_OFF = 4 * NV_TILE;
+
+__device__ __forceinline__ int nv_key(int row) { return (row >> 2) & 3; }
+
+struct NvDirect {
+  const uint8_t* base;
+  uint32_t off[4];
+};
+
+// load i (of 4) of wave w fills rows 16 q .. 16 q + 15, q = 4 w + i; lane l
+// owns row 16 q + l / 4, physical chunk l % 4.
+__device__ __forceinline__ void nv_direct_init(NvDirect& d, const uint8_t* p, int64_t ld, int rows0, int nrows,
+                                               int w) {
+  const int lane = threadIdx.x & 63;
+  d.base = p + (int64_t)rows0 * ld;
+  const int lim = nrows - rows0 - 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float v0 = acc[i][j][4 * q] * post, v1 = acc[i][j][4 * q + 1] * post;
-          const float v2 = acc[i][j][4 * q + 2] * post, v3 = acc[i][j][4 * q + 3] * post;
-          const uint32_t own = par ? pk_bf16(v2, v3) : pk_bf16(v0, v1);
-          const uint32_t snd = par ? pk_bf16(v0, v1) : pk_bf16(v2, v3);
-          const uint32_t rcv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0xB1, 0xF, 0xF, false);
-          const uint32_t lo = par ? rcv : own, hi = par ? own : rcv;
-          const int row = wm * 128 + 32 * i + 8 * q + 4 * lg + 2 * par;
-          const int colb = (wn * 128 + 32 * j + (lr & ~1)) * 2;
-          *(uint32_t*)(smem + row * STG_BF16 + colb) = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-          *(uint32_t*)(smem + (row + 1) * STG_BF16 + colb) = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
-        }
-    __syncthreads();
-    const int ch = lane & 31;
-#pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-      const int s = 64 * w + 2 * it + (lane >> 5);
-      const uint4 val = *(const uint4*)(smem + s * STG_BF16 + ch * 16);
-      const int grow = m0 + s, gcol = n0 + ch * 8;
-      if (full || (grow < g.M && gcol < g.N))
-        *(uint4*)((uint16_t*)g.C + (int64_t)grow * g.ldc + gcol) = val;
-    }
-  } else {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = wm * 64 + 32 * ii + 8 * (r >> 2) + 4 * lg + (r & 3);
-            const int col = wn * 128 + 32 * j + lr;
-            *(float*)(smem + row * STG_F32 + col * 4) = acc[2 * p + ii][j][r] * post;
-          }
-      __syncthreads();
-#pragma unroll 4
-      for (int it = 0; it < 32; ++it) {
-        const int s = 32 * w + it;
-        const uint4 val = *(const uint4*)(smem + s * STG_F32 + lane * 16);
-        const int grow = m0 + (s >> 6) * 128 + 64 * p + (s & 63), gcol = n0 + lane * 4;
-        if (full || (grow < g.M && gcol < g.N)) *(uint4*)((float*)g.C + (int64_t)grow * g.ldc + gcol) = val;
-      }
-      if (p == 0) __syncthreads();
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int trow = 16 * (4 * w + i) + (lane >> 2);
+    const int lc = (lane & 3) ^ nv_key(trow);
+    const int r = trow < lim ? trow : lim;
+    d.off[i] = (uint32_t)r * (uint32_t)ld + (uint32_t)(lc << 4);
   }
+}
+
+__device__ __forceinline__ void nv_direct_item(const NvDirect& d, int kt, uint8_t* tile, int w, int i) {
+  __builtin_amdgcn_global_load_lds(d.base + (int64_t)kt * NV_ROWB + d.off[i],
+                                   (lds_ptr_t)(tile + (4 * w + i) * 1024), 16, 0, 0);
+}
+
+// Scale rows: load i (of 2) of wave w fills rows 32 q .. 32 q + 31, q = 2 w + i,
+// one dword per lane (lane l: row 32 q + l / 2, dword l % 2).
+struct NvScale {
+  const uint8_t* p[2];
+};
+
+__device__ __forceinline__ void nv_scale_init(NvScale& s, const uint8_t* scale, int K, int rows0, int nrows,
+                                              bool twod, int w) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int row = rows0 + 32 * (2 * w + i) + (lane >> 1);
+    row = row < nrows ? row : nrows - 1;
+    const int64_t srow = twod ? row / 16 : row;
+    s.p[i] = scale + srow * (int64_t)(K / 16) + (lane & 1) * 4;
+  }
+}
+
+__device__ __forceinline__ void nv_scale_item(const NvScale& s, int kt, uint8_t* ring_slot, int w, int i) {
+  __builtin_amdgcn_global_load_lds(s.p[i] + (int64_t)kt * 8, (lds_ptr_t)(ring_slot + (2 * w + i) * 256), 4, 0, 0);
+}
+
+// 8 E2M1 codes (element 2k in the low nibble of byte k) times an fp16 scale,
+// as the fp16 operand of one K=16 step.
+__device__ __forceinline__ i32x4 nv_decode(uint32_t raw, f16x2 sc) {
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 0) * sc;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 1) * sc;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 2) * sc;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 3) * sc;
+  i32x4 r;
+  r.x = __builtin_bit_cast(int, p0);
+  r.y = __builtin_bit_cast(int, p1);
+  r.z = __builtin_bit_cast(int, p2);
+  r.w = __builtin_bit_cast(int, p3);
+  return r;
+}
+
+// The two E4M3 block scales of one lane for one half stage (blocks
+// 4 h + 2 lg and + 1), exactly as fp16 (v_cvt_scalef32_pk_f16_fp8, scale 1).
+__device__ __forceinline__ f16x2 nv_scale_pair(uint32_t dword_h, int sh) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(dword_h >> sh, 1.0f, false);
+}
+
+template <bool B2D, bool OUT_BF16>
+__global__ __launch_bounds__(NTHR, 1) void gemm_nvfp4_kernel(GemmArgs g) {
+  __shared__ __align__(16) uint8_t smem[SMEM];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  int tm, tn;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = g.K / 128;
+
+  auto tileA = [&](int buf) { return smem + (buf * 2 + 0) * NV_TILE; };
+  auto tileB = [&](int buf) { return smem + (buf * 2 + 1) * NV_TILE; };
+  auto ring = [&](int slot, int o) { return smem + NV_SC_OFF + (slot * 2 + o) * NV_SC; };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  NvDirect da, db;
+  NvScale sa, sb;
+  nv_direct_init(da, g.A, g.lda, m0, g.M, w);
+  nv_direct_init(db, g.B, g.ldb, n0, g.N, w);
+  nv_scale_init(sa, g.a_scale, g.K, m0, g.M, false, w);
+  nv_scale_init(sb, g.b_scale, g.K, n0, g.N, B2D, w);
+
+  constexpr int NVM = 12;              // global loads per stage and wave: 4 + 4 data, 2 + 2 scales
+  auto issue_item = [&](int kt, int v) {
+    const int buf = kt & 1, slot = kt % SC_RING;
+    if (v < 4) nv_direct_item(da, kt, tileA(buf), w, v);
+    else if (v < 8) nv_direct_item(db, kt, tileB(buf), w, v - 4);
+    else if (v < 10) nv_scale_item(sa, kt, ring(slot, 0), w, v - 8);
+    else nv_scale_item(sb, kt, ring(slot, 1), w, v - 10);
+  };
+
+  const int lr = lane & 31, lg = lane >> 5;
+  const int key = nv_key(lr);
+  const uint32_t lb[2] = {(uint32_t)(lr * NV_ROWB + (((0 + lg) ^ key) << 4)),
+                          (uint32_t)(lr * NV_ROWB + (((2 + lg) ^ key) << 4))};
+  const int sh = 16 * lg;
+  const int rowA = wm * 128, rowB = wn * 128;
+
+  // raw[0] / raw[1]: halves 0 / 1 of the stage being multiplied; raw[2]:
+  // half 1 of the next stage (read in phase C while raw[1] is still in use)
+  uint4 raw[3][8];          // [buffer][tile: 0-3 A, 4-7 B]
+  uint2 scw[8], scn[8];     // this stage's / the next stage's scale bytes per tile row
+  i32x4 dec[2][8];          // decoded operands of two consecutive K=16 steps
+  f16x2 sp[8];              // fp16 block-scale pair of the half being decoded
+
+  // raw read e (of 8) of half h from the tiles at pa / pb (this wave's rows);
+  // scale read e (of 8) from the ring slot rows at qa / qb
+  auto raw_item = [&](uint4* dst, const uint8_t* pa, const uint8_t* pb, int h, int e) {
+    const uint8_t* base = (e < 4) ? pa + (32 * e) * NV_ROWB : pb + (32 * (e - 4)) * NV_ROWB;
+    dst[e] = *(const uint4*)(base + lb[h]);
+  };
+  auto sc_item = [&](uint2* dst, const uint8_t* qa, const uint8_t* qb, int e) {
+    const uint8_t* base = (e < 4) ? qa + (32 * e) * 8 : qb + (32 * (e - 4)) * 8;
+    dst[e] = *(const uint2*)base;
+  };
+  auto set_scales = [&](const uint2* s, int h) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sp[e] = nv_scale_pair(h ? s[e].y : s[e].x, sh);
+  };
+  // decode operand e (of 8) of step d of the half held in raw[r] into dec[slot]
+  auto dec_item = [&](int slot, int r, int d, int e) {
+    const uint32_t rw = d == 0 ? raw[r][e].x : d == 1 ? raw[r][e].y : d == 2 ? raw[r][e].z : raw[r][e].w;
+    const f16x2 s2 = d < 2 ? __builtin_shufflevector(sp[e], sp[e], 0, 0) : __builtin_shufflevector(sp[e], sp[e], 1, 1);
+    dec[slot][e] = nv_decode(rw, s2);
+  };
+  auto mfma_item = [&](int slot, int m) {
+    const int i = m >> 2, j = m & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, dec[slot][i]),
+                                                       __builtin_bit_cast(f16x8, dec[slot][4 + j]), acc[i][j], 0, 0, 0);
+  };
+
+  // prologue: stage 0 in LDS, stage 1 in flight, stage 0 read, step 0 decoded
+#pragma unroll
+  for (int v = 0; v < NVM; ++v) issue_item(0, v);
+  wait_vm0();
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    raw_item(raw[0], tileA(0) + rowA * NV_ROWB, tileB(0) + rowB * NV_ROWB, 0, e);
+    raw_item(raw[1], tileA(0) + rowA * NV_ROWB, tileB(0) + rowB * NV_ROWB, 1, e);
+    sc_item(scw, ring(0, 0) + (rowA + lr) * 8, ring(0, 1) + (rowB + lr) * 8, e);
+  }
+  if (nk > 1) {
+#pragma unroll
+    for (int v = 0; v < NVM; ++v) issue_item(1, v);
+  }
+  set_scales(scw, 0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dec_item(0, 0, 0, e);
+
+  // One stage: 8 steps of 16 MFMAs on dec[d & 1]; between them the decode of
+  // the following step (one operand per 2 MFMAs).  All LDS reads of a stage
+  // (the next stage's raw chunks and scales) come first in phase C and all
+  // its global loads after them, so no LDS read ever waits behind a load
+  // that is still writing LDS.
+  auto body = [&](int kt, auto issue_c, auto next_c) {
+    constexpr bool ISSUE = decltype(issue_c)::value;
+    constexpr bool NEXT = decltype(next_c)::value;
+    const int buf = kt & 1, nslot = (kt + 1) % SC_RING;
+    const uint8_t* nxtA = tileA(buf ^ 1) + rowA * NV_ROWB;
+    const uint8_t* nxtB = tileB(buf ^ 1) + rowB * NV_ROWB;
+    const uint8_t* nqa = ring(nslot, 0) + (rowA + lr) * 8;
+    const uint8_t* nqb = ring(nslot, 1) + (rowB + lr) * 8;
+    // phase A: half 0 (raw[0]); its last step decodes half 1's first
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      if (d == 3) set_scales(scw, 1);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        mfma_item(d & 1, m);
+        __builtin_amdgcn_sched_barrier(0);
+        if ((m & 1) == 1) {
+          if (d < 3) dec_item((d + 1) & 1, 0, d + 1, m >> 1);
+          else dec_item(0, 1, 0, m >> 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // phase B
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // phase C: half 1 (raw[1]); steps 0-1 read the next stage (24 LDS
+    // reads), steps 2-3 issue the loads of stage kt+2 (12)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      if (d == 3 && NEXT) set_scales(scn, 0);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        mfma_item(d & 1, m);
+        __builtin_amdgcn_sched_barrier(0);
+        if (NEXT && d == 0 && m < 8) raw_item(raw[0], nxtA, nxtB, 0, m);
+        if (NEXT && d == 0 && m >= 8) raw_item(raw[2], nxtA, nxtB, 1, m - 8);
+        if (NEXT && d == 1 && m < 8) sc_item(scn, nqa, nqb, m);
+        if (ISSUE && d >= 2 && m < 12 && (m & 1) == 0) issue_item(kt + 2, (d - 2) * 6 + (m >> 1));
+        if ((m & 1) == 1) {
+          if (d < 3) dec_item((d + 1) & 1, 1, d + 1, m >> 1);
+          else if (NEXT) dec_item(0, 0, 0, m >> 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (NEXT) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        scw[e] = scn[e];
+        raw[1][e] = raw[2][e];
+      }
+    }
+  };
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  for (int kt = 0; kt < nk - 2; ++kt) body(kt, T_{}, T_{});
+  if (nk >= 2) body(nk - 2, F_{}, T_{});
+  body(nk - 1, F_{}, F_{});
+
+  store_tile<OUT_BF16>(acc, g, smem, m0, n0, w, wm, wn, lane, (*g.a_ts) * (*g.b_ts));
 }
 
 __global__ void zero_c_kernel(uint8_t* c, int64_t bytes) {
@@ -794,12 +1069,12 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
                   "pbs_gemm: NVFP4 takes E2M1 operands");
       PBS_REQUIRE(a_scale && b_scale && a_tensor_scale && b_tensor_scale, PBS_ERR_INVALID_ARG,
                   "pbs_gemm: NVFP4 needs block and tensor scales");
-      PBS_REQUIRE(K % 64 == 0, PBS_ERR_SHAPE, "pbs_gemm: NVFP4 needs K %% 64 == 0");
-      PBS_REQUIRE(((uintptr_t)a_scale & 1) == 0 && ((uintptr_t)b_scale & 1) == 0, PBS_ERR_INVALID_ARG,
-                  "pbs_gemm: NVFP4 block scales must be 2-byte aligned");
+      PBS_REQUIRE(K % 128 == 0, PBS_ERR_SHAPE, "pbs_gemm: NVFP4 needs K %% 128 == 0");
+      PBS_REQUIRE(((uintptr_t)a_scale & 3) == 0 && ((uintptr_t)b_scale & 3) == 0, PBS_ERR_INVALID_ARG,
+                  "pbs_gemm: NVFP4 block scales must be 4-byte aligned");
       g.lda = K / 2; g.ldb = K / 2;
-      fn = w2d ? pick_out<OP_F16, LD_NVFP4, LD_NVFP4, SC_NV, 0, 0, true>(bf16_out)
-               : pick_out<OP_F16, LD_NVFP4, LD_NVFP4, SC_NV, 0, 0, false>(bf16_out);
+      if (bf16_out) fn = w2d ? gemm_nvfp4_kernel<true, true> : gemm_nvfp4_kernel<false, true>;
+      else fn = w2d ? gemm_nvfp4_kernel<true, false> : gemm_nvfp4_kernel<false, false>;
       name = "gemm_nvfp4";
       break;
     }
