@@ -534,30 +534,55 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
         fb[0][i] = read2(lbp + i * 4096, lb, (uint32_t)((2 * i) << 4));
         fb[1][i] = read2(lbp + i * 4096, lb, (uint32_t)((4 ^ (2 * i)) << 4));
       }
-      const uint32_t* sca = ring(slot, 0);
-      const uint32_t* scb = ring(slot, 1);
+      // scale factors of this K block: a_scale of the lane's 16 rows per row
+      // tile (4 consecutive rows per 16-byte read), b_scale of its column per
+      // column tile; with 128x128 weight blocks the wave's 128 columns share
+      // one b_scale, which is folded into the row factors up front
+      const float* sca = (const float*)ring(slot, 0) + wm * 128 + lg * 4;
+      const float* scb = (const float*)ring(slot, 1) + wn * 128 + lr;
       float sbv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sbv[j] = __uint_as_float(scb[wn * 128 + 32 * j + lr]);
-      // the whole 128-long K block of each 32x32 tile accumulates into fresh
-      // registers, then acc += part * a_scale[row] * b_scale[col]
+      for (int j = 0; j < 4; ++j) sbv[j] = scb[32 * j];
+      // fac[i & 1]: the factors of row tile i, loaded as tile (i, 0) starts
+      // (the fold of tile (i - 1, 3) still reads the other entry)
+      float fac[2][16];
+      auto load_fac = [&](int i) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float sav[16];
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *(const float4*)(sca + 32 * i + 8 * q);
+          fac[i & 1][4 * q] = v.x;
+          fac[i & 1][4 * q + 1] = v.y;
+          fac[i & 1][4 * q + 2] = v.z;
+          fac[i & 1][4 * q + 3] = v.w;
+        }
+        if (B2D) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) fac[i & 1][r] *= sbv[0];
+        }
+      };
+      // each 32x32 tile's 128-long K block accumulates into fresh registers;
+      // the fold acc += part * a_scale[row] * b_scale[col] of tile t - 1 runs
+      // on the vector unit while the matrix core works on tile t
+      f32x16 part[2];
+      auto fold = [&](int t) {
+        const int i = t >> 2, j = t & 3;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          sav[r] = __uint_as_float(sca[wm * 128 + 32 * i + (r >> 2) * 8 + lg * 4 + (r & 3)]);
+          acc[i][j][r] = __builtin_fmaf(part[t & 1][r], B2D ? fac[i & 1][r] : fac[i & 1][r] * sbv[j], acc[i][j][r]);
+      };
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x16 part;
+      for (int t = 0; t < 16; ++t) {
+        const int i = t >> 2, j = t & 3;
+        if (j == 0) load_fac(i);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) part[r] = 0.0f;
-          part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0][i], fb[0][j], part, 0, 0, 0, 0, 0, 0);
-          part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[1][i], fb[1][j], part, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[r], sav[r] * sbv[j], acc[i][j][r]);
-        }
+        for (int r = 0; r < 16; ++r) part[t & 1][r] = 0.0f;
+        part[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0][i], fb[0][j], part[t & 1], 0, 0, 0, 0, 0, 0);
+        part[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[1][i], fb[1][j], part[t & 1], 0, 0, 0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t > 0) fold(t - 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      fold(15);
       wait_vm0();
       __syncthreads();
     }
