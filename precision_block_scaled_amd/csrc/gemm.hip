@@ -9,9 +9,9 @@
 // Mapping of each recipe onto the gfx950 MFMA instructions:
 //  BF16        v_mfma_f32_32x32x16_bf16.  Operands may be stored
 //              contraction-contiguous or, for the Dgrad / Wgrad products of
-//              natural-layout tensors, MN-contiguous; MN-contiguous tiles are
-//              transposed in registers (8x8 bf16 blocks) on their way into
-//              LDS, so the MFMA always reads contraction-contiguous rows.
+//              natural-layout tensors, MN-contiguous; MN-contiguous tiles go
+//              to LDS as stored and are transposed by the fragment reads
+//              (ds_read_b64_tr_b16).
 //  FP8 per-tensor  v_mfma_f32_32x32x64_f8f6f4 (format per operand: E4M3 or
 //              E5M2), scales applied once in the epilogue.
 //  FP8 1x128 / 128x128  the same instruction; each 128-long slice of the
@@ -24,24 +24,27 @@
 //              supply the E8M0 scale of one of its blocks, and the hardware
 //              applies it to that block's 32 products.
 //  NVFP4       E2M1 x E4M3 block scale has up to 6 significant bits, more
-//              than any 4-, 6- or 8-bit MFMA input holds, so the operands are
-//              decoded exactly into fp16 (E2M1 -> fp16 by conversion, times
-//              the block scale by an exact fp16 multiply: the product needs
-//              <= 6 bits and lies in [2^-10, 2688]) on their way into LDS,
-//              and the product runs on v_mfma_f32_32x32x16_f16.  The two
-//              fp32 tensor scales are applied in the epilogue.
+//              than any 4-, 6- or 8-bit MFMA input holds, and the E4M3 scale
+//              is no power of two, so it cannot ride on the instruction's
+//              E8M0 scale either.  The scales are applied in registers: raw
+//              E2M1 tiles sit in LDS and every wave decodes its operands
+//              exactly into fp16 (E2M1 -> fp16 by conversion, times the block
+//              scale by an exact fp16 multiply: the product needs <= 6 bits
+//              and lies in [2^-10, 2688]) right before
+//              v_mfma_f32_32x32x16_f16 (gemm_nvfp4_kernel).  The two fp32
+//              tensor scales are applied in the epilogue.
 //
 // Tiling: 256 x 256 output tile per workgroup of 256 threads (4 waves in a
 // 2 x 2 grid, 128 x 128 per wave = 4 x 4 MFMA 32x32 tiles, 256 fp32
 // accumulators per lane).  Each K stage moves 128 bytes per operand row
-// (64 bf16 / fp16, 128 fp8): 32 KB per operand, double-buffered in LDS
-// (128 KB).  Contraction-contiguous operands go global -> LDS directly
-// (global_load_lds_dwordx4, no registers), each lane fetching the 16-byte
-// chunk whose XOR-swizzled LDS slot it owns; the swizzle makes the MFMA
-// fragment reads (ds_read_b128) bank-conflict-free.  Operands that must be transformed
-// (MN-major bf16, NVFP4) are staged through registers.  Workgroups are
-// mapped to tiles so that each of the 8 XCDs (each with its own L2) works on
-// a contiguous, row-grouped range of tiles.
+// (64 bf16, 128 fp8, 256 E2M1): 32 KB per operand (16 KB for E2M1),
+// double-buffered in LDS.  Contraction-contiguous operands go global -> LDS
+// directly (global_load_lds_dwordx4, no registers), each lane fetching the
+// 16-byte chunk whose XOR-swizzled LDS slot it owns; the swizzle makes the
+// MFMA fragment reads (ds_read_b128) bank-conflict-free.  MN-major bf16
+// tiles are read with the transposing ds_read_b64_tr_b16.  Workgroups are mapped to tiles
+// so that each of the 8 XCDs (each with its own L2) works on a contiguous,
+// row-grouped range of tiles.
 #include "device.hpp"
 #include "host.hpp"
 
@@ -58,9 +61,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-enum { OP_BF16 = 0, OP_F16 = 1, OP_FP8 = 2 };                 // what the MFMA consumes
-enum { LD_KMAJOR = 0, LD_MNMAJOR = 1, LD_NVFP4 = 2 };         // how a tile reaches LDS
-enum { SC_NONE = 0, SC_TENSOR = 1, SC_MX = 2, SC_BLK = 3, SC_NV = 4 };
+enum { OP_BF16 = 0, OP_FP8 = 2 };                            // what the MFMA consumes
+enum { LD_KMAJOR = 0, LD_MNMAJOR = 1 };                      // how a tile reaches LDS
+enum { SC_NONE = 0, SC_TENSOR = 1, SC_MX = 2, SC_BLK = 3 };
 
 constexpr int BM = 256, BN = 256, NTHR = 256;
 constexpr int ROWB = 128;               // bytes per LDS row per K stage
@@ -95,8 +98,8 @@ struct GemmArgs {
 // LDS tile layout: row r, 16-byte chunk c lives at r * 128 + ((c ^ key(r)) << 4).
 // gfx950's LDS serves a 16-byte-per-lane access 16 lanes (256 bytes, 64
 // banks) at a time; key(r) = (r ^ r >> 1 ^ r >> 4) & 7 makes the MFMA
-// fragment reads (16 consecutive rows, one chunk) and the NVFP4 decode
-// stores conflict-free, and the MN-major bf16 stores at most 2-way (a plain
+// fragment reads (16 consecutive rows, one chunk) conflict-free, and the
+// MN-major bf16 stores at most 2-way (a plain
 // r & 7 leaves every fragment read 2-way conflicted).
 __device__ __forceinline__ int swz_key(int row) { return (row ^ (row >> 1) ^ (row >> 4)) & 7; }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ swz_key(row)) << 4); }
@@ -163,110 +166,35 @@ __device__ __forceinline__ void rowdw_issue(const RowDword& d, int kt, uint32_t*
   __builtin_amdgcn_global_load_lds(d.p + (int64_t)kt * 4, (lds_ptr_t)(ring_slot + 64 * w), 4, 0, 0);
 }
 
-// Register-staged operands.
-struct RegStage {
-  uint4 v[8];
-  uint32_t s[2];
+// MN-major bf16 (stored [K][MN], the Dgrad / Wgrad operands in natural
+// layout): the stage's 64 K rows of the tile's 256 MN values (512 bytes)
+// go to LDS as they are, rows K-indexed, with 16-byte chunk c of row k at
+// k * 512 + ((c ^ 4 (k & 3)) << 4).  Load i (of 8) of wave w fills rows
+// 2 q, 2 q + 1 (q = 8 w + i); lane l owns row 2 q + l / 32, physical chunk
+// l % 32.  Chunks past the MN extent re-read the last valid chunk.
+struct MnDirect {
+  const uint8_t* base;    // operand + mn0 * 2 (wave-uniform)
+  int64_t kstep;          // bytes per K stage: 64 rows
+  uint32_t off[8];
 };
 
-// MN-major bf16: stored [K][MN]; thread: k rows 8 kq .. 8 kq + 7, mn 8 mq .. 8 mq + 7.
-__device__ __forceinline__ void load_mn(RegStage& st, const uint8_t* base, int64_t ld, int rows0,
-                                        int nrows, int kt) {
-  const int t = threadIdx.x, kq = t >> 5, mq = t & 31;
-  int mn = rows0 + 8 * mq;
-  mn = mn < nrows ? mn : nrows - 8;
-  const int64_t k = (int64_t)kt * 64 + 8 * kq;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st.v[i] = *(const uint4*)(base + (k + i) * ld + (int64_t)mn * 2);
-}
-
-__device__ __forceinline__ void load_mn_item(RegStage& st, const uint8_t* base, int64_t ld, int rows0,
-                                             int nrows, int kt, int i) {
-  const int t = threadIdx.x, kq = t >> 5, mq = t & 31;
-  int mn = rows0 + 8 * mq;
-  mn = mn < nrows ? mn : nrows - 8;
-  const int64_t k = (int64_t)kt * 64 + 8 * kq;
-  st.v[i] = *(const uint4*)(base + (k + i) * ld + (int64_t)mn * 2);
-}
-
-__device__ __forceinline__ void store_mn(const RegStage& st, uint8_t* lds) {
-  const int t = threadIdx.x, kq = t >> 5, mq = t & 31;
+__device__ __forceinline__ void mn_direct_init(MnDirect& d, const uint8_t* p, int64_t ld, int mn0, int nmn, int w) {
+  const int lane = threadIdx.x & 63;
+  d.base = p + (int64_t)mn0 * 2;
+  d.kstep = 64 * ld;
+  const int lastc = (nmn - mn0 - 8) >> 3;     // last chunk of the tile with valid columns
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    // mn row 8 mq + i receives element i of each of the 8 loaded k rows
-    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t w_[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const uint4 v = st.v[r];
-      const int j = i >> 1;
-      w_[r] = j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
-    }
-    uint4 o;
-    o.x = __builtin_amdgcn_perm(w_[1], w_[0], sel);
-    o.y = __builtin_amdgcn_perm(w_[3], w_[2], sel);
-    o.z = __builtin_amdgcn_perm(w_[5], w_[4], sel);
-    o.w = __builtin_amdgcn_perm(w_[7], w_[6], sel);
-    *(uint4*)(lds + swz(8 * mq + i, kq)) = o;
+    const int row = 2 * (8 * w + i) + (lane >> 5);
+    int lc = (lane & 31) ^ (4 * (row & 3));
+    lc = lc < lastc ? lc : lastc;
+    d.off[i] = (uint32_t)row * (uint32_t)ld + (uint32_t)(lc << 4);
   }
 }
 
-// NVFP4: thread handles rows r = t / 2 and r + 128; 32 values (16 bytes) at
-// K offset 64 kt + 32 (t & 1); two E4M3 block-scale bytes for each.
-template <bool SCALE2D>
-__device__ __forceinline__ void load_nv(RegStage& st, const uint8_t* base, int64_t ld, int rows0,
-                                        int nrows, int kt, int K, const uint8_t* scale) {
-  const int t = threadIdx.x, half = t & 1;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    int row = rows0 + (t >> 1) + 128 * h;
-    row = row < nrows ? row : nrows - 1;
-    st.v[h] = *(const uint4*)(base + (int64_t)row * ld + (int64_t)kt * 32 + half * 16);
-    const int64_t kb = ((int64_t)kt * 64 + 32 * half) / 16;
-    const int64_t srow = SCALE2D ? row / 16 : row;
-    st.s[h] = *(const uint16_t*)(scale + srow * (K / 16) + kb);
-  }
-}
-
-// item it of 4: it / 2 = row half h, it % 2 = 0: 16 data bytes, 1: scale bytes
-template <bool SCALE2D>
-__device__ __forceinline__ void load_nv_item(RegStage& st, const uint8_t* base, int64_t ld, int rows0,
-                                             int nrows, int kt, int K, const uint8_t* scale, int it) {
-  const int t = threadIdx.x, half = t & 1, h = it >> 1;
-  int row = rows0 + (t >> 1) + 128 * h;
-  row = row < nrows ? row : nrows - 1;
-  if ((it & 1) == 0) {
-    st.v[h] = *(const uint4*)(base + (int64_t)row * ld + (int64_t)kt * 32 + half * 16);
-  } else {
-    const int64_t kb = ((int64_t)kt * 64 + 32 * half) / 16;
-    const int64_t srow = SCALE2D ? row / 16 : row;
-    st.s[h] = *(const uint16_t*)(scale + srow * (K / 16) + kb);
-  }
-}
-
-__device__ __forceinline__ void store_nv(const RegStage& st, uint8_t* lds) {
-  const int t = threadIdx.x, half = t & 1;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = (t >> 1) + 128 * h;
-    const uint32_t w[4] = {st.v[h].x, st.v[h].y, st.v[h].z, st.v[h].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t dcode = (st.s[h] >> (8 * (j >> 1))) & 0x7Fu;   // words 0,1: block 0; 2,3: block 1
-      const _Float16 dh = (_Float16)dec_e4m3_pos(dcode);              // exact: E4M3 fits fp16
-      const f16x2 dd = {dh, dh};
-      const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 0) * dd;
-      const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 1) * dd;
-      const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 2) * dd;
-      const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 3) * dd;
-      uint4 o;
-      o.x = __builtin_bit_cast(uint32_t, h0);
-      o.y = __builtin_bit_cast(uint32_t, h1);
-      o.z = __builtin_bit_cast(uint32_t, h2);
-      o.w = __builtin_bit_cast(uint32_t, h3);
-      *(uint4*)(lds + swz(r, half * 4 + j)) = o;
-    }
-  }
+__device__ __forceinline__ void mn_direct_item(const MnDirect& d, int kt, uint8_t* tile, int w, int i) {
+  __builtin_amdgcn_global_load_lds(d.base + kt * d.kstep + d.off[i], (lds_ptr_t)(tile + (w * 8 + i) * 1024), 16,
+                                   0, 0);
 }
 
 // XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a
@@ -302,15 +230,48 @@ struct Frags {
   i32x4 a[4][2], b[4][2];     // [tile][lower / upper 16 bytes]
 };
 
-// LDS read d (of 16) of a half stage: operand d / 8, tile (d / 2) % 4, part d % 2.
-template <int H>
-__device__ __forceinline__ void frag_read(Frags& f, int d, const uint8_t* la, const uint8_t* lbp, uint32_t lb) {
-  const int op = d >> 3, tile = (d >> 1) & 3, part = d & 1;
-  const uint32_t x = (uint32_t)((((4 * H) ^ (2 * tile)) << 4) ^ (part << 5));
-  const uint8_t* base = (op == 0 ? la : lbp) + tile * 4096;
-  const i32x4 v = *(const i32x4*)(base + (lb ^ x));
-  if (op == 0) f.a[tile][part] = v;
-  else f.b[tile][part] = v;
+// LDS reads of one operand for a half stage.  K-major: read d (of 8) is
+// tile d / 2, part d % 2 (one ds_read_b128).  MN-major: read d (of 16) is
+// tile d / 4, K=16 step s = (d / 2) % 2 of the half, 4-value quarter q = d % 2,
+// one ds_read_b64_tr_b16: within each 16-lane group, lane j addresses 4
+// consecutive MN values of K row 16 S + 8 lg + 4 q + j / 4 (S = 2 H + s), and
+// the transposing read hands lane i the 4 K values of MN column i.  The
+// per-lane part of that address is lm = (8 lg + j / 4) * 512 + 64 (j / 4) +
+// 16 (2 h' + (j % 4) / 2) + 8 (j % 2) + 256 wm (h' = lr / 16, j = lr % 16);
+// tile i XORs 64 i into it (the chunk swizzle 4 (k & 3) = 4 (j / 4)).
+template <int H, int LD>
+__device__ __forceinline__ void op_read(i32x4 (&x)[4][2], int d, const uint8_t* base, uint32_t lb) {
+  if (LD == LD_KMAJOR) {
+    const int tile = d >> 1, part = d & 1;
+    const uint32_t xo = (uint32_t)((((4 * H) ^ (2 * tile)) << 4) ^ (part << 5));
+    x[tile][part] = *(const i32x4*)(base + tile * 4096 + (lb ^ xo));
+  } else {
+    const int tile = d >> 2, s = (d >> 1) & 1, q = d & 1;
+    const int S = 2 * H + s;
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const uint8_t* p = base + (16 * S + 4 * q) * 512 + (lb ^ (uint32_t)(64 * tile));
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    const int2 w2 = __builtin_bit_cast(int2, v);
+    if (q == 0) {
+      x[tile][s].x = w2.x;
+      x[tile][s].y = w2.y;
+    } else {
+      x[tile][s].z = w2.x;
+      x[tile][s].w = w2.y;
+    }
+  }
+}
+
+template <int LD>
+constexpr int op_reads() { return LD == LD_KMAJOR ? 8 : 16; }
+
+// LDS read d of a half stage: A's reads first, then B's.
+template <int H, int LDA, int LDB>
+__device__ __forceinline__ void frag_read(Frags& f, int d, const uint8_t* la, const uint8_t* lbp, uint32_t lba,
+                                          uint32_t lbb) {
+  if (d < op_reads<LDA>()) op_read<H, LDA>(f.a, d, la, lba);
+  else op_read<H, LDB>(f.b, d - op_reads<LDA>(), lbp, lbb);
 }
 
 __device__ __forceinline__ i32x8 read2(const uint8_t* tile_row0, uint32_t lb, uint32_t x) {
@@ -344,12 +305,8 @@ __device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const Frags& f, co
   } else {
     const int s = m >> 4, i = (m >> 2) & 3, j = m & 3;
     const i32x4 a = f.a[i][s], b = f.b[j][s];
-    if (OP == OP_BF16)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                          acc[i][j], 0, 0, 0);
-    else
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
-                                                         acc[i][j], 0, 0, 0);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                        acc[i][j], 0, 0, 0);
   }
 }
 
@@ -437,8 +394,7 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], const GemmArgs& 
 // Schedule of K stage kt (LDS buffer b = kt & 1; f0 = fragments of its first
 // half, already in registers):
 //   phase A: MFMA(f0), interleaved with the reads f1 <- LDS b, second half
-//   phase B: (register-staged operands) wait for stage kt+1's loads and write
-//            them into LDS b^1; barrier: b^1 complete, nobody reads b any more
+//   phase B: barrier: b^1 complete, nobody reads b any more
 //   phase C: MFMA(f1), interleaved with the loads of stage kt+2 into b and
 //            the reads f0 <- LDS b^1, first half
 // so LDS reads and global loads ride between MFMAs and global loads get
@@ -476,10 +432,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   Direct da, db;
+  MnDirect ma, mb;
   RowDword sa, sb;
-  RegStage ra, rb;
   if (LDA == LD_KMAJOR) direct_init(da, g.A, g.lda, m0, g.M, w);
+  else mn_direct_init(ma, g.A, g.lda, m0, g.M, w);
   if (LDB == LD_KMAJOR) direct_init(db, g.B, g.ldb, n0, g.N, w);
+  else mn_direct_init(mb, g.B, g.ldb, n0, g.N, w);
   if (SC == SC_MX) {
     rowdw_init(sa, g.a_scale, g.K / 32, m0, g.M, 1, w);
     rowdw_init(sb, g.b_scale, g.K / 32, n0, g.N, 1, w);
@@ -490,29 +448,29 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
 
   auto issue = [&](int kt) {
     const int buf = kt & 1;
-    if (LDA == LD_KMAJOR) direct_issue(da, kt, tileA(buf), w);
-    else if (LDA == LD_MNMAJOR) load_mn(ra, g.A, g.lda, m0, g.M, kt);
-    else load_nv<false>(ra, g.A, g.lda, m0, g.M, kt, g.K, g.a_scale);
-    if (LDB == LD_KMAJOR) direct_issue(db, kt, tileB(buf), w);
-    else if (LDB == LD_MNMAJOR) load_mn(rb, g.B, g.ldb, n0, g.N, kt);
-    else load_nv<B2D>(rb, g.B, g.ldb, n0, g.N, kt, g.K, g.b_scale);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (LDA == LD_KMAJOR) direct_item(da, kt, tileA(buf), w, i);
+      else mn_direct_item(ma, kt, tileA(buf), w, i);
+      if (LDB == LD_KMAJOR) direct_item(db, kt, tileB(buf), w, i);
+      else mn_direct_item(mb, kt, tileB(buf), w, i);
+    }
     if (SC == SC_MX || SC == SC_BLK) {
       const int slot = kt % SC_RING;
       rowdw_issue(sa, kt, ring(slot, 0), w);
       rowdw_issue(sb, kt, ring(slot, 1), w);
     }
   };
-  auto commit = [&](int kt) {        // register-staged operands of stage kt -> LDS
-    const int buf = kt & 1;
-    if (LDA == LD_MNMAJOR) store_mn(ra, tileA(buf));
-    if (LDA == LD_NVFP4) store_nv(ra, tileA(buf));
-    if (LDB == LD_MNMAJOR) store_mn(rb, tileB(buf));
-    if (LDB == LD_NVFP4) store_nv(rb, tileB(buf));
-  };
-
   const int lr = lane & 31, lg = lane >> 5;     // row within a 32-tile, K group
   const uint32_t lb = (uint32_t)(lr * 128 + ((lg ^ swz_key(lr)) << 4));
-  const int offA = wm * 16384, offB = wn * 16384;   // the wave's 128 rows within a tile
+  // per-lane part of the MN-major transposing reads (see op_read)
+  const int jj = (lr & 15) >> 2;
+  const uint32_t lbm = (uint32_t)((8 * lg + jj) * 512 + 64 * jj + 32 * (lr >> 4) + 16 * ((lr & 3) >> 1) + 8 * (lr & 1));
+  const uint32_t lba = LDA == LD_KMAJOR ? lb : lbm + 256 * wm;
+  const uint32_t lbb = LDB == LD_KMAJOR ? lb : lbm + 256 * wn;
+  // where the wave's fragments start within a tile: K-major tiles hold its
+  // 128 rows at 128 x 128 B; MN-major tiles put its columns in lba / lbb
+  const int offA = LDA == LD_KMAJOR ? wm * 16384 : 0, offB = LDB == LD_KMAJOR ? wn * 16384 : 0;
 
   if constexpr (SC == SC_BLK) {
     // Block-128: the VALU fold needs both halves of a stage per tile, so this
@@ -587,12 +545,20 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
       __syncthreads();
     }
   } else {
-    constexpr bool REG_A = LDA != LD_KMAJOR, REG_B = LDB != LD_KMAJOR;
     constexpr int NMFMA = (OP == OP_FP8) ? 16 : 32;                // per half stage
-    constexpr int VM_A = LDA == LD_KMAJOR ? 8 : LDA == LD_MNMAJOR ? 8 : 4;
-    constexpr int VM_B = LDB == LD_KMAJOR ? 8 : LDB == LD_MNMAJOR ? 8 : 4;
+    constexpr int VM_A = 8;
+    constexpr int VM_B = 8;
     constexpr int VM_STAGE = VM_A + VM_B + (SC == SC_MX ? 2 : 0);
-    constexpr int DS_NEXT = 16 + (SC == SC_MX ? 8 : 0);
+    constexpr int DS_HALF = op_reads<LDA>() + op_reads<LDB>();       // fragment reads per half stage
+    constexpr int DS_NEXT = DS_HALF + (SC == SC_MX ? 8 : 0);
+    // The compiler makes a transposing LDS read wait for every LDS-DMA load
+    // still in flight.  With an MN-major operand the schedule therefore keeps
+    // them apart: phase A reads on its second half of MFMAs (the previous
+    // loads have landed by then), phase C reads on its first half and issues
+    // the loads on its second half.
+    constexpr bool SPLIT = LDA == LD_MNMAJOR || LDB == LD_MNMAJOR;
+    constexpr int A_DS0 = SPLIT ? NMFMA / 2 : 0;        // first MFMA carrying phase A's reads
+    constexpr int C_VM0 = SPLIT ? NMFMA / 2 : 0;        // first MFMA carrying phase C's loads
 
     Frags f0, f1;
     uint32_t mxa[4] = {0, 0, 0, 0}, mxb[4] = {0, 0, 0, 0};
@@ -603,13 +569,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
       const int buf = kt & 1;
       if (v < VM_A) {
         if (LDA == LD_KMAJOR) direct_item(da, kt, tileA(buf), w, v);
-        else if (LDA == LD_MNMAJOR) load_mn_item(ra, g.A, g.lda, m0, g.M, kt, v);
-        else load_nv_item<false>(ra, g.A, g.lda, m0, g.M, kt, g.K, g.a_scale, v);
+        else mn_direct_item(ma, kt, tileA(buf), w, v);
       } else if (v < VM_A + VM_B) {
         const int u = v - VM_A;
         if (LDB == LD_KMAJOR) direct_item(db, kt, tileB(buf), w, u);
-        else if (LDB == LD_MNMAJOR) load_mn_item(rb, g.B, g.ldb, n0, g.N, kt, u);
-        else load_nv_item<B2D>(rb, g.B, g.ldb, n0, g.N, kt, g.K, g.b_scale, u);
+        else mn_direct_item(mb, kt, tileB(buf), w, u);
       } else {
         const int slot = kt % SC_RING;
         if (v == VM_A + VM_B) rowdw_issue(sa, kt, ring(slot, 0), w);
@@ -625,11 +589,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
 
     issue(0);
     wait_vm0();
-    commit(0);
     __syncthreads();
     if (nk > 1) issue(1);
 #pragma unroll
-    for (int d = 0; d < 16; ++d) frag_read<0>(f0, d, tileA(0) + offA, tileB(0) + offB, lb);
+    for (int d = 0; d < DS_HALF; ++d) frag_read<0, LDA, LDB>(f0, d, tileA(0) + offA, tileB(0) + offB, lba, lbb);
     if (SC == SC_MX) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx_item(mxa, mxb, 0, e);
@@ -643,20 +606,19 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
       const uint8_t* curB = tileB(buf) + offB;
       const uint8_t* nxtA = tileA(buf ^ 1) + offA;
       const uint8_t* nxtB = tileB(buf ^ 1) + offB;
-      // phase A: MFMA(f0); the 16 reads of f1 ride on the first half of the MFMAs
+      // phase A: MFMA(f0); the reads of f1 ride on the first half of the MFMAs
 #pragma unroll
       for (int m = 0; m < NMFMA; ++m) {
         mfma_one<OP, SC, AFMT, BFMT>(acc, f0, mxa, mxb, 0, lg, m);
         __builtin_amdgcn_sched_barrier(0);
+        if (m >= A_DS0) {
 #pragma unroll
-        for (int d = share_lo(16, HALF, m); d < share_hi(16, HALF, m); ++d) frag_read<1>(f1, d, curA, curB, lb);
+          for (int d = share_lo(DS_HALF, HALF, m - A_DS0); d < share_hi(DS_HALF, HALF, m - A_DS0); ++d)
+            frag_read<1, LDA, LDB>(f1, d, curA, curB, lba, lbb);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       // phase B
-      if constexpr (NEXT && (REG_A || REG_B)) {
-        wait_vm0();
-        commit(kt + 1);
-      }
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       // phase C: MFMA(f1); reads of the next f0 (and MX words) on the first
@@ -670,11 +632,14 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int d = share_lo(NDS, HALF, m); d < share_hi(NDS, HALF, m); ++d) {
-          if (d < 16) frag_read<0>(f0, d, nxtA, nxtB, lb);
-          else mx_item(nxa, nxb, kt + 1, d - 16);
+          if (d < DS_HALF) frag_read<0, LDA, LDB>(f0, d, nxtA, nxtB, lba, lbb);
+          else mx_item(nxa, nxb, kt + 1, d - DS_HALF);
         }
+        if (m >= C_VM0) {
 #pragma unroll
-        for (int v = share_lo(NVM, NMFMA, m); v < share_hi(NVM, NMFMA, m); ++v) issue_item(kt + 2, v);
+          for (int v = share_lo(NVM, NMFMA - C_VM0, m - C_VM0); v < share_hi(NVM, NMFMA - C_VM0, m - C_VM0); ++v)
+            issue_item(kt + 2, v);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (NEXT && SC == SC_MX) {
@@ -693,7 +658,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   }
 
   float post = 1.0f;
-  if (SC == SC_TENSOR || SC == SC_NV) post = (*g.a_ts) * (*g.b_ts);
+  if (SC == SC_TENSOR) post = (*g.a_ts) * (*g.b_ts);
   store_tile<OUT_BF16>(acc, g, smem, m0, n0, w, wm, wn, lane, post);
 }
 
