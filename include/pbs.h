@@ -33,9 +33,9 @@
  *  - Tensors are row-major.  bf16 inputs are raw bf16 bit patterns.
  *  - Identical inputs give identical output bytes (amax reductions use an
  *    order-independent maximum).
- *  - Shapes: every dimension that a block or a GEMM tile runs along must
- *    be a multiple of that block (16, 32 or 128) or of the GEMM's tile
- *    multiple (128); otherwise PBS_ERR_SHAPE.
+ *  - Shapes: every dimension that a block runs along must be a multiple
+ *    of that block (16, 32 or 128), every cast dimension a multiple of 16,
+ *    and GEMM dimensions as stated at pbs_gemm; otherwise PBS_ERR_SHAPE.
  */
 #ifndef PBS_H
 #define PBS_H
@@ -214,7 +214,16 @@ pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t
  *    B = W [N, K]; DGRAD: A = dY [M, K], B = W stored [K, N]; WGRAD:
  *    A = X stored [K, M], B = dY stored [K, N].
  * c_fmt: PBS_FMT_F32 or PBS_FMT_BF16 (round-to-nearest-even).
- * Shapes: M, N multiples of 128; K a multiple of 128 (256 for NVFP4).
+ * Shapes (else PBS_ERR_SHAPE): M, N multiples of 16 (ragged 256-tiles are
+ *   masked); K a multiple of 128 (FP8 recipes, NVFP4) or 64 (BF16); each
+ *   stored operand row at most 16 MiB.  K == 0 writes zeros to C.
+ * Alignment (else PBS_ERR_INVALID_ARG): A, B, C 16-byte aligned; MXFP8
+ *   and NVFP4 block scales 4-byte aligned.
+ * Accuracy: fp32 accumulation; the 8-bit instructions (FP8 recipes) sum
+ *   each aligned group of 8 products in one step that keeps bits down to
+ *   2^-13 of the group's largest product; BF16 and NVFP4 (decoded exactly to
+ *   fp16 in registers) accumulate at fp32 precision.
+ * C is overwritten; calls on one stream are ordered, nothing is allocated.
  * ------------------------------------------------------------------- */
 pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, int64_t N, int64_t K,
                     const void* A, pbs_format a_fmt, const void* a_scale,
