@@ -148,13 +148,12 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
                                                  uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    uint32_t lo0 = 0xD2511F53u * c0;
-    uint32_t hi0 = __umulhi(0xD2511F53u, c0);
-    uint32_t lo1 = 0xCD9E8D57u * c2;
-    uint32_t hi1 = __umulhi(0xCD9E8D57u, c2);
-    uint32_t n0 = hi1 ^ c1 ^ k0;
-    uint32_t n2 = hi0 ^ c3 ^ k1;
-    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    // one 32x32->64 product each (v_mad_u64_u32), not separate lo / hi halves
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c0 = n0; c1 = (uint32_t)p1; c2 = n2; c3 = (uint32_t)p0;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -165,27 +164,21 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
 // 6; otherwise with lo <= |v| < hi adjacent E2M1 magnitudes, round up iff
 // r < ceil((|v| - lo) / (hi - lo) * 2^32).  |v| - lo is exact (Sterbenz or
 // lo = 0) and the scaling by 2^32 / (hi - lo) is a power of two, so the
-// threshold is computed exactly.
+// threshold is computed exactly.  Branch-free: below 2 the grid step is 0.5
+// (lo = floor(2|v|) / 2), in [2, 4) it is 1, in [4, 6) it is 2.
 __device__ __forceinline__ uint32_t sr_e2m1(float v, uint32_t r) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 28) & 0x8u;
-  float a = __uint_as_float(u & 0x7FFFFFFFu);
-  uint32_t code;
-  if (a >= 6.0f) {
-    code = 7u;
-  } else {
-    uint32_t lo_code;
-    float lo, scale;                                   // scale = 2^32 / (hi - lo)
-    if (a < 0.5f)      { lo_code = 0; lo = 0.0f; scale = 8589934592.0f; }
-    else if (a < 2.0f) { lo_code = (uint32_t)((a - 0.5f) * 2.0f) + 1u;   // 1,2,3 (exact floor)
-                         lo = 0.5f * (float)lo_code; scale = 8589934592.0f; }
-    else if (a < 4.0f) { lo_code = (a < 3.0f) ? 4u : 5u; lo = (a < 3.0f) ? 2.0f : 3.0f;
-                         scale = 4294967296.0f; }
-    else               { lo_code = 6u; lo = 4.0f; scale = 2147483648.0f; }
-    float x = (a - lo) * scale;
-    uint64_t T = (uint64_t)ceilf(x);
-    code = lo_code + (((uint64_t)r < T) ? 1u : 0u);
-  }
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 28) & 0x8u;
+  const float a = __uint_as_float(u & 0x7FFFFFFFu);
+  const bool r1 = a < 2.0f, r2 = a < 4.0f;
+  const float f1 = floorf(a * 2.0f);                   // exact: a * 2 is exact
+  const float f2 = floorf(a);
+  const float lo = r1 ? f1 * 0.5f : (r2 ? f2 : 4.0f);
+  const uint32_t lo_code = r1 ? (uint32_t)f1 : (r2 ? (f2 < 3.0f ? 4u : 5u) : 6u);
+  const float scale = r1 ? 8589934592.0f : (r2 ? 4294967296.0f : 2147483648.0f);   // 2^32 / step
+  const float T = ceilf((a - lo) * scale);             // 0 <= T <= 2^32, exact
+  const bool up = (T >= 4294967296.0f) || (r < (uint32_t)T);
+  const uint32_t code = a >= 6.0f ? 7u : lo_code + (up ? 1u : 0u);
   return sign | code;
 }
 
