@@ -19,6 +19,14 @@ dY; sub-channel and MXFP8 use E4M3 for every role; NVFP4 uses E2M1.
 Weights take 2D blocks (128x128 sub-channel, 16x16 NVFP4).  NVFP4 applies
 the 16x16 random Hadamard transform to both Wgrad operands (along M) and
 stochastic rounding to dY (both copies); everything else rounds to nearest.
+
+MXFP4 ("Accelerate LLM training with NVFP4 on Blackwell", "Technical
+deep-dive": the 32-value format NVFP4 refines) is built as the next recipe
+after the pages' six.  Reading taken: E2M1 values with one E8M0 scale per
+1x32 block along the contraction axis for every operand (each orientation
+quantized from the source, as MXFP8 does), and NVFP4's 4-bit training
+treatment kept: the Hadamard transform on both Wgrad operands and
+stochastic rounding of dY.
 """
 from __future__ import annotations
 
@@ -30,6 +38,8 @@ from . import recipes as R
 from .formats import bf16_to_f32
 
 RECIPES = ("bf16", "fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "nvfp4")
+NEXT_RECIPES = ("mxfp4",)
+ALL_RECIPES = RECIPES + NEXT_RECIPES
 
 
 @dataclass
@@ -54,6 +64,8 @@ class QOperand:
             return R.dequant_mxfp8(self.codes, self.scale)
         if self.recipe == "nvfp4":
             return R.dequant_nvfp4(self.codes, self.scale, self.tensor_scale_inv, self.weight_2d)
+        if self.recipe == "mxfp4":
+            return R.dequant_mxfp4(self.codes, self.scale)
         raise ValueError(self.recipe)
 
 
@@ -106,6 +118,16 @@ def quantize_operand(recipe, src, orient, x_bits, pass_, delayed_state=None, see
         return QOperand(recipe, "e2m1", packed, scale=d_codes, tensor_scale_inv=S_dec,
                         weight_2d=w2d, extra={"amax": A, "S_enc": S_enc, "rht": rht,
                                               "sr": sr is not None})
+    if recipe == "mxfp4":
+        t = bf16_to_f32(x_bits)
+        rht = pass_ == "wgrad"
+        if rht:
+            t = R.rht16_along_rows(t, seed)
+        t_o = t if orient == "row" else np.ascontiguousarray(t.T)
+        sr = R.sr_random_for(x_bits.shape, orient, seed) if src == "dy" else None
+        packed, e8 = R.quantize_mxfp4(t_o, sr_random=sr)
+        return QOperand(recipe, "e2m1", packed, scale=e8,
+                        extra={"rht": rht, "sr": sr is not None})
     raise ValueError(recipe)
 
 

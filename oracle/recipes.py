@@ -14,7 +14,7 @@ Conventions
   in both cases the quantization blocks run along the last (contiguous)
   axis of the returned array: the GEMM contraction axis.
 * Any scale division that overflows float32 gives FLT_MAX; a zero amax gives
-  scale 1 (per-tensor, sub-channel), E8M0 exponent -127 (MXFP8), or block
+  scale 1 (per-tensor, sub-channel), E8M0 exponent -127 (MXFP8, MXFP4), or block
   scale 0 with +-0 codes (NVFP4).  The pages do not say what happens in
   these corner cases; this is the reading taken.
 """
@@ -314,6 +314,44 @@ def sr_random_for(shape_mn, orient, seed=42):
 
 
 # ---------------------------------------------------------------------------
+# MXFP4: E2M1 values, E8M0 power-of-two scale per 32 values
+# ---------------------------------------------------------------------------
+_E8M0_THRESHOLDS_FP4 = 6.0 * np.ldexp(1.0, np.arange(255) - 127)   # 6 * 2**e, e = -127..127
+
+
+def mx4_block_exponent_code(a_b):
+    """E8M0 code c = e + 127 of the smallest e in [-127, 127] with a_b <= 6 * 2**e.
+
+    "Accelerate LLM training with NVFP4 on Blackwell", "Technical
+    deep-dive": NVFP4's 16-value micro-blocks are a reduction from MXFP4's
+    32.  MXFP4 keeps the MX scale (one E8M0 power of two per block, as for
+    MXFP8) over E2M1 values.  Reading taken for the exponent, the same as
+    for MXFP8 with E2M1's maximum 6: the smallest power of two that brings
+    the block maximum into range, so that no element saturates.
+    """
+    a = np.asarray(a_b, dtype=np.float64)
+    return np.searchsorted(_E8M0_THRESHOLDS_FP4, a, side="left").astype(np.uint8)
+
+
+def quantize_mxfp4(t, sr_random=None):
+    """MXFP4 cast of fp32 values ``t`` (quantization axis last, 1x32 blocks).
+
+    Per block b: c = mx4_block_exponent_code(max |t|), e = c - 127,
+    v = fp32(t * 2**-e), q = enc_E2M1(v) (round to nearest even), or the
+    stochastic rounding of v when ``sr_random`` (uint32, same shape as t)
+    is given.  A zero block gets c = 0 and +-0 codes.
+    Returns (packed codes [rows, cols/2], E8M0 codes [rows, cols/32]).
+    """
+    t = _f32(t)
+    a_b = _block_amax(t, 1, 32)
+    c = mx4_block_exponent_code(a_b)
+    e = c.astype(np.int64) - 127
+    v = (t.astype(np.float64) * np.ldexp(1.0, -_expand(e, 1, 32))).astype(np.float32)
+    q = E2M1.encode(v) if sr_random is None else sr_e2m1(v, sr_random)
+    return pack_e2m1(q), c
+
+
+# ---------------------------------------------------------------------------
 # Random Hadamard transform, 16x16
 # ---------------------------------------------------------------------------
 def rht_signs(seed=42):
@@ -366,6 +404,10 @@ def dequant_block128(codes, s_inv, weight_2d=False):
 
 def dequant_mxfp8(codes, e8m0_codes):
     return E4M3.decode(codes) * _expand(e8m0_decode(e8m0_codes), 1, 32)
+
+
+def dequant_mxfp4(packed, e8m0_codes):
+    return E2M1.decode(unpack_e2m1(packed)) * _expand(e8m0_decode(e8m0_codes), 1, 32)
 
 
 def dequant_nvfp4(packed, d_codes, S_dec, weight_2d=False):

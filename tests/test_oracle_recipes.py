@@ -21,7 +21,7 @@ from oracle import recipes as R
 from oracle.formats import E2M1, E4M3, E5M2, bf16_to_f32, e8m0_decode
 from oracle.philox import philox4x32_10, philox_word0_for_index
 from oracle.gemm_ref import gemm_ref, gemm_ref_bruteforce, check_gemm, ulp_bf16
-from oracle.passes import pass_operands, RECIPES
+from oracle.passes import pass_operands, RECIPES, ALL_RECIPES
 
 HERE = os.path.dirname(__file__)
 GOLDEN = json.load(open(os.path.join(HERE, "golden", "page_facts.json")))
@@ -311,6 +311,141 @@ def test_nvfp4_2d_col_is_transpose():
 
 
 # ---------------------------------------------------------------------------
+# MXFP4 (E2M1 values, E8M0 scale per 32)
+# ---------------------------------------------------------------------------
+def test_mx4_exponent_closed_form_all_bf16():
+    _, a = positive_finite_bf16()
+    got = R.mx4_block_exponent_code(a).astype(np.int64) - 127
+    f, ex = np.frexp(a.astype(np.float64))          # a = f * 2**ex, f in [0.5, 1)
+    mant = 2 * f                                     # in [1, 2)
+    E = ex - 1
+    # 6 * 2**e >= mant * 2**E  <=>  e >= E - 2 + log2(mant / 1.5)
+    want = np.clip(E - 2 + (mant > 1.5), -127, 127)
+    assert (got == want).all()
+    assert R.mx4_block_exponent_code(np.float32(0.0)) == 0
+
+
+def _brute_e2m1_code(q):
+    """Nearest E2M1 magnitude to |q| (an exact Fraction), ties to the even code; sign bit 8."""
+    mags = [Fraction(float(m)) for m in E2M1.magnitudes]
+    a = abs(q)
+    if a > 6:
+        code = 7
+    else:
+        d = [abs(a - m) for m in mags]
+        best = min(d)
+        cands = [i for i, di in enumerate(d) if di == best]
+        code = min(cands, key=lambda i: (i % 2, i))
+    return code | (8 if q < 0 else 0)
+
+
+def _mx4_brute_block(vals):
+    """(E8M0 code, E2M1 codes) of one 32-value block by direct search, exact arithmetic."""
+    fr = [Fraction(float(v)) for v in vals]
+    a = max(abs(f) for f in fr)
+    e = next(e for e in range(-127, 128) if a <= 6 * Fraction(2) ** e)
+    codes = []
+    for v, f in zip(vals, fr):
+        if f == 0:
+            codes.append(8 if np.signbit(v) else 0)
+        else:
+            codes.append(_brute_e2m1_code(Fraction(frac_to_f32(f / Fraction(2) ** e))))
+    return e + 127, codes
+
+
+def test_mxfp4_bruteforce():
+    rng = np.random.default_rng(31)
+    t = bf16_to_f32(W.activations(6, 128, seed=31)).copy()
+    t[0, :32] = 0.0
+    t[0, 5] = -0.0
+    t[1, :32] = rng.choice(np.float32([0.5, 1.5, 3, 6]), 32) * np.float32(2.0 ** 10)  # max 6*2^10: e = 10
+    t[1, 3] = 6 * 2.0 ** 10
+    t[1, 32:64] *= 0
+    t[1, 40] = np.float32(6 * 2.0 ** 10) * np.float32(1 + 2 ** -7)              # just above: e = 11
+    t[2, 64:96] = np.float32(2.0 ** -133)                                        # bf16 subnormals: e = -127
+    t[2, 70] = np.float32(2.0 ** -126)
+    t[3, 96:128] = np.float32(1.25) * rng.choice([-1, 1], 32)                    # ties at 1.25 -> 1.0
+    t[4, :32] = np.float32(3e38) * rng.random(32, dtype=np.float32)
+    packed, e8 = R.quantize_mxfp4(t)
+    codes = R.unpack_e2m1(packed)
+    assert codes.shape == t.shape and e8.shape == (6, 4)
+    for i in range(t.shape[0]):
+        for b in range(4):
+            ce, cc = _mx4_brute_block(t[i, 32 * b:32 * b + 32])
+            assert e8[i, b] == ce, (i, b)
+            assert list(codes[i, 32 * b:32 * b + 32]) == cc, (i, b)
+    assert e8[1, 0] == 127 + 10 and e8[1, 1] == 127 + 11 and e8[2, 2] == 0
+
+
+def test_mxfp4_no_saturation_and_half_scale_would():
+    x = W.activations(16, 512, seed=22)
+    t = bf16_to_f32(x)
+    packed, e8 = R.quantize_mxfp4(t)
+    tt = t.astype(np.float64).reshape(16, 16, 32)
+    scale = e8m0_decode(e8)[..., None]
+    assert (np.abs(tt) / scale <= 6.0).all()
+    bm = np.abs(tt).max(axis=-1)
+    e = e8.astype(np.int64) - 127
+    assert ((bm / np.ldexp(1.0, e - 1) > 6.0) | (e == -127)).all()
+    deq = R.dequant_mxfp4(packed, e8).reshape(16, 16, 32)
+    # within half an E2M1 step of the scaled value: 0.25 below 2, |v|/4 above
+    v = np.abs(tt) / scale
+    assert np.all(np.abs(deq - tt) <= scale * np.maximum(0.25, v / 4))
+
+
+def test_mxfp4_sr_extremes_and_grid():
+    t = bf16_to_f32(W.grads(4, 64, seed=23))
+    _, e8 = R.quantize_mxfp4(t)
+    scale = e8m0_decode(e8)
+    zeros = np.zeros(t.shape, np.uint32)
+    ones = np.full(t.shape, 0xFFFFFFFF, np.uint32)
+    up = E2M1.decode(R.unpack_e2m1(R.quantize_mxfp4(t, sr_random=zeros)[0]))
+    dn = E2M1.decode(R.unpack_e2m1(R.quantize_mxfp4(t, sr_random=ones)[0]))
+    mags = E2M1.magnitudes
+    for i in range(t.shape[0]):
+        for j in range(t.shape[1]):
+            v = Fraction(float(t[i, j])) / Fraction(float(scale[i, j // 32]))
+            a = abs(v)
+            lo = max(float(m) for m in mags if Fraction(float(m)) <= a)
+            hi = min([float(m) for m in mags if Fraction(float(m)) >= a])
+            sgn = -1.0 if v < 0 else 1.0
+            assert up[i, j] == sgn * hi and dn[i, j] == sgn * lo, (i, j, float(v))
+    # on-grid blocks never move
+    g = np.tile(np.float32([0, 0.5, 1, 1.5, 2, 3, 4, 6]), 4)[None, :] * np.float32(0.25)
+    r = philox_word0_for_index(np.arange(32), 42)[None, :]
+    p, e = R.quantize_mxfp4(g, sr_random=r)
+    assert (R.dequant_mxfp4(p, e) == g).all()
+
+
+@pytest.mark.parametrize("rec", ["nvfp4", "mxfp4"])
+def test_fp4_wgrad_with_rht_tracks_exact_product(rec):
+    """Both Wgrad operands carry the same orthogonal transform, so their product
+    still approximates X^T dY (a transform on one side only would not)."""
+    x = W.activations(256, 128, seed=25)
+    dy = W.grads(256, 96, seed=26)
+    A, B = pass_operands(rec, "wgrad", x=x, w=None, dy=dy)
+    assert A.extra["rht"] and B.extra["rht"] and B.extra["sr"] and not A.extra["sr"]
+    ref = bf16_to_f32(x).astype(np.float64).T @ bf16_to_f32(dy).astype(np.float64)
+    c, _ = gemm_ref(A.dequant(), B.dequant())
+    rel = np.linalg.norm(c - ref) / np.linalg.norm(ref)
+    assert rel < 0.2, rel
+    A0 = pass_operands(rec, "fprop", x=np.ascontiguousarray(x.T), w=np.ascontiguousarray(dy.T),
+                       dy=None)[0]
+    c0, _ = gemm_ref(A0.dequant(), B.dequant())
+    assert np.linalg.norm(c0 - ref) / np.linalg.norm(ref) > 0.5
+
+
+def test_mxfp4_coarser_than_nvfp4():
+    """NVFP4's 16-value blocks with fractional scales lose less than MXFP4's 32-value
+    power-of-two blocks on the same activations (the reason the pages give for NVFP4)."""
+    t = bf16_to_f32(W.activations(64, 1024, seed=24))
+    S_enc, S_dec = R.nvfp4_tensor_scales(R.amax(t))
+    e_nv = np.abs(R.dequant_nvfp4(*R.quantize_nvfp4(t, S_enc), S_dec) - t).mean()
+    e_mx = np.abs(R.dequant_mxfp4(*R.quantize_mxfp4(t)) - t).mean()
+    assert e_nv < e_mx
+
+
+# ---------------------------------------------------------------------------
 # Philox and stochastic rounding
 # ---------------------------------------------------------------------------
 def _rocrand_helper():
@@ -471,7 +606,7 @@ def test_tiny_case_all_recipes_gemm_close_to_bf16_product():
     tw = bf16_to_f32(w).astype(np.float64)
     ref = ta @ tw.T
     errs = {}
-    for rec in RECIPES:
+    for rec in ALL_RECIPES:
         st = None
         if rec == "fp8_delayed":
             st = {"x": R.DelayedScaling("e4m3"), "w": R.DelayedScaling("e4m3")}
@@ -483,7 +618,7 @@ def test_tiny_case_all_recipes_gemm_close_to_bf16_product():
     assert errs["bf16"] == 0.0
     # finer granularity tracks the bf16 product more closely
     assert errs["fp8_block128"] <= errs["fp8_current"] * 1.05
-    assert errs["mxfp8"] < 0.1 and errs["nvfp4"] < 0.3
+    assert errs["mxfp8"] < 0.1 and errs["nvfp4"] < 0.3 and errs["mxfp4"] < 0.3
     for rec in ("fp8_current", "fp8_delayed", "fp8_block128", "mxfp8"):
         assert errs[rec] < 0.1, (rec, errs[rec])
 
