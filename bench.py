@@ -33,6 +33,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 RECIPES = ["bf16", "fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "nvfp4"]
+# built beyond the pages' six (MXFP4: E2M1 with E8M0 per 32 on the FP4 matrix
+# rate); timed after the step and reported apart, never part of `value`
+NEXT_RECIPES = ["mxfp4"]
 PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2, "fp4": 10066.3}
 HBM_GBPS = 8000.0
 
@@ -52,6 +55,8 @@ def kernel_key(recipe, pass_):
         return ("gemm_fp8_block128_w2d" if pass_ != "wgrad" else "gemm_fp8_block128_1d"), "fp8"
     if recipe == "mxfp8":
         return "gemm_mxfp8", "fp8"
+    if recipe == "mxfp4":
+        return "gemm_mxfp4", "fp4"
     return ("gemm_nvfp4_w2d" if pass_ != "wgrad" else "gemm_nvfp4_1d"), "fp16"
 
 
@@ -178,6 +183,8 @@ def quant_bandwidth(runner, iters=5):
         ("mxfp8_cast_col", "mxfp8", "x", "col", "wgrad", 2 + 1 + 1 / 32),
         ("nvfp4_cast_row", "nvfp4", "x", "row", "fprop", 2 + 0.5 + 1 / 16),
         ("nvfp4_rht_sr_cast_col", "nvfp4", "dy", "col", "wgrad", 2 + 0.5 + 1 / 16),
+        ("mxfp4_cast_row", "mxfp4", "x", "row", "fprop", 2 + 0.5 + 1 / 32),
+        ("mxfp4_rht_sr_cast_col", "mxfp4", "dy", "col", "wgrad", 2 + 0.5 + 1 / 32),
     ]
     res = {}
     P = runner.P
@@ -207,9 +214,9 @@ def quant_bandwidth(runner, iters=5):
                               else (None, None, out.codes, out.scales))
             flags = 0
             scale = None
-            if r == "nvfp4":
+            if r in ("nvfp4", "mxfp4"):
                 flags = (P.PBS_FLAG_RHT16 if p == "wgrad" else 0) | (P.PBS_FLAG_SR if src == "dy" else 0)
-                scale = out._scal[1:2]
+                scale = out._scal[1:2] if r == "nvfp4" else None
             elif r == "fp8_current":
                 scale = out._scal[1:2]
             P.pbs_cast(rec, t, rows, cols, PL.fmt_for(r, src), rmask, 0, flags, 42, scale, None,
@@ -220,6 +227,40 @@ def quant_bandwidth(runner, iters=5):
         ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
         res[label] = {"ms": round(ms, 4), "GBps": round(bpe * t.numel() / ms / 1e6, 1)}
     return res
+
+
+def per_gemm_times(events):
+    """Per-(recipe, layer, pass) autocast and in-step GEMM times, and per-kernel totals."""
+    per = {}
+    for (r, name, p, M, N, K, e0, e1, e2) in events:
+        d = per.setdefault((r, name, p), {"auto": [], "gemm": [], "flop": 2.0 * M * N * K})
+        d["auto"].append(e0.elapsed_time(e2))
+        d["gemm"].append(e1.elapsed_time(e2))
+    kern = {}
+    for (r, name, p), d in per.items():
+        key, dt = kernel_key(r, p)
+        k = kern.setdefault(key, {"ms": 0.0, "flop": 0.0, "launches": 0, "dtype": dt})
+        k["ms"] += float(np.sum(d["gemm"]))
+        k["flop"] += d["flop"] * len(d["gemm"])
+        k["launches"] += len(d["gemm"])
+    return per, kern
+
+
+def recipe_table(runner, recipes, per, pre):
+    """ms per layer and TFLOP/s per recipe, autocast (and pre-quantized when timed)."""
+    out = {}
+    layer_flop = sum(2.0 * M * N * K for (_, _, M, N, K) in runner.gemms)
+    for r in recipes:
+        auto_ms = sum(float(np.median(per[(r, n, p)]["auto"])) for (n, p, *_) in runner.gemms)
+        ent = {"autocast_ms_per_layer": round(auto_ms, 3),
+               "autocast_TFLOPs": round(layer_flop / (auto_ms * 1e-3) / 1e12, 1)}
+        if pre:
+            pre_ms = sum(pre[(r, n, p)] for (n, p, *_) in runner.gemms)
+            ent["prequant_ms_per_layer"] = round(pre_ms, 3)
+            ent["prequant_TFLOPs"] = round(layer_flop / (pre_ms * 1e-3) / 1e12, 1)
+            ent["ms_per_gemm_prequant"] = {f"{n}.{p}": round(pre[(r, n, p)], 4) for (n, p, *_) in runner.gemms}
+        out[r] = ent
+    return out
 
 
 def cpu_baseline(seconds_target=20.0):
@@ -283,6 +324,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--tokens", type=int, default=15872)
     ap.add_argument("--recipes", default=",".join(RECIPES))
+    ap.add_argument("--next-recipes", default=",".join(NEXT_RECIPES),
+                    help="recipes beyond the six, timed after the step and reported apart")
     ap.add_argument("--prequant-iters", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip pre-quant and GB/s passes")
@@ -329,19 +372,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / a.steps
 
-    # per-GEMM autocast and GEMM-only (in-step) times
-    per = {}
-    for (r, name, p, M, N, K, e0, e1, e2) in events:
-        d = per.setdefault((r, name, p), {"auto": [], "gemm": [], "flop": 2.0 * M * N * K})
-        d["auto"].append(e0.elapsed_time(e2))
-        d["gemm"].append(e1.elapsed_time(e2))
-    kern = {}
-    for (r, name, p), d in per.items():
-        key, dt = kernel_key(r, p)
-        k = kern.setdefault(key, {"ms": 0.0, "flop": 0.0, "launches": 0, "dtype": dt})
-        k["ms"] += float(np.sum(d["gemm"]))
-        k["flop"] += d["flop"] * len(d["gemm"])
-        k["launches"] += len(d["gemm"])
+    per, kern = per_gemm_times(events)
     dom = max(kern.items(), key=lambda kv: kv[1]["ms"])
     dom_name, dk = dom
     avg_ms = dk["ms"] / dk["launches"]
@@ -353,18 +384,26 @@ def main():
     if not a.no_extras:
         log("pre-quantized GEMM timing")
         pre = runner.prequant_pass(recipes, a.prequant_iters)
-    per_recipe = {}
-    layer_flop = sum(2.0 * M * N * K for (_, _, M, N, K) in runner.gemms)
-    for r in recipes:
-        auto_ms = sum(float(np.median(per[(r, n, p)]["auto"])) for (n, p, *_) in runner.gemms)
-        ent = {"autocast_ms_per_layer": round(auto_ms, 3),
-               "autocast_TFLOPs": round(layer_flop / (auto_ms * 1e-3) / 1e12, 1)}
-        if pre:
-            pre_ms = sum(pre[(r, n, p)] for (n, p, *_) in runner.gemms)
-            ent["prequant_ms_per_layer"] = round(pre_ms, 3)
-            ent["prequant_TFLOPs"] = round(layer_flop / (pre_ms * 1e-3) / 1e12, 1)
-            ent["ms_per_gemm_prequant"] = {f"{n}.{p}": round(pre[(r, n, p)], 4) for (n, p, *_) in runner.gemms}
-        per_recipe[r] = ent
+    per_recipe = recipe_table(runner, recipes, per, pre)
+
+    next_recipes = [r for r in a.next_recipes.split(",") if r]
+    nxt = {}
+    if not a.no_extras and next_recipes:
+        log(f"next recipes {next_recipes} (reported apart from value)")
+        for _ in range(a.warmup):
+            runner.step(next_recipes)
+        ev2 = []
+        for _ in range(a.steps):
+            runner.step(next_recipes, ev2)
+        torch.cuda.synchronize()
+        per2, kern2 = per_gemm_times(ev2)
+        pre2 = runner.prequant_pass(next_recipes, a.prequant_iters)
+        nxt = recipe_table(runner, next_recipes, per2, pre2)
+        for key, k in kern2.items():
+            tf = k["flop"] / (k["ms"] * 1e-3) / 1e12
+            nxt.setdefault("kernels", {})[key] = {
+                "avg_launch_ms": round(k["ms"] / k["launches"], 4), "achieved_TFLOPs": round(tf, 1),
+                "peak": PEAK_TFLOPS[k["dtype"]], "frac": round(tf / PEAK_TFLOPS[k["dtype"]], 4)}
     qbw = {}
     if not a.no_extras:
         log("quantize-pass bandwidth")
@@ -397,6 +436,7 @@ def main():
                      "avg_launch_ms": round(avg_ms, 4), "launches": dk["launches"],
                      "traffic": traffic},
         "per_recipe": per_recipe,
+        "next_recipes": nxt,
         "quant_GBps": qbw,
         "cpu_baseline": cpu,
     }

@@ -78,8 +78,9 @@ typedef enum {
   PBS_RECIPE_FP8_BLOCK128 = 3, /* fp32 scale per 1x128 (act/grad) or
                                   128x128 (weight) block, E4M3 values       */
   PBS_RECIPE_MXFP8 = 4,        /* E8M0 scale per 32 values, E4M3 values     */
-  PBS_RECIPE_NVFP4 = 5         /* E2M1 values, E4M3 scale per 16 values (1x16
+  PBS_RECIPE_NVFP4 = 5,        /* E2M1 values, E4M3 scale per 16 values (1x16
                                   act/grad, 16x16 weight), fp32 per tensor  */
+  PBS_RECIPE_MXFP4 = 6         /* E2M1 values, E8M0 scale per 32 values     */
 } pbs_recipe;
 
 /* The three GEMMs of a linear layer ([LP] "Using autocast mode vs
@@ -100,9 +101,9 @@ typedef enum { PBS_FPROP = 0, PBS_DGRAD = 1, PBS_WGRAD = 2 } pbs_layout;
 
 /* Cast / amax flags. */
 #define PBS_FLAG_RHT16 1   /* apply the 16x16 random Hadamard transform along
-                              the rows first (NVFP4 Wgrad operands)         */
+                              the rows first (NVFP4 / MXFP4 Wgrad operands) */
 #define PBS_FLAG_SR 2      /* stochastic rounding of the E2M1 values
-                              (NVFP4 gradients)                             */
+                              (NVFP4 / MXFP4 gradients)                     */
 
 /* ---------------------------------------------------------------------
  * pbs_amax: amax_out[0] = max |x| over a bf16 tensor [rows, cols].
@@ -179,6 +180,13 @@ float* pbs_delayed_scale_inv(void* state); /* device address of `scale_inv` */
  *    flags: PBS_FLAG_RHT16 (col copy only, rows % 16 == 0; sign seed
  *    `seed`), PBS_FLAG_SR (stochastic rounding with Philox4x32-10, key =
  *    `seed`, counter = logical element index r * cols + c of x).
+ *  recipe MXFP4 ([FP4] "Technical deep-dive": the 32-value MX format that
+ *    NVFP4's 16-value blocks refine): fmt E2M1, codes packed as for NVFP4;
+ *    E8M0 scale bytes per 1x32 block along the contraction axis, [rows,
+ *    cols/32] / [cols, rows/32]; the exponent is the smallest e with
+ *    amax_b <= 6 * 2^e (no element saturates), codes = enc_E2M1(x * 2^-e).
+ *    Same flags as NVFP4 (PBS_FLAG_RHT16 col copy only, PBS_FLAG_SR).
+ *    `scale` unused.
  *  Outputs for an orientation not in orient_mask may be NULL.
  * ------------------------------------------------------------------- */
 pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t cols,
@@ -210,19 +218,23 @@ pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t
  *  - NVFP4: A, B packed E2M1 [M, K/2], [N, K/2]; a_scale = E4M3 [M, K/16];
  *    b_scale = E4M3 [N/16, K/16] for FPROP / DGRAD (weights, 2D) or
  *    [N, K/16] for WGRAD; a_tensor_scale / b_tensor_scale = S_dec of each.
+ *  - MXFP4: A, B packed E2M1 [M, K/2], [N, K/2]; a_scale = E8M0 [M, K/32],
+ *    b_scale = E8M0 [N, K/32]; tensor scales unused.
  * BF16 recipe: operands in their natural storage -- FPROP: A = X [M, K],
  *    B = W [N, K]; DGRAD: A = dY [M, K], B = W stored [K, N]; WGRAD:
  *    A = X stored [K, M], B = dY stored [K, N].
  * c_fmt: PBS_FMT_F32 or PBS_FMT_BF16 (round-to-nearest-even).
  * Shapes (else PBS_ERR_SHAPE): M, N multiples of 16 (ragged 256-tiles are
- *   masked); K a multiple of 128 (FP8 recipes, NVFP4) or 64 (BF16); each
- *   stored operand row at most 16 MiB.  K == 0 writes zeros to C.
- * Alignment (else PBS_ERR_INVALID_ARG): A, B, C 16-byte aligned; MXFP8
- *   and NVFP4 block scales 4-byte aligned.
+ *   masked); K a multiple of 128 (FP8 recipes, NVFP4), 256 (MXFP4) or 64
+ *   (BF16); each stored operand row at most 16 MiB.  K == 0 writes zeros
+ *   to C.
+ * Alignment (else PBS_ERR_INVALID_ARG): A, B, C 16-byte aligned; MXFP8,
+ *   MXFP4 and NVFP4 block scales 4-byte aligned.
  * Accuracy: fp32 accumulation; the 8-bit instructions (FP8 recipes) sum
  *   each aligned group of 8 products in one step that keeps bits down to
  *   2^-13 of the group's largest product; BF16 and NVFP4 (decoded exactly to
- *   fp16 in registers) accumulate at fp32 precision.
+ *   fp16 in registers) accumulate at fp32 precision; MXFP4 uses the same
+ *   instruction as the FP8 recipes with E2M1 inputs.
  * C is overwritten; calls on one stream are ordered, nothing is allocated.
  * ------------------------------------------------------------------- */
 pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, int64_t N, int64_t K,

@@ -29,6 +29,11 @@
 //    gradients.  d = enc_E4M3(fp32(fp32(amax_b / 6) * S_enc)), e_b =
 //    fp32(S_enc / d), codes = enc_E2M1(fp32(x * e_b)) or its stochastic
 //    rounding with Philox4x32-10 (counter = logical element index).
+//  MXFP4 -- "Accelerate LLM training with NVFP4 on Blackwell", "Technical
+//    deep-dive" (the 32-value MX format NVFP4 refines): E2M1 values, E8M0
+//    power-of-two scale per 32, the smallest exponent that brings the block
+//    maximum within 6; the Hadamard transform and stochastic rounding as for
+//    NVFP4.
 #include "device.hpp"
 #include "host.hpp"
 
@@ -36,7 +41,7 @@
 
 namespace pbs {
 
-enum { R_TENSOR = 0, R_BLOCK128 = 1, R_MX = 2, R_NV = 3 };
+enum { R_TENSOR = 0, R_BLOCK128 = 1, R_MX = 2, R_NV = 3, R_MX4 = 4 };
 enum { F_E4M3 = 0, F_E5M2 = 1 };
 
 constexpr int TILE = 128;
@@ -201,6 +206,38 @@ __device__ __forceinline__ void quantize_strip(const bf16_t* tile, int strip, in
       for (int i = 0; i < 16; ++i) code[i] = enc_e4m3(bf16_to_float(b1[i]) * inv);
       store16(out_codes + j + 16, code);
     }
+  } else if (RECIPE == R_MX4) {
+    for (int j = 0; j < len; j += 32) {
+      uint32_t b[32], q[32];
+      float v[32];
+      read16<ROWDIR>(tile, strip, j, b);
+      read16<ROWDIR>(tile, strip, j + 16, b + 16);
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        v[i] = bf16_to_float(b[i]);
+        const uint32_t x = b[i] & 0x7FFFu;
+        m = m > x ? m : x;
+      }
+      const uint32_t c = mx4_e8m0_from_f32_amax(m << 16);
+      const float inv = mx_inv_scale(c);
+      out_scales8[j / 32] = (uint8_t)c;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float x = v[i] * inv;
+        if (SR) {
+          const int64_t gr = ROWDIR ? g_row0 : g_row0 + j + i;
+          const int64_t gc = ROWDIR ? g_col0 + j + i : g_col0;
+          const uint64_t idx = (uint64_t)(gr * a.C + gc);
+          q[i] = sr_e2m1(x, philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
+                                         (uint32_t)(a.seed >> 32)));
+        } else {
+          q[i] = enc_e2m1(x);
+        }
+      }
+      *(uint2*)(out_codes + j / 2) = pack_e2m1_16(q);
+      *(uint2*)(out_codes + j / 2 + 8) = pack_e2m1_16(q + 16);
+    }
   } else {  // R_NV
     const float S = tile_scale;
     for (int j = 0; j < len; j += 16) {
@@ -296,7 +333,8 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
 
   if (ROW && t < rlim) {
     const int64_t gr = r0 + t;
-    uint8_t* codes = (RECIPE == R_NV) ? a.row_codes + gr * (a.C / 2) + c0 / 2 : a.row_codes + gr * a.C + c0;
+    uint8_t* codes = (RECIPE == R_NV || RECIPE == R_MX4) ? a.row_codes + gr * (a.C / 2) + c0 / 2
+                                                         : a.row_codes + gr * a.C + c0;
     uint8_t* sc8 = nullptr;
     float* sc32 = nullptr;
     bool writer = true;
@@ -304,7 +342,7 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
       sc32 = W2D ? (float*)a.row_scales + (r0 / 128) * (a.C / 128) + c0 / 128
                  : (float*)a.row_scales + gr * (a.C / 128) + c0 / 128;
     if (RECIPE == R_BLOCK128 && W2D) writer = (t == 0);
-    if (RECIPE == R_MX) sc8 = (uint8_t*)a.row_scales + gr * (a.C / 32) + c0 / 32;
+    if (RECIPE == R_MX || RECIPE == R_MX4) sc8 = (uint8_t*)a.row_scales + gr * (a.C / 32) + c0 / 32;
     if (RECIPE == R_NV) {
       sc8 = W2D ? (uint8_t*)a.row_scales + (gr / 16) * (a.C / 16) + c0 / 16
                 : (uint8_t*)a.row_scales + gr * (a.C / 16) + c0 / 16;
@@ -315,7 +353,8 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
   }
   if (COL && t < clim) {
     const int64_t gc = c0 + t;
-    uint8_t* codes = (RECIPE == R_NV) ? a.col_codes + gc * (a.R / 2) + r0 / 2 : a.col_codes + gc * a.R + r0;
+    uint8_t* codes = (RECIPE == R_NV || RECIPE == R_MX4) ? a.col_codes + gc * (a.R / 2) + r0 / 2
+                                                         : a.col_codes + gc * a.R + r0;
     uint8_t* sc8 = nullptr;
     float* sc32 = nullptr;
     bool writer = true;
@@ -323,7 +362,7 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
       sc32 = W2D ? (float*)a.col_scales + (c0 / 128) * (a.R / 128) + r0 / 128
                  : (float*)a.col_scales + gc * (a.R / 128) + r0 / 128;
     if (RECIPE == R_BLOCK128 && W2D) writer = (t == 0);
-    if (RECIPE == R_MX) sc8 = (uint8_t*)a.col_scales + gc * (a.R / 32) + r0 / 32;
+    if (RECIPE == R_MX || RECIPE == R_MX4) sc8 = (uint8_t*)a.col_scales + gc * (a.R / 32) + r0 / 32;
     if (RECIPE == R_NV) {
       sc8 = W2D ? (uint8_t*)a.col_scales + (gc / 16) * (a.R / 16) + r0 / 16
                 : (uint8_t*)a.col_scales + gc * (a.R / 16) + r0 / 16;
@@ -410,7 +449,8 @@ __device__ __forceinline__ void bf16x16_to_f32(const uint32_t* w, float* v) {
 // codes to `codes` (16 bytes for FP8, 8 for E2M1) and, from the lane that
 // owns the block's first segment, the block scale.
 //  RECIPE R_TENSOR: s = tensor scale; R_MX: 2-lane blocks; R_BLOCK128:
-//  8-lane blocks; R_NV: one-segment blocks with encode scale S = tscale.
+//  8-lane blocks; R_NV: one-segment blocks with encode scale S = tscale;
+//  R_MX4: 2-lane blocks, E2M1 codes.
 template <int RECIPE, int FMT, bool SR>
 __device__ __forceinline__ void quantize_segment(const float* v, uint32_t mbits, float tscale, bool valid,
                                                  uint8_t* codes, uint8_t* sc8, float* sc32, bool writer,
@@ -434,6 +474,24 @@ __device__ __forceinline__ void quantize_segment(const float* v, uint32_t mbits,
     o.z = hw_fp8x4<FMT>(v[8] * s, v[9] * s, v[10] * s, v[11] * s);
     o.w = hw_fp8x4<FMT>(v[12] * s, v[13] * s, v[14] * s, v[15] * s);
     if (valid) *(uint4*)codes = o;
+  } else if (RECIPE == R_MX4) {
+    const uint32_t c = mx4_e8m0_from_f32_amax(group_max<2>(mbits));
+    const float s = mx_inv_scale(c);
+    if (valid && writer) *sc8 = (uint8_t)c;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = v[i] * s;
+    uint2 o;
+    if (SR) {
+      uint32_t q[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) q[i] = sr_e2m1(x[i], rnd[i]);
+      o = pack_e2m1_16(q);
+    } else {
+      o.x = hw_fp4x8(x);
+      o.y = hw_fp4x8(x + 8);
+    }
+    if (valid) *(uint2*)codes = o;
   } else {  // R_NV
     const float S = tscale;
     const float a_b = __uint_as_float(mbits);
@@ -528,11 +586,12 @@ __global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg)
                                 (uint32_t)(a.seed >> 32));
         }
       }
-      uint8_t* codes = (RECIPE == R_NV) ? a.row_codes + row * (a.C / 2) + seg * 8 : a.row_codes + row * a.C + seg * 16;
+      uint8_t* codes = (RECIPE == R_NV || RECIPE == R_MX4) ? a.row_codes + row * (a.C / 2) + seg * 8
+                                                           : a.row_codes + row * a.C + seg * 16;
       uint8_t* sc8 = nullptr;
       float* sc32 = nullptr;
       bool writer = true;
-      if (RECIPE == R_MX) {
+      if (RECIPE == R_MX || RECIPE == R_MX4) {
         sc8 = (uint8_t*)a.row_scales + row * (a.C / 32) + seg / 2;
         writer = (seg & 1) == 0;
       } else if (RECIPE == R_NV) {
@@ -642,11 +701,12 @@ __global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
                               (uint32_t)(a.seed >> 32));
       }
     }
-    uint8_t* codes = (RECIPE == R_NV) ? a.col_codes + gc * (a.R / 2) + gr / 2 : a.col_codes + gc * a.R + gr;
+    uint8_t* codes = (RECIPE == R_NV || RECIPE == R_MX4) ? a.col_codes + gc * (a.R / 2) + gr / 2
+                                                         : a.col_codes + gc * a.R + gr;
     uint8_t* sc8 = nullptr;
     float* sc32 = nullptr;
     bool writer = true;
-    if (RECIPE == R_MX) {
+    if (RECIPE == R_MX || RECIPE == R_MX4) {
       sc8 = (uint8_t*)a.col_scales + gc * (a.R / 32) + gr / 32;
       writer = (rs & 1) == 0;
     } else if (RECIPE == R_NV) {
@@ -715,8 +775,8 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
   PBS_REQUIRE(!col || col_codes, PBS_ERR_INVALID_ARG, "pbs_cast: col_codes is null");
   PBS_REQUIRE(!row || ((uintptr_t)row_codes & 15) == 0, PBS_ERR_INVALID_ARG, "pbs_cast: row_codes not 16-byte aligned");
   PBS_REQUIRE(!col || ((uintptr_t)col_codes & 15) == 0, PBS_ERR_INVALID_ARG, "pbs_cast: col_codes not 16-byte aligned");
-  PBS_REQUIRE(!rht && !sr || recipe == PBS_RECIPE_NVFP4, PBS_ERR_UNSUPPORTED,
-              "pbs_cast: RHT16 / SR flags apply to the NVFP4 recipe only");
+  PBS_REQUIRE(!rht && !sr || recipe == PBS_RECIPE_NVFP4 || recipe == PBS_RECIPE_MXFP4, PBS_ERR_UNSUPPORTED,
+              "pbs_cast: RHT16 / SR flags apply to the NVFP4 and MXFP4 recipes only");
   PBS_REQUIRE(!rht || orient_mask == PBS_COL, PBS_ERR_UNSUPPORTED,
               "pbs_cast: RHT16 runs along the rows and produces the col copy only");
   PBS_REQUIRE(!w2d || recipe == PBS_RECIPE_FP8_BLOCK128 || recipe == PBS_RECIPE_NVFP4,
@@ -792,6 +852,21 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
         fn = sr ? pick_orient<R_NV, F_E4M3, false, false, true, false>(orient_mask)
                 : pick_orient<R_NV, F_E4M3, false, false, false, false>(orient_mask);
       name = "cast_nvfp4";
+      break;
+    }
+    case PBS_RECIPE_MXFP4: {
+      PBS_REQUIRE(fmt == PBS_FMT_E2M1, PBS_ERR_UNSUPPORTED, "pbs_cast: MXFP4 takes E2M1");
+      PBS_REQUIRE((!row || cols % 32 == 0) && (!col || rows % 32 == 0), PBS_ERR_SHAPE,
+                  "pbs_cast: MXFP4 needs the blocked dim to be a multiple of 32");
+      PBS_REQUIRE((!row || row_scales) && (!col || col_scales), PBS_ERR_INVALID_ARG,
+                  "pbs_cast: block scales output is null");
+      if (rht)
+        fn = sr ? pick_orient<R_MX4, F_E4M3, false, true, true, false>(orient_mask)
+                : pick_orient<R_MX4, F_E4M3, false, true, false, false>(orient_mask);
+      else
+        fn = sr ? pick_orient<R_MX4, F_E4M3, false, false, true, false>(orient_mask)
+                : pick_orient<R_MX4, F_E4M3, false, false, false, false>(orient_mask);
+      name = "cast_mxfp4";
       break;
     }
     case PBS_RECIPE_BF16:

@@ -132,6 +132,17 @@ __device__ __forceinline__ uint32_t mx_e8m0_from_bf16_amax(uint32_t abits) {
   return (uint32_t)c;
 }
 
+// MXFP4 E8M0 code from the fp32 bits of a block maximum a (sign clear):
+// the smallest e in [-127, 127] with a <= 6 * 2^e.  With a = m * 2^E, m in
+// [1, 2): e = E - 2 if m <= 1.5, else E - 1; zero and fp32 subnormals give
+// the clamp -127.  Returns c = e + 127.
+__device__ __forceinline__ uint32_t mx4_e8m0_from_f32_amax(uint32_t abits) {
+  const int E = (int)(abits >> 23);
+  int c = E - 2 + (((abits & 0x7FFFFFu) > 0x400000u) ? 1 : 0);
+  c = c < 0 ? 0 : (c > 254 ? 254 : c);
+  return (uint32_t)c;
+}
+
 // 2^(127 - c) as float for an E8M0 code c in [0, 254]: the factor that
 // divides a block by its scale.  Normal for every c that can occur (c <= 247).
 __device__ __forceinline__ float mx_inv_scale(uint32_t c) {

@@ -61,7 +61,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-enum { OP_BF16 = 0, OP_FP8 = 2 };                            // what the MFMA consumes
+enum { OP_BF16 = 0, OP_FP8 = 2, OP_FP4 = 3 };               // what the MFMA consumes
 enum { LD_KMAJOR = 0, LD_MNMAJOR = 1 };                      // how a tile reaches LDS
 enum { SC_NONE = 0, SC_TENSOR = 1, SC_MX = 2, SC_BLK = 3 };
 
@@ -73,7 +73,12 @@ constexpr int SC_RING = 3;
 constexpr int STG_BF16 = 544;           // epilogue staging row pitch, bf16 output (256 rows)
 constexpr int STG_F32 = 1056;           // epilogue staging row pitch, fp32 output (128 rows a pass)
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
-constexpr int SMEM = cmax(SC_OFF + SC_RING * 2 * BM * 4, cmax(256 * STG_BF16, 128 * STG_F32));
+// scale dwords per row per stage: MXFP8 4 E8M0 bytes (128 values), MXFP4 8 (256)
+constexpr int sc_dw(int op) { return op == OP_FP4 ? 2 : 1; }
+constexpr int smem_bytes(int op) {
+  return cmax(SC_OFF + SC_RING * 2 * BM * 4 * sc_dw(op), cmax(256 * STG_BF16, 128 * STG_F32));
+}
+constexpr int SMEM = smem_bytes(OP_FP8);
 constexpr int GROUP_M = 8;              // tile rows walked together (L2 reuse)
 constexpr int NXCD = 8;
 
@@ -164,6 +169,14 @@ __device__ __forceinline__ void rowdw_init(RowDword& d, const uint8_t* scale, in
 
 __device__ __forceinline__ void rowdw_issue(const RowDword& d, int kt, uint32_t* ring_slot, int w) {
   __builtin_amdgcn_global_load_lds(d.p + (int64_t)kt * 4, (lds_ptr_t)(ring_slot + 64 * w), 4, 0, 0);
+}
+
+// Dword q of DW per row per stage (MXFP4: 8 scale bytes per row and stage),
+// into plane q of the ring slot (planes BM dwords apart).
+template <int DW>
+__device__ __forceinline__ void rowdw_issue_q(const RowDword& d, int kt, int q, uint32_t* ring_slot, int w) {
+  __builtin_amdgcn_global_load_lds(d.p + (int64_t)kt * 4 * DW + 4 * q, (lds_ptr_t)(ring_slot + q * BM + 64 * w), 4,
+                                   0, 0);
 }
 
 // MN-major bf16 (stored [K][MN], the Dgrad / Wgrad operands in natural
@@ -286,11 +299,28 @@ __device__ __forceinline__ i32x8 cat(const i32x4 (&p)[2]) {
 
 // MFMA m of one half stage (every recipe but block-128): 8-bit operands
 // issue 16 (tile i = m / 4, j = m % 4, one K=64 step), 16-bit operands 32
-// (K=16 step s = m / 16 of the half, then i, j).
+// (K=16 step s = m / 16 of the half, then i, j), E2M1 operands 32 (K=64
+// step p = m / 16 of the half, then i, j).
+//
+// E2M1 on v_mfma_scale_f32_32x32x64_f8f6f4 (format 4): a lane's operand is
+// its first four dwords, the 32 consecutive values K 32 lg .. 32 lg + 31 of
+// the step (low nibble first), and the lane's E8M0 scale applies to exactly
+// those 32 values (probed on gfx950).  One 16-byte LDS chunk is therefore one
+// lane's whole operand and one MX block: step p of half h takes chunk
+// 4 h + 2 p + lg, whose scale is byte 2 p + lg of the row's scale dword h.
+// mxa / mxb then hold the words of dword h.
 template <int OP, int SC, int AFMT, int BFMT>
 __device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const Frags& f, const uint32_t* mxa,
                                          const uint32_t* mxb, int h, int lg, int m) {
-  if (OP == OP_FP8) {
+  if (OP == OP_FP4) {
+    const int p = m >> 4, i = (m >> 2) & 3, j = m & 3;
+    const int sa_ = (int)((mxa[i] >> (8 * (2 * p + lg))) & 0xFFu);
+    const int sb_ = (int)((mxb[j] >> (8 * (2 * p + lg))) & 0xFFu);
+    const i32x4 a = f.a[i][p], b = f.b[j][p];
+    const i32x8 a8 = __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3);
+    const i32x8 b8 = __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3);
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], AFMT, BFMT, 0, sa_, 0, sb_);
+  } else if (OP == OP_FP8) {
     const int i = m >> 2, j = m & 3;
     if (SC == SC_MX) {
       // the lane supplies the scale of MX block 2 h + lg of this stage
@@ -408,7 +438,7 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], const GemmArgs& 
 // ---------------------------------------------------------------------------
 template <int OP, int LDA, int LDB, int SC, int AFMT, int BFMT, bool B2D, bool OUT_BF16>
 __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
-  __shared__ __align__(16) uint8_t smem[SMEM];
+  __shared__ __align__(16) uint8_t smem[smem_bytes(OP)];
 
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -416,12 +446,13 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   int tm, tn;
   tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  constexpr int KST = (OP == OP_FP8) ? 128 : 64;         // K elements per stage
+  constexpr int KST = (OP == OP_FP8) ? 128 : (OP == OP_FP4 ? 256 : 64);   // K elements per stage
+  constexpr int SDW = sc_dw(OP);
   const int nk = g.K / KST;
 
   auto tileA = [&](int buf) { return smem + (buf * 2 + 0) * TILEB; };
   auto tileB = [&](int buf) { return smem + (buf * 2 + 1) * TILEB; };
-  auto ring = [&](int slot, int o) { return (uint32_t*)(smem + SC_OFF + (slot * 2 + o) * BM * 4); };
+  auto ring = [&](int slot, int o) { return (uint32_t*)(smem + SC_OFF + (slot * 2 + o) * BM * 4 * SDW); };
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -457,8 +488,16 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
     }
     if (SC == SC_MX || SC == SC_BLK) {
       const int slot = kt % SC_RING;
-      rowdw_issue(sa, kt, ring(slot, 0), w);
-      rowdw_issue(sb, kt, ring(slot, 1), w);
+      if (OP == OP_FP4) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          rowdw_issue_q<2>(sa, kt, q, ring(slot, 0), w);
+          rowdw_issue_q<2>(sb, kt, q, ring(slot, 1), w);
+        }
+      } else {
+        rowdw_issue(sa, kt, ring(slot, 0), w);
+        rowdw_issue(sb, kt, ring(slot, 1), w);
+      }
     }
   };
   const int lr = lane & 31, lg = lane >> 5;     // row within a 32-tile, K group
@@ -548,9 +587,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
     constexpr int NMFMA = (OP == OP_FP8) ? 16 : 32;                // per half stage
     constexpr int VM_A = 8;
     constexpr int VM_B = 8;
-    constexpr int VM_STAGE = VM_A + VM_B + (SC == SC_MX ? 2 : 0);
+    constexpr int VM_STAGE = VM_A + VM_B + (SC == SC_MX ? 2 * SDW : 0);
     constexpr int DS_HALF = op_reads<LDA>() + op_reads<LDB>();       // fragment reads per half stage
     constexpr int DS_NEXT = DS_HALF + (SC == SC_MX ? 8 : 0);
+    // MXFP4: phase A also reads the stage's second scale dword (used in phase C)
+    constexpr int DS_A = DS_HALF + (OP == OP_FP4 ? 8 : 0);
     // The compiler makes a transposing LDS read wait for every LDS-DMA load
     // still in flight.  With an MN-major operand the schedule therefore keeps
     // them apart: phase A reads on its second half of MFMAs (the previous
@@ -561,7 +602,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
     constexpr int C_VM0 = SPLIT ? NMFMA / 2 : 0;        // first MFMA carrying phase C's loads
 
     Frags f0, f1;
+    // MX scale words of the tiles: MXFP8 one dword per row and stage (mxa /
+    // mxb, the next stage's in nxa / nxb); MXFP4 dword 0 in mxa / mxb (phase
+    // A, refilled for the next stage in phase C) and dword 1 in m1a / m1b
+    // (read in phase A, used in phase C)
     uint32_t mxa[4] = {0, 0, 0, 0}, mxb[4] = {0, 0, 0, 0};
+    uint32_t m1a[4] = {0, 0, 0, 0}, m1b[4] = {0, 0, 0, 0};
     constexpr int HALF = NMFMA / 2;
 
     // global load v (of VM_STAGE) of stage kt
@@ -576,15 +622,17 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
         else mn_direct_item(mb, kt, tileB(buf), w, u);
       } else {
         const int slot = kt % SC_RING;
-        if (v == VM_A + VM_B) rowdw_issue(sa, kt, ring(slot, 0), w);
+        const int u = v - VM_A - VM_B;
+        if (OP == OP_FP4) rowdw_issue_q<2>((u & 1) ? sb : sa, kt, u >> 1, ring(slot, u & 1), w);
+        else if (u == 0) rowdw_issue(sa, kt, ring(slot, 0), w);
         else rowdw_issue(sb, kt, ring(slot, 1), w);
       }
     };
-    // LDS read e (of 8) of the MX scale words of stage kt
-    auto mx_item = [&](uint32_t* xa, uint32_t* xb, int kt, int e) {
+    // LDS read e (of 8) of the MX scale words (dword q) of stage kt
+    auto mx_item = [&](uint32_t* xa, uint32_t* xb, int kt, int e, int q) {
       const int slot = kt % SC_RING;
-      if (e < 4) xa[e] = ring(slot, 0)[wm * 128 + 32 * e + lr];
-      else xb[e - 4] = ring(slot, 1)[wn * 128 + 32 * (e - 4) + lr];
+      if (e < 4) xa[e] = ring(slot, 0)[q * BM + wm * 128 + 32 * e + lr];
+      else xb[e - 4] = ring(slot, 1)[q * BM + wn * 128 + 32 * (e - 4) + lr];
     };
 
     issue(0);
@@ -595,7 +643,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
     for (int d = 0; d < DS_HALF; ++d) frag_read<0, LDA, LDB>(f0, d, tileA(0) + offA, tileB(0) + offB, lba, lbb);
     if (SC == SC_MX) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mx_item(mxa, mxb, 0, e);
+      for (int e = 0; e < 8; ++e) mx_item(mxa, mxb, 0, e, 0);
     }
 
     auto body = [&](int kt, auto issue_c, auto next_c) {
@@ -613,8 +661,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
         if (m >= A_DS0) {
 #pragma unroll
-          for (int d = share_lo(DS_HALF, HALF, m - A_DS0); d < share_hi(DS_HALF, HALF, m - A_DS0); ++d)
-            frag_read<1, LDA, LDB>(f1, d, curA, curB, lba, lbb);
+          for (int d = share_lo(DS_A, HALF, m - A_DS0); d < share_hi(DS_A, HALF, m - A_DS0); ++d) {
+            if (d < DS_HALF) frag_read<1, LDA, LDB>(f1, d, curA, curB, lba, lbb);
+            else mx_item(m1a, m1b, kt, d - DS_HALF, 1);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -628,12 +678,14 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
       constexpr int NVM = ISSUE ? VM_STAGE : 0;
 #pragma unroll
       for (int m = 0; m < NMFMA; ++m) {
-        mfma_one<OP, SC, AFMT, BFMT>(acc, f1, mxa, mxb, 1, lg, m);
+        if (OP == OP_FP4) mfma_one<OP, SC, AFMT, BFMT>(acc, f1, m1a, m1b, 1, lg, m);
+        else mfma_one<OP, SC, AFMT, BFMT>(acc, f1, mxa, mxb, 1, lg, m);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int d = share_lo(NDS, HALF, m); d < share_hi(NDS, HALF, m); ++d) {
           if (d < DS_HALF) frag_read<0, LDA, LDB>(f0, d, nxtA, nxtB, lba, lbb);
-          else mx_item(nxa, nxb, kt + 1, d - DS_HALF);
+          else if (OP == OP_FP4) mx_item(mxa, mxb, kt + 1, d - DS_HALF, 0);
+          else mx_item(nxa, nxb, kt + 1, d - DS_HALF, 0);
         }
         if (m >= C_VM0) {
 #pragma unroll
@@ -642,7 +694,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (NEXT && SC == SC_MX) {
+      if constexpr (NEXT && SC == SC_MX && OP != OP_FP4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           mxa[i] = nxa[i];
@@ -1052,6 +1104,18 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
       g.lda = K; g.ldb = K;
       fn = pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_MX, 0, 0, false>(bf16_out);
       name = "gemm_mxfp8";
+      break;
+    }
+    case PBS_RECIPE_MXFP4: {
+      PBS_REQUIRE(a_fmt == PBS_FMT_E2M1 && b_fmt == PBS_FMT_E2M1, PBS_ERR_UNSUPPORTED,
+                  "pbs_gemm: MXFP4 takes E2M1 operands");
+      PBS_REQUIRE(a_scale && b_scale, PBS_ERR_INVALID_ARG, "pbs_gemm: block scales are null");
+      PBS_REQUIRE(K % 256 == 0, PBS_ERR_SHAPE, "pbs_gemm: MXFP4 needs K %% 256 == 0");
+      PBS_REQUIRE(((uintptr_t)a_scale & 3) == 0 && ((uintptr_t)b_scale & 3) == 0, PBS_ERR_INVALID_ARG,
+                  "pbs_gemm: MXFP4 block scales must be 4-byte aligned");
+      g.lda = K / 2; g.ldb = K / 2;
+      fn = pick_out<OP_FP4, LD_KMAJOR, LD_KMAJOR, SC_MX, 4, 4, false>(bf16_out);
+      name = "gemm_mxfp4";
       break;
     }
     case PBS_RECIPE_NVFP4: {

@@ -11,9 +11,11 @@ separate GEMMs), with X [M, K], W stored [N, K], dY [M, N]:
   wgrad: A = X col copy,  B = dY col copy
 
 Format roles: per-tensor FP8 uses E4M3 for X and W, E5M2 for dY;
-sub-channel FP8 and MXFP8 use E4M3; NVFP4 uses E2M1.  Weights take 2D
-blocks (128x128 sub-channel, 16x16 NVFP4).  NVFP4 applies the random
-Hadamard transform to both Wgrad operands and stochastic rounding to dY.
+sub-channel FP8 and MXFP8 use E4M3; NVFP4 and MXFP4 use E2M1.  Weights
+take 2D blocks (128x128 sub-channel, 16x16 NVFP4; MXFP4 keeps 1x32 blocks
+along the contraction axis for every operand).  NVFP4 and MXFP4 apply the
+random Hadamard transform to both Wgrad operands and stochastic rounding
+to dY.
 """
 from __future__ import annotations
 
@@ -24,7 +26,8 @@ import torch
 from . import (PBS_COL, PBS_DGRAD, PBS_FLAG_RHT16, PBS_FLAG_SR, PBS_FMT_BF16, PBS_FMT_E2M1,
                PBS_FMT_E4M3, PBS_FMT_E5M2, PBS_FMT_F32, PBS_FPROP, PBS_RECIPE_BF16,
                PBS_RECIPE_FP8_BLOCK128, PBS_RECIPE_FP8_CURRENT, PBS_RECIPE_FP8_DELAYED,
-               PBS_RECIPE_MXFP8, PBS_RECIPE_NVFP4, PBS_ROW, PBS_WGRAD, pbs_amax, pbs_cast,
+               PBS_RECIPE_MXFP4, PBS_RECIPE_MXFP8, PBS_RECIPE_NVFP4, PBS_ROW, PBS_WGRAD, pbs_amax,
+               pbs_cast,
                pbs_delayed_init, pbs_delayed_scale, pbs_delayed_scale_inv, pbs_delayed_state_bytes,
                pbs_delayed_update, pbs_gemm, pbs_scale_from_amax)
 
@@ -35,6 +38,7 @@ RECIPES = {
     "fp8_block128": PBS_RECIPE_FP8_BLOCK128,
     "mxfp8": PBS_RECIPE_MXFP8,
     "nvfp4": PBS_RECIPE_NVFP4,
+    "mxfp4": PBS_RECIPE_MXFP4,
 }
 LAYOUTS = {"fprop": PBS_FPROP, "dgrad": PBS_DGRAD, "wgrad": PBS_WGRAD}
 ROLES = {"fprop": (("x", "row"), ("w", "row")),
@@ -63,7 +67,7 @@ class QTensor:
 def fmt_for(recipe, src):
     if recipe in ("fp8_current", "fp8_delayed"):
         return PBS_FMT_E5M2 if src == "dy" else PBS_FMT_E4M3
-    if recipe == "nvfp4":
+    if recipe in ("nvfp4", "mxfp4"):
         return PBS_FMT_E2M1
     if recipe == "bf16":
         return PBS_FMT_BF16
@@ -77,6 +81,9 @@ def _empty_copy(recipe, rows, cols, w2d, device):
         sc = (torch.empty((rows // 16, cols // 16), dtype=torch.uint8, device=device) if w2d
               else torch.empty((rows, cols // 16), dtype=torch.uint8, device=device))
         return codes, sc
+    if recipe == "mxfp4":
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+        return codes, torch.empty((rows, cols // 32), dtype=torch.uint8, device=device)
     codes = torch.empty((rows, cols), dtype=torch.uint8, device=device)
     if recipe == "fp8_block128":
         sc = (torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=device) if w2d
@@ -177,6 +184,13 @@ def quantize(recipe, x, src, orient, pass_, state=None, out=None, ws=None, strea
         pbs_cast(rec, x, R, C, fmt, rmask, int(w2d), flags, seed, scal[1:2], None, row_c, row_s,
                  col_c, col_s, stream)
         out.tensor_scale_inv = scal[2:3]
+    elif recipe == "mxfp4":
+        flags = (PBS_FLAG_RHT16 if pass_ == "wgrad" else 0) | (PBS_FLAG_SR if src == "dy" else 0)
+        if flags == (PBS_FLAG_RHT16 | PBS_FLAG_SR) and RHT_SEED != SR_SEED:
+            raise ValueError("one seed drives both the RHT signs and SR")
+        pbs_cast(rec, x, R, C, fmt, rmask, 0, flags, SR_SEED if src == "dy" else RHT_SEED, None, None,
+                 row_c, row_s, col_c, col_s, stream)
+        out.tensor_scale_inv = None
     else:
         raise ValueError(recipe)
     return out

@@ -96,10 +96,8 @@ class OracleCopy:
         elif recipe == "mxfp8":
             self.codes, self.scales = R.quantize_mxfp8(sl, orient)
             self.deq = R.dequant_mxfp8(self.codes, self.scales)
-        elif recipe == "nvfp4":
+        elif recipe in ("nvfp4", "mxfp4"):
             rht = pass_ == "wgrad"
-            A = R.amax(R.rht16_along_rows(bf16_to_f32(bits), SEED) if rht else bits)
-            S_enc, S_dec = R.nvfp4_tensor_scales(A)
             t = bf16_to_f32(sl)
             if rht:
                 t = R.rht16_along_rows(t, SEED)          # col slices hold whole columns
@@ -113,9 +111,15 @@ class OracleCopy:
                 else:
                     idx = np.arange(M, dtype=np.uint64)[None, :] * np.uint64(N) + r[:, None]
                 sr = philox_word0_for_index(idx, SEED)
-            self.codes, self.scales = R.quantize_nvfp4(t_o, S_enc, weight_2d=w2d, sr_random=sr)
-            self.tsi = np.float32(S_dec)
-            self.deq = R.dequant_nvfp4(self.codes, self.scales, self.tsi, w2d)
+            if recipe == "nvfp4":
+                A = R.amax(R.rht16_along_rows(bf16_to_f32(bits), SEED) if rht else bits)
+                S_enc, S_dec = R.nvfp4_tensor_scales(A)
+                self.codes, self.scales = R.quantize_nvfp4(t_o, S_enc, weight_2d=w2d, sr_random=sr)
+                self.tsi = np.float32(S_dec)
+                self.deq = R.dequant_nvfp4(self.codes, self.scales, self.tsi, w2d)
+            else:
+                self.codes, self.scales = R.quantize_mxfp4(t_o, sr_random=sr)
+                self.deq = R.dequant_mxfp4(self.codes, self.scales)
         else:  # bf16: the operand is the natural-layout tensor
             self.codes = sl if orient == "row" else np.ascontiguousarray(sl.T)
             self.deq = bf16_to_f32(self.codes).astype(np.float64)
@@ -204,7 +208,8 @@ def run_pass(recipe, model, name, pass_):
 RECIPES = ["bf16", "fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "nvfp4"]
 CASES = ([("codonfm", n, r) for n in ("qkv", "attn_out", "mlp_up", "mlp_down") for r in RECIPES]
          + [("llama3_8b", n, r) for n in ("qkv", "attn_out", "mlp_up", "mlp_down") for r in RECIPES]
-         + [("codonfm_32k", n, r) for n in ("mlp_up", "mlp_down") for r in ("mxfp8", "nvfp4", "fp8_block128")])
+         + [("codonfm_32k", n, r) for n in ("mlp_up", "mlp_down") for r in ("mxfp8", "nvfp4", "fp8_block128")]
+         + [(m, n, "mxfp4") for m in ("codonfm", "llama3_8b") for n in ("qkv", "attn_out", "mlp_up", "mlp_down")])
 
 
 @pytest.mark.parametrize("model,name,recipe", CASES)
