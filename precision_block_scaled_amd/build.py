@@ -11,6 +11,9 @@ Every source is compiled by hipcc for gfx950 only.  Flags:
   -mllvm -disable-promote-alloca-to-lds
                          keep private arrays in registers (the GEMM's LDS
                          budget is spoken for)
+gemm_blk.hip adds -mllvm -amdgpu-mfma-vgpr-form=1: its MFMAs write their
+partial products to VGPRs, where the vector unit folds them (the other GEMMs
+keep 256 accumulators per lane in AGPRs and must not take it).
 fp32 division stays IEEE correctly rounded (hipcc's default) and fp32
 denormals are kept (no flush-to-zero), which the bit-exact casts rely on.
 """
@@ -27,7 +30,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libpbs.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "amax.hip", "cast.hip", "gemm.hip"]
+SOURCES = ["api.hip", "amax.hip", "cast.hip", "gemm.hip", "gemm_blk.hip"]
+EXTRA_FLAGS = {"gemm_blk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 
@@ -53,7 +57,7 @@ def build(jobs=None, verbose=False):
 
     def one(src):
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *compile_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

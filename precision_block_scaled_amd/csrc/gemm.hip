@@ -14,11 +14,8 @@
 //              (ds_read_b64_tr_b16).
 //  FP8 per-tensor  v_mfma_f32_32x32x64_f8f6f4 (format per operand: E4M3 or
 //              E5M2), scales applied once in the epilogue.
-//  FP8 1x128 / 128x128  the same instruction; each 128-long slice of the
-//              contraction accumulates into fresh registers, then is added
-//              into the result times a_scale[m] * b_scale[n] (fp32 block
-//              scales are not powers of two, so they cannot ride on the
-//              instruction's E8M0 scale).
+//  FP8 1x128 / 128x128  gemm_blk.hip (the fp32 block scales are folded in
+//              by the vector unit; that kernel keeps its accumulators in VGPRs).
 //  MXFP8       v_mfma_scale_f32_32x32x64_f8f6f4: each K=64 step covers two
 //              MX blocks; the two lanes that hold a row (or column) each
 //              supply the E8M0 scale of one of its blocks, and the hardware
@@ -46,130 +43,32 @@
 // so that each of the 8 XCDs (each with its own L2) works on a contiguous,
 // row-grouped range of tiles.
 #include "device.hpp"
+#include "gemm_common.hpp"
 #include "host.hpp"
 
 #include <type_traits>
 
 namespace pbs {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 enum { OP_BF16 = 0, OP_FP8 = 2, OP_FP4 = 3 };               // what the MFMA consumes
 enum { LD_KMAJOR = 0, LD_MNMAJOR = 1 };                      // how a tile reaches LDS
-enum { SC_NONE = 0, SC_TENSOR = 1, SC_MX = 2, SC_BLK = 3 };
+enum { SC_NONE = 0, SC_TENSOR = 1, SC_MX = 2 };
 
-constexpr int BM = 256, BN = 256, NTHR = 256;
-constexpr int ROWB = 128;               // bytes per LDS row per K stage
-constexpr int TILEB = BM * ROWB;        // 32 KB per operand per stage
+constexpr int BN = 256;
 constexpr int SC_OFF = 4 * TILEB;       // scale-row ring after 2 stages x 2 operands
 constexpr int SC_RING = 3;
 constexpr int STG_BF16 = 544;           // epilogue staging row pitch, bf16 output (256 rows)
 constexpr int STG_F32 = 1056;           // epilogue staging row pitch, fp32 output (128 rows a pass)
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // scale dwords per row per stage: MXFP8 4 E8M0 bytes (128 values), MXFP4 8 (256)
 constexpr int sc_dw(int op) { return op == OP_FP4 ? 2 : 1; }
 constexpr int smem_bytes(int op) {
   return cmax(SC_OFF + SC_RING * 2 * BM * 4 * sc_dw(op), cmax(256 * STG_BF16, 128 * STG_F32));
 }
 constexpr int SMEM = smem_bytes(OP_FP8);
-constexpr int GROUP_M = 8;              // tile rows walked together (L2 reuse)
-constexpr int NXCD = 8;
 
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
 enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM = 0x010, SG_DSR = 0x100, SG_DSW = 0x200 };
 #define PBS_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
-
-struct GemmArgs {
-  const uint8_t* A;
-  const uint8_t* B;
-  const uint8_t* a_scale;
-  const uint8_t* b_scale;
-  const float* a_ts;
-  const float* b_ts;
-  void* C;
-  int M, N, K;            // GEMM dims, K in elements
-  int64_t lda, ldb;       // bytes between stored rows of A / B
-  int ldc;                // elements between rows of C
-  int tiles_m, tiles_n;
-};
-
-// LDS tile layout: row r, 16-byte chunk c lives at r * 128 + ((c ^ key(r)) << 4).
-// gfx950's LDS serves a 16-byte-per-lane access 16 lanes (256 bytes, 64
-// banks) at a time; key(r) = (r ^ r >> 1 ^ r >> 4) & 7 makes the MFMA
-// fragment reads (16 consecutive rows, one chunk) conflict-free, and the
-// MN-major bf16 stores at most 2-way (a plain
-// r & 7 leaves every fragment read 2-way conflicted).
-__device__ __forceinline__ int swz_key(int row) { return (row ^ (row >> 1) ^ (row >> 4)) & 7; }
-__device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ swz_key(row)) << 4); }
-
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// ---------------------------------------------------------------------------
-// Operand staging.  Every variant fills one [256 rows][128 B] swizzled LDS
-// tile for K stage kt.  rows0 / nrows: first tile row and valid rows (rows
-// past the end re-read the last valid row; their results are never stored).
-// ---------------------------------------------------------------------------
-
-// K-major, direct to LDS (global_load_lds_dwordx4, no registers): load i (of
-// 8) of wave w fills LDS rows 64 w + 8 i .. + 7; lane l owns row
-// 64 w + 8 i + l / 8, physical chunk l % 8, i.e. the logical chunk that the
-// swizzle places there.  The tile's row base is wave-uniform; each lane keeps
-// eight 32-bit offsets (row * ld < 2^32 is checked on the host).
-struct Direct {
-  const uint8_t* base;
-  uint32_t off[8];
-};
-
-__device__ __forceinline__ void direct_init(Direct& d, const uint8_t* p, int64_t ld, int rows0, int nrows,
-                                            int w) {
-  const int lane = threadIdx.x & 63;
-  d.base = p + (int64_t)rows0 * ld;
-  const int lim = nrows - rows0 - 1;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int trow = 64 * w + 8 * i + (lane >> 3);
-    const int lc = (lane & 7) ^ swz_key(trow);
-    const int r = trow < lim ? trow : lim;
-    d.off[i] = (uint32_t)r * (uint32_t)ld + (uint32_t)(lc << 4);
-  }
-}
-
-__device__ __forceinline__ void direct_issue(const Direct& d, int kt, uint8_t* tile, int w) {
-  const uint8_t* g = d.base + (int64_t)kt * ROWB;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_global_load_lds(g + d.off[i], (lds_ptr_t)(tile + (w * 8 + i) * 1024), 16, 0, 0);
-}
-
-__device__ __forceinline__ void direct_item(const Direct& d, int kt, uint8_t* tile, int w, int i) {
-  const uint8_t* g = d.base + (int64_t)kt * ROWB;
-  __builtin_amdgcn_global_load_lds(g + d.off[i], (lds_ptr_t)(tile + (w * 8 + i) * 1024), 16, 0, 0);
-}
-
-// One dword per tile row per stage (MX scales: 4 E8M0 bytes; block-128: one
-// fp32 scale), direct to LDS: wave w loads rows 64 w .. 64 w + 63.
-struct RowDword {
-  const uint8_t* p;        // this lane's row of the scale array
-};
-
-__device__ __forceinline__ void rowdw_init(RowDword& d, const uint8_t* scale, int64_t row_stride, int rows0,
-                                           int nrows, int div_rows, int w) {
-  const int lane = threadIdx.x & 63;
-  int row = rows0 + 64 * w + lane;
-  row = row < nrows ? row : nrows - 1;
-  d.p = scale + (int64_t)(row / div_rows) * row_stride;
-}
-
-__device__ __forceinline__ void rowdw_issue(const RowDword& d, int kt, uint32_t* ring_slot, int w) {
-  __builtin_amdgcn_global_load_lds(d.p + (int64_t)kt * 4, (lds_ptr_t)(ring_slot + 64 * w), 4, 0, 0);
-}
 
 // Dword q of DW per row per stage (MXFP4: 8 scale bytes per row and stage),
 // into plane q of the ring slot (planes BM dwords apart).
@@ -210,22 +109,6 @@ __device__ __forceinline__ void mn_direct_item(const MnDirect& d, int kt, uint8_
                                    0, 0);
 }
 
-// XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a
-// contiguous range of logical tiles, then walk tiles GROUP_M rows at a time.
-__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int T = tiles_m * tiles_n;
-  const int q = T / NXCD, r = T % NXCD;
-  const int x = b % NXCD, idx = b / NXCD;
-  const int id = x * q + (x < r ? x : r) + idx;
-  const int per_group = GROUP_M * tiles_n;
-  const int g = id / per_group;
-  const int first_m = g * GROUP_M;
-  const int gm = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
-  const int in = id - g * per_group;
-  tm = first_m + in % gm;
-  tn = in / gm;
-}
-
 // Fragments of one half K-stage (64 of the 128 bytes of every LDS row): for
 // each of the wave's 4 row tiles (A) and 4 column tiles (B), lane (lr, lg)
 // holds 16-byte chunks 4h + lg (elements 0-3) and 4h + 2 + lg (elements
@@ -237,8 +120,6 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
 // physical chunk is (lg ^ key(lr)) ^ 4 h ^ 2 i (^ 2 for the upper half): one
 // per-lane constant lb = 128 lr + ((lg ^ key(lr)) << 4), XOR-ed with a
 // compile-time pattern.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
 struct Frags {
   i32x4 a[4][2], b[4][2];     // [tile][lower / upper 16 bytes]
 };
@@ -285,12 +166,6 @@ __device__ __forceinline__ void frag_read(Frags& f, int d, const uint8_t* la, co
                                           uint32_t lbb) {
   if (d < op_reads<LDA>()) op_read<H, LDA>(f.a, d, la, lba);
   else op_read<H, LDB>(f.b, d - op_reads<LDA>(), lbp, lbb);
-}
-
-__device__ __forceinline__ i32x8 read2(const uint8_t* tile_row0, uint32_t lb, uint32_t x) {
-  const i32x4 lo = *(const i32x4*)(tile_row0 + (lb ^ x));
-  const i32x4 hi = *(const i32x4*)(tile_row0 + (lb ^ x ^ 32u));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ i32x8 cat(const i32x4 (&p)[2]) {
@@ -345,11 +220,6 @@ __device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const Frags& f, co
 __device__ __forceinline__ constexpr int share_lo(int n, int over, int m) { return m < over ? n * m / over : n; }
 __device__ __forceinline__ constexpr int share_hi(int n, int over, int m) {
   return m < over ? n * (m + 1) / over : n;
-}
-
-__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
-  const f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Epilogue shared by the kernels.  Lane (lr, lg) of tile (i, j) holds column
@@ -430,13 +300,13 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], const GemmArgs& 
 // so LDS reads and global loads ride between MFMAs and global loads get
 // about one stage of lead.  The last two stages are peeled (no loads, then
 // no reads), so every phase is straight-line code.  Scale rows use a 3-deep
-// LDS ring.  Block-128 keeps a plain double-buffered loop (see below).
+// LDS ring.  (Block-128 has its own kernel, gemm_blk.hip.)
 //
 // Epilogue: the accumulators go through LDS (bf16: adjacent lanes swap
 // halves so each lane writes two 4-byte column pairs; fp32: 128 rows per
 // pass), then every lane stores 16 contiguous bytes of C.
 // ---------------------------------------------------------------------------
-template <int OP, int LDA, int LDB, int SC, int AFMT, int BFMT, bool B2D, bool OUT_BF16>
+template <int OP, int LDA, int LDB, int SC, int AFMT, int BFMT, bool OUT_BF16>
 __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   __shared__ __align__(16) uint8_t smem[smem_bytes(OP)];
 
@@ -472,9 +342,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   if (SC == SC_MX) {
     rowdw_init(sa, g.a_scale, g.K / 32, m0, g.M, 1, w);
     rowdw_init(sb, g.b_scale, g.K / 32, n0, g.N, 1, w);
-  } else if (SC == SC_BLK) {
-    rowdw_init(sa, g.a_scale, (g.K / 128) * 4, m0, g.M, 1, w);
-    rowdw_init(sb, g.b_scale, (g.K / 128) * 4, n0, g.N, B2D ? 128 : 1, w);
   }
 
   auto issue = [&](int kt) {
@@ -486,7 +353,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
       if (LDB == LD_KMAJOR) direct_item(db, kt, tileB(buf), w, i);
       else mn_direct_item(mb, kt, tileB(buf), w, i);
     }
-    if (SC == SC_MX || SC == SC_BLK) {
+    if (SC == SC_MX) {
       const int slot = kt % SC_RING;
       if (OP == OP_FP4) {
 #pragma unroll
@@ -511,203 +378,129 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   // 128 rows at 128 x 128 B; MN-major tiles put its columns in lba / lbb
   const int offA = LDA == LD_KMAJOR ? wm * 16384 : 0, offB = LDB == LD_KMAJOR ? wn * 16384 : 0;
 
-  if constexpr (SC == SC_BLK) {
-    // Block-128: the VALU fold needs both halves of a stage per tile, so this
-    // recipe keeps the plain double-buffered loop (loads of stage kt+1 issued
-    // at the top of stage kt, one barrier at its end).
-    issue(0);
-    wait_vm0();
+  constexpr int NMFMA = (OP == OP_FP8) ? 16 : 32;                // per half stage
+  constexpr int VM_A = 8;
+  constexpr int VM_B = 8;
+  constexpr int VM_STAGE = VM_A + VM_B + (SC == SC_MX ? 2 * SDW : 0);
+  constexpr int DS_HALF = op_reads<LDA>() + op_reads<LDB>();       // fragment reads per half stage
+  constexpr int DS_NEXT = DS_HALF + (SC == SC_MX ? 8 : 0);
+  // MXFP4: phase A also reads the stage's second scale dword (used in phase C)
+  constexpr int DS_A = DS_HALF + (OP == OP_FP4 ? 8 : 0);
+  // The compiler makes a transposing LDS read wait for every LDS-DMA load
+  // still in flight.  With an MN-major operand the schedule therefore keeps
+  // them apart: phase A reads on its second half of MFMAs (the previous
+  // loads have landed by then), phase C reads on its first half and issues
+  // the loads on its second half.
+  constexpr bool SPLIT = LDA == LD_MNMAJOR || LDB == LD_MNMAJOR;
+  constexpr int A_DS0 = SPLIT ? NMFMA / 2 : 0;        // first MFMA carrying phase A's reads
+  constexpr int C_VM0 = SPLIT ? NMFMA / 2 : 0;        // first MFMA carrying phase C's loads
+
+  Frags f0, f1;
+  // MX scale words of the tiles: MXFP8 one dword per row and stage (mxa /
+  // mxb, the next stage's in nxa / nxb); MXFP4 dword 0 in mxa / mxb (phase
+  // A, refilled for the next stage in phase C) and dword 1 in m1a / m1b
+  // (read in phase A, used in phase C)
+  uint32_t mxa[4] = {0, 0, 0, 0}, mxb[4] = {0, 0, 0, 0};
+  uint32_t m1a[4] = {0, 0, 0, 0}, m1b[4] = {0, 0, 0, 0};
+  constexpr int HALF = NMFMA / 2;
+
+  // global load v (of VM_STAGE) of stage kt
+  auto issue_item = [&](int kt, int v) {
+    const int buf = kt & 1;
+    if (v < VM_A) {
+      if (LDA == LD_KMAJOR) direct_item(da, kt, tileA(buf), w, v);
+      else mn_direct_item(ma, kt, tileA(buf), w, v);
+    } else if (v < VM_A + VM_B) {
+      const int u = v - VM_A;
+      if (LDB == LD_KMAJOR) direct_item(db, kt, tileB(buf), w, u);
+      else mn_direct_item(mb, kt, tileB(buf), w, u);
+    } else {
+      const int slot = kt % SC_RING;
+      const int u = v - VM_A - VM_B;
+      if (OP == OP_FP4) rowdw_issue_q<2>((u & 1) ? sb : sa, kt, u >> 1, ring(slot, u & 1), w);
+      else if (u == 0) rowdw_issue(sa, kt, ring(slot, 0), w);
+      else rowdw_issue(sb, kt, ring(slot, 1), w);
+    }
+  };
+  // LDS read e (of 8) of the MX scale words (dword q) of stage kt
+  auto mx_item = [&](uint32_t* xa, uint32_t* xb, int kt, int e, int q) {
+    const int slot = kt % SC_RING;
+    if (e < 4) xa[e] = ring(slot, 0)[q * BM + wm * 128 + 32 * e + lr];
+    else xb[e - 4] = ring(slot, 1)[q * BM + wn * 128 + 32 * (e - 4) + lr];
+  };
+
+  issue(0);
+  wait_vm0();
+  __syncthreads();
+  if (nk > 1) issue(1);
+#pragma unroll
+  for (int d = 0; d < DS_HALF; ++d) frag_read<0, LDA, LDB>(f0, d, tileA(0) + offA, tileB(0) + offB, lba, lbb);
+  if (SC == SC_MX) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx_item(mxa, mxb, 0, e, 0);
+  }
+
+  auto body = [&](int kt, auto issue_c, auto next_c) {
+    constexpr bool ISSUE = decltype(issue_c)::value;
+    constexpr bool NEXT = decltype(next_c)::value;
+    const int buf = kt & 1;
+    const uint8_t* curA = tileA(buf) + offA;
+    const uint8_t* curB = tileB(buf) + offB;
+    const uint8_t* nxtA = tileA(buf ^ 1) + offA;
+    const uint8_t* nxtB = tileB(buf ^ 1) + offB;
+    // phase A: MFMA(f0); the reads of f1 ride on the first half of the MFMAs
+#pragma unroll
+    for (int m = 0; m < NMFMA; ++m) {
+      mfma_one<OP, SC, AFMT, BFMT>(acc, f0, mxa, mxb, 0, lg, m);
+      __builtin_amdgcn_sched_barrier(0);
+      if (m >= A_DS0) {
+#pragma unroll
+        for (int d = share_lo(DS_A, HALF, m - A_DS0); d < share_hi(DS_A, HALF, m - A_DS0); ++d) {
+          if (d < DS_HALF) frag_read<1, LDA, LDB>(f1, d, curA, curB, lba, lbb);
+          else mx_item(m1a, m1b, kt, d - DS_HALF, 1);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase B
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1, slot = kt % SC_RING;
-      if (kt + 1 < nk) issue(kt + 1);
-      const uint8_t* la = tileA(buf) + offA;
-      const uint8_t* lbp = tileB(buf) + offB;
-      i32x8 fa[2][4], fb[2][4];
+    __builtin_amdgcn_sched_barrier(0);
+    // phase C: MFMA(f1); reads of the next f0 (and MX words) on the first
+    // half of the MFMAs, the loads of stage kt+2 spread over all of them
+    uint32_t nxa[4] = {0, 0, 0, 0}, nxb[4] = {0, 0, 0, 0};
+    constexpr int NDS = NEXT ? DS_NEXT : 0;
+    constexpr int NVM = ISSUE ? VM_STAGE : 0;
+#pragma unroll
+    for (int m = 0; m < NMFMA; ++m) {
+      if (OP == OP_FP4) mfma_one<OP, SC, AFMT, BFMT>(acc, f1, m1a, m1b, 1, lg, m);
+      else mfma_one<OP, SC, AFMT, BFMT>(acc, f1, mxa, mxb, 1, lg, m);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int d = share_lo(NDS, HALF, m); d < share_hi(NDS, HALF, m); ++d) {
+        if (d < DS_HALF) frag_read<0, LDA, LDB>(f0, d, nxtA, nxtB, lba, lbb);
+        else if (OP == OP_FP4) mx_item(mxa, mxb, kt + 1, d - DS_HALF, 0);
+        else mx_item(nxa, nxb, kt + 1, d - DS_HALF, 0);
+      }
+      if (m >= C_VM0) {
+#pragma unroll
+        for (int v = share_lo(NVM, NMFMA - C_VM0, m - C_VM0); v < share_hi(NVM, NMFMA - C_VM0, m - C_VM0); ++v)
+          issue_item(kt + 2, v);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NEXT && SC == SC_MX && OP != OP_FP4) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        fa[0][i] = read2(la + i * 4096, lb, (uint32_t)((2 * i) << 4));
-        fa[1][i] = read2(la + i * 4096, lb, (uint32_t)((4 ^ (2 * i)) << 4));
-        fb[0][i] = read2(lbp + i * 4096, lb, (uint32_t)((2 * i) << 4));
-        fb[1][i] = read2(lbp + i * 4096, lb, (uint32_t)((4 ^ (2 * i)) << 4));
+        mxa[i] = nxa[i];
+        mxb[i] = nxb[i];
       }
-      // scale factors of this K block: a_scale of the lane's 16 rows per row
-      // tile (4 consecutive rows per 16-byte read), b_scale of its column per
-      // column tile; with 128x128 weight blocks the wave's 128 columns share
-      // one b_scale, which is folded into the row factors up front
-      const float* sca = (const float*)ring(slot, 0) + wm * 128 + lg * 4;
-      const float* scb = (const float*)ring(slot, 1) + wn * 128 + lr;
-      float sbv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sbv[j] = scb[32 * j];
-      // fac[i & 1]: the factors of row tile i, loaded as tile (i, 0) starts
-      // (the fold of tile (i - 1, 3) still reads the other entry)
-      float fac[2][16];
-      auto load_fac = [&](int i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = *(const float4*)(sca + 32 * i + 8 * q);
-          fac[i & 1][4 * q] = v.x;
-          fac[i & 1][4 * q + 1] = v.y;
-          fac[i & 1][4 * q + 2] = v.z;
-          fac[i & 1][4 * q + 3] = v.w;
-        }
-        if (B2D) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) fac[i & 1][r] *= sbv[0];
-        }
-      };
-      // each 32x32 tile's 128-long K block accumulates into fresh registers;
-      // the fold acc += part * a_scale[row] * b_scale[col] of tile t - 1 runs
-      // on the vector unit while the matrix core works on tile t
-      f32x16 part[2];
-      auto fold = [&](int t) {
-        const int i = t >> 2, j = t & 3;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[i][j][r] = __builtin_fmaf(part[t & 1][r], B2D ? fac[i & 1][r] : fac[i & 1][r] * sbv[j], acc[i][j][r]);
-      };
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int i = t >> 2, j = t & 3;
-        if (j == 0) load_fac(i);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) part[t & 1][r] = 0.0f;
-        part[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0][i], fb[0][j], part[t & 1], 0, 0, 0, 0, 0, 0);
-        part[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[1][i], fb[1][j], part[t & 1], 0, 0, 0, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (t > 0) fold(t - 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      fold(15);
-      wait_vm0();
-      __syncthreads();
     }
-  } else {
-    constexpr int NMFMA = (OP == OP_FP8) ? 16 : 32;                // per half stage
-    constexpr int VM_A = 8;
-    constexpr int VM_B = 8;
-    constexpr int VM_STAGE = VM_A + VM_B + (SC == SC_MX ? 2 * SDW : 0);
-    constexpr int DS_HALF = op_reads<LDA>() + op_reads<LDB>();       // fragment reads per half stage
-    constexpr int DS_NEXT = DS_HALF + (SC == SC_MX ? 8 : 0);
-    // MXFP4: phase A also reads the stage's second scale dword (used in phase C)
-    constexpr int DS_A = DS_HALF + (OP == OP_FP4 ? 8 : 0);
-    // The compiler makes a transposing LDS read wait for every LDS-DMA load
-    // still in flight.  With an MN-major operand the schedule therefore keeps
-    // them apart: phase A reads on its second half of MFMAs (the previous
-    // loads have landed by then), phase C reads on its first half and issues
-    // the loads on its second half.
-    constexpr bool SPLIT = LDA == LD_MNMAJOR || LDB == LD_MNMAJOR;
-    constexpr int A_DS0 = SPLIT ? NMFMA / 2 : 0;        // first MFMA carrying phase A's reads
-    constexpr int C_VM0 = SPLIT ? NMFMA / 2 : 0;        // first MFMA carrying phase C's loads
-
-    Frags f0, f1;
-    // MX scale words of the tiles: MXFP8 one dword per row and stage (mxa /
-    // mxb, the next stage's in nxa / nxb); MXFP4 dword 0 in mxa / mxb (phase
-    // A, refilled for the next stage in phase C) and dword 1 in m1a / m1b
-    // (read in phase A, used in phase C)
-    uint32_t mxa[4] = {0, 0, 0, 0}, mxb[4] = {0, 0, 0, 0};
-    uint32_t m1a[4] = {0, 0, 0, 0}, m1b[4] = {0, 0, 0, 0};
-    constexpr int HALF = NMFMA / 2;
-
-    // global load v (of VM_STAGE) of stage kt
-    auto issue_item = [&](int kt, int v) {
-      const int buf = kt & 1;
-      if (v < VM_A) {
-        if (LDA == LD_KMAJOR) direct_item(da, kt, tileA(buf), w, v);
-        else mn_direct_item(ma, kt, tileA(buf), w, v);
-      } else if (v < VM_A + VM_B) {
-        const int u = v - VM_A;
-        if (LDB == LD_KMAJOR) direct_item(db, kt, tileB(buf), w, u);
-        else mn_direct_item(mb, kt, tileB(buf), w, u);
-      } else {
-        const int slot = kt % SC_RING;
-        const int u = v - VM_A - VM_B;
-        if (OP == OP_FP4) rowdw_issue_q<2>((u & 1) ? sb : sa, kt, u >> 1, ring(slot, u & 1), w);
-        else if (u == 0) rowdw_issue(sa, kt, ring(slot, 0), w);
-        else rowdw_issue(sb, kt, ring(slot, 1), w);
-      }
-    };
-    // LDS read e (of 8) of the MX scale words (dword q) of stage kt
-    auto mx_item = [&](uint32_t* xa, uint32_t* xb, int kt, int e, int q) {
-      const int slot = kt % SC_RING;
-      if (e < 4) xa[e] = ring(slot, 0)[q * BM + wm * 128 + 32 * e + lr];
-      else xb[e - 4] = ring(slot, 1)[q * BM + wn * 128 + 32 * (e - 4) + lr];
-    };
-
-    issue(0);
-    wait_vm0();
-    __syncthreads();
-    if (nk > 1) issue(1);
-#pragma unroll
-    for (int d = 0; d < DS_HALF; ++d) frag_read<0, LDA, LDB>(f0, d, tileA(0) + offA, tileB(0) + offB, lba, lbb);
-    if (SC == SC_MX) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx_item(mxa, mxb, 0, e, 0);
-    }
-
-    auto body = [&](int kt, auto issue_c, auto next_c) {
-      constexpr bool ISSUE = decltype(issue_c)::value;
-      constexpr bool NEXT = decltype(next_c)::value;
-      const int buf = kt & 1;
-      const uint8_t* curA = tileA(buf) + offA;
-      const uint8_t* curB = tileB(buf) + offB;
-      const uint8_t* nxtA = tileA(buf ^ 1) + offA;
-      const uint8_t* nxtB = tileB(buf ^ 1) + offB;
-      // phase A: MFMA(f0); the reads of f1 ride on the first half of the MFMAs
-#pragma unroll
-      for (int m = 0; m < NMFMA; ++m) {
-        mfma_one<OP, SC, AFMT, BFMT>(acc, f0, mxa, mxb, 0, lg, m);
-        __builtin_amdgcn_sched_barrier(0);
-        if (m >= A_DS0) {
-#pragma unroll
-          for (int d = share_lo(DS_A, HALF, m - A_DS0); d < share_hi(DS_A, HALF, m - A_DS0); ++d) {
-            if (d < DS_HALF) frag_read<1, LDA, LDB>(f1, d, curA, curB, lba, lbb);
-            else mx_item(m1a, m1b, kt, d - DS_HALF, 1);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // phase B
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      // phase C: MFMA(f1); reads of the next f0 (and MX words) on the first
-      // half of the MFMAs, the loads of stage kt+2 spread over all of them
-      uint32_t nxa[4] = {0, 0, 0, 0}, nxb[4] = {0, 0, 0, 0};
-      constexpr int NDS = NEXT ? DS_NEXT : 0;
-      constexpr int NVM = ISSUE ? VM_STAGE : 0;
-#pragma unroll
-      for (int m = 0; m < NMFMA; ++m) {
-        if (OP == OP_FP4) mfma_one<OP, SC, AFMT, BFMT>(acc, f1, m1a, m1b, 1, lg, m);
-        else mfma_one<OP, SC, AFMT, BFMT>(acc, f1, mxa, mxb, 1, lg, m);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int d = share_lo(NDS, HALF, m); d < share_hi(NDS, HALF, m); ++d) {
-          if (d < DS_HALF) frag_read<0, LDA, LDB>(f0, d, nxtA, nxtB, lba, lbb);
-          else if (OP == OP_FP4) mx_item(mxa, mxb, kt + 1, d - DS_HALF, 0);
-          else mx_item(nxa, nxb, kt + 1, d - DS_HALF, 0);
-        }
-        if (m >= C_VM0) {
-#pragma unroll
-          for (int v = share_lo(NVM, NMFMA - C_VM0, m - C_VM0); v < share_hi(NVM, NMFMA - C_VM0, m - C_VM0); ++v)
-            issue_item(kt + 2, v);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (NEXT && SC == SC_MX && OP != OP_FP4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          mxa[i] = nxa[i];
-          mxb[i] = nxb[i];
-        }
-      }
-    };
-    using T_ = std::integral_constant<bool, true>;
-    using F_ = std::integral_constant<bool, false>;
-    for (int kt = 0; kt < nk - 2; ++kt) body(kt, T_{}, T_{});
-    if (nk >= 2) body(nk - 2, F_{}, T_{});
-    body(nk - 1, F_{}, F_{});
-  }
+  };
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  for (int kt = 0; kt < nk - 2; ++kt) body(kt, T_{}, T_{});
+  if (nk >= 2) body(nk - 2, F_{}, T_{});
+  body(nk - 1, F_{}, F_{});
 
   float post = 1.0f;
   if (SC == SC_TENSOR) post = (*g.a_ts) * (*g.b_ts);
@@ -987,20 +780,18 @@ __global__ void zero_c_kernel(uint8_t* c, int64_t bytes) {
     c[i] = 0;
 }
 
-typedef void (*gemm_fn)(GemmArgs);
 
-template <int OP, int LDA, int LDB, int SC, int AFMT, int BFMT, bool B2D>
+template <int OP, int LDA, int LDB, int SC, int AFMT, int BFMT>
 static gemm_fn pick_out(bool bf16_out) {
-  return bf16_out ? gemm_kernel<OP, LDA, LDB, SC, AFMT, BFMT, B2D, true>
-                  : gemm_kernel<OP, LDA, LDB, SC, AFMT, BFMT, B2D, false>;
+  return bf16_out ? gemm_kernel<OP, LDA, LDB, SC, AFMT, BFMT, true> : gemm_kernel<OP, LDA, LDB, SC, AFMT, BFMT, false>;
 }
 
-template <int SC, bool B2D>
+template <int SC>
 static gemm_fn pick_fp8(int afmt, int bfmt, bool bf16_out) {
-  if (afmt == 0 && bfmt == 0) return pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC, 0, 0, B2D>(bf16_out);
-  if (afmt == 1 && bfmt == 0) return pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC, 1, 0, B2D>(bf16_out);
-  if (afmt == 0 && bfmt == 1) return pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC, 0, 1, B2D>(bf16_out);
-  return pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC, 1, 1, B2D>(bf16_out);
+  if (afmt == 0 && bfmt == 0) return pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC, 0, 0>(bf16_out);
+  if (afmt == 1 && bfmt == 0) return pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC, 1, 0>(bf16_out);
+  if (afmt == 0 && bfmt == 1) return pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC, 0, 1>(bf16_out);
+  return pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC, 1, 1>(bf16_out);
 }
 
 }  // namespace pbs
@@ -1058,13 +849,13 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
       PBS_REQUIRE(K % 64 == 0, PBS_ERR_SHAPE, "pbs_gemm: BF16 needs K %% 64 == 0");
       if (layout == PBS_FPROP) {
         g.lda = K * 2; g.ldb = K * 2;
-        fn = pick_out<OP_BF16, LD_KMAJOR, LD_KMAJOR, SC_NONE, 0, 0, false>(bf16_out);
+        fn = pick_out<OP_BF16, LD_KMAJOR, LD_KMAJOR, SC_NONE, 0, 0>(bf16_out);
       } else if (layout == PBS_DGRAD) {
         g.lda = K * 2; g.ldb = N * 2;               // B = W stored [K, N]
-        fn = pick_out<OP_BF16, LD_KMAJOR, LD_MNMAJOR, SC_NONE, 0, 0, false>(bf16_out);
+        fn = pick_out<OP_BF16, LD_KMAJOR, LD_MNMAJOR, SC_NONE, 0, 0>(bf16_out);
       } else {
         g.lda = M * 2; g.ldb = N * 2;               // A = X stored [K, M], B = dY stored [K, N]
-        fn = pick_out<OP_BF16, LD_MNMAJOR, LD_MNMAJOR, SC_NONE, 0, 0, false>(bf16_out);
+        fn = pick_out<OP_BF16, LD_MNMAJOR, LD_MNMAJOR, SC_NONE, 0, 0>(bf16_out);
       }
       name = "gemm_bf16";
       break;
@@ -1078,7 +869,7 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
                   "pbs_gemm: per-tensor FP8 needs both tensor scales");
       PBS_REQUIRE(K % 128 == 0, PBS_ERR_SHAPE, "pbs_gemm: FP8 needs K %% 128 == 0");
       g.lda = K; g.ldb = K;
-      fn = pick_fp8<SC_TENSOR, false>(a_fmt == PBS_FMT_E5M2, b_fmt == PBS_FMT_E5M2, bf16_out);
+      fn = pick_fp8<SC_TENSOR>(a_fmt == PBS_FMT_E5M2, b_fmt == PBS_FMT_E5M2, bf16_out);
       name = "gemm_fp8_tensor";
       break;
     }
@@ -1089,8 +880,8 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
       PBS_REQUIRE(K % 128 == 0, PBS_ERR_SHAPE, "pbs_gemm: FP8_BLOCK128 needs K %% 128 == 0");
       PBS_REQUIRE(!w2d || N % 128 == 0, PBS_ERR_SHAPE, "pbs_gemm: 128x128 weight blocks need N %% 128 == 0");
       g.lda = K; g.ldb = K;
-      fn = w2d ? pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_BLK, 0, 0, true>(bf16_out)
-               : pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_BLK, 0, 0, false>(bf16_out);
+      g.tiles_n = (int)ceil_div(N, 128);          // gemm_blk.hip: 256 x 128 tiles
+      fn = blk_kernel_for(w2d, bf16_out);
       name = "gemm_fp8_block128";
       break;
     }
@@ -1102,7 +893,7 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
       PBS_REQUIRE(((uintptr_t)a_scale & 3) == 0 && ((uintptr_t)b_scale & 3) == 0, PBS_ERR_INVALID_ARG,
                   "pbs_gemm: MXFP8 block scales must be 4-byte aligned");
       g.lda = K; g.ldb = K;
-      fn = pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_MX, 0, 0, false>(bf16_out);
+      fn = pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_MX, 0, 0>(bf16_out);
       name = "gemm_mxfp8";
       break;
     }
@@ -1114,7 +905,7 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
       PBS_REQUIRE(((uintptr_t)a_scale & 3) == 0 && ((uintptr_t)b_scale & 3) == 0, PBS_ERR_INVALID_ARG,
                   "pbs_gemm: MXFP4 block scales must be 4-byte aligned");
       g.lda = K / 2; g.ldb = K / 2;
-      fn = pick_out<OP_FP4, LD_KMAJOR, LD_KMAJOR, SC_MX, 4, 4, false>(bf16_out);
+      fn = pick_out<OP_FP4, LD_KMAJOR, LD_KMAJOR, SC_MX, 4, 4>(bf16_out);
       name = "gemm_mxfp4";
       break;
     }

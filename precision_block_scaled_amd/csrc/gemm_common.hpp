@@ -1,0 +1,145 @@
+// Pieces shared by the GEMM kernels (gemm.hip, gemm_blk.hip): vector
+// types, the kernel argument block, the swizzled LDS tile layout, operand
+// and scale-row staging straight into LDS, and the XCD-aware tile order.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pbs {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256, NTHR = 256;     // tile rows per workgroup, threads per workgroup
+constexpr int ROWB = 128;               // bytes per LDS row per K stage
+constexpr int TILEB = BM * ROWB;        // 32 KB per 256-row operand tile per stage
+constexpr int GROUP_M = 8;              // tile rows walked together (L2 reuse)
+constexpr int NXCD = 8;
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+struct GemmArgs {
+  const uint8_t* A;
+  const uint8_t* B;
+  const uint8_t* a_scale;
+  const uint8_t* b_scale;
+  const float* a_ts;
+  const float* b_ts;
+  void* C;
+  int M, N, K;            // GEMM dims, K in elements
+  int64_t lda, ldb;       // bytes between stored rows of A / B
+  int ldc;                // elements between rows of C
+  int tiles_m, tiles_n;
+};
+
+// LDS tile layout: row r, 16-byte chunk c lives at r * 128 + ((c ^ key(r)) << 4).
+// gfx950's LDS serves a 16-byte-per-lane access 16 lanes (256 bytes, 64
+// banks) at a time; key(r) = (r ^ r >> 1 ^ r >> 4) & 7 makes the MFMA
+// fragment reads (16 consecutive rows, one chunk) conflict-free, and the
+// MN-major bf16 stores at most 2-way (a plain
+// r & 7 leaves every fragment read 2-way conflicted).
+__device__ __forceinline__ int swz_key(int row) { return (row ^ (row >> 1) ^ (row >> 4)) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ swz_key(row)) << 4); }
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
+// Operand staging.  Every variant fills one [256 rows][128 B] swizzled LDS
+// tile for K stage kt.  rows0 / nrows: first tile row and valid rows (rows
+// past the end re-read the last valid row; their results are never stored).
+// ---------------------------------------------------------------------------
+
+// K-major, direct to LDS (global_load_lds_dwordx4, no registers): load i (of
+// 8) of wave w fills LDS rows 64 w + 8 i .. + 7; lane l owns row
+// 64 w + 8 i + l / 8, physical chunk l % 8, i.e. the logical chunk that the
+// swizzle places there.  The tile's row base is wave-uniform; each lane keeps
+// eight 32-bit offsets (row * ld < 2^32 is checked on the host).
+struct Direct {
+  const uint8_t* base;
+  uint32_t off[8];
+};
+
+__device__ __forceinline__ void direct_init(Direct& d, const uint8_t* p, int64_t ld, int rows0, int nrows,
+                                            int w) {
+  const int lane = threadIdx.x & 63;
+  d.base = p + (int64_t)rows0 * ld;
+  const int lim = nrows - rows0 - 1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int trow = 64 * w + 8 * i + (lane >> 3);
+    const int lc = (lane & 7) ^ swz_key(trow);
+    const int r = trow < lim ? trow : lim;
+    d.off[i] = (uint32_t)r * (uint32_t)ld + (uint32_t)(lc << 4);
+  }
+}
+
+__device__ __forceinline__ void direct_issue(const Direct& d, int kt, uint8_t* tile, int w) {
+  const uint8_t* g = d.base + (int64_t)kt * ROWB;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_global_load_lds(g + d.off[i], (lds_ptr_t)(tile + (w * 8 + i) * 1024), 16, 0, 0);
+}
+
+__device__ __forceinline__ void direct_item(const Direct& d, int kt, uint8_t* tile, int w, int i) {
+  const uint8_t* g = d.base + (int64_t)kt * ROWB;
+  __builtin_amdgcn_global_load_lds(g + d.off[i], (lds_ptr_t)(tile + (w * 8 + i) * 1024), 16, 0, 0);
+}
+
+// One dword per tile row per stage (MX scales: 4 E8M0 bytes; block-128: one
+// fp32 scale), direct to LDS: wave w loads rows 64 w .. 64 w + 63.
+struct RowDword {
+  const uint8_t* p;        // this lane's row of the scale array
+};
+
+__device__ __forceinline__ void rowdw_init(RowDword& d, const uint8_t* scale, int64_t row_stride, int rows0,
+                                           int nrows, int div_rows, int w) {
+  const int lane = threadIdx.x & 63;
+  int row = rows0 + 64 * w + lane;
+  row = row < nrows ? row : nrows - 1;
+  d.p = scale + (int64_t)(row / div_rows) * row_stride;
+}
+
+__device__ __forceinline__ void rowdw_issue(const RowDword& d, int kt, uint32_t* ring_slot, int w) {
+  __builtin_amdgcn_global_load_lds(d.p + (int64_t)kt * 4, (lds_ptr_t)(ring_slot + 64 * w), 4, 0, 0);
+}
+
+// XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a
+// contiguous range of logical tiles, then walk tiles GROUP_M rows at a time.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int q = T / NXCD, r = T % NXCD;
+  const int x = b % NXCD, idx = b / NXCD;
+  const int id = x * q + (x < r ? x : r) + idx;
+  const int per_group = GROUP_M * tiles_n;
+  const int g = id / per_group;
+  const int first_m = g * GROUP_M;
+  const int gm = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+  const int in = id - g * per_group;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+__device__ __forceinline__ i32x8 read2(const uint8_t* tile_row0, uint32_t lb, uint32_t x) {
+  const i32x4 lo = *(const i32x4*)(tile_row0 + (lb ^ x));
+  const i32x4 hi = *(const i32x4*)(tile_row0 + (lb ^ x ^ 32u));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+typedef void (*gemm_fn)(GemmArgs);
+
+// Sub-channel (block-128) FP8 kernel of gemm_blk.hip: 128x128 (b2d) or
+// 1x128 blocks for B, bf16 or fp32 output.
+gemm_fn blk_kernel_for(bool b2d, bool bf16_out);
+
+}  // namespace pbs
