@@ -37,7 +37,7 @@ constexpr int KB_TB = KB_BN * ROWB;                // 16 KB of B per stage
 constexpr int KB_STAGE = TILEB + KB_TB;            // 48 KB per stage
 constexpr int KB_NSTAGE = 3;
 constexpr int KB_RING = KB_NSTAGE * KB_STAGE;      // scale ring after the stage buffers
-constexpr int KB_NSLOT = 2;
+constexpr int KB_NSLOT = 3;
 constexpr int KB_SLOT = (BM + KB_BN + KB_BN) * 4;  // a_scale[256], b_scale[128], a sink for waves 2-3
 constexpr int KB_STG_BF16 = 272;                   // epilogue staging pitch, bf16 (256 rows)
 constexpr int KB_STG_F32 = 528;                    // epilogue staging pitch, fp32 (128 rows a pass)
@@ -69,30 +69,27 @@ __device__ __forceinline__ void direct4_item(const Direct4& d, int kt, uint8_t* 
   __builtin_amdgcn_global_load_lds(g + d.off[i], (lds_ptr_t)(tile + (w * 4 + i) * 1024), 16, 0, 0);
 }
 
+// Epilogue.  The MFMAs compute each 32 x 32 tile transposed (B rows as the
+// instruction's rows): lane (lr, lg) of tile (i, j) holds row
+// m = 128 wm + 32 i + lr and columns n = 64 wn + 32 j + 8 q + 4 lg + {0..3}
+// in values 4 q .. 4 q + 3.  Those go through LDS (4 consecutive columns per
+// store) and every lane then writes 16 contiguous bytes of C.
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_blk(f32x16 (&acc)[4][2], const GemmArgs& g, uint8_t* smem, int m0, int n0,
                                           int w, int wm, int wn, int lane) {
   const int lr = lane & 31, lg = lane >> 5;
   const bool full = (m0 + BM <= g.M) && (n0 + KB_BN <= g.N);
   if constexpr (OUT_BF16) {
-    // lanes lr and lr ^ 1 swap halves so each writes two rows of a column pair
-    const int par = lr & 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
-          const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-          const uint32_t own = par ? pk_bf16(v2, v3) : pk_bf16(v0, v1);
-          const uint32_t snd = par ? pk_bf16(v0, v1) : pk_bf16(v2, v3);
-          const uint32_t rcv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0xB1, 0xF, 0xF, false);
-          const uint32_t lo = par ? rcv : own, hi = par ? own : rcv;
-          const int row = wm * 128 + 32 * i + 8 * q + 4 * lg + 2 * par;
-          const int colb = (wn * 64 + 32 * j + (lr & ~1)) * 2;
-          *(uint32_t*)(smem + row * KB_STG_BF16 + colb) = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-          *(uint32_t*)(smem + (row + 1) * KB_STG_BF16 + colb) = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+          const int row = wm * 128 + 32 * i + lr;
+          const int colb = (wn * 64 + 32 * j + 8 * q + 4 * lg) * 2;
+          *(uint2*)(smem + row * KB_STG_BF16 + colb) =
+              make_uint2(pk_bf16(acc[i][j][4 * q], acc[i][j][4 * q + 1]), pk_bf16(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
         }
     __syncthreads();
     const int ch = lane & 15;
@@ -113,10 +110,11 @@ __device__ __forceinline__ void store_blk(f32x16 (&acc)[4][2], const GemmArgs& g
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-              const int col = wn * 64 + 32 * j + lr;
-              *(float*)(smem + row * KB_STG_F32 + col * 4) = acc[i][j][r];
+            for (int q = 0; q < 4; ++q) {
+              const int row = 32 * i + lr;
+              const int col = wn * 64 + 32 * j + 8 * q + 4 * lg;
+              *(float4*)(smem + row * KB_STG_F32 + col * 4) =
+                  make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
             }
       }
       __syncthreads();
@@ -216,6 +214,74 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_blk_kernel(GemmArgs g) {
   // B rows 64 wn + 32 j + lr have key(lr) ^ 2 j ^ 4 wn
   const uint32_t bx = (uint32_t)(wn << 6);
 
+  // Operands of the current stage, carried across stages: B fragments of the
+  // wave's two column tiles, A fragments of the current row tile, and the
+  // raw scale words of the stage (read by inline assembly): a_scale of the
+  // lane's row in each row tile, and b_scale -- one word for 128x128 weight
+  // blocks, else the lane's 16 columns of each column tile.
+  i32x8 fb[2][2], fa[2];
+  uint32_t asw[4];
+  i32x4 bsw[2][4];
+  float fac[4];          // per row tile: a_scale (times the weight scale for 128x128 blocks)
+  float bsv[2][16];      // 1x128 B blocks: b_scale of the lane's columns
+  typedef __attribute__((address_space(3))) const float* lds_f32_p;
+  auto read_fb = [&](int kt, int j) {
+    const uint8_t* lbq = tB(kt % KB_NSTAGE) + wn * 8192;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) fb[j][h] = read2(lbq + j * 4096, lb, ((uint32_t)(((4 * h) ^ (2 * j)) << 4)) ^ bx);
+  };
+  auto read_fa = [&](int kt, int i) {
+    const uint8_t* la = tA(kt % KB_NSTAGE) + wm * 16384;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) fa[h] = read2(la + i * 4096, lb, (uint32_t)(((4 * h) ^ (2 * i)) << 4));
+  };
+  auto load_scales = [&](int kt) {
+    const lds_f32_p pa_ = (lds_f32_p)(ringA(kt % KB_NSLOT) + wm * 128 + lr);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(asw[i]) : "v"(pa_), "i"(128 * i));
+    if (B2D) {
+      const lds_f32_p pb_ = (lds_f32_p)ringB(kt % KB_NSLOT);
+      asm volatile("ds_read_b32 %0, %1" : "=v"(bsw[0][0].x) : "v"(pb_));
+    } else {
+      const lds_f32_p pb_ = (lds_f32_p)(ringB(kt % KB_NSLOT) + wn * 64 + 4 * lg);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(bsw[j][q]) : "v"(pb_), "i"(128 * j + 32 * q));
+    }
+  };
+  // Wait for the scale reads (the wait names their results as operands, so
+  // nothing that uses them is scheduled before it) and form the factors.
+  auto finish_scales = [&]() {
+    if (B2D) {
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(asw[0]), "+v"(asw[1]), "+v"(asw[2]), "+v"(asw[3]), "+v"(bsw[0][0].x)::"memory");
+      const float bs = __uint_as_float(bsw[0][0].x);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fac[i] = __uint_as_float(asw[i]) * bs;
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(asw[0]), "+v"(asw[1]), "+v"(asw[2]), "+v"(asw[3]), "+v"(bsw[0][0]), "+v"(bsw[0][1]),
+                     "+v"(bsw[0][2]), "+v"(bsw[0][3]), "+v"(bsw[1][0]), "+v"(bsw[1][1]), "+v"(bsw[1][2]),
+                     "+v"(bsw[1][3])::"memory");
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fac[i] = __uint_as_float(asw[i]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = __builtin_bit_cast(float4, bsw[j][q]);
+          bsv[j][4 * q] = v.x;
+          bsv[j][4 * q + 1] = v.y;
+          bsv[j][4 * q + 2] = v.z;
+          bsv[j][4 * q + 3] = v.w;
+        }
+    }
+  };
+
+  // Prologue: scale words and tiles of stage 0, tiles of stage 1, then the
+  // operands of stage 0.
   {
     const float a0 = pa[0], b0 = pb[0];
 #pragma unroll
@@ -225,118 +291,84 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_blk_kernel(GemmArgs g) {
       for (int v = 0; v < KB_VM_TILES; ++v) issue_tile(1, v);
     }
     put_scales(0, a0, b0);
-    wait_vm0();
-    __syncthreads();
+    if (nk > 1) wait_vm_ahead();
+    else wait_vm0();
+    barrier_lds();
+    read_fb(0, 0);
+    read_fb(0, 1);
+    read_fa(0, 0);
+    load_scales(0);
   }
 
   // One K stage.  MORE: stage kt + 2 exists and its tiles are loaded during
-  // this one; NEXT: stage kt + 1 exists (its scale words are loaded here).
-  // The last two stages are peeled so that every stage is straight-line code
-  // and the fenced schedule holds.
+  // tiles 0-5 of this one; NEXT: stage kt + 1 exists (its scale words are
+  // loaded here).  Tiles t = (i, j) = (t / 2, t % 2): tile t multiplies into
+  // part[t % 2] while tile t - 1 is folded, acc += part * a_scale[m] *
+  // b_scale[n].  A fragments of row tile i + 1 are read once tile (i, 1) has
+  // issued.  After tile 5 every wave waits for the next stage's data and
+  // meets at a barrier (this stage's tile buffer is no longer read by then),
+  // so tiles 6-7 read the next stage's first operands and scale words as
+  // their registers free up, and the next stage starts without an LDS round
+  // trip.  The last two stages are peeled so that every stage is
+  // straight-line code and the fenced schedule holds.
   auto stage = [&](int kt, auto more_c, auto next_c) {
     constexpr bool MORE = decltype(more_c)::value;
     constexpr bool NEXT = decltype(next_c)::value;
-    const int s = kt % KB_NSTAGE;
-    const uint8_t* la = tA(s) + wm * 16384;
-    const uint8_t* lbq = tB(s) + wn * 8192;
-    const float* sca = ringA(kt % KB_NSLOT) + wm * 128 + lg * 4;
-    const float* scb = ringB(kt % KB_NSLOT) + wn * 64 + lr;
     float a_nx = 0.0f, b_nx = 0.0f;
     if (NEXT) {
       a_nx = load_word_untracked(pa + kt + 1);
       b_nx = load_word_untracked(pb + kt + 1);
     }
-
-    i32x8 fb[2][2], fa[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) fb[j][h] = read2(lbq + j * 4096, lb, ((uint32_t)(((4 * h) ^ (2 * j)) << 4)) ^ bx);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) fa[h] = read2(la, lb, (uint32_t)((4 * h) << 4));
-    float sbv[2];
-    sbv[0] = scb[0];
-    sbv[1] = B2D ? sbv[0] : scb[32];
-    // scale factors of one row tile: a_scale of the lane's 16 rows (4
-    // consecutive rows per 16-byte read), times the weight scale for 128x128
-    // blocks
-    float fac[16];
-    i32x4 facw[4];
-    auto load_fac = [&](int i) {
-      typedef __attribute__((address_space(3))) const float* lds_f32_p;
-      const lds_f32_p p = (lds_f32_p)(sca + 32 * i);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(facw[q]) : "v"(p), "i"(32 * q));
-    };
-    // after load_fac: wait for the reads (the wait names their results as
-    // operands, so nothing that uses them is scheduled before it), then fold
-    // in the weight scale of 128x128 blocks
-    auto finish_fac = [&]() {
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(facw[0]), "+v"(facw[1]), "+v"(facw[2]), "+v"(facw[3]) :: "memory");
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = __builtin_bit_cast(float4, facw[q]);
-        fac[4 * q] = v.x;
-        fac[4 * q + 1] = v.y;
-        fac[4 * q + 2] = v.z;
-        fac[4 * q + 3] = v.w;
-      }
-      if (B2D) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) fac[r] *= sbv[0];
-      }
-    };
-    load_fac(0);
-    finish_fac();
-
-    // Tiles t = (i, j) = (t / 2, t % 2).  Tile t multiplies into part[t % 2]
-    // while tile t - 1 is folded.  A fragments of row tile i + 1 are read once
-    // tile (i, 1) has issued; the scale factors of row tile i once tile
-    // (i - 1, 1) is folded, one MFMA pair before their first use.
     f32x16 part[2];
-    auto fold = [&](int tt) {
-      const int j = tt & 1;
+    // fold values r0 .. r0 + 7 of tile tt
+    auto fold8 = [&](int tt, int r0) {
+      const int i = tt >> 1, j = tt & 1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        acc[tt >> 1][j][r] = __builtin_fmaf(part[tt & 1][r], B2D ? fac[r] : fac[r] * sbv[j], acc[tt >> 1][j][r]);
+      for (int r = r0; r < r0 + 8; ++r)
+        acc[i][j][r] = __builtin_fmaf(part[tt & 1][r], B2D ? fac[i] : fac[i] * bsv[j][r], acc[i][j][r]);
     };
     const f32x16 zero = {};
+    // Each MFMA is followed by half a fold of the previous tile, so the
+    // vector unit works while the matrix core does and the second MFMA of a
+    // tile (which accumulates onto the first) finds the first one done.
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       const int i = tt >> 1, j = tt & 1;
-      part[tt & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0], fb[j][0], zero, 0, 0, 0, 0, 0, 0);
-      part[tt & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[1], fb[j][1], part[tt & 1], 0, 0, 0, 0, 0, 0);
+      // transposed tile: B rows are the instruction's rows, A rows its columns
+      part[tt & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][0], fa[0], zero, 0, 0, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (j == 1 && i > 0) finish_fac();
-      if (tt > 0) fold(tt - 1);
-      if (j == 1 && i < 3) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) fa[h] = read2(la + (i + 1) * 4096, lb, (uint32_t)(((4 * h) ^ (2 * (i + 1))) << 4));
+      if (tt == 0) finish_scales();
+      if (tt > 0) fold8(tt - 1, 0);
+      if (MORE && tt < 6) issue_tile(kt + 2, 2 * tt);
+      __builtin_amdgcn_sched_barrier(0);
+      part[tt & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][1], fa[1], part[tt & 1], 0, 0, 0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (tt > 0) fold8(tt - 1, 8);
+      if (j == 1 && i < 3) read_fa(kt, i + 1);
+      if (MORE && tt < 6) issue_tile(kt + 2, 2 * tt + 1);
+      if (tt == 5 && NEXT) {
+        if (MORE) wait_vm_ahead();
+        else wait_vm0();
+        put_scales(kt + 1, a_nx, b_nx);
+        barrier_lds();
       }
-      if (j == 0 && i > 0) load_fac(i);
-      if (MORE) {
-#pragma unroll
-        for (int v = (KB_VM_TILES * tt) / 8; v < (KB_VM_TILES * (tt + 1)) / 8; ++v) issue_tile(kt + 2, v);
+      if (tt == 6 && NEXT) read_fb(kt + 1, 0);     // fb[0] is free once tile (3, 0) has issued
+      if (tt == 7 && NEXT) {                       // fa, fb[1] are free after tile (3, 1)
+        read_fb(kt + 1, 1);
+        read_fa(kt + 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    fold(7);
-    if (MORE) {
-      wait_vm_ahead();
-      put_scales(kt + 1, a_nx, b_nx);
-      barrier_lds();
-    } else {
-      wait_vm0();
-      if (NEXT) put_scales(kt + 1, a_nx, b_nx);
-      __syncthreads();
-    }
+    fold8(7, 0);
+    fold8(7, 8);
+    if (NEXT) load_scales(kt + 1);                 // every fold of this stage is done
   };
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
   for (int kt = 0; kt < nk - 2; ++kt) stage(kt, T_{}, T_{});
   if (nk >= 2) stage(nk - 2, F_{}, T_{});
   stage(nk - 1, F_{}, F_{});
+  __syncthreads();                                   // the epilogue reuses the tile buffers
   store_blk<OUT_BF16>(acc, g, smem, m0, n0, w, wm, wn, lane);
 }
 

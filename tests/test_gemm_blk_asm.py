@@ -50,7 +50,7 @@ def check_asm(lines):
     checked, bad = 0, []
     for n, line in enumerate(lines):
         op, ops = _split(line)
-        if op not in ("ds_read_b128", "global_load_dword"):
+        if op not in ("ds_read_b32", "ds_read_b128", "global_load_dword"):
             continue
         if n == 0 or not lines[n - 1].strip().startswith(";;#ASMSTART"):
             continue                      # compiler-issued: the compiler tracks it
@@ -89,7 +89,7 @@ def test_inline_asm_loads_are_waited_for_before_use():
         assert r.returncode == 0, r.stderr[-2000:]
         lines = open(out).read().split("\n")
     checked, bad = check_asm(lines)
-    assert checked >= 4 * 40, f"expected the inline-asm loads of all 4 instantiations, found {checked}"
+    assert checked >= 4 * 20, f"expected the inline-asm loads of all 4 instantiations, found {checked}"
     assert not bad, "\n".join(bad[:10])
 
 
