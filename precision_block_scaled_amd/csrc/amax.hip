@@ -27,7 +27,10 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-// Block-wide max of a per-thread value, then one atomic max per block.
+// Block-wide max of a per-thread value, then at most one atomic max per
+// block: only when the block's maximum exceeds what *out already holds (the
+// running maximum settles early, so most blocks skip the same-address
+// atomic, which would otherwise serialize thousands of blocks at the end).
 __device__ __forceinline__ void block_max_atomic(uint32_t v, uint32_t* out) {
   __shared__ uint32_t part[16];
   v = wave_max_u32(v);
@@ -37,7 +40,8 @@ __device__ __forceinline__ void block_max_atomic(uint32_t v, uint32_t* out) {
   if (threadIdx.x == 0) {
     uint32_t m = 0;
     for (int i = 0; i < (int)(blockDim.x >> 6); ++i) m = m > part[i] ? m : part[i];
-    atomicMax(out, m);
+    const uint32_t cur = __builtin_nontemporal_load(out);
+    if (m > cur) atomicMax(out, m);
   }
 }
 
@@ -46,7 +50,9 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v) {
 }
 
 // Plain amax over n bf16 values; n8 = n / 8 full 16-byte chunks, the rest
-// (n % 8 values) handled by block 0.
+// (n % 8 values) handled by block 0.  Eight 16-byte loads per thread in
+// flight before any arithmetic (measured best against 4, and against
+// 2048 / 8192 workgroups).
 __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint4* __restrict__ x, int64_t n8,
                                                         const bf16_t* __restrict__ tail, int tail_n,
                                                         uint32_t* out) {
@@ -54,12 +60,12 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint4* __restrict_
   const us2 mask = {0x7FFF, 0x7FFF};
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n8; i += 4 * stride) {
-    uint4 v[4];
+  for (; i + 7 * stride < n8; i += 8 * stride) {
+    uint4 v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = ld_nt16(&x[i + u * stride]);
+    for (int u = 0; u < 8; ++u) v[u] = ld_nt16(&x[i + u * stride]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[u].x) & mask);
       m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[u].y) & mask);
       m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[u].z) & mask);
@@ -209,7 +215,7 @@ pbs_status pbs_amax(const void* x_bf16, int64_t rows, int64_t cols, int flags, u
     PBS_REQUIRE(((uintptr_t)x_bf16 & 15) == 0, PBS_ERR_INVALID_ARG, "pbs_amax: x not 16-byte aligned");
     const int64_t n8 = n / 8;
     const int tail_n = (int)(n - n8 * 8);
-    int grid = amax_grid(n8, 16);
+    int grid = amax_grid(n8, 32);
     log_dispatch("amax_bf16_kernel n=%lld grid=%d", (long long)n, grid);
     hipLaunchKernelGGL(amax_bf16_kernel, dim3(grid), dim3(256), 0, stream, (const uint4*)x_bf16, n8,
                        (const bf16_t*)x_bf16 + n8 * 8, tail_n, out);

@@ -543,8 +543,8 @@ __device__ __forceinline__ void wg_amax_fold(uint32_t v, uint32_t* out, uint32_t
   }
 }
 
-// Row copy: thread = 16-value segment of a row.  Each lane does U = 2
-// segments per step (the wave covers 128 consecutive segments), both loads
+// Row copy: thread = 16-value segment of a row.  Each lane does U = 4
+// segments per step (the wave covers 256 consecutive segments), all loads
 // issued before any arithmetic.  No LDS.
 template <int RECIPE, int FMT, bool SR, bool AMAX>
 __global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg) {
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg)
   float tscale = 0.0f;
   if (RECIPE == R_TENSOR || RECIPE == R_NV) tscale = *a.scale;
   uint32_t amx = 0;
-  constexpr int U = 2;
+  constexpr int U = 4;
   for (int64_t wt = wave0; wt * 64 * U < nseg; wt += waves) {
     uint32_t w[U][8];
     bool ok[U];
@@ -878,8 +878,9 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
   if (rows == 0 || cols == 0) return check_launch("pbs_cast");
   if (fn.row) {
     const int64_t nseg = rows * cols / 16;
-    // fused amax: fewer, longer-lived workgroups (one atomic at most each)
-    const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(nseg, 512), amax_out ? 2048 : 8192);
+    // one pass of the wave loop per wave (measured best); with fused amax
+    // fewer, longer-lived workgroups (one atomic at most each)
+    const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(nseg, 1024), amax_out ? 2048 : (1 << 20));
     log_dispatch("%s_row recipe=%d fmt=%d flags=%d rows=%lld cols=%lld grid=%u", name, (int)recipe, (int)fmt,
                  flags, (long long)rows, (long long)cols, grid);
     hipLaunchKernelGGL(fn.row, dim3(grid), dim3(256), 0, stream, a, nseg);
