@@ -348,3 +348,24 @@ def test_fp8_instruction_drops_small_products_within_8_groups():
                P.PBS_FMT_BF16, None, None, C2, P.PBS_FMT_F32)
     _sync()
     assert (to_np_f32(C2) == np.float32(exact)).all()
+
+
+# Contraction lengths of one, two, three and five K stages (the kernels peel
+# their last two or three stages, so every schedule variant runs), with M and
+# N inside a single ragged output tile.
+STAGE_K = {"bf16": 64, "fp8_current": 128, "fp8_delayed": 128, "fp8_block128": 128, "mxfp8": 128, "nvfp4": 128}
+
+
+@pytest.mark.parametrize("recipe", GEMM_RECIPES)
+@pytest.mark.parametrize("stages", [1, 2, 3, 5])
+@pytest.mark.parametrize("pass_", ["fprop", "wgrad"])
+def test_gemm_short_k(recipe, stages, pass_):
+    K = STAGE_K[recipe] * stages
+    M, N = 48, 256                  # 128x128 weight blocks need N % 128 == 0
+    M_tok, K_in, N_out = tensor_shapes(pass_, M, N, K)
+    x = W.activations(M_tok, K_in, seed=4)
+    w = W.weights(N_out, K_in, seed=5)
+    dy = W.grads(M_tok, N_out, seed=6)
+    c, cref, bnd, extra = _run_pass(recipe, pass_, x, w, dy, torch.float32)
+    ok, tol, err = check_gemm(c, cref, bnd, False, extra)
+    assert ok.all(), f"{(~ok).sum()} of {ok.size} outside bound"
