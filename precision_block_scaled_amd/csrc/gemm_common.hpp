@@ -20,7 +20,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int BM = 256, NTHR = 256;     // tile rows per workgroup, threads per workgroup
 constexpr int ROWB = 128;               // bytes per LDS row per K stage
 constexpr int TILEB = BM * ROWB;        // 32 KB per 256-row operand tile per stage
-constexpr int GROUP_M = 8;              // tile rows walked together (L2 reuse)
+constexpr int GROUP_M = 4;              // tile rows walked together (L2 reuse; 4 measured best of 1-32)
 constexpr int NXCD = 8;
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
