@@ -52,7 +52,7 @@ namespace pbs {
 
 enum { OP_BF16 = 0, OP_FP8 = 2, OP_FP4 = 3 };               // what the MFMA consumes
 enum { LD_KMAJOR = 0, LD_MNMAJOR = 1 };                      // how a tile reaches LDS
-enum { SC_NONE = 0, SC_TENSOR = 1, SC_MX = 2 };
+enum { SC_NONE = 0, SC_TENSOR = 1, SC_MX = 2, SC_MXC = 3 };   // SC_MXC: MX scales loaded in 16-byte chunks
 
 constexpr int BN = 256;
 constexpr int SC_OFF = 4 * TILEB;       // scale-row ring after 2 stages x 2 operands
@@ -61,10 +61,13 @@ constexpr int STG_BF16 = 544;           // epilogue staging row pitch, bf16 outp
 constexpr int STG_F32 = 1056;           // epilogue staging row pitch, fp32 output (128 rows a pass)
 // scale dwords per row per stage: MXFP8 4 E8M0 bytes (128 values), MXFP4 8 (256)
 constexpr int sc_dw(int op) { return op == OP_FP4 ? 2 : 1; }
-constexpr int smem_bytes(int op) {
-  return cmax(SC_OFF + SC_RING * 2 * BM * 4 * sc_dw(op), cmax(256 * STG_BF16, 128 * STG_F32));
+// MX scale chunks: 16 bytes per row (4 stages of MXFP8, 2 of MXFP4), two
+// slots per operand
+constexpr int smem_bytes(int op, int sc) {
+  return cmax(SC_OFF + (sc == SC_MXC ? 2 * 2 * BM * 16 : SC_RING * 2 * BM * 4 * sc_dw(op)),
+              cmax(256 * STG_BF16, 128 * STG_F32));
 }
-constexpr int SMEM = smem_bytes(OP_FP8);
+constexpr int SMEM = smem_bytes(OP_FP8, SC_TENSOR);
 
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
 enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM = 0x010, SG_DSR = 0x100, SG_DSW = 0x200 };
@@ -197,7 +200,7 @@ __device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const Frags& f, co
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], AFMT, BFMT, 0, sa_, 0, sb_);
   } else if (OP == OP_FP8) {
     const int i = m >> 2, j = m & 3;
-    if (SC == SC_MX) {
+    if (SC == SC_MX || SC == SC_MXC) {
       // the lane supplies the scale of MX block 2 h + lg of this stage
       const int sa_ = (int)((mxa[i] >> (8 * (2 * h + lg))) & 0xFFu);
       const int sb_ = (int)((mxb[j] >> (8 * (2 * h + lg))) & 0xFFu);
@@ -308,7 +311,8 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], const GemmArgs& 
 // ---------------------------------------------------------------------------
 template <int OP, int LDA, int LDB, int SC, int AFMT, int BFMT, bool OUT_BF16>
 __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
-  __shared__ __align__(16) uint8_t smem[smem_bytes(OP)];
+  __shared__ __align__(16) uint8_t smem[smem_bytes(OP, SC)];
+  constexpr bool MX = SC == SC_MX || SC == SC_MXC;
 
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -339,10 +343,30 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   else mn_direct_init(ma, g.A, g.lda, m0, g.M, w);
   if (LDB == LD_KMAJOR) direct_init(db, g.B, g.ldb, n0, g.N, w);
   else mn_direct_init(mb, g.B, g.ldb, n0, g.N, w);
-  if (SC == SC_MX) {
+  if (MX) {
     rowdw_init(sa, g.a_scale, g.K / 32, m0, g.M, 1, w);
     rowdw_init(sb, g.b_scale, g.K / 32, n0, g.N, 1, w);
   }
+  // SC_MXC: a lane loads 16 bytes of its row's scales at once (CH stages), one
+  // load per row every CH stages instead of every stage.  Chunks are aligned
+  // to the end of K: a chunk starts at stage s when s + delta is a multiple
+  // of CH, delta = (CH - nk % CH) % CH; the first one may be shorter and its
+  // 16-byte window then starts at stage 0.  Every window lies inside the row
+  // (the host takes this path only when nk >= CH).  Chunk c sits in slot c % 2.
+  constexpr int CH = 4 / SDW;
+  const int delta = (CH - nk % CH) % CH;
+  auto chunk_ws = [&](int s) {
+    const int t0 = ((s + delta) / CH) * CH - delta;
+    return t0 > 0 ? t0 : 0;
+  };
+  auto chunk_slot = [&](int s) { return ((s + delta) / CH) & 1; };
+  auto chunk_start = [&](int s) { return s == 0 || (s + delta) % CH == 0; };
+  auto ring16 = [&](int slot, int o) { return (uint32_t*)(smem + SC_OFF + (slot * 2 + o) * BM * 16); };
+  auto chunk_issue = [&](int s) {
+    const int ws = chunk_ws(s), slot = chunk_slot(s);
+    __builtin_amdgcn_global_load_lds(sa.p + ws * SDW * 4, (lds_ptr_t)(ring16(slot, 0) + 64 * w * 4), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(sb.p + ws * SDW * 4, (lds_ptr_t)(ring16(slot, 1) + 64 * w * 4), 16, 0, 0);
+  };
 
   auto issue = [&](int kt) {
     const int buf = kt & 1;
@@ -353,7 +377,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
       if (LDB == LD_KMAJOR) direct_item(db, kt, tileB(buf), w, i);
       else mn_direct_item(mb, kt, tileB(buf), w, i);
     }
-    if (SC == SC_MX) {
+    if (SC == SC_MXC) {
+      if (chunk_start(kt)) chunk_issue(kt);
+    } else if (SC == SC_MX) {
       const int slot = kt % SC_RING;
       if (OP == OP_FP4) {
 #pragma unroll
@@ -383,7 +409,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   constexpr int VM_B = 8;
   constexpr int VM_STAGE = VM_A + VM_B + (SC == SC_MX ? 2 * SDW : 0);
   constexpr int DS_HALF = op_reads<LDA>() + op_reads<LDB>();       // fragment reads per half stage
-  constexpr int DS_NEXT = DS_HALF + (SC == SC_MX ? 8 : 0);
+  constexpr int DS_NEXT = DS_HALF + (MX ? 8 : 0);
   // MXFP4: phase A also reads the stage's second scale dword (used in phase C)
   constexpr int DS_A = DS_HALF + (OP == OP_FP4 ? 8 : 0);
   // The compiler makes a transposing LDS read wait for every LDS-DMA load
@@ -424,9 +450,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   };
   // LDS read e (of 8) of the MX scale words (dword q) of stage kt
   auto mx_item = [&](uint32_t* xa, uint32_t* xb, int kt, int e, int q) {
-    const int slot = kt % SC_RING;
-    if (e < 4) xa[e] = ring(slot, 0)[q * BM + wm * 128 + 32 * e + lr];
-    else xb[e - 4] = ring(slot, 1)[q * BM + wn * 128 + 32 * (e - 4) + lr];
+    if (SC == SC_MXC) {
+      const int slot = chunk_slot(kt), wd = (kt - chunk_ws(kt)) * SDW + q;
+      if (e < 4) xa[e] = ring16(slot, 0)[(wm * 128 + 32 * e + lr) * 4 + wd];
+      else xb[e - 4] = ring16(slot, 1)[(wn * 128 + 32 * (e - 4) + lr) * 4 + wd];
+    } else {
+      const int slot = kt % SC_RING;
+      if (e < 4) xa[e] = ring(slot, 0)[q * BM + wm * 128 + 32 * e + lr];
+      else xb[e - 4] = ring(slot, 1)[q * BM + wn * 128 + 32 * (e - 4) + lr];
+    }
   };
 
   issue(0);
@@ -435,7 +467,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   if (nk > 1) issue(1);
 #pragma unroll
   for (int d = 0; d < DS_HALF; ++d) frag_read<0, LDA, LDB>(f0, d, tileA(0) + offA, tileB(0) + offB, lba, lbb);
-  if (SC == SC_MX) {
+  if (MX) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) mx_item(mxa, mxb, 0, e, 0);
   }
@@ -464,6 +496,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
     }
     // phase B
     __syncthreads();
+    // SC_MXC: the scale chunk that starts at stage kt+2 goes with its tiles
+    if (SC == SC_MXC && ISSUE) {
+      if (chunk_start(kt + 2)) chunk_issue(kt + 2);
+    }
     __builtin_amdgcn_sched_barrier(0);
     // phase C: MFMA(f1); reads of the next f0 (and MX words) on the first
     // half of the MFMAs, the loads of stage kt+2 spread over all of them
@@ -488,7 +524,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (NEXT && SC == SC_MX && OP != OP_FP4) {
+    if constexpr (NEXT && MX && OP != OP_FP4) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         mxa[i] = nxa[i];
@@ -893,7 +929,9 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
       PBS_REQUIRE(((uintptr_t)a_scale & 3) == 0 && ((uintptr_t)b_scale & 3) == 0, PBS_ERR_INVALID_ARG,
                   "pbs_gemm: MXFP8 block scales must be 4-byte aligned");
       g.lda = K; g.ldb = K;
-      fn = pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_MX, 0, 0>(bf16_out);
+      // scale rows in 16-byte chunks once the row holds 4 stages of them
+      fn = K / 128 >= 4 ? pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_MXC, 0, 0>(bf16_out)
+                        : pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_MX, 0, 0>(bf16_out);
       name = "gemm_mxfp8";
       break;
     }
@@ -905,7 +943,8 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
       PBS_REQUIRE(((uintptr_t)a_scale & 3) == 0 && ((uintptr_t)b_scale & 3) == 0, PBS_ERR_INVALID_ARG,
                   "pbs_gemm: MXFP4 block scales must be 4-byte aligned");
       g.lda = K / 2; g.ldb = K / 2;
-      fn = pick_out<OP_FP4, LD_KMAJOR, LD_KMAJOR, SC_MX, 4, 4>(bf16_out);
+      fn = K / 256 >= 2 ? pick_out<OP_FP4, LD_KMAJOR, LD_KMAJOR, SC_MXC, 4, 4>(bf16_out)
+                        : pick_out<OP_FP4, LD_KMAJOR, LD_KMAJOR, SC_MX, 4, 4>(bf16_out);
       name = "gemm_mxfp4";
       break;
     }
