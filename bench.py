@@ -263,6 +263,49 @@ def recipe_table(runner, recipes, per, pre):
     return out
 
 
+def model_analysis(runner, recipes, per, pre, layers=24):
+    """The pages' model-level reading of the per-GEMM times ("How to optimize
+    Transformer-based models for low-precision training", "Using autocast mode
+    vs pre-quantized mode" and "Interpreting results for a real model"):
+    per-recipe speedup over BF16 in both modes, the model's GEMM time for its
+    24 identical layers, the MXFP8 / NVFP4 Fprop ratio per layer, the Dgrad /
+    Fprop asymmetry per layer, and the weight bytes each recipe stores."""
+    P = runner.P
+    names = [ls.name for (_, _, _, ls) in runner.layers.values()]
+    med = lambda r, n, p: float(np.median(per[(r, n, p)]["auto"]))
+    auto = {r: sum(med(r, n, p) for (n, p, *_) in runner.gemms) for r in recipes}
+    out = {"layers": layers, "per_recipe": {}}
+    for r in recipes:
+        e = {"autocast_ms_per_model": round(layers * auto[r], 2)}
+        if "bf16" in auto:
+            e["speedup_vs_bf16_autocast"] = round(auto["bf16"] / auto[r], 3)
+        if pre:
+            pm = sum(pre[(r, n, p)] for (n, p, *_) in runner.gemms)
+            e["prequant_ms_per_model"] = round(layers * pm, 2)
+            if "bf16" in recipes:
+                pb = sum(pre[("bf16", n, p)] for (n, p, *_) in runner.gemms)
+                e["speedup_vs_bf16_prequant"] = round(pb / pm, 3)
+        # stored weight bytes of the layer (codes + block scales + fp32 tensor scalars)
+        wb = 0
+        for (_, w, _, ls) in runner.layers.values():
+            if r == "bf16":
+                wb += w.numel() * 2
+                continue
+            rec = runner.PL.RECIPES[r]
+            w2d = r in ("fp8_block128", "nvfp4")
+            cb, sb = P.pbs_quantized_bytes(rec, ls.n_out, ls.k_in, int(w2d))
+            wb += cb + sb + (4 if r in ("fp8_current", "fp8_delayed", "nvfp4") else 0)
+        e["weight_MB_per_layer"] = round(wb / 1e6, 2)
+        out["per_recipe"][r] = e
+    if "mxfp8" in recipes and "nvfp4" in recipes:
+        out["mxfp8_over_nvfp4_fprop_autocast"] = {n: round(med("mxfp8", n, "fprop") / med("nvfp4", n, "fprop"), 3)
+                                                  for n in names}
+    if pre:
+        out["dgrad_over_fprop_prequant"] = {r: {n: round(pre[(r, n, "dgrad")] / pre[(r, n, "fprop")], 3) for n in names}
+                                            for r in recipes}
+    return out
+
+
 def cpu_baseline(seconds_target=20.0):
     """The CPU oracle on a bounded sample of the workload: autocast Fprop of the
     attention-out layer (W [4096, 4096]) for the first `rows` tokens, every
@@ -385,6 +428,7 @@ def main():
         log("pre-quantized GEMM timing")
         pre = runner.prequant_pass(recipes, a.prequant_iters)
     per_recipe = recipe_table(runner, recipes, per, pre)
+    model = model_analysis(runner, recipes, per, pre)
 
     next_recipes = [r for r in a.next_recipes.split(",") if r]
     nxt = {}
@@ -437,6 +481,7 @@ def main():
                      "traffic": traffic},
         "per_recipe": per_recipe,
         "next_recipes": nxt,
+        "model": model,
         "quant_GBps": qbw,
         "cpu_baseline": cpu,
     }
