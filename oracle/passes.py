@@ -27,6 +27,11 @@ after the pages' six.  Reading taken: E2M1 values with one E8M0 scale per
 quantized from the source, as MXFP8 does), and NVFP4's 4-bit training
 treatment kept: the Hadamard transform on both Wgrad operands and
 stochastic rounding of dY.
+
+Channel-wise FP8 ("Faster training throughput in FP8 precision with NVIDIA
+NeMo", "Scaling recipe granularity": one factor per channel, between
+per-tensor and 2D blocks) is the other next recipe: E4M3 for every role, one
+fp32 scale per row of each contraction-contiguous copy.
 """
 from __future__ import annotations
 
@@ -38,7 +43,7 @@ from . import recipes as R
 from .formats import bf16_to_f32
 
 RECIPES = ("bf16", "fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "nvfp4")
-NEXT_RECIPES = ("mxfp4",)
+NEXT_RECIPES = ("mxfp4", "fp8_channel")
 ALL_RECIPES = RECIPES + NEXT_RECIPES
 
 
@@ -66,6 +71,8 @@ class QOperand:
             return R.dequant_nvfp4(self.codes, self.scale, self.tensor_scale_inv, self.weight_2d)
         if self.recipe == "mxfp4":
             return R.dequant_mxfp4(self.codes, self.scale)
+        if self.recipe == "fp8_channel":
+            return R.dequant_channel(self.codes, self.scale)
         raise ValueError(self.recipe)
 
 
@@ -118,6 +125,9 @@ def quantize_operand(recipe, src, orient, x_bits, pass_, delayed_state=None, see
         return QOperand(recipe, "e2m1", packed, scale=d_codes, tensor_scale_inv=S_dec,
                         weight_2d=w2d, extra={"amax": A, "S_enc": S_enc, "rht": rht,
                                               "sr": sr is not None})
+    if recipe == "fp8_channel":
+        codes, s_inv = R.quantize_channel(x_bits, orient)
+        return QOperand(recipe, "e4m3", codes, scale=s_inv)
     if recipe == "mxfp4":
         t = bf16_to_f32(x_bits)
         rht = pass_ == "wgrad"

@@ -180,6 +180,29 @@ def quantize_block128(x_bits, orient="row", weight_2d=False):
 
 
 # ---------------------------------------------------------------------------
+# Channel-wise FP8: one fp32 scale per row of the contraction-contiguous copy
+# ---------------------------------------------------------------------------
+def quantize_channel(x_bits, orient="row"):
+    """Channel-wise FP8 (E4M3): one scale per row of the copy.
+
+    "Faster training throughput in FP8 precision with NVIDIA NeMo",
+    "Scaling recipe granularity": channel-wise scaling applies one factor per
+    channel (row or column), a granularity between per-tensor and 2D blocks.
+    Reading taken: one scale per row of the contraction-contiguous copy (the
+    row copy: per row of x; the col copy: per column of x), computed like the
+    sub-channel scales -- s_r = fp32(448 / amax_r) with the per-tensor corner
+    rules, stored as fp32(1 / s_r); codes = enc_E4M3(fp32(x * s_r)).  In the
+    GEMM both factors are constant along K, so C = acc * fp32(sa_inv[m] *
+    sb_inv[n]).  Returns (codes [rows, cols], s_inv [rows]).
+    """
+    t = _oriented(x_bits, orient)
+    a = np.max(np.abs(t), axis=1) if t.shape[1] else np.zeros(t.shape[0], np.float32)
+    s, s_inv = scale_from_amax(a.astype(np.float32), 448.0)
+    v = (t * s[:, None]).astype(np.float32)
+    return E4M3.encode(v), s_inv.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
 # MXFP8: 32-value blocks, E8M0 power-of-two scales
 # ---------------------------------------------------------------------------
 _E8M0_THRESHOLDS = 448.0 * np.ldexp(1.0, np.arange(255) - 127)   # 448 * 2**e, e = -127..127
@@ -400,6 +423,10 @@ def dequant_pertensor(codes, fmt, s_inv):
 def dequant_block128(codes, s_inv, weight_2d=False):
     br, bc = (128, 128) if weight_2d else (1, 128)
     return E4M3.decode(codes) * _expand(np.asarray(s_inv, dtype=np.float32).astype(np.float64), br, bc)
+
+
+def dequant_channel(codes, s_inv):
+    return E4M3.decode(codes) * np.asarray(s_inv, np.float32).astype(np.float64)[:, None]
 
 
 def dequant_mxfp8(codes, e8m0_codes):

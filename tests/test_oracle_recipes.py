@@ -216,6 +216,49 @@ def test_block128_2d_col_is_transpose():
 
 
 # ---------------------------------------------------------------------------
+# channel-wise FP8
+# ---------------------------------------------------------------------------
+def test_channel_row_is_pertensor_of_each_row():
+    """A row of the channel-wise copy is that row quantized on its own with
+    per-tensor current scaling (pinned above exhaustively)."""
+    x = W.activations(24, 384, seed=15)
+    codes, s_inv = R.quantize_channel(x, "row")
+    for i in range(x.shape[0]):
+        c1, si1, _ = R.quantize_current(x[i:i + 1], "e4m3", "row")
+        assert (codes[i] == c1[0]).all() and s_inv[i] == si1, i
+
+
+def test_channel_bruteforce_and_col_copy():
+    x = W.grads(3, 256, seed=16)
+    codes, s_inv = R.quantize_channel(x, "row")
+    t = bf16_to_f32(x)
+    for i in range(3):
+        a = max(abs(float(z)) for z in t[i])
+        s = frac_to_f32(Fraction(448) / Fraction(a)) if a else 1.0
+        assert float(s_inv[i]) == frac_to_f32(1 / Fraction(s))
+        v = np.array([frac_to_f32(Fraction(float(z)) * Fraction(s)) for z in t[i]], dtype=np.float32)
+        assert (codes[i] == _brute_e4m3(v)).all()
+        assert np.abs(E4M3.decode(codes[i])).max() == 448.0
+    cc, sc = R.quantize_channel(x, "col")
+    cr, sr_ = R.quantize_channel(np.ascontiguousarray(x.T), "row")
+    assert (cc == cr).all() and (sc == sr_).all()
+
+
+def test_channel_outlier_stays_in_its_row_and_zero_row():
+    x = W.activations(6, 256, seed=17, n_outlier_channels=0)
+    t = bf16_to_f32(x).copy()
+    t[2, 100] = 3e4
+    t[4, :] = 0.0
+    t[4, 7] = -0.0
+    xo = W.f32_to_bf16_bits(t)
+    c0, s0 = R.quantize_channel(x, "row")
+    c1, s1 = R.quantize_channel(xo, "row")
+    changed = sorted(set(np.nonzero((c0 != c1).any(axis=1))[0]) | set(np.nonzero(s0 != s1)[0]))
+    assert changed == [2, 4]
+    assert s1[4] == 1.0 and (c1[4] & 0x7F == 0).all() and c1[4, 7] == 0x80
+
+
+# ---------------------------------------------------------------------------
 # MXFP8
 # ---------------------------------------------------------------------------
 def test_mx_exponent_closed_form_all_bf16():
@@ -619,6 +662,8 @@ def test_tiny_case_all_recipes_gemm_close_to_bf16_product():
     # finer granularity tracks the bf16 product more closely
     assert errs["fp8_block128"] <= errs["fp8_current"] * 1.05
     assert errs["mxfp8"] < 0.1 and errs["nvfp4"] < 0.3 and errs["mxfp4"] < 0.3
+    # one scale per row tracks at least as well as one per tensor
+    assert errs["fp8_channel"] <= errs["fp8_current"] * 1.05 and errs["fp8_channel"] < 0.1
     for rec in ("fp8_current", "fp8_delayed", "fp8_block128", "mxfp8"):
         assert errs[rec] < 0.1, (rec, errs[rec])
 
