@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 RECIPES = ["bf16", "fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "nvfp4"]
 # built beyond the pages' six (MXFP4: E2M1 with E8M0 per 32 on the FP4 matrix
 # rate); timed after the step and reported apart, never part of `value`
-NEXT_RECIPES = ["mxfp4"]
+NEXT_RECIPES = ["mxfp4", "fp8_channel"]
 PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2, "fp4": 10066.3}
 HBM_GBPS = 8000.0
 
@@ -57,6 +57,8 @@ def kernel_key(recipe, pass_):
         return "gemm_mxfp8", "fp8"
     if recipe == "mxfp4":
         return "gemm_mxfp4", "fp4"
+    if recipe == "fp8_channel":
+        return "gemm_fp8_channel", "fp8"
     return ("gemm_nvfp4_w2d" if pass_ != "wgrad" else "gemm_nvfp4_1d"), "fp16"
 
 
@@ -185,6 +187,10 @@ def quant_bandwidth(runner, iters=5):
         ("nvfp4_rht_sr_cast_col", "nvfp4", "dy", "col", "wgrad", 2 + 0.5 + 1 / 16),
         ("mxfp4_cast_row", "mxfp4", "x", "row", "fprop", 2 + 0.5 + 1 / 32),
         ("mxfp4_rht_sr_cast_col", "mxfp4", "dy", "col", "wgrad", 2 + 0.5 + 1 / 32),
+        # one fp32 scale per 16384-long row (row copy) / 15872-long column (col
+        # copy); the col copy reads x twice (column maxima, then the cast)
+        ("fp8_channel_cast_row", "fp8_channel", "x", "row", "fprop", 2 + 1 + 4 / 16384),
+        ("fp8_channel_cast_col", "fp8_channel", "x", "col", "wgrad", 2 + 1 + 4 / 15872),
     ]
     res = {}
     P = runner.P

@@ -70,7 +70,8 @@ typedef enum {
 } pbs_format;
 
 /* Scaling recipes ([NEMO] "What are the strengths and trade-offs of the
- * FP8 scaling recipes?"; [FP4] "Technical deep-dive"). */
+ * FP8 scaling recipes?", "Scaling recipe granularity"; [FP4] "Technical
+ * deep-dive"). */
 typedef enum {
   PBS_RECIPE_BF16 = 0,         /* no quantization: bf16 operands            */
   PBS_RECIPE_FP8_CURRENT = 1,  /* per-tensor scale from this tensor's amax  */
@@ -80,7 +81,9 @@ typedef enum {
   PBS_RECIPE_MXFP8 = 4,        /* E8M0 scale per 32 values, E4M3 values     */
   PBS_RECIPE_NVFP4 = 5,        /* E2M1 values, E4M3 scale per 16 values (1x16
                                   act/grad, 16x16 weight), fp32 per tensor  */
-  PBS_RECIPE_MXFP4 = 6         /* E2M1 values, E8M0 scale per 32 values     */
+  PBS_RECIPE_MXFP4 = 6,        /* E2M1 values, E8M0 scale per 32 values     */
+  PBS_RECIPE_FP8_CHANNEL = 7   /* fp32 scale per row of each copy (per
+                                  channel), E4M3 values                     */
 } pbs_recipe;
 
 /* The three GEMMs of a linear layer ([LP] "Using autocast mode vs
@@ -187,6 +190,15 @@ float* pbs_delayed_scale_inv(void* state); /* device address of `scale_inv` */
  *    amax_b <= 6 * 2^e (no element saturates), codes = enc_E2M1(x * 2^-e).
  *    Same flags as NVFP4 (PBS_FLAG_RHT16 col copy only, PBS_FLAG_SR).
  *    `scale` unused.
+ *  recipe FP8_CHANNEL ([NEMO] "Scaling recipe granularity": per-channel
+ *    scaling, between one scale per tensor and blocks): fmt E4M3; one fp32
+ *    scale per row of each copy, i.e. per row of x for the row copy
+ *    (row_scales [rows]) and per column of x for the col copy (col_scales
+ *    [cols]); stored scale = fp32(1 / s_r), s_r = fp32(448 / amax_r) (1 for
+ *    an all-zero row, FLT_MAX on overflow); codes = enc(fp32(x * s_r)).
+ *    Scales 4-byte aligned.  The row copy reads x once; the col copy reads
+ *    it twice (column maxima, then the cast) and uses col_scales as the
+ *    running maxima in between.  `scale` unused.
  *  Outputs for an orientation not in orient_mask may be NULL.
  * ------------------------------------------------------------------- */
 pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t cols,
@@ -220,6 +232,10 @@ pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t
  *    [N, K/16] for WGRAD; a_tensor_scale / b_tensor_scale = S_dec of each.
  *  - MXFP4: A, B packed E2M1 [M, K/2], [N, K/2]; a_scale = E8M0 [M, K/32],
  *    b_scale = E8M0 [N, K/32]; tensor scales unused.
+ *  - FP8_CHANNEL: a_fmt = b_fmt = E4M3; a_scale = fp32 [M] and b_scale =
+ *    fp32 [N] (the stored scale of each operand row, pbs_cast's channel
+ *    scales), 16-byte aligned; C[m, n] = acc * fp32(a_scale[m] *
+ *    b_scale[n]); tensor scales unused.
  * BF16 recipe: operands in their natural storage -- FPROP: A = X [M, K],
  *    B = W [N, K]; DGRAD: A = dY [M, K], B = W stored [K, N]; WGRAD:
  *    A = X stored [K, M], B = dY stored [K, N].
@@ -229,7 +245,8 @@ pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t
  *   (BF16); each stored operand row at most 16 MiB.  K == 0 writes zeros
  *   to C.
  * Alignment (else PBS_ERR_INVALID_ARG): A, B, C 16-byte aligned; MXFP8,
- *   MXFP4 and NVFP4 block scales 4-byte aligned.
+ *   MXFP4 and NVFP4 block scales 4-byte aligned; FP8_CHANNEL scales
+ *   16-byte aligned.
  * Accuracy: fp32 accumulation; the 8-bit instructions (FP8 recipes) sum
  *   each aligned group of 8 products in one step that keeps bits down to
  *   2^-13 of the group's largest product; BF16 and NVFP4 (decoded exactly to

@@ -76,6 +76,8 @@ pbs_status pbs_quantized_bytes(pbs_recipe recipe, int64_t rows, int64_t cols, in
       *code_bytes = (size_t)(n / 2);
       *scale_bytes = (size_t)(weight_2d ? (rows / 16) * (cols / 16) : rows * (cols / 16));
       break;
+    case PBS_RECIPE_FP8_CHANNEL:
+      *code_bytes = (size_t)n; *scale_bytes = (size_t)rows * 4; break;
     case PBS_RECIPE_MXFP4:
       PBS_REQUIRE(cols % 32 == 0, PBS_ERR_SHAPE, "MXFP4 needs cols % 32 == 0");
       *code_bytes = (size_t)(n / 2); *scale_bytes = (size_t)(rows * (cols / 32)); break;

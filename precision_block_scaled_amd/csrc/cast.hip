@@ -29,6 +29,10 @@
 //    gradients.  d = enc_E4M3(fp32(fp32(amax_b / 6) * S_enc)), e_b =
 //    fp32(S_enc / d), codes = enc_E2M1(fp32(x * e_b)) or its stochastic
 //    rounding with Philox4x32-10 (counter = logical element index).
+//  channel-wise FP8 -- "Faster training throughput in FP8 precision with
+//    NVIDIA NeMo", "Scaling recipe granularity" (per-channel scaling): one
+//    scale per row of each contraction-contiguous copy, s_r = fp32(448 /
+//    amax_r) with the per-tensor corner rules, stored as fp32(1 / s_r).
 //  MXFP4 -- "Accelerate LLM training with NVFP4 on Blackwell", "Technical
 //    deep-dive" (the 32-value MX format NVFP4 refines): E2M1 values, E8M0
 //    power-of-two scale per 32, the smallest exponent that brings the block
@@ -41,7 +45,7 @@
 
 namespace pbs {
 
-enum { R_TENSOR = 0, R_BLOCK128 = 1, R_MX = 2, R_NV = 3, R_MX4 = 4 };
+enum { R_TENSOR = 0, R_BLOCK128 = 1, R_MX = 2, R_NV = 3, R_MX4 = 4, R_CHAN = 5 };
 enum { F_E4M3 = 0, F_E5M2 = 1 };
 
 constexpr int TILE = 128;
@@ -692,6 +696,8 @@ __global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
     }
     if (AMAX && valid) amx = amx > mbits ? amx : mbits;
     const int64_t gc = c0 + col, gr = r0 + 16 * rs;
+    if (RECIPE == R_CHAN)   // the column's amax (fp32 bits), measured by chan_colmax_kernel
+      tscale = scale_from_amax(__uint_as_float(((const uint32_t*)a.col_scales)[valid ? gc : c0]), 448.0f);
     uint32_t rnd[16];
     if (SR) {
 #pragma unroll
@@ -715,12 +721,217 @@ __global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
       sc32 = (float*)a.col_scales + gc * (a.R / 128) + gr / 128;
       writer = (rs & 7) == 0;
     }
-    quantize_segment<RECIPE, FMT, SR>(v, mbits, tscale, valid, codes, sc8, sc32, writer, rnd);
+    quantize_segment<RECIPE == R_CHAN ? R_TENSOR : RECIPE, FMT, SR>(v, mbits, tscale, valid, codes, sc8, sc32,
+                                                                     writer, rnd);
   }
   if (AMAX) {
     __shared__ uint32_t s_part[4];
     wg_amax_fold(amx, a.amax_out, s_part);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Channel-wise FP8: one scale per row of the copy.
+//
+// Row copy: a team of T lanes (one wave, or the whole 256-thread workgroup
+// for long rows) owns a row; lane l holds the row's 16-value segments
+// l, l + T, ... (up to NCH of them) in registers, so the row is read from
+// HBM once: max over the team, scale, encode, store.  Rows longer than
+// 256 * 16 * 16 values (NCH = 0) are read twice (the second read mostly
+// from L2).
+//
+// Col copy: one scale per column of x.  chan_colmax_kernel folds column
+// maxima into col_scales (fp32 bits, cleared first); cast_col_kernel
+// <R_CHAN> encodes with them; chan_finalize_kernel turns each maximum into
+// the stored fp32(1 / s) in place.
+// ---------------------------------------------------------------------------
+template <int T, int NCH>
+__global__ __launch_bounds__(256) void chan_row_kernel(CastArgs a) {
+  constexpr int TEAMS = 256 / T;
+  const int tl = threadIdx.x % T;
+  const int64_t row = (int64_t)blockIdx.x * TEAMS + threadIdx.x / T;
+  const bool live = row < a.R;
+  const int64_t spr = a.C / 16;
+  const bf16_t* xr = a.x + (live ? row : 0) * a.C;
+  uint8_t* cr = a.row_codes + (live ? row : 0) * a.C;
+  __shared__ uint32_t s_part[4];
+  uint32_t m = 0;
+  if (NCH > 0) {
+    uint32_t w[NCH > 0 ? NCH : 1][8];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int64_t sg = (int64_t)j * T + tl;
+      if (live && sg < spr) {
+        const uint4 v0 = ld_nt16(xr + sg * 16), v1 = ld_nt16(xr + sg * 16 + 8);
+        w[j][0] = v0.x; w[j][1] = v0.y; w[j][2] = v0.z; w[j][3] = v0.w;
+        w[j][4] = v1.x; w[j][5] = v1.y; w[j][6] = v1.z; w[j][7] = v1.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[j][i] = 0u;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const uint32_t mj = bf16_absmax16(w[j]);
+      m = m > mj ? m : mj;
+    }
+    m = group_max<64>(m);
+    if (T == 256) {
+      if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = m;
+      __syncthreads();
+      m = s_part[0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) m = m > s_part[i] ? m : s_part[i];
+    }
+    const float s = scale_from_amax(__uint_as_float(m << 16), 448.0f);
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int64_t sg = (int64_t)j * T + tl;
+      float v[16];
+      bf16x16_to_f32(w[j], v);
+      quantize_segment<R_TENSOR, F_E4M3, false>(v, 0u, s, live && sg < spr, cr + sg * 16, nullptr, nullptr,
+                                                false, nullptr);
+    }
+    if (live && tl == 0) ((float*)a.row_scales)[row] = 1.0f / s;
+  } else {
+    for (int64_t sg = tl; sg < spr; sg += T) {
+      uint32_t w[8];
+      const uint4 v0 = ld_nt16(xr + sg * 16), v1 = ld_nt16(xr + sg * 16 + 8);
+      w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+      w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+      const uint32_t mj = bf16_absmax16(w);
+      m = m > mj ? m : mj;
+    }
+    m = group_max<64>(m);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = s_part[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) m = m > s_part[i] ? m : s_part[i];
+    const float s = scale_from_amax(__uint_as_float(m << 16), 448.0f);
+    for (int64_t sg = tl; sg < spr; sg += T) {
+      uint32_t w[8];
+      const uint4 v0 = *(const uint4*)(xr + sg * 16), v1 = *(const uint4*)(xr + sg * 16 + 8);
+      w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+      w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+      float v[16];
+      bf16x16_to_f32(w, v);
+      quantize_segment<R_TENSOR, F_E4M3, false>(v, 0u, s, true, cr + sg * 16, nullptr, nullptr, false, nullptr);
+    }
+    if (tl == 0) ((float*)a.row_scales)[row] = 1.0f / s;
+  }
+}
+
+// Column maxima of x: lane l of a wave reads columns c0 + 8 l .. + 7 of one
+// row at a time (a wave covers 512 columns of a row, 1 KB contiguous); the
+// four waves take rows 4 apart in a chunk of `rows_per_wg` rows.  The
+// workgroup's 512 maxima then go to col_scales (fp32 bits of |x|) with one
+// atomic max each, skipped when the stored value is already as large.
+constexpr int CM_COLS = 512;
+
+__global__ __launch_bounds__(256) void chan_colmax_kernel(CastArgs a, int rows_per_wg) {
+  __shared__ uint32_t part[4][CM_COLS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * CM_COLS + 8 * lane;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_wg;
+  const int64_t r1 = min(a.R, r0 + rows_per_wg);
+  u16x2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+  if (c < a.C) {
+    int64_t r = r0 + w;
+    for (; r + 12 < r1; r += 16) {          // four rows per step, loads first
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = ld_nt16(a.x + (r + 4 * u) * a.C + c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        m[0] = __builtin_elementwise_max(m[0], __builtin_bit_cast(u16x2, v[u].x & 0x7FFF7FFFu));
+        m[1] = __builtin_elementwise_max(m[1], __builtin_bit_cast(u16x2, v[u].y & 0x7FFF7FFFu));
+        m[2] = __builtin_elementwise_max(m[2], __builtin_bit_cast(u16x2, v[u].z & 0x7FFF7FFFu));
+        m[3] = __builtin_elementwise_max(m[3], __builtin_bit_cast(u16x2, v[u].w & 0x7FFF7FFFu));
+      }
+    }
+    for (; r < r1; r += 4) {
+      const uint4 v = ld_nt16(a.x + r * a.C + c);
+      m[0] = __builtin_elementwise_max(m[0], __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu));
+      m[1] = __builtin_elementwise_max(m[1], __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu));
+      m[2] = __builtin_elementwise_max(m[2], __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu));
+      m[3] = __builtin_elementwise_max(m[3], __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    part[w][8 * lane + 2 * i] = m[i].x;
+    part[w][8 * lane + 2 * i + 1] = m[i].y;
+  }
+  __syncthreads();
+  uint32_t* amax = (uint32_t*)a.col_scales;
+  for (int i = threadIdx.x; i < CM_COLS; i += 256) {
+    const int64_t col = (int64_t)blockIdx.x * CM_COLS + i;
+    if (col >= a.C) break;
+    uint32_t v = part[0][i];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) v = v > part[k][i] ? v : part[k][i];
+    v <<= 16;                                // fp32 bits of the bf16 maximum
+    if (v > __builtin_nontemporal_load(amax + col)) atomicMax(amax + col, v);
+  }
+}
+
+__global__ void chan_finalize_kernel(float* sc, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) sc[i] = 1.0f / scale_from_amax(sc[i], 448.0f);
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+template <int T, int NCH>
+static void launch_chan_row(const CastArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((chan_row_kernel<T, NCH>), dim3((unsigned)ceil_div(a.R, 256 / T)), dim3(256), 0, stream, a);
+}
+
+// The channel-wise cast: row copy, then col copy.
+static pbs_status cast_channel(const CastArgs& a, bool row, bool col, hipStream_t stream) {
+  if (row && a.R > 0) {
+    if (a.C == 0) {   // empty rows: scale 1
+      hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(a.R, 256), 1024)), dim3(256), 0,
+                         stream, (uint32_t*)a.row_scales, a.R, 0x3F800000u);
+    } else {
+      const int64_t spr = a.C / 16;
+      log_dispatch("cast_channel_row rows=%lld cols=%lld", (long long)a.R, (long long)a.C);
+      if (spr <= 64) launch_chan_row<64, 1>(a, stream);
+      else if (spr <= 128) launch_chan_row<64, 2>(a, stream);
+      else if (spr <= 256) launch_chan_row<64, 4>(a, stream);
+      else if (spr <= 512) launch_chan_row<64, 8>(a, stream);
+      else if (spr <= 1024) launch_chan_row<256, 4>(a, stream);
+      else if (spr <= 2048) launch_chan_row<256, 8>(a, stream);
+      else if (spr <= 4096) launch_chan_row<256, 16>(a, stream);
+      else launch_chan_row<256, 0>(a, stream);
+    }
+  }
+  if (col && a.C > 0) {
+    if (a.R == 0) {
+      hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(a.C, 256), 1024)), dim3(256), 0,
+                         stream, (uint32_t*)a.col_scales, a.C, 0x3F800000u);
+    } else {
+      hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(a.C, 256), 1024)), dim3(256), 0,
+                         stream, (uint32_t*)a.col_scales, a.C, 0u);
+      // about 2048 workgroups, chunks of whole 16-row steps
+      const int64_t gx = ceil_div(a.C, CM_COLS);
+      int64_t rpw = ceil_div(a.R * gx, 2048);
+      rpw = std::max<int64_t>(16, ceil_div(rpw, 16) * 16);
+      const dim3 g1((unsigned)gx, (unsigned)ceil_div(a.R, rpw));
+      log_dispatch("cast_channel_col rows=%lld cols=%lld colmax grid=%ux%u", (long long)a.R, (long long)a.C, g1.x,
+                   g1.y);
+      hipLaunchKernelGGL(chan_colmax_kernel, g1, dim3(256), 0, stream, a, (int)rpw);
+      const dim3 g2((unsigned)ceil_div(a.C, CT_C), (unsigned)ceil_div(a.R, CT_R));
+      hipLaunchKernelGGL((cast_col_kernel<R_CHAN, F_E4M3, false, false, false>), g2, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(chan_finalize_kernel, dim3((unsigned)ceil_div(a.C, 256)), dim3(256), 0, stream,
+                         (float*)a.col_scales, a.C);
+    }
+  }
+  return check_launch("pbs_cast");
 }
 
 __global__ void zero_u32_kernel(uint32_t* p) {
@@ -868,6 +1079,14 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
                 : pick_orient<R_MX4, F_E4M3, false, false, false, false>(orient_mask);
       name = "cast_mxfp4";
       break;
+    }
+    case PBS_RECIPE_FP8_CHANNEL: {
+      PBS_REQUIRE(fmt == PBS_FMT_E4M3, PBS_ERR_UNSUPPORTED, "pbs_cast: FP8_CHANNEL takes E4M3");
+      PBS_REQUIRE((!row || row_scales) && (!col || col_scales), PBS_ERR_INVALID_ARG,
+                  "pbs_cast: channel scales output is null");
+      PBS_REQUIRE((!row || ((uintptr_t)row_scales & 3) == 0) && (!col || ((uintptr_t)col_scales & 3) == 0),
+                  PBS_ERR_INVALID_ARG, "pbs_cast: channel scales must be 4-byte aligned");
+      return cast_channel(a, row, col, stream);
     }
     case PBS_RECIPE_BF16:
       return set_error(PBS_ERR_UNSUPPORTED, "pbs_cast: the BF16 recipe has no cast");

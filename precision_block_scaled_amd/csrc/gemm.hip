@@ -52,7 +52,9 @@ namespace pbs {
 
 enum { OP_BF16 = 0, OP_FP8 = 2, OP_FP4 = 3 };               // what the MFMA consumes
 enum { LD_KMAJOR = 0, LD_MNMAJOR = 1 };                      // how a tile reaches LDS
-enum { SC_NONE = 0, SC_TENSOR = 1, SC_MX = 2, SC_MXC = 3 };   // SC_MXC: MX scales loaded in 16-byte chunks
+// SC_MXC: MX scales loaded in 16-byte chunks; SC_CHAN: one fp32 scale per row
+// of A and of B, applied in the epilogue
+enum { SC_NONE = 0, SC_TENSOR = 1, SC_MX = 2, SC_MXC = 3, SC_CHAN = 4 };
 
 constexpr int BN = 256;
 constexpr int SC_OFF = 4 * TILEB;       // scale-row ring after 2 stages x 2 operands
@@ -540,6 +542,34 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
 
   float post = 1.0f;
   if (SC == SC_TENSOR) post = (*g.a_ts) * (*g.b_ts);
+  if constexpr (SC == SC_CHAN) {
+    // acc[i][j][4 q + r] is C[row, col] with row = m0 + 128 wm + 32 i + 8 q +
+    // 4 lg + r, col = n0 + 128 wn + 32 j + lr (store_tile's lane layout);
+    // rows and columns past the end read the last scale (never stored)
+    const float* sa = (const float*)g.a_scale;
+    const float* sb = (const float*)g.b_scale;
+    const int lr = lane & 31, lg = lane >> 5;
+    float fb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 128 * wn + 32 * j + lr;
+      fb[j] = sb[n < g.N ? n : g.N - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int mr = m0 + 128 * wm + 32 * i + 8 * q + 4 * lg;   // a multiple of 4, as is M
+        const float4 s4 = *(const float4*)(sa + (mr < g.M ? mr : g.M - 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j][4 * q + 0] *= s4.x * fb[j];
+          acc[i][j][4 * q + 1] *= s4.y * fb[j];
+          acc[i][j][4 * q + 2] *= s4.z * fb[j];
+          acc[i][j][4 * q + 3] *= s4.w * fb[j];
+        }
+      }
+  }
   store_tile<OUT_BF16>(acc, g, smem, m0, n0, w, wm, wn, lane, post);
 }
 
@@ -907,6 +937,18 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
       g.lda = K; g.ldb = K;
       fn = pick_fp8<SC_TENSOR>(a_fmt == PBS_FMT_E5M2, b_fmt == PBS_FMT_E5M2, bf16_out);
       name = "gemm_fp8_tensor";
+      break;
+    }
+    case PBS_RECIPE_FP8_CHANNEL: {
+      PBS_REQUIRE(a_fmt == PBS_FMT_E4M3 && b_fmt == PBS_FMT_E4M3, PBS_ERR_UNSUPPORTED,
+                  "pbs_gemm: FP8_CHANNEL takes E4M3 operands");
+      PBS_REQUIRE(a_scale && b_scale, PBS_ERR_INVALID_ARG, "pbs_gemm: channel scales are null");
+      PBS_REQUIRE(((uintptr_t)a_scale & 15) == 0 && ((uintptr_t)b_scale & 15) == 0, PBS_ERR_INVALID_ARG,
+                  "pbs_gemm: FP8_CHANNEL scales must be 16-byte aligned");
+      PBS_REQUIRE(K % 128 == 0, PBS_ERR_SHAPE, "pbs_gemm: FP8 needs K %% 128 == 0");
+      g.lda = K; g.ldb = K;
+      fn = pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_CHAN, 0, 0>(bf16_out);
+      name = "gemm_fp8_channel";
       break;
     }
     case PBS_RECIPE_FP8_BLOCK128: {

@@ -11,7 +11,8 @@ separate GEMMs), with X [M, K], W stored [N, K], dY [M, N]:
   wgrad: A = X col copy,  B = dY col copy
 
 Format roles: per-tensor FP8 uses E4M3 for X and W, E5M2 for dY;
-sub-channel FP8 and MXFP8 use E4M3; NVFP4 and MXFP4 use E2M1.  Weights
+sub-channel FP8, channel-wise FP8 (one fp32 scale per row of each copy) and
+MXFP8 use E4M3; NVFP4 and MXFP4 use E2M1.  Weights
 take 2D blocks (128x128 sub-channel, 16x16 NVFP4; MXFP4 keeps 1x32 blocks
 along the contraction axis for every operand).  NVFP4 and MXFP4 apply the
 random Hadamard transform to both Wgrad operands and stochastic rounding
@@ -25,7 +26,8 @@ import torch
 
 from . import (PBS_COL, PBS_DGRAD, PBS_FLAG_RHT16, PBS_FLAG_SR, PBS_FMT_BF16, PBS_FMT_E2M1,
                PBS_FMT_E4M3, PBS_FMT_E5M2, PBS_FMT_F32, PBS_FPROP, PBS_RECIPE_BF16,
-               PBS_RECIPE_FP8_BLOCK128, PBS_RECIPE_FP8_CURRENT, PBS_RECIPE_FP8_DELAYED,
+               PBS_RECIPE_FP8_BLOCK128, PBS_RECIPE_FP8_CHANNEL, PBS_RECIPE_FP8_CURRENT,
+               PBS_RECIPE_FP8_DELAYED,
                PBS_RECIPE_MXFP4, PBS_RECIPE_MXFP8, PBS_RECIPE_NVFP4, PBS_ROW, PBS_WGRAD, pbs_amax,
                pbs_cast,
                pbs_delayed_init, pbs_delayed_scale, pbs_delayed_scale_inv, pbs_delayed_state_bytes,
@@ -39,6 +41,7 @@ RECIPES = {
     "mxfp8": PBS_RECIPE_MXFP8,
     "nvfp4": PBS_RECIPE_NVFP4,
     "mxfp4": PBS_RECIPE_MXFP4,
+    "fp8_channel": PBS_RECIPE_FP8_CHANNEL,
 }
 LAYOUTS = {"fprop": PBS_FPROP, "dgrad": PBS_DGRAD, "wgrad": PBS_WGRAD}
 ROLES = {"fprop": (("x", "row"), ("w", "row")),
@@ -90,6 +93,8 @@ def _empty_copy(recipe, rows, cols, w2d, device):
               else torch.empty((rows, cols // 128), dtype=torch.float32, device=device))
     elif recipe == "mxfp8":
         sc = torch.empty((rows, cols // 32), dtype=torch.uint8, device=device)
+    elif recipe == "fp8_channel":
+        sc = torch.empty((rows,), dtype=torch.float32, device=device)
     else:
         sc = None
     return codes, sc
@@ -170,7 +175,7 @@ def quantize(recipe, x, src, orient, pass_, state=None, out=None, ws=None, strea
         pbs_cast(rec, x, R, C, fmt, rmask, 0, 0, 0, state.scale_ptr, state.amax, row_c, row_s,
                  col_c, col_s, stream)
         out.tensor_scale_inv = state.scale_inv_ptr
-    elif recipe in ("fp8_block128", "mxfp8"):
+    elif recipe in ("fp8_block128", "mxfp8", "fp8_channel"):
         pbs_cast(rec, x, R, C, fmt, rmask, int(w2d), 0, 0, None, None, row_c, row_s, col_c, col_s,
                  stream)
     elif recipe == "nvfp4":

@@ -127,3 +127,5 @@ def test_quantized_bytes_accounting():
     assert P.pbs_quantized_bytes(P.PBS_RECIPE_FP8_BLOCK128, 256, 256, 1) == (65536, 16)
     assert P.pbs_quantized_bytes(P.PBS_RECIPE_FP8_BLOCK128, 256, 256, 0) == (65536, 256 * 2 * 4)
     _expect(2, P.pbs_quantized_bytes, P.PBS_RECIPE_MXFP8, 16, 48, 0)
+    # channel-wise FP8: one fp32 scale per row
+    assert P.pbs_quantized_bytes(P.PBS_RECIPE_FP8_CHANNEL, 48, 80, 0) == (48 * 80, 48 * 4)

@@ -45,7 +45,7 @@ MODELS = {
     "llama3_8b": (8192, W.layer_shapes(L3["hidden"], L3["intermediate"], L3["heads"], L3["kv_heads"],
                                        L3["gated"])),
 }
-FP8_MFMA = {"fp8_current", "fp8_delayed", "fp8_block128", "mxfp8"}
+FP8_MFMA = {"fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "fp8_channel"}
 FMAX = {"e4m3": 448.0, "e5m2": 57344.0}
 SEED = 42
 
@@ -93,6 +93,9 @@ class OracleCopy:
         elif recipe == "fp8_block128":
             self.codes, self.scales = R.quantize_block128(sl, orient, weight_2d=w2d)
             self.deq = R.dequant_block128(self.codes, self.scales, w2d)
+        elif recipe == "fp8_channel":                   # a copy row's scale is its own
+            self.codes, self.scales = R.quantize_channel(sl, orient)
+            self.deq = R.dequant_channel(self.codes, self.scales)
         elif recipe == "mxfp8":
             self.codes, self.scales = R.quantize_mxfp8(sl, orient)
             self.deq = R.dequant_mxfp8(self.codes, self.scales)
@@ -209,7 +212,8 @@ RECIPES = ["bf16", "fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "nvfp4
 CASES = ([("codonfm", n, r) for n in ("qkv", "attn_out", "mlp_up", "mlp_down") for r in RECIPES]
          + [("llama3_8b", n, r) for n in ("qkv", "attn_out", "mlp_up", "mlp_down") for r in RECIPES]
          + [("codonfm_32k", n, r) for n in ("mlp_up", "mlp_down") for r in ("mxfp8", "nvfp4", "fp8_block128")]
-         + [(m, n, "mxfp4") for m in ("codonfm", "llama3_8b") for n in ("qkv", "attn_out", "mlp_up", "mlp_down")])
+         + [(m, n, r) for r in ("mxfp4", "fp8_channel") for m in ("codonfm", "llama3_8b")
+            for n in ("qkv", "attn_out", "mlp_up", "mlp_down")])
 
 
 @pytest.mark.parametrize("model,name,recipe", CASES)
