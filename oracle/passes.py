@@ -32,6 +32,14 @@ Channel-wise FP8 ("Faster training throughput in FP8 precision with NVIDIA
 NeMo", "Scaling recipe granularity": one factor per channel, between
 per-tensor and 2D blocks) is the other next recipe: E4M3 for every role, one
 fp32 scale per row of each contraction-contiguous copy.
+
+The other sub-channel block pairings (same page, same section: "1D1D" and
+"1D2D" beside the 1x128-activation / 128x128-weight example) are read as
+naming the block shape of (activations and gradients, weights), 1D = 1x128
+and 2D = 128x128: the recipe above is 1D2D; "fp8_block128_1d1d" gives every
+tensor 1x128 blocks along the contraction axis (the weight's col copy is
+quantized from the source, not transposed), "fp8_block128_2d2d" gives every
+tensor 128x128 blocks (each col copy is the transposed row copy).
 """
 from __future__ import annotations
 
@@ -43,7 +51,9 @@ from . import recipes as R
 from .formats import bf16_to_f32
 
 RECIPES = ("bf16", "fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "nvfp4")
-NEXT_RECIPES = ("mxfp4", "fp8_channel")
+# sub-channel recipes -> the sources that take 128x128 blocks (the rest 1x128)
+BLOCK128_2D = {"fp8_block128": ("w",), "fp8_block128_1d1d": (), "fp8_block128_2d2d": ("x", "w", "dy")}
+NEXT_RECIPES = ("mxfp4", "fp8_channel", "fp8_block128_1d1d", "fp8_block128_2d2d")
 ALL_RECIPES = RECIPES + NEXT_RECIPES
 
 
@@ -63,7 +73,7 @@ class QOperand:
             return bf16_to_f32(self.codes).astype(np.float64)
         if self.recipe in ("fp8_current", "fp8_delayed"):
             return R.dequant_pertensor(self.codes, self.fmt, self.tensor_scale_inv)
-        if self.recipe == "fp8_block128":
+        if self.recipe in BLOCK128_2D:
             return R.dequant_block128(self.codes, self.scale, self.weight_2d)
         if self.recipe == "mxfp8":
             return R.dequant_mxfp8(self.codes, self.scale)
@@ -102,8 +112,8 @@ def quantize_operand(recipe, src, orient, x_bits, pass_, delayed_state=None, see
         codes, s_inv, a = delayed_state.cast(x_bits, orient)
         return QOperand(recipe, delayed_state.fmt, codes, tensor_scale_inv=s_inv,
                         extra={"amax": a})
-    if recipe == "fp8_block128":
-        w2d = src == "w"
+    if recipe in BLOCK128_2D:
+        w2d = src in BLOCK128_2D[recipe]
         codes, s_inv = R.quantize_block128(x_bits, orient, weight_2d=w2d)
         return QOperand(recipe, "e4m3", codes, scale=s_inv, weight_2d=w2d)
     if recipe == "mxfp8":

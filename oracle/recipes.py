@@ -162,7 +162,10 @@ def quantize_block128(x_bits, orient="row", weight_2d=False):
 
     "Faster training throughput in FP8 precision with NVIDIA NeMo",
     "Scaling recipe granularity": activations in 1x128 blocks and weights in
-    128x128 blocks ("2D2D"); strengths and trade-offs, sub-channel item:
+    128x128 blocks (the page's example; its label for it is garbled, and the
+    pairings are read as (activations, weights) with 1D = 1x128 and 2D =
+    128x128, so this is 1D2D; oracle.passes selects the shape per source for
+    the 1D1D and 2D2D pairings); strengths and trade-offs, sub-channel item:
     configurable block dimensions, finer blocks cost more scale storage.
     Reading taken: per block, s_b = fp32(448 / amax_b) (same corner rules as
     the per-tensor scale), q = enc_E4M3(fp32(x * s_b)), and the stored scale

@@ -259,6 +259,43 @@ def test_channel_outlier_stays_in_its_row_and_zero_row():
 
 
 # ---------------------------------------------------------------------------
+# sub-channel block pairings: 1D1D and 2D2D beside the 1D2D recipe
+# ---------------------------------------------------------------------------
+def test_block128_pairings_choose_block_shapes_per_source():
+    x = W.activations(256, 384, seed=61)
+    w = W.weights(256, 384, seed=62)
+    dy = W.grads(256, 256, seed=63)
+    src = {"x": x, "w": w, "dy": dy}
+    from oracle.passes import operand_roles
+    for rec, two_d in (("fp8_block128", {"w"}), ("fp8_block128_1d1d", set()),
+                       ("fp8_block128_2d2d", {"x", "w", "dy"})):
+        for pass_ in ("fprop", "dgrad", "wgrad"):
+            ops = pass_operands(rec, pass_, x=x, w=w, dy=dy)
+            for (name, orient), q in zip(operand_roles(pass_), ops):
+                c, si = R.quantize_block128(src[name], orient, weight_2d=name in two_d)
+                assert q.weight_2d == (name in two_d), (rec, pass_, name)
+                assert (q.codes == c).all() and (q.scale.view(np.uint32) == si.view(np.uint32)).all()
+                rows, cols = q.codes.shape
+                assert q.scale.shape == ((rows // 128, cols // 128) if name in two_d else (rows, cols // 128))
+
+
+def test_block128_2d_scale_is_max_of_1d_scales_and_col_is_transpose():
+    """A 128x128 block's stored scale fp32(1 / fp32(448 / amax)) is monotone in
+    amax, so it equals the largest 1x128 stored scale of its 128 rows; a
+    2D col copy is the row copy transposed, block by block."""
+    x = W.grads(384, 256, seed=64)
+    c1, s1 = R.quantize_block128(x, "row", weight_2d=False)
+    c2, s2 = R.quantize_block128(x, "row", weight_2d=True)
+    assert (s2 == s1.reshape(3, 128, 2).max(axis=1)).all()
+    cc, sc = R.quantize_block128(x, "col", weight_2d=True)
+    assert (cc == c2.T).all() and (sc == s2.T).all()
+    # 1x128 col copy of the source: blocks along the source's rows
+    cc1, sc1 = R.quantize_block128(x, "col", weight_2d=False)
+    cr1, sr1 = R.quantize_block128(np.ascontiguousarray(x.T), "row", weight_2d=False)
+    assert (cc1 == cr1).all() and (sc1 == sr1).all()
+
+
+# ---------------------------------------------------------------------------
 # MXFP8
 # ---------------------------------------------------------------------------
 def test_mx_exponent_closed_form_all_bf16():
@@ -662,6 +699,10 @@ def test_tiny_case_all_recipes_gemm_close_to_bf16_product():
     # finer granularity tracks the bf16 product more closely
     assert errs["fp8_block128"] <= errs["fp8_current"] * 1.05
     assert errs["mxfp8"] < 0.1 and errs["nvfp4"] < 0.3 and errs["mxfp4"] < 0.3
+    # 1x128 weight blocks track at least as well as 128x128 ones, which track
+    # at least as well as 128x128 blocks on the activations too
+    assert errs["fp8_block128_1d1d"] <= errs["fp8_block128"] * 1.05
+    assert errs["fp8_block128"] <= errs["fp8_block128_2d2d"] * 1.05
     # one scale per row tracks at least as well as one per tensor
     assert errs["fp8_channel"] <= errs["fp8_current"] * 1.05 and errs["fp8_channel"] < 0.1
     for rec in ("fp8_current", "fp8_delayed", "fp8_block128", "mxfp8"):
