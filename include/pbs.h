@@ -82,8 +82,12 @@ typedef enum {
   PBS_RECIPE_NVFP4 = 5,        /* E2M1 values, E4M3 scale per 16 values (1x16
                                   act/grad, 16x16 weight), fp32 per tensor  */
   PBS_RECIPE_MXFP4 = 6,        /* E2M1 values, E8M0 scale per 32 values     */
-  PBS_RECIPE_FP8_CHANNEL = 7   /* fp32 scale per row of each copy (per
+  PBS_RECIPE_FP8_CHANNEL = 7,  /* fp32 scale per row of each copy (per
                                   channel), E4M3 values                     */
+  PBS_RECIPE_FP8_BLOCK128_1D1D = 8, /* as FP8_BLOCK128 with 1x128 blocks on
+                                  every tensor, weights included           */
+  PBS_RECIPE_FP8_BLOCK128_2D2D = 9  /* as FP8_BLOCK128 with 128x128 blocks on
+                                  every tensor                              */
 } pbs_recipe;
 
 /* The three GEMMs of a linear layer ([LP] "Using autocast mode vs
@@ -170,6 +174,11 @@ float* pbs_delayed_scale_inv(void* state); /* device address of `scale_inv` */
  *    weight_2d = 1: one scale per 128x128 tile, [rows/128, cols/128] /
  *    [cols/128, rows/128].  Stored scale = fp32(1 / s_b), s_b =
  *    fp32(448 / amax_b).  `scale` unused.
+ *  recipes FP8_BLOCK128_1D1D / FP8_BLOCK128_2D2D ([NEMO] "Scaling recipe
+ *    granularity": the other block pairings, read as (activations and
+ *    gradients, weights) with 1D = 1x128 and 2D = 128x128): the same cast;
+ *    the caller passes weight_2d = 0 for every tensor (1D1D) or 1 for every
+ *    tensor (2D2D).
  *  recipe MXFP8 ([NEMO] MXFP8 item): fmt E4M3, 32-value blocks along the
  *    contraction axis, E8M0 scale bytes [rows, cols/32] / [cols, rows/32];
  *    the exponent is the smallest e with amax_b <= 448 * 2^e.
@@ -226,6 +235,10 @@ pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t
  *    for FPROP / DGRAD (weights, 2D) or [N, K/128] for WGRAD; each 128-long
  *    slice of the contraction is accumulated apart and added in with the
  *    product of its two scales.
+ *  - FP8_BLOCK128_1D1D: a_scale = fp32 [M, K/128], b_scale = fp32
+ *    [N, K/128] in every pass.
+ *  - FP8_BLOCK128_2D2D: a_scale = fp32 [M/128, K/128], b_scale = fp32
+ *    [N/128, K/128] in every pass; M and N multiples of 128.
  *  - MXFP8: a_scale = E8M0 [M, K/32], b_scale = E8M0 [N, K/32].
  *  - NVFP4: A, B packed E2M1 [M, K/2], [N, K/2]; a_scale = E4M3 [M, K/16];
  *    b_scale = E4M3 [N/16, K/16] for FPROP / DGRAD (weights, 2D) or

@@ -62,6 +62,8 @@ pbs_status pbs_quantized_bytes(pbs_recipe recipe, int64_t rows, int64_t cols, in
     case PBS_RECIPE_FP8_DELAYED:
       *code_bytes = (size_t)n; *scale_bytes = 0; break;
     case PBS_RECIPE_FP8_BLOCK128:
+    case PBS_RECIPE_FP8_BLOCK128_1D1D:
+    case PBS_RECIPE_FP8_BLOCK128_2D2D:
       PBS_REQUIRE(cols % 128 == 0 && (!weight_2d || rows % 128 == 0), PBS_ERR_SHAPE,
                   "block128 needs dims that are multiples of 128");
       *code_bytes = (size_t)n;

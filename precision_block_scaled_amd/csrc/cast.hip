@@ -990,8 +990,9 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
               "pbs_cast: RHT16 / SR flags apply to the NVFP4 and MXFP4 recipes only");
   PBS_REQUIRE(!rht || orient_mask == PBS_COL, PBS_ERR_UNSUPPORTED,
               "pbs_cast: RHT16 runs along the rows and produces the col copy only");
-  PBS_REQUIRE(!w2d || recipe == PBS_RECIPE_FP8_BLOCK128 || recipe == PBS_RECIPE_NVFP4,
-              PBS_ERR_UNSUPPORTED, "pbs_cast: 2D blocks exist for FP8_BLOCK128 and NVFP4 only");
+  PBS_REQUIRE(!w2d || recipe == PBS_RECIPE_FP8_BLOCK128 || recipe == PBS_RECIPE_FP8_BLOCK128_2D2D ||
+                  recipe == PBS_RECIPE_NVFP4,
+              PBS_ERR_UNSUPPORTED, "pbs_cast: 2D blocks exist for FP8_BLOCK128(_2D2D) and NVFP4 only");
   PBS_REQUIRE(!(w2d && (rht || sr)), PBS_ERR_UNSUPPORTED,
               "pbs_cast: 2D weight blocks take neither RHT16 nor SR");
   PBS_REQUIRE(amax_out == nullptr || recipe == PBS_RECIPE_FP8_CURRENT || recipe == PBS_RECIPE_FP8_DELAYED,
@@ -1027,7 +1028,9 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
       name = "cast_tensor_fp8";
       break;
     }
-    case PBS_RECIPE_FP8_BLOCK128: {
+    case PBS_RECIPE_FP8_BLOCK128:
+    case PBS_RECIPE_FP8_BLOCK128_1D1D:
+    case PBS_RECIPE_FP8_BLOCK128_2D2D: {
       PBS_REQUIRE(fmt == PBS_FMT_E4M3, PBS_ERR_UNSUPPORTED, "pbs_cast: FP8_BLOCK128 takes E4M3");
       PBS_REQUIRE((!row || cols % 128 == 0) && (!col || rows % 128 == 0) &&
                       (!w2d || (rows % 128 == 0 && cols % 128 == 0)),

@@ -959,8 +959,23 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
       PBS_REQUIRE(!w2d || N % 128 == 0, PBS_ERR_SHAPE, "pbs_gemm: 128x128 weight blocks need N %% 128 == 0");
       g.lda = K; g.ldb = K;
       g.tiles_n = (int)ceil_div(N, 128);          // gemm_blk.hip: 256 x 128 tiles
-      fn = blk_kernel_for(w2d, bf16_out);
+      fn = blk_kernel_for(false, w2d, bf16_out);
       name = "gemm_fp8_block128";
+      break;
+    }
+    case PBS_RECIPE_FP8_BLOCK128_1D1D:
+    case PBS_RECIPE_FP8_BLOCK128_2D2D: {
+      const bool two = recipe == PBS_RECIPE_FP8_BLOCK128_2D2D;
+      PBS_REQUIRE(a_fmt == PBS_FMT_E4M3 && b_fmt == PBS_FMT_E4M3, PBS_ERR_UNSUPPORTED,
+                  "pbs_gemm: sub-channel FP8 takes E4M3 operands");
+      PBS_REQUIRE(a_scale && b_scale, PBS_ERR_INVALID_ARG, "pbs_gemm: block scales are null");
+      PBS_REQUIRE(K % 128 == 0, PBS_ERR_SHAPE, "pbs_gemm: sub-channel FP8 needs K %% 128 == 0");
+      PBS_REQUIRE(!two || (M % 128 == 0 && N % 128 == 0), PBS_ERR_SHAPE,
+                  "pbs_gemm: 128x128 blocks on both operands need M and N %% 128 == 0");
+      g.lda = K; g.ldb = K;
+      g.tiles_n = (int)ceil_div(N, 128);
+      fn = blk_kernel_for(two, two, bf16_out);
+      name = two ? "gemm_fp8_block128_2d2d" : "gemm_fp8_block128_1d1d";
       break;
     }
     case PBS_RECIPE_MXFP8: {

@@ -1,7 +1,8 @@
-// Sub-channel FP8 GEMM: 1x128 blocks for activations and gradients, 128x128
-// (Fprop / Dgrad weights) or 1x128 (Wgrad) blocks for the other operand
+// Sub-channel FP8 GEMM: 1x128 or 128x128 fp32 block scales on either operand
 // ("Faster training throughput in FP8 precision with NVIDIA NeMo",
-// "Scaling recipe granularity").
+// "Scaling recipe granularity": 1x128 activations and gradients with 128x128
+// weights, and the other block pairings).  A 128x128-block operand stores one
+// scale per 128 rows; the kernel reads it through the same per-row path.
 //
 //   C[m, n] = sum_kb (sum_{k in kb} A[m, k] B[n, k]) * a_scale[m, kb] * b_scale[n, kb]
 //
@@ -151,7 +152,7 @@ __device__ __forceinline__ float load_word_untracked(const float* p) {
   return v;
 }
 
-template <bool B2D, bool OUT_BF16>
+template <bool A2D, bool B2D, bool OUT_BF16>
 __global__ __launch_bounds__(NTHR, 1) void gemm_blk_kernel(GemmArgs g) {
   static_assert(KB_VM_TILES == 12, "wait_vm_ahead counts 12 tile loads per stage");
   __shared__ __align__(16) uint8_t smem[KB_SMEM];
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_blk_kernel(GemmArgs g) {
   int ra = m0 + 64 * w + lane, rb = n0 + 64 * (w & 1) + lane;
   ra = ra < g.M ? ra : g.M - 1;
   rb = rb < g.N ? rb : g.N - 1;
-  const float* pa = (const float*)g.a_scale + (int64_t)ra * sstride;
+  const float* pa = (const float*)g.a_scale + (int64_t)(A2D ? ra / 128 : ra) * sstride;
   const float* pb = (const float*)g.b_scale + (int64_t)(B2D ? rb / 128 : rb) * sstride;
   auto put_scales = [&](int kt, float a, float b) {
     typedef __attribute__((address_space(3))) float* lds_f32_w;
@@ -372,9 +373,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_blk_kernel(GemmArgs g) {
   store_blk<OUT_BF16>(acc, g, smem, m0, n0, w, wm, wn, lane);
 }
 
-gemm_fn blk_kernel_for(bool b2d, bool bf16_out) {
-  if (b2d) return bf16_out ? gemm_blk_kernel<true, true> : gemm_blk_kernel<true, false>;
-  return bf16_out ? gemm_blk_kernel<false, true> : gemm_blk_kernel<false, false>;
+gemm_fn blk_kernel_for(bool a2d, bool b2d, bool bf16_out) {
+  if (a2d) {   // 128x128 blocks on A come with 128x128 blocks on B
+    return bf16_out ? gemm_blk_kernel<true, true, true> : gemm_blk_kernel<true, true, false>;
+  }
+  if (b2d) return bf16_out ? gemm_blk_kernel<false, true, true> : gemm_blk_kernel<false, true, false>;
+  return bf16_out ? gemm_blk_kernel<false, false, true> : gemm_blk_kernel<false, false, false>;
 }
 
 }  // namespace pbs

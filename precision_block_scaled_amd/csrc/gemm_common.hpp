@@ -138,8 +138,8 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
 
 typedef void (*gemm_fn)(GemmArgs);
 
-// Sub-channel (block-128) FP8 kernel of gemm_blk.hip: 128x128 (b2d) or
-// 1x128 blocks for B, bf16 or fp32 output.
-gemm_fn blk_kernel_for(bool b2d, bool bf16_out);
+// Sub-channel (block-128) FP8 kernel of gemm_blk.hip: 128x128 (a2d / b2d)
+// or 1x128 blocks for A and B (a2d implies b2d), bf16 or fp32 output.
+gemm_fn blk_kernel_for(bool a2d, bool b2d, bool bf16_out);
 
 }  // namespace pbs

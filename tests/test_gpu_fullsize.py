@@ -29,6 +29,7 @@ from precision_block_scaled_amd import pipeline as PL
 from oracle import recipes as R
 from oracle.formats import bf16_to_f32
 from oracle.gemm_ref import check_gemm, fp8_dot_unit_bound
+from oracle.passes import BLOCK128_2D
 from oracle.philox import philox_word0_for_index
 from tests.gpu_util import to_gpu_bf16
 
@@ -45,7 +46,7 @@ MODELS = {
     "llama3_8b": (8192, W.layer_shapes(L3["hidden"], L3["intermediate"], L3["heads"], L3["kv_heads"],
                                        L3["gated"])),
 }
-FP8_MFMA = {"fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "fp8_channel"}
+FP8_MFMA = {"fp8_current", "fp8_delayed", "mxfp8", "fp8_channel"} | set(BLOCK128_2D)
 FMAX = {"e4m3": 448.0, "e5m2": 57344.0}
 SEED = 42
 
@@ -78,7 +79,7 @@ class OracleCopy:
     def __init__(self, recipe, src, orient, bits, pass_, dstate, rows):
         self.recipe, self.rows = recipe, rows
         sl = copy_rows(bits, orient, rows)
-        w2d = src == "w" and recipe in ("fp8_block128", "nvfp4")
+        w2d = src in BLOCK128_2D.get(recipe, ()) or (src == "w" and recipe == "nvfp4")
         self.tsi = None
         self.scales = None
         if recipe in ("fp8_current", "fp8_delayed"):
@@ -90,7 +91,7 @@ class OracleCopy:
                 self.codes, s_inv, _ = dstate.cast(sl, orient)
             self.tsi = np.float32(s_inv)
             self.deq = R.dequant_pertensor(self.codes, fmt, self.tsi)
-        elif recipe == "fp8_block128":
+        elif recipe in BLOCK128_2D:
             self.codes, self.scales = R.quantize_block128(sl, orient, weight_2d=w2d)
             self.deq = R.dequant_block128(self.codes, self.scales, w2d)
         elif recipe == "fp8_channel":                   # a copy row's scale is its own
@@ -136,7 +137,7 @@ def gpu_rows(q, rows, w2d):
     sc = None
     if q.scales is not None:
         if w2d:
-            div = 128 if q.recipe == "fp8_block128" else 16
+            div = 128 if q.recipe in BLOCK128_2D else 16
             g = torch.from_numpy(np.unique(np.asarray(rows) // div).astype(np.int64)).to(q.codes.device)
             sc = q.scales[g].cpu().numpy()
         else:
@@ -213,6 +214,8 @@ CASES = ([("codonfm", n, r) for n in ("qkv", "attn_out", "mlp_up", "mlp_down") f
          + [("llama3_8b", n, r) for n in ("qkv", "attn_out", "mlp_up", "mlp_down") for r in RECIPES]
          + [("codonfm_32k", n, r) for n in ("mlp_up", "mlp_down") for r in ("mxfp8", "nvfp4", "fp8_block128")]
          + [(m, n, r) for r in ("mxfp4", "fp8_channel") for m in ("codonfm", "llama3_8b")
+            for n in ("qkv", "attn_out", "mlp_up", "mlp_down")]
+         + [("codonfm", n, r) for r in ("fp8_block128_1d1d", "fp8_block128_2d2d")
             for n in ("qkv", "attn_out", "mlp_up", "mlp_down")])
 
 
