@@ -76,6 +76,11 @@ def lib():
         if not os.path.exists(lib_path):
             raise PBSError(-1, f"{lib_path} is not built; run "
                                "`python -m precision_block_scaled_amd.build` (no CPU fallback exists)")
+        # torch ships its own HIP runtime under the same soname as ROCm's
+        # (libamdhip64.so.7).  Loading torch first makes this library bind to
+        # that one; loaded the other way round, the process would hold two
+        # runtimes and the second would find no device.
+        import torch  # noqa: F401
         L = _c.CDLL(lib_path)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(L, name)
