@@ -40,6 +40,12 @@ and 2D = 128x128: the recipe above is 1D2D; "fp8_block128_1d1d" gives every
 tensor 1x128 blocks along the contraction axis (the weight's col copy is
 quantized from the source, not transposed), "fp8_block128_2d2d" gives every
 tensor 128x128 blocks (each col copy is the transposed row copy).
+
+"fp8_block128_pow2" keeps the 1D2D block shapes (1x128 activations and
+gradients, 128x128 weights) and takes MXFP8's power-of-two scale rule per
+block instead of the fp32 scale: the sub-channel granularity with
+hardware-native (E8M0) block scales, which the same section sets against
+generic block scaling.
 """
 from __future__ import annotations
 
@@ -53,7 +59,7 @@ from .formats import bf16_to_f32
 RECIPES = ("bf16", "fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "nvfp4")
 # sub-channel recipes -> the sources that take 128x128 blocks (the rest 1x128)
 BLOCK128_2D = {"fp8_block128": ("w",), "fp8_block128_1d1d": (), "fp8_block128_2d2d": ("x", "w", "dy")}
-NEXT_RECIPES = ("mxfp4", "fp8_channel", "fp8_block128_1d1d", "fp8_block128_2d2d")
+NEXT_RECIPES = ("mxfp4", "fp8_channel", "fp8_block128_1d1d", "fp8_block128_2d2d", "fp8_block128_pow2")
 ALL_RECIPES = RECIPES + NEXT_RECIPES
 
 
@@ -75,6 +81,8 @@ class QOperand:
             return R.dequant_pertensor(self.codes, self.fmt, self.tensor_scale_inv)
         if self.recipe in BLOCK128_2D:
             return R.dequant_block128(self.codes, self.scale, self.weight_2d)
+        if self.recipe == "fp8_block128_pow2":
+            return R.dequant_block128_pow2(self.codes, self.scale, self.weight_2d)
         if self.recipe == "mxfp8":
             return R.dequant_mxfp8(self.codes, self.scale)
         if self.recipe == "nvfp4":
@@ -116,6 +124,10 @@ def quantize_operand(recipe, src, orient, x_bits, pass_, delayed_state=None, see
         w2d = src in BLOCK128_2D[recipe]
         codes, s_inv = R.quantize_block128(x_bits, orient, weight_2d=w2d)
         return QOperand(recipe, "e4m3", codes, scale=s_inv, weight_2d=w2d)
+    if recipe == "fp8_block128_pow2":
+        w2d = src == "w"
+        codes, e8 = R.quantize_block128_pow2(x_bits, orient, weight_2d=w2d)
+        return QOperand(recipe, "e4m3", codes, scale=e8, weight_2d=w2d)
     if recipe == "mxfp8":
         codes, e8 = R.quantize_mxfp8(x_bits, orient)
         return QOperand(recipe, "e4m3", codes, scale=e8)

@@ -234,6 +234,31 @@ def quantize_mxfp8(x_bits, orient="row"):
     return E4M3.encode(v), c
 
 
+def quantize_block128_pow2(x_bits, orient="row", weight_2d=False):
+    """Sub-channel FP8 with power-of-two (E8M0) block scales.
+
+    "Faster training throughput in FP8 precision with NVIDIA NeMo":
+    "Scaling recipe granularity" sets the sub-channel blocks (1x128
+    activations and gradients, 128x128 weights) and closes on the trade-off
+    between granularity and throughput that hardware-native block scaling
+    (MXFP8's E8M0 power-of-two scales, same page, strengths and trade-offs,
+    MXFP8 item) avoids.  Reading taken for this variant: the sub-channel
+    block shapes with MXFP8's scale rule -- per block, the smallest e in
+    [-127, 127] with amax_b <= 448 * 2**e (stored as the E8M0 code e + 127),
+    codes = enc_E4M3(x * 2**-e) (scaling by a power of two is exact, so only
+    the encode rounds), x_hat = dec(q) * 2**e.  E4M3 for every role.
+
+    Returns (codes [rows, cols], E8M0 codes [rows, cols/128] or
+    [rows/128, cols/128]) in the requested orientation.
+    """
+    t = _oriented(x_bits, orient)
+    br, bc = (128, 128) if weight_2d else (1, 128)
+    c = mx_block_exponent_code(_block_amax(t, br, bc))
+    e = c.astype(np.int64) - 127
+    v = t.astype(np.float64) * np.ldexp(1.0, -_expand(e, br, bc))   # exact
+    return E4M3.encode(v), c
+
+
 # ---------------------------------------------------------------------------
 # NVFP4: E2M1 values, E4M3 scale per 16 values, FP32 scale per tensor
 # ---------------------------------------------------------------------------
@@ -434,6 +459,11 @@ def dequant_channel(codes, s_inv):
 
 def dequant_mxfp8(codes, e8m0_codes):
     return E4M3.decode(codes) * _expand(e8m0_decode(e8m0_codes), 1, 32)
+
+
+def dequant_block128_pow2(codes, e8m0_codes, weight_2d=False):
+    br, bc = (128, 128) if weight_2d else (1, 128)
+    return E4M3.decode(codes) * _expand(e8m0_decode(e8m0_codes), br, bc)
 
 
 def dequant_mxfp4(packed, e8m0_codes):

@@ -296,6 +296,100 @@ def test_block128_2d_scale_is_max_of_1d_scales_and_col_is_transpose():
 
 
 # ---------------------------------------------------------------------------
+# sub-channel FP8 with power-of-two block scales
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("weight_2d,shape", [(False, (3, 256)), (True, (128, 256))])
+def test_block128_pow2_bruteforce(weight_2d, shape):
+    """Per block: the E8M0 code is the smallest of all 255 finite codes whose
+    power of two brings every element within 448 (exact rationals), and each
+    code is the brute-force nearest-even E4M3 code of the exactly scaled value."""
+    x = W.activations(*shape, seed=19)
+    t = bf16_to_f32(x)
+    t[0, :128] *= np.float32(2.0 ** -100)         # a block that needs a large scale
+    x = W.f32_to_bf16_bits(t)
+    t = bf16_to_f32(x)
+    codes, e8 = R.quantize_block128_pow2(x, "row", weight_2d)
+    br, bc = (128, 128) if weight_2d else (1, 128)
+    assert e8.shape == (shape[0] // br, shape[1] // bc) and e8.dtype == np.uint8
+    for bi in range(shape[0] // br):
+        for bj in range(shape[1] // bc):
+            blk = t[bi * br:(bi + 1) * br, bj * bc:(bj + 1) * bc].reshape(-1)
+            a = max(abs(Fraction(float(z))) for z in blk)
+            c = next(c for c in range(255) if a <= 448 * Fraction(2) ** (c - 127))
+            assert int(e8[bi, bj]) == c
+            sc = Fraction(2) ** (127 - c)
+            v = np.array([frac_to_f32(Fraction(float(z)) * sc) for z in blk], dtype=np.float32)
+            got = codes[bi * br:(bi + 1) * br, bj * bc:(bj + 1) * bc].reshape(-1)
+            assert (got == _brute_e4m3(v)).all()
+            # the scaled block maximum lies in (224, 448]: half the scale would saturate
+            m = np.abs(E4M3.decode(got)).max()
+            assert 224.0 <= m <= 448.0 and (c == 0 or a * sc > 224)
+
+
+def test_block128_pow2_scale_is_power_of_two_below_fp32_scale():
+    """2**-e is the largest power of two not above the exact 448 / amax_b
+    (the fp32 sub-channel scale before rounding)."""
+    x = W.grads(8, 1024, seed=20)
+    codes, e8 = R.quantize_block128_pow2(x, "row")
+    a_b = np.abs(bf16_to_f32(x)).reshape(8, 8, 128).max(axis=-1)
+    for a, c in zip(a_b.reshape(-1), e8.reshape(-1)):
+        q = Fraction(448) / Fraction(float(a))
+        s = Fraction(2) ** (127 - int(c))
+        assert s <= q < 2 * s
+
+
+def test_block128_pow2_reduces_to_mxfp8_when_sub_blocks_share_the_max():
+    """When every 32-value sub-block holds its 128-block's maximum magnitude,
+    the MXFP8 rule gives each sub-block the 128-block's exponent: codes agree
+    with the MXFP8 oracle and its four scales repeat the block's one."""
+    t = bf16_to_f32(W.activations(16, 512, seed=21)).copy()
+    blocks = t.reshape(16, 4, 4, 32)
+    bmax = np.abs(blocks).max(axis=(2, 3))
+    blocks[:, :, :, 0] = -bmax[:, :, None]       # same magnitude in every sub-block
+    x = W.f32_to_bf16_bits(blocks.reshape(16, 512))
+    cp, ep = R.quantize_block128_pow2(x, "row")
+    cm, em = R.quantize_mxfp8(x, "row")
+    assert (cp == cm).all() and (np.repeat(ep, 4, axis=1) == em).all()
+    # without that structure the sub-blocks may take smaller exponents
+    x2 = W.activations(16, 512, seed=22)
+    ep2 = R.quantize_block128_pow2(x2, "row")[1]
+    em2 = R.quantize_mxfp8(x2, "row")[1]
+    assert (np.repeat(ep2, 4, axis=1) >= em2).all() and (np.repeat(ep2, 4, axis=1) > em2).any()
+
+
+def test_block128_pow2_2d_is_max_of_1d_and_col_is_transpose():
+    x = W.weights(384, 256, seed=23)
+    c1, e1 = R.quantize_block128_pow2(x, "row", weight_2d=False)
+    c2, e2 = R.quantize_block128_pow2(x, "row", weight_2d=True)
+    assert (e2 == e1.reshape(3, 128, 2).max(axis=1)).all()
+    cc, ec = R.quantize_block128_pow2(x, "col", weight_2d=True)
+    assert (cc == c2.T).all() and (ec == e2.T).all()
+    cc1, ec1 = R.quantize_block128_pow2(x, "col", weight_2d=False)
+    cr1, er1 = R.quantize_block128_pow2(np.ascontiguousarray(x.T), "row", weight_2d=False)
+    assert (cc1 == cr1).all() and (ec1 == er1).all()
+    # dequantization: code value times 2**e exactly, per 128x128 block
+    d = R.dequant_block128_pow2(c2, e2, weight_2d=True)
+    assert d[0, 0] == float(E4M3.decode(c2[:1, :1])[0, 0]) * 2.0 ** (int(e2[0, 0]) - 127)
+
+
+def test_block128_pow2_pairing_and_zero_block():
+    x = W.activations(256, 384, seed=24)
+    w = W.weights(256, 384, seed=25)
+    dy = W.grads(256, 256, seed=26)
+    from oracle.passes import operand_roles
+    src = {"x": x, "w": w, "dy": dy}
+    for pass_ in ("fprop", "dgrad", "wgrad"):
+        ops = pass_operands("fp8_block128_pow2", pass_, x=x, w=w, dy=dy)
+        for (name, orient), q in zip(operand_roles(pass_), ops):
+            c, e = R.quantize_block128_pow2(src[name], orient, weight_2d=name == "w")
+            assert q.weight_2d == (name == "w") and (q.codes == c).all() and (q.scale == e).all()
+    z = np.zeros((2, 256), np.uint16)
+    z[1, 5] = 0x8000                               # -0
+    c, e = R.quantize_block128_pow2(z, "row")
+    assert (e == 0).all() and (c & 0x7F == 0).all() and c[1, 5] == 0x80
+
+
+# ---------------------------------------------------------------------------
 # MXFP8
 # ---------------------------------------------------------------------------
 def test_mx_exponent_closed_form_all_bf16():
@@ -703,6 +797,8 @@ def test_tiny_case_all_recipes_gemm_close_to_bf16_product():
     # at least as well as 128x128 blocks on the activations too
     assert errs["fp8_block128_1d1d"] <= errs["fp8_block128"] * 1.05
     assert errs["fp8_block128"] <= errs["fp8_block128_2d2d"] * 1.05
+    # power-of-two block scales use at most one binade less of E4M3's range
+    assert errs["fp8_block128_pow2"] < 0.1
     # one scale per row tracks at least as well as one per tensor
     assert errs["fp8_channel"] <= errs["fp8_current"] * 1.05 and errs["fp8_channel"] < 0.1
     for rec in ("fp8_current", "fp8_delayed", "fp8_block128", "mxfp8"):
