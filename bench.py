@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 RECIPES = ["bf16", "fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "nvfp4"]
 # built beyond the pages' six (MXFP4: E2M1 with E8M0 per 32 on the FP4 matrix
 # rate); timed after the step and reported apart, never part of `value`
-NEXT_RECIPES = ["mxfp4", "fp8_channel", "fp8_block128_1d1d", "fp8_block128_2d2d"]
+NEXT_RECIPES = ["mxfp4", "fp8_channel", "fp8_block128_1d1d", "fp8_block128_2d2d", "fp8_block128_pow2"]
 PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2, "fp4": 10066.3}
 HBM_GBPS = 8000.0
 
@@ -63,6 +63,8 @@ def kernel_key(recipe, pass_):
         return "gemm_fp8_block128_1d", "fp8"
     if recipe == "fp8_block128_2d2d":
         return "gemm_fp8_block128_2d2d", "fp8"
+    if recipe == "fp8_block128_pow2":
+        return "gemm_fp8_block128_pow2", "fp8"
     return ("gemm_nvfp4_w2d" if pass_ != "wgrad" else "gemm_nvfp4_1d"), "fp16"
 
 

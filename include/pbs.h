@@ -86,8 +86,10 @@ typedef enum {
                                   channel), E4M3 values                     */
   PBS_RECIPE_FP8_BLOCK128_1D1D = 8, /* as FP8_BLOCK128 with 1x128 blocks on
                                   every tensor, weights included           */
-  PBS_RECIPE_FP8_BLOCK128_2D2D = 9  /* as FP8_BLOCK128 with 128x128 blocks on
+  PBS_RECIPE_FP8_BLOCK128_2D2D = 9, /* as FP8_BLOCK128 with 128x128 blocks on
                                   every tensor                              */
+  PBS_RECIPE_FP8_BLOCK128_POW2 = 10 /* FP8_BLOCK128's blocks with power-of-two
+                                  (E8M0) scales, E4M3 values                */
 } pbs_recipe;
 
 /* The three GEMMs of a linear layer ([LP] "Using autocast mode vs
@@ -179,6 +181,16 @@ float* pbs_delayed_scale_inv(void* state); /* device address of `scale_inv` */
  *    gradients, weights) with 1D = 1x128 and 2D = 128x128): the same cast;
  *    the caller passes weight_2d = 0 for every tensor (1D1D) or 1 for every
  *    tensor (2D2D).
+ *  recipe FP8_BLOCK128_POW2 ([NEMO] "Scaling recipe granularity" for the
+ *    blocks, its MXFP8 item for the power-of-two scale): fmt E4M3; the
+ *    blocks of FP8_BLOCK128 (weight_2d selects 128x128), each with MXFP8's
+ *    exponent rule (smallest e in [-127, 127] with amax_b <= 448 * 2^e,
+ *    codes = enc(x * 2^-e)).  Each block's scale is stored as one 32-bit
+ *    word holding its E8M0 code e + 127 in all four bytes (the 4 bytes per
+ *    block FP8_BLOCK128 stores, in the form the scaled matrix instruction
+ *    reads per 32-value step): uint32 [rows, cols/128] / [cols, rows/128],
+ *    or [rows/128, cols/128] / [cols/128, rows/128] with weight_2d = 1.
+ *    Scales 4-byte aligned.  `scale` unused.
  *  recipe MXFP8 ([NEMO] MXFP8 item): fmt E4M3, 32-value blocks along the
  *    contraction axis, E8M0 scale bytes [rows, cols/32] / [cols, rows/32];
  *    the exponent is the smallest e with amax_b <= 448 * 2^e.
@@ -240,6 +252,10 @@ pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t
  *  - FP8_BLOCK128_2D2D: a_scale = fp32 [M/128, K/128], b_scale = fp32
  *    [N/128, K/128] in every pass; M and N multiples of 128.
  *  - MXFP8: a_scale = E8M0 [M, K/32], b_scale = E8M0 [N, K/32].
+ *  - FP8_BLOCK128_POW2: a_scale = uint32 [M, K/128] (pbs_cast's E8M0 words);
+ *    b_scale = uint32 [N/128, K/128] for FPROP / DGRAD (weights, 2D) or
+ *    [N, K/128] for WGRAD; 4-byte aligned.  The power-of-two scales are
+ *    applied by the matrix instruction itself, as for MXFP8.
  *  - NVFP4: A, B packed E2M1 [M, K/2], [N, K/2]; a_scale = E4M3 [M, K/16];
  *    b_scale = E4M3 [N/16, K/16] for FPROP / DGRAD (weights, 2D) or
  *    [N, K/16] for WGRAD; a_tensor_scale / b_tensor_scale = S_dec of each.
@@ -258,7 +274,8 @@ pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t
  *   (BF16); each stored operand row at most 16 MiB.  K == 0 writes zeros
  *   to C.
  * Alignment (else PBS_ERR_INVALID_ARG): A, B, C 16-byte aligned; MXFP8,
- *   MXFP4 and NVFP4 block scales 4-byte aligned; FP8_CHANNEL scales
+ *   MXFP4, NVFP4 and FP8_BLOCK128_POW2 block scales 4-byte aligned;
+ *   FP8_CHANNEL scales
  *   16-byte aligned.
  * Accuracy: fp32 accumulation; the 8-bit instructions (FP8 recipes) sum
  *   each aligned group of 8 products in one step that keeps bits down to

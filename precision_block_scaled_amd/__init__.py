@@ -19,6 +19,7 @@ __all__ = [
     "PBS_RECIPE_BF16", "PBS_RECIPE_FP8_CURRENT", "PBS_RECIPE_FP8_DELAYED",
     "PBS_RECIPE_FP8_BLOCK128", "PBS_RECIPE_MXFP8", "PBS_RECIPE_NVFP4", "PBS_RECIPE_MXFP4",
     "PBS_RECIPE_FP8_CHANNEL", "PBS_RECIPE_FP8_BLOCK128_1D1D", "PBS_RECIPE_FP8_BLOCK128_2D2D",
+    "PBS_RECIPE_FP8_BLOCK128_POW2",
     "PBS_FPROP", "PBS_DGRAD", "PBS_WGRAD", "PBS_ROW", "PBS_COL",
     "PBS_FLAG_RHT16", "PBS_FLAG_SR",
     "pbs_amax", "pbs_scale_from_amax", "pbs_delayed_state_bytes", "pbs_delayed_init",
@@ -30,7 +31,7 @@ PBS_OK, PBS_ERR_INVALID_ARG, PBS_ERR_SHAPE, PBS_ERR_UNSUPPORTED, PBS_ERR_HIP = r
 PBS_FMT_BF16, PBS_FMT_E4M3, PBS_FMT_E5M2, PBS_FMT_E2M1, PBS_FMT_F32 = range(5)
 (PBS_RECIPE_BF16, PBS_RECIPE_FP8_CURRENT, PBS_RECIPE_FP8_DELAYED, PBS_RECIPE_FP8_BLOCK128,
  PBS_RECIPE_MXFP8, PBS_RECIPE_NVFP4, PBS_RECIPE_MXFP4, PBS_RECIPE_FP8_CHANNEL,
- PBS_RECIPE_FP8_BLOCK128_1D1D, PBS_RECIPE_FP8_BLOCK128_2D2D) = range(10)
+ PBS_RECIPE_FP8_BLOCK128_1D1D, PBS_RECIPE_FP8_BLOCK128_2D2D, PBS_RECIPE_FP8_BLOCK128_POW2) = range(11)
 PBS_FPROP, PBS_DGRAD, PBS_WGRAD = range(3)
 PBS_ROW, PBS_COL = 1, 2
 PBS_FLAG_RHT16, PBS_FLAG_SR = 1, 2

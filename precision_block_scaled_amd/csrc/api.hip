@@ -69,6 +69,12 @@ pbs_status pbs_quantized_bytes(pbs_recipe recipe, int64_t rows, int64_t cols, in
       *code_bytes = (size_t)n;
       *scale_bytes = (size_t)(weight_2d ? (rows / 128) * (cols / 128) : rows * (cols / 128)) * 4;
       break;
+    case PBS_RECIPE_FP8_BLOCK128_POW2:
+      PBS_REQUIRE(cols % 128 == 0 && (!weight_2d || rows % 128 == 0), PBS_ERR_SHAPE,
+                  "block128 needs dims that are multiples of 128");
+      *code_bytes = (size_t)n;
+      *scale_bytes = (size_t)(weight_2d ? (rows / 128) * (cols / 128) : rows * (cols / 128)) * 4;
+      break;
     case PBS_RECIPE_MXFP8:
       PBS_REQUIRE(cols % 32 == 0, PBS_ERR_SHAPE, "MXFP8 needs cols % 32 == 0");
       *code_bytes = (size_t)n; *scale_bytes = (size_t)(rows * (cols / 32)); break;

@@ -21,6 +21,9 @@
 //    amax_b), stored as fp32(1 / s_b).
 //  MXFP8 -- same page, MXFP8 item: 32-value blocks, E8M0 power-of-two scale,
 //    the smallest exponent that brings the block maximum within 448.
+//  sub-channel FP8 with power-of-two scales -- the sub-channel blocks with
+//    MXFP8's exponent rule; each block's E8M0 code is stored in all four
+//    bytes of a 32-bit word (the form the scaled matrix instruction reads).
 //  NVFP4 -- "Accelerate LLM training with NVFP4 on Blackwell", "Technical
 //    deep-dive": E2M1 values, E4M3 scale per 16 values, fp32 per tensor;
 //    "How to optimize Transformer-based models for low-precision training",
@@ -45,7 +48,7 @@
 
 namespace pbs {
 
-enum { R_TENSOR = 0, R_BLOCK128 = 1, R_MX = 2, R_NV = 3, R_MX4 = 4, R_CHAN = 5 };
+enum { R_TENSOR = 0, R_BLOCK128 = 1, R_MX = 2, R_NV = 3, R_MX4 = 4, R_CHAN = 5, R_B128P2 = 6 };
 enum { F_E4M3 = 0, F_E5M2 = 1 };
 
 constexpr int TILE = 128;
@@ -194,6 +197,27 @@ __device__ __forceinline__ void quantize_strip(const bf16_t* tile, int strip, in
       for (int i = 0; i < 16; ++i) code[i] = enc_e4m3(bf16_to_float(b[i]) * s);
       store16(out_codes + j, code);
     }
+  } else if (RECIPE == R_B128P2) {
+    float s = tile_scale;
+    if (!W2D) {                 // one 1x128 block = the whole strip
+      uint32_t m = 0;
+      for (int j = 0; j < TILE; j += 16) {
+        uint32_t b[16];
+        read16<ROWDIR>(tile, strip, j, b);
+        uint32_t mm = max_abs_bits16(b);
+        m = m > mm ? m : mm;
+      }
+      s = mx_inv_scale(mx_e8m0_from_bf16_amax(m));
+    }
+    if (!W2D || scale_writer)   // s = 2^(127 - c): its exponent field is 254 - c
+      *(uint32_t*)out_scales32 = (254u - (__float_as_uint(s) >> 23)) * 0x01010101u;
+    for (int j = 0; j < TILE; j += 16) {
+      uint32_t b[16], code[16];
+      read16<ROWDIR>(tile, strip, j, b);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) code[i] = enc_e4m3(bf16_to_float(b[i]) * s);
+      store16(out_codes + j, code);
+    }
   } else if (RECIPE == R_MX) {
     for (int j = 0; j < len; j += 32) {
       uint32_t b0[16], b1[16], code[16];
@@ -298,7 +322,7 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
       if (row < rlim && ch * 8 < clim)
         v = ld_nt16(a.x + (r0 + row) * a.C + c0 + ch * 8);
       *(uint4*)&tile[row * LDS_STRIDE + ch * 8] = v;
-      if (AMAX || (RECIPE == R_BLOCK128 && W2D)) {
+      if (AMAX || ((RECIPE == R_BLOCK128 || RECIPE == R_B128P2) && W2D)) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -315,7 +339,7 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
     const uint64_t bal = __ballot(bit);
     if (t == 0) s_rht_mask = (uint32_t)bal;
   }
-  if (AMAX || (RECIPE == R_BLOCK128 && W2D)) {
+  if (AMAX || ((RECIPE == R_BLOCK128 || RECIPE == R_B128P2) && W2D)) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
       uint32_t w = (uint32_t)__shfl_xor((int)mx, o, 64);
@@ -325,7 +349,7 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
   }
   __syncthreads();
   uint32_t tile_max_bits = 0;
-  if (AMAX || (RECIPE == R_BLOCK128 && W2D)) {
+  if (AMAX || ((RECIPE == R_BLOCK128 || RECIPE == R_B128P2) && W2D)) {
     tile_max_bits = s_part[0] > s_part[1] ? s_part[0] : s_part[1];
     if (AMAX && t == 0) atomicMax(a.amax_out, tile_max_bits << 16);
   }
@@ -334,6 +358,7 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
   float tile_scale = 0.0f;
   if (RECIPE == R_TENSOR || RECIPE == R_NV) tile_scale = *a.scale;
   if (RECIPE == R_BLOCK128 && W2D) tile_scale = scale_from_amax(bf16_to_float(tile_max_bits), 448.0f);
+  if (RECIPE == R_B128P2 && W2D) tile_scale = mx_inv_scale(mx_e8m0_from_bf16_amax(tile_max_bits));
 
   if (ROW && t < rlim) {
     const int64_t gr = r0 + t;
@@ -342,10 +367,10 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
     uint8_t* sc8 = nullptr;
     float* sc32 = nullptr;
     bool writer = true;
-    if (RECIPE == R_BLOCK128)
+    if (RECIPE == R_BLOCK128 || RECIPE == R_B128P2)
       sc32 = W2D ? (float*)a.row_scales + (r0 / 128) * (a.C / 128) + c0 / 128
                  : (float*)a.row_scales + gr * (a.C / 128) + c0 / 128;
-    if (RECIPE == R_BLOCK128 && W2D) writer = (t == 0);
+    if ((RECIPE == R_BLOCK128 || RECIPE == R_B128P2) && W2D) writer = (t == 0);
     if (RECIPE == R_MX || RECIPE == R_MX4) sc8 = (uint8_t*)a.row_scales + gr * (a.C / 32) + c0 / 32;
     if (RECIPE == R_NV) {
       sc8 = W2D ? (uint8_t*)a.row_scales + (gr / 16) * (a.C / 16) + c0 / 16
@@ -362,10 +387,10 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
     uint8_t* sc8 = nullptr;
     float* sc32 = nullptr;
     bool writer = true;
-    if (RECIPE == R_BLOCK128)
+    if (RECIPE == R_BLOCK128 || RECIPE == R_B128P2)
       sc32 = W2D ? (float*)a.col_scales + (c0 / 128) * (a.R / 128) + r0 / 128
                  : (float*)a.col_scales + gc * (a.R / 128) + r0 / 128;
-    if (RECIPE == R_BLOCK128 && W2D) writer = (t == 0);
+    if ((RECIPE == R_BLOCK128 || RECIPE == R_B128P2) && W2D) writer = (t == 0);
     if (RECIPE == R_MX || RECIPE == R_MX4) sc8 = (uint8_t*)a.col_scales + gc * (a.R / 32) + r0 / 32;
     if (RECIPE == R_NV) {
       sc8 = W2D ? (uint8_t*)a.col_scales + (gc / 16) * (a.R / 16) + r0 / 16
@@ -459,7 +484,7 @@ template <int RECIPE, int FMT, bool SR>
 __device__ __forceinline__ void quantize_segment(const float* v, uint32_t mbits, float tscale, bool valid,
                                                  uint8_t* codes, uint8_t* sc8, float* sc32, bool writer,
                                                  const uint32_t* rnd) {
-  if (RECIPE == R_TENSOR || RECIPE == R_MX || RECIPE == R_BLOCK128) {
+  if (RECIPE == R_TENSOR || RECIPE == R_MX || RECIPE == R_BLOCK128 || RECIPE == R_B128P2) {
     float s = tscale;
     if (RECIPE == R_MX) {
       const uint32_t m = group_max<2>(mbits);
@@ -471,6 +496,10 @@ __device__ __forceinline__ void quantize_segment(const float* v, uint32_t mbits,
       const uint32_t m = group_max<8>(mbits);
       s = scale_from_amax(__uint_as_float(m), 448.0f);
       if (valid && writer) *sc32 = 1.0f / s;
+    } else if (RECIPE == R_B128P2) {
+      const uint32_t c = mx_e8m0_from_bf16_amax(group_max<8>(mbits) >> 16);
+      s = mx_inv_scale(c);
+      if (valid && writer) *(uint32_t*)sc32 = c * 0x01010101u;
     }
     uint4 o;
     o.x = hw_fp8x4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
@@ -600,7 +629,7 @@ __global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg)
         writer = (seg & 1) == 0;
       } else if (RECIPE == R_NV) {
         sc8 = (uint8_t*)a.row_scales + row * (a.C / 16) + seg;
-      } else if (RECIPE == R_BLOCK128) {
+      } else if (RECIPE == R_BLOCK128 || RECIPE == R_B128P2) {
         sc32 = (float*)a.row_scales + row * (a.C / 128) + seg / 8;
         writer = (seg & 7) == 0;
       }
@@ -717,7 +746,7 @@ __global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
       writer = (rs & 1) == 0;
     } else if (RECIPE == R_NV) {
       sc8 = (uint8_t*)a.col_scales + gc * (a.R / 16) + gr / 16;
-    } else if (RECIPE == R_BLOCK128) {
+    } else if (RECIPE == R_BLOCK128 || RECIPE == R_B128P2) {
       sc32 = (float*)a.col_scales + gc * (a.R / 128) + gr / 128;
       writer = (rs & 7) == 0;
     }
@@ -991,8 +1020,8 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
   PBS_REQUIRE(!rht || orient_mask == PBS_COL, PBS_ERR_UNSUPPORTED,
               "pbs_cast: RHT16 runs along the rows and produces the col copy only");
   PBS_REQUIRE(!w2d || recipe == PBS_RECIPE_FP8_BLOCK128 || recipe == PBS_RECIPE_FP8_BLOCK128_2D2D ||
-                  recipe == PBS_RECIPE_NVFP4,
-              PBS_ERR_UNSUPPORTED, "pbs_cast: 2D blocks exist for FP8_BLOCK128(_2D2D) and NVFP4 only");
+                  recipe == PBS_RECIPE_FP8_BLOCK128_POW2 || recipe == PBS_RECIPE_NVFP4,
+              PBS_ERR_UNSUPPORTED, "pbs_cast: 2D blocks exist for FP8_BLOCK128(_2D2D, _POW2) and NVFP4 only");
   PBS_REQUIRE(!(w2d && (rht || sr)), PBS_ERR_UNSUPPORTED,
               "pbs_cast: 2D weight blocks take neither RHT16 nor SR");
   PBS_REQUIRE(amax_out == nullptr || recipe == PBS_RECIPE_FP8_CURRENT || recipe == PBS_RECIPE_FP8_DELAYED,
@@ -1040,6 +1069,20 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
       fn = w2d ? pick_orient<R_BLOCK128, F_E4M3, true, false, false, false>(orient_mask)
                : pick_orient<R_BLOCK128, F_E4M3, false, false, false, false>(orient_mask);
       name = "cast_block128";
+      break;
+    }
+    case PBS_RECIPE_FP8_BLOCK128_POW2: {
+      PBS_REQUIRE(fmt == PBS_FMT_E4M3, PBS_ERR_UNSUPPORTED, "pbs_cast: FP8_BLOCK128_POW2 takes E4M3");
+      PBS_REQUIRE((!row || cols % 128 == 0) && (!col || rows % 128 == 0) &&
+                      (!w2d || (rows % 128 == 0 && cols % 128 == 0)),
+                  PBS_ERR_SHAPE, "pbs_cast: FP8_BLOCK128_POW2 needs the blocked dims to be multiples of 128");
+      PBS_REQUIRE((!row || row_scales) && (!col || col_scales), PBS_ERR_INVALID_ARG,
+                  "pbs_cast: block scales output is null");
+      PBS_REQUIRE((!row || ((uintptr_t)row_scales & 3) == 0) && (!col || ((uintptr_t)col_scales & 3) == 0),
+                  PBS_ERR_INVALID_ARG, "pbs_cast: FP8_BLOCK128_POW2 scale words must be 4-byte aligned");
+      fn = w2d ? pick_orient<R_B128P2, F_E4M3, true, false, false, false>(orient_mask)
+               : pick_orient<R_B128P2, F_E4M3, false, false, false, false>(orient_mask);
+      name = "cast_block128_pow2";
       break;
     }
     case PBS_RECIPE_MXFP8: {

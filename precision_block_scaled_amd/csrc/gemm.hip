@@ -20,6 +20,11 @@
 //              MX blocks; the two lanes that hold a row (or column) each
 //              supply the E8M0 scale of one of its blocks, and the hardware
 //              applies it to that block's 32 products.
+//  FP8 1x128 / 128x128 with power-of-two scales  the MXFP8 kernel: a
+//              128-long K stage is one block, and its scale word repeats the
+//              block's E8M0 code in all four bytes, so the instruction applies
+//              it to each 32-value step; the 128x128 weight blocks share one
+//              scale row per 128 operand rows.
 //  NVFP4       E2M1 x E4M3 block scale has up to 6 significant bits, more
 //              than any 4-, 6- or 8-bit MFMA input holds, and the E4M3 scale
 //              is no power of two, so it cannot ride on the instruction's
@@ -346,8 +351,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   if (LDB == LD_KMAJOR) direct_init(db, g.B, g.ldb, n0, g.N, w);
   else mn_direct_init(mb, g.B, g.ldb, n0, g.N, w);
   if (MX) {
-    rowdw_init(sa, g.a_scale, g.K / 32, m0, g.M, 1, w);
-    rowdw_init(sb, g.b_scale, g.K / 32, n0, g.N, 1, w);
+    rowdw_init(sa, g.a_scale, g.K / 32, m0, g.M, g.a_sdiv, w);
+    rowdw_init(sb, g.b_scale, g.K / 32, n0, g.N, g.b_sdiv, w);
   }
   // SC_MXC: a lane loads 16 bytes of its row's scales at once (CH stages), one
   // load per row every CH stages instead of every stage.  Chunks are aligned
@@ -904,6 +909,8 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
   g.ldc = (int)N;
   g.tiles_m = (int)ceil_div(M, BM);
   g.tiles_n = (int)ceil_div(N, BN);
+  g.a_sdiv = 1;
+  g.b_sdiv = 1;
 
   gemm_fn fn = nullptr;
   const char* name = "";
@@ -990,6 +997,24 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
       fn = K / 128 >= 4 ? pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_MXC, 0, 0>(bf16_out)
                         : pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_MX, 0, 0>(bf16_out);
       name = "gemm_mxfp8";
+      break;
+    }
+    case PBS_RECIPE_FP8_BLOCK128_POW2: {
+      // Power-of-two block scales ride on the scaled MFMA like MXFP8's: each
+      // 128-long K stage is one block, whose scale word holds its E8M0 code
+      // in all four bytes, so every 32-value step of the stage reads it.
+      PBS_REQUIRE(a_fmt == PBS_FMT_E4M3 && b_fmt == PBS_FMT_E4M3, PBS_ERR_UNSUPPORTED,
+                  "pbs_gemm: FP8_BLOCK128_POW2 takes E4M3 operands");
+      PBS_REQUIRE(a_scale && b_scale, PBS_ERR_INVALID_ARG, "pbs_gemm: block scales are null");
+      PBS_REQUIRE(K % 128 == 0, PBS_ERR_SHAPE, "pbs_gemm: FP8_BLOCK128_POW2 needs K %% 128 == 0");
+      PBS_REQUIRE(!w2d || N % 128 == 0, PBS_ERR_SHAPE, "pbs_gemm: 128x128 weight blocks need N %% 128 == 0");
+      PBS_REQUIRE(((uintptr_t)a_scale & 3) == 0 && ((uintptr_t)b_scale & 3) == 0, PBS_ERR_INVALID_ARG,
+                  "pbs_gemm: FP8_BLOCK128_POW2 scale words must be 4-byte aligned");
+      g.lda = K; g.ldb = K;
+      g.b_sdiv = w2d ? 128 : 1;                   // 128x128 weight blocks: one scale row per 128 rows
+      fn = K / 128 >= 4 ? pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_MXC, 0, 0>(bf16_out)
+                        : pick_out<OP_FP8, LD_KMAJOR, LD_KMAJOR, SC_MX, 0, 0>(bf16_out);
+      name = "gemm_fp8_block128_pow2";
       break;
     }
     case PBS_RECIPE_MXFP4: {

@@ -36,6 +36,7 @@ struct GemmArgs {
   int64_t lda, ldb;       // bytes between stored rows of A / B
   int ldc;                // elements between rows of C
   int tiles_m, tiles_n;
+  int a_sdiv, b_sdiv;     // MX scale rows: operand rows per stored scale row (1, or 128 for 128x128 blocks)
 };
 
 // LDS tile layout: row r, 16-byte chunk c lives at r * 128 + ((c ^ key(r)) << 4).

@@ -11,8 +11,8 @@ separate GEMMs), with X [M, K], W stored [N, K], dY [M, N]:
   wgrad: A = X col copy,  B = dY col copy
 
 Format roles: per-tensor FP8 uses E4M3 for X and W, E5M2 for dY;
-sub-channel FP8, channel-wise FP8 (one fp32 scale per row of each copy) and
-MXFP8 use E4M3; NVFP4 and MXFP4 use E2M1.  Weights
+sub-channel FP8 (fp32 or power-of-two block scales), channel-wise FP8 (one
+fp32 scale per row of each copy) and MXFP8 use E4M3; NVFP4 and MXFP4 use E2M1.  Weights
 take 2D blocks (128x128 sub-channel, 16x16 NVFP4; MXFP4 keeps 1x32 blocks
 along the contraction axis for every operand); the sub-channel pairings
 take 1x128 blocks on every tensor (1D1D) or 128x128 on every tensor (2D2D).  NVFP4 and MXFP4 apply the
@@ -28,6 +28,7 @@ import torch
 from . import (PBS_COL, PBS_DGRAD, PBS_FLAG_RHT16, PBS_FLAG_SR, PBS_FMT_BF16, PBS_FMT_E2M1,
                PBS_FMT_E4M3, PBS_FMT_E5M2, PBS_FMT_F32, PBS_FPROP, PBS_RECIPE_BF16,
                PBS_RECIPE_FP8_BLOCK128, PBS_RECIPE_FP8_BLOCK128_1D1D, PBS_RECIPE_FP8_BLOCK128_2D2D,
+               PBS_RECIPE_FP8_BLOCK128_POW2,
                PBS_RECIPE_FP8_CHANNEL, PBS_RECIPE_FP8_CURRENT,
                PBS_RECIPE_FP8_DELAYED,
                PBS_RECIPE_MXFP4, PBS_RECIPE_MXFP8, PBS_RECIPE_NVFP4, PBS_ROW, PBS_WGRAD, pbs_amax,
@@ -46,9 +47,11 @@ RECIPES = {
     "fp8_channel": PBS_RECIPE_FP8_CHANNEL,
     "fp8_block128_1d1d": PBS_RECIPE_FP8_BLOCK128_1D1D,
     "fp8_block128_2d2d": PBS_RECIPE_FP8_BLOCK128_2D2D,
+    "fp8_block128_pow2": PBS_RECIPE_FP8_BLOCK128_POW2,
 }
 # sources that take 2D blocks, per recipe
-TWO_D = {"fp8_block128": ("w",), "nvfp4": ("w",), "fp8_block128_2d2d": ("x", "w", "dy")}
+TWO_D = {"fp8_block128": ("w",), "nvfp4": ("w",), "fp8_block128_2d2d": ("x", "w", "dy"),
+         "fp8_block128_pow2": ("w",)}
 SUBCHANNEL = ("fp8_block128", "fp8_block128_1d1d", "fp8_block128_2d2d")
 LAYOUTS = {"fprop": PBS_FPROP, "dgrad": PBS_DGRAD, "wgrad": PBS_WGRAD}
 ROLES = {"fprop": (("x", "row"), ("w", "row")),
@@ -95,7 +98,10 @@ def _empty_copy(recipe, rows, cols, w2d, device):
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
         return codes, torch.empty((rows, cols // 32), dtype=torch.uint8, device=device)
     codes = torch.empty((rows, cols), dtype=torch.uint8, device=device)
-    if recipe in SUBCHANNEL:
+    if recipe == "fp8_block128_pow2":      # one 32-bit word per block: its E8M0 code in every byte
+        sc = (torch.empty((rows // 128, cols // 128), dtype=torch.int32, device=device) if w2d
+              else torch.empty((rows, cols // 128), dtype=torch.int32, device=device))
+    elif recipe in SUBCHANNEL:
         sc = (torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=device) if w2d
               else torch.empty((rows, cols // 128), dtype=torch.float32, device=device))
     elif recipe == "mxfp8":
@@ -182,7 +188,7 @@ def quantize(recipe, x, src, orient, pass_, state=None, out=None, ws=None, strea
         pbs_cast(rec, x, R, C, fmt, rmask, 0, 0, 0, state.scale_ptr, state.amax, row_c, row_s,
                  col_c, col_s, stream)
         out.tensor_scale_inv = state.scale_inv_ptr
-    elif recipe in SUBCHANNEL + ("mxfp8", "fp8_channel"):
+    elif recipe in SUBCHANNEL + ("mxfp8", "fp8_channel", "fp8_block128_pow2"):
         pbs_cast(rec, x, R, C, fmt, rmask, int(w2d), 0, 0, None, None, row_c, row_s, col_c, col_s,
                  stream)
     elif recipe == "nvfp4":

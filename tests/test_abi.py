@@ -68,6 +68,13 @@ def test_cast_validation_codes():
     # block128 needs the blocked dim to be a multiple of 128
     _expect(2, c, P.PBS_RECIPE_FP8_BLOCK128, FAKE, 64, 96, P.PBS_FMT_E4M3, 1, 0, 0, 0, None, None, FAKE,
             FAKE, None, None, 0)
+    # power-of-two sub-channel: blocked dims multiples of 128, E4M3 only, scale words 4-byte aligned
+    _expect(2, c, P.PBS_RECIPE_FP8_BLOCK128_POW2, FAKE, 64, 96, P.PBS_FMT_E4M3, 1, 0, 0, 0, None, None, FAKE,
+            FAKE, None, None, 0)
+    _expect(3, c, P.PBS_RECIPE_FP8_BLOCK128_POW2, FAKE, 64, 128, P.PBS_FMT_E5M2, 1, 0, 0, 0, None, None, FAKE,
+            FAKE, None, None, 0)
+    _expect(1, c, P.PBS_RECIPE_FP8_BLOCK128_POW2, FAKE, 64, 128, P.PBS_FMT_E4M3, 1, 0, 0, 0, None, None, FAKE,
+            FAKE + 2, None, None, 0)
     # per-tensor FP8 needs the scale
     _expect(1, c, P.PBS_RECIPE_FP8_CURRENT, FAKE, 64, 64, P.PBS_FMT_E4M3, 1, 0, 0, 0, None, None, FAKE,
             None, None, None, 0)
@@ -100,6 +107,11 @@ def test_gemm_validation_codes():
             FAKE, P.PBS_FMT_E4M3, None, None, FAKE, P.PBS_FMT_F32, 0)
     _expect(1, g, P.PBS_RECIPE_BF16, 7, 64, 64, 64, FAKE, P.PBS_FMT_BF16, None, None, FAKE,
             P.PBS_FMT_BF16, None, None, FAKE, P.PBS_FMT_F32, 0)
+    # power-of-two sub-channel: 128x128 weight blocks need N % 128; scale words 4-byte aligned
+    _expect(2, g, P.PBS_RECIPE_FP8_BLOCK128_POW2, P.PBS_FPROP, 64, 80, 128, FAKE, P.PBS_FMT_E4M3, FAKE, None,
+            FAKE, P.PBS_FMT_E4M3, FAKE, None, FAKE, P.PBS_FMT_F32, 0)
+    _expect(1, g, P.PBS_RECIPE_FP8_BLOCK128_POW2, P.PBS_WGRAD, 64, 80, 128, FAKE, P.PBS_FMT_E4M3, FAKE + 1,
+            None, FAKE, P.PBS_FMT_E4M3, FAKE, None, FAKE, P.PBS_FMT_F32, 0)
 
 
 def test_scalar_entry_validation():
@@ -127,5 +139,8 @@ def test_quantized_bytes_accounting():
     assert P.pbs_quantized_bytes(P.PBS_RECIPE_FP8_BLOCK128, 256, 256, 1) == (65536, 16)
     assert P.pbs_quantized_bytes(P.PBS_RECIPE_FP8_BLOCK128, 256, 256, 0) == (65536, 256 * 2 * 4)
     _expect(2, P.pbs_quantized_bytes, P.PBS_RECIPE_MXFP8, 16, 48, 0)
+    # power-of-two sub-channel: one 4-byte word per block, like the fp32 scales
+    assert P.pbs_quantized_bytes(P.PBS_RECIPE_FP8_BLOCK128_POW2, 256, 256, 1) == (65536, 16)
+    assert P.pbs_quantized_bytes(P.PBS_RECIPE_FP8_BLOCK128_POW2, 256, 256, 0) == (65536, 256 * 2 * 4)
     # channel-wise FP8: one fp32 scale per row
     assert P.pbs_quantized_bytes(P.PBS_RECIPE_FP8_CHANNEL, 48, 80, 0) == (48 * 80, 48 * 4)

@@ -46,7 +46,7 @@ MODELS = {
     "llama3_8b": (8192, W.layer_shapes(L3["hidden"], L3["intermediate"], L3["heads"], L3["kv_heads"],
                                        L3["gated"])),
 }
-FP8_MFMA = {"fp8_current", "fp8_delayed", "mxfp8", "fp8_channel"} | set(BLOCK128_2D)
+FP8_MFMA = {"fp8_current", "fp8_delayed", "mxfp8", "fp8_channel", "fp8_block128_pow2"} | set(BLOCK128_2D)
 FMAX = {"e4m3": 448.0, "e5m2": 57344.0}
 SEED = 42
 
@@ -79,7 +79,7 @@ class OracleCopy:
     def __init__(self, recipe, src, orient, bits, pass_, dstate, rows):
         self.recipe, self.rows = recipe, rows
         sl = copy_rows(bits, orient, rows)
-        w2d = src in BLOCK128_2D.get(recipe, ()) or (src == "w" and recipe == "nvfp4")
+        w2d = src in BLOCK128_2D.get(recipe, ()) or (src == "w" and recipe in ("nvfp4", "fp8_block128_pow2"))
         self.tsi = None
         self.scales = None
         if recipe in ("fp8_current", "fp8_delayed"):
@@ -94,6 +94,9 @@ class OracleCopy:
         elif recipe in BLOCK128_2D:
             self.codes, self.scales = R.quantize_block128(sl, orient, weight_2d=w2d)
             self.deq = R.dequant_block128(self.codes, self.scales, w2d)
+        elif recipe == "fp8_block128_pow2":             # scales compared as E8M0 codes
+            self.codes, self.scales = R.quantize_block128_pow2(sl, orient, weight_2d=w2d)
+            self.deq = R.dequant_block128_pow2(self.codes, self.scales, w2d)
         elif recipe == "fp8_channel":                   # a copy row's scale is its own
             self.codes, self.scales = R.quantize_channel(sl, orient)
             self.deq = R.dequant_channel(self.codes, self.scales)
@@ -137,7 +140,7 @@ def gpu_rows(q, rows, w2d):
     sc = None
     if q.scales is not None:
         if w2d:
-            div = 128 if q.recipe in BLOCK128_2D else 16
+            div = 128 if q.recipe in BLOCK128_2D or q.recipe == "fp8_block128_pow2" else 16
             g = torch.from_numpy(np.unique(np.asarray(rows) // div).astype(np.int64)).to(q.codes.device)
             sc = q.scales[g].cpu().numpy()
         else:
@@ -184,7 +187,10 @@ def run_pass(recipe, model, name, pass_):
             if (codes != o.codes).any():
                 i = tuple(np.argwhere(codes != o.codes)[0])
                 out.append(f"codes differ at sampled {i}: {codes[i]} vs {o.codes[i]}")
-            if o.scales is not None and (sc.view(np.uint8) != np.ascontiguousarray(o.scales).view(np.uint8)).any():
+            if recipe == "fp8_block128_pow2":            # each word: the E8M0 code in all four bytes
+                if (sc.view(np.uint32) != o.scales.astype(np.uint32) * np.uint32(0x01010101)).any():
+                    out.append("block scale words differ")
+            elif o.scales is not None and (sc.view(np.uint8) != np.ascontiguousarray(o.scales).view(np.uint8)).any():
                 out.append("block scales differ")
             if o.tsi is not None:
                 if isinstance(q.tensor_scale_inv, int):   # delayed: the state's scale_inv word
@@ -216,6 +222,8 @@ CASES = ([("codonfm", n, r) for n in ("qkv", "attn_out", "mlp_up", "mlp_down") f
          + [(m, n, r) for r in ("mxfp4", "fp8_channel") for m in ("codonfm", "llama3_8b")
             for n in ("qkv", "attn_out", "mlp_up", "mlp_down")]
          + [("codonfm", n, r) for r in ("fp8_block128_1d1d", "fp8_block128_2d2d")
+            for n in ("qkv", "attn_out", "mlp_up", "mlp_down")]
+         + [(m, n, "fp8_block128_pow2") for m in ("codonfm", "llama3_8b")
             for n in ("qkv", "attn_out", "mlp_up", "mlp_down")])
 
 
