@@ -68,10 +68,29 @@ def kernel_key(recipe, pass_):
     return ("gemm_nvfp4_w2d" if pass_ != "wgrad" else "gemm_nvfp4_1d"), "fp16"
 
 
-def source_digest():
+# the sources each kernel family is built from: its HBM counters stay valid
+# while these files are unchanged
+KERNEL_SOURCES = {
+    "gemm_": ("gemm.hip", "gemm_blk.hip", "gemm_common.hpp", "device.hpp", "host.hpp"),
+    "cast_": ("cast.hip", "device.hpp", "host.hpp"),
+    "chan_": ("cast.hip", "device.hpp", "host.hpp"),
+    "amax": ("amax.hip", "device.hpp", "host.hpp"),
+}
+
+
+def kernel_source_files(kernel_name):
+    for prefix, files in KERNEL_SOURCES.items():
+        if kernel_name.startswith(prefix):
+            return files
+    return tuple(sorted(os.listdir(os.path.join(ROOT, "precision_block_scaled_amd", "csrc"))))
+
+
+def source_digest(files=None):
+    """Digest of the HIP sources `files` (default: all of them)."""
+    d = os.path.join(ROOT, "precision_block_scaled_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "precision_block_scaled_amd", "csrc"))):
-        with open(os.path.join(ROOT, "precision_block_scaled_amd", "csrc", f), "rb") as fh:
+    for f in sorted(files if files is not None else os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
@@ -367,7 +386,7 @@ def load_traffic(kernel_name):
     except Exception:
         return None
     rec = d.get(kernel_name)
-    if not rec or rec.get("source_digest") != source_digest():
+    if not rec or rec.get("source_digest") != source_digest(kernel_source_files(kernel_name)):
         return None
     return rec
 
