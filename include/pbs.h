@@ -291,6 +291,25 @@ pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, int64_t N, 
                     pbs_format c_fmt, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
+ * pbs_gemm_amax: pbs_gemm that also returns max |C| over the stored output
+ * ([LP] "Interpreting results for a real model" counts the extra memory
+ * pass for the per-tensor maximum among the quantization overheads; a
+ * tensor that a GEMM produces gets its maximum from the GEMM's epilogue
+ * instead, with no second read of C).
+ *  c_amax: device fp32, receives max |C| of the values as stored (after
+ *    the epilogue scale and, for bf16 output, after rounding to bf16), i.e.
+ *    what pbs_amax would return on C; reset to 0 first (stream-ordered), 0
+ *    for an empty C.  Must be non-null and 4-byte aligned (else
+ *    PBS_ERR_INVALID_ARG); the other arguments and errors are pbs_gemm's,
+ *    and C is bit-identical to pbs_gemm's.
+ * ------------------------------------------------------------------- */
+pbs_status pbs_gemm_amax(pbs_recipe recipe, pbs_layout layout, int64_t M, int64_t N, int64_t K,
+                         const void* A, pbs_format a_fmt, const void* a_scale,
+                         const float* a_tensor_scale, const void* B, pbs_format b_fmt,
+                         const void* b_scale, const float* b_tensor_scale, void* C,
+                         pbs_format c_fmt, float* c_amax, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
  * pbs_quantized_bytes [host]: bytes of the codes and of the block scales
  * of one quantized copy of a [rows, cols] tensor (not counting per-tensor
  * fp32 scalars).  For NVFP4 with 1x16 blocks this is n/2 + n/16 bytes,

@@ -24,7 +24,7 @@ __all__ = [
     "PBS_FLAG_RHT16", "PBS_FLAG_SR",
     "pbs_amax", "pbs_scale_from_amax", "pbs_delayed_state_bytes", "pbs_delayed_init",
     "pbs_delayed_update", "pbs_delayed_scale", "pbs_delayed_scale_inv", "pbs_cast",
-    "pbs_gemm", "pbs_quantized_bytes", "pbs_last_error", "pbs_version",
+    "pbs_gemm", "pbs_gemm_amax", "pbs_quantized_bytes", "pbs_last_error", "pbs_version",
 ]
 
 PBS_OK, PBS_ERR_INVALID_ARG, PBS_ERR_SHAPE, PBS_ERR_UNSUPPORTED, PBS_ERR_HIP = range(5)
@@ -54,6 +54,8 @@ SIGNATURES = {
                         _vp, _vp, _vp, _vp, _vp]),
     "pbs_gemm": (_i32, [_i32, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _vp,
                         _vp, _vp, _i32, _vp]),
+    "pbs_gemm_amax": (_i32, [_i32, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _vp,
+                             _vp, _vp, _i32, _vp, _vp]),
     "pbs_quantized_bytes": (_i32, [_i32, _i64, _i64, _i32, _c.POINTER(_c.c_size_t),
                                    _c.POINTER(_c.c_size_t)]),
     "pbs_last_error": (_c.c_char_p, []),
@@ -155,6 +157,13 @@ def pbs_gemm(recipe, layout, M, N, K, A, a_fmt, a_scale, a_tensor_scale, B, b_fm
     _check(lib().pbs_gemm(recipe, layout, M, N, K, _ptr(A), a_fmt, _ptr(a_scale), _ptr(a_tensor_scale),
                           _ptr(B), b_fmt, _ptr(b_scale), _ptr(b_tensor_scale), _ptr(C), c_fmt,
                           _stream(stream)))
+
+
+def pbs_gemm_amax(recipe, layout, M, N, K, A, a_fmt, a_scale, a_tensor_scale, B, b_fmt, b_scale,
+                  b_tensor_scale, C, c_fmt, c_amax, stream=None):
+    _check(lib().pbs_gemm_amax(recipe, layout, M, N, K, _ptr(A), a_fmt, _ptr(a_scale), _ptr(a_tensor_scale),
+                               _ptr(B), b_fmt, _ptr(b_scale), _ptr(b_tensor_scale), _ptr(C), c_fmt,
+                               _ptr(c_amax), _stream(stream)))
 
 
 def pbs_quantized_bytes(recipe, rows, cols, weight_2d):

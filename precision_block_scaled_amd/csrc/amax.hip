@@ -50,34 +50,35 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v) {
 }
 
 // Plain amax over n bf16 values; n8 = n / 8 full 16-byte chunks, the rest
-// (n % 8 values) handled by block 0.  Eight 16-byte loads per thread in
-// flight before any arithmetic (measured best against 4, and against
-// 2048 / 8192 workgroups).
+// (n % 8 values) handled by block 0.  Each block reads 32 KB contiguous per
+// iteration (chunks [(j * grid + b) * 2048, + 2048): thread t takes chunks
+// t, t + 256, ... of them, eight 16-byte loads in flight before any
+// arithmetic).  Measured on a 1 GiB read: 7.0 TB/s with this block-contiguous
+// order against 5.6-6.0 TB/s when consecutive blocks interleave their 4 KB
+// pieces (grid-stride order); 1024-16384 blocks all within 1%.  Chunks past
+// the end re-read the last one (harmless for a maximum).
 __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint4* __restrict__ x, int64_t n8,
                                                         const bf16_t* __restrict__ tail, int tail_n,
                                                         uint32_t* out) {
+  constexpr int U = 8;
   us2 m = {0, 0};
   const us2 mask = {0x7FFF, 0x7FFF};
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 7 * stride < n8; i += 8 * stride) {
-    uint4 v[8];
+  const int64_t span = 256 * U;
+  for (int64_t base = (int64_t)blockIdx.x * span; base < n8; base += (int64_t)gridDim.x * span) {
+    uint4 v[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = ld_nt16(&x[i + u * stride]);
+    for (int u = 0; u < U; ++u) {
+      int64_t j = base + u * 256 + threadIdx.x;
+      j = j < n8 ? j : n8 - 1;
+      v[u] = ld_nt16(&x[j]);
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[u].x) & mask);
       m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[u].y) & mask);
       m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[u].z) & mask);
       m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[u].w) & mask);
     }
-  }
-  for (; i < n8; i += stride) {
-    uint4 v = x[i];
-    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v.x) & mask);
-    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v.y) & mask);
-    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v.z) & mask);
-    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v.w) & mask);
   }
   uint32_t mm = m.x > m.y ? m.x : m.y;
   if (blockIdx.x == 0 && (int)threadIdx.x < tail_n) {

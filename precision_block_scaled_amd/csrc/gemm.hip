@@ -264,15 +264,23 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], const GemmArgs& 
         }
     __syncthreads();
     const int ch = lane & 31;
+    uint32_t mx = 0;
 #pragma unroll 4
     for (int it = 0; it < 32; ++it) {
       const int s = 64 * w + 2 * it + (lane >> 5);
       const uint4 val = *(const uint4*)(smem + s * STG_BF16 + ch * 16);
       const int grow = m0 + s, gcol = n0 + ch * 8;
-      if (full || (grow < g.M && gcol < g.N))
+      if (full || (grow < g.M && gcol < g.N)) {
         *(uint4*)((uint16_t*)g.C + (int64_t)grow * g.ldc + gcol) = val;
+        if (g.c_amax) {
+          const uint32_t a = absmax_bf16x8(val);
+          mx = mx > a ? mx : a;
+        }
+      }
     }
+    if (g.c_amax) amax_fold_wave(mx, g.c_amax);
   } else {
+    uint32_t mx = 0;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
 #pragma unroll
@@ -291,10 +299,17 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], const GemmArgs& 
         const int s = 32 * w + it;
         const uint4 val = *(const uint4*)(smem + s * STG_F32 + lane * 16);
         const int grow = m0 + (s >> 6) * 128 + 64 * p + (s & 63), gcol = n0 + lane * 4;
-        if (full || (grow < g.M && gcol < g.N)) *(uint4*)((float*)g.C + (int64_t)grow * g.ldc + gcol) = val;
+        if (full || (grow < g.M && gcol < g.N)) {
+          *(uint4*)((float*)g.C + (int64_t)grow * g.ldc + gcol) = val;
+          if (g.c_amax) {
+            const uint32_t a = absmax_f32x4(val);
+            mx = mx > a ? mx : a;
+          }
+        }
       }
       if (p == 0) __syncthreads();
     }
+    if (g.c_amax) amax_fold_wave(mx, g.c_amax);
   }
 }
 
@@ -869,11 +884,17 @@ static gemm_fn pick_fp8(int afmt, int bfmt, bool bf16_out) {
 
 using namespace pbs;
 
-extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, int64_t N, int64_t K,
-                               const void* A, pbs_format a_fmt, const void* a_scale,
-                               const float* a_tensor_scale, const void* B, pbs_format b_fmt,
-                               const void* b_scale, const float* b_tensor_scale, void* C,
-                               pbs_format c_fmt, hipStream_t stream) {
+__global__ void zero_word_kernel(uint32_t* p) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0u;
+}
+
+// pbs_gemm, and with c_amax non-null pbs_gemm_amax: the epilogue also folds
+// max |C| of the stored values into *c_amax (reset to 0 first, stream-ordered).
+static pbs_status gemm_impl(pbs_recipe recipe, pbs_layout layout, int64_t M, int64_t N, int64_t K,
+                            const void* A, pbs_format a_fmt, const void* a_scale,
+                            const float* a_tensor_scale, const void* B, pbs_format b_fmt,
+                            const void* b_scale, const float* b_tensor_scale, void* C,
+                            pbs_format c_fmt, float* c_amax, hipStream_t stream) {
   PBS_REQUIRE(layout >= PBS_FPROP && layout <= PBS_WGRAD, PBS_ERR_INVALID_ARG, "pbs_gemm: unknown layout %d",
               (int)layout);
   PBS_REQUIRE(c_fmt == PBS_FMT_F32 || c_fmt == PBS_FMT_BF16, PBS_ERR_UNSUPPORTED,
@@ -884,8 +905,13 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
   PBS_REQUIRE(M <= (1 << 30) && N <= (1 << 30) && K <= (1 << 30), PBS_ERR_SHAPE, "pbs_gemm: dims too large");
   PBS_REQUIRE(M * N == 0 || C, PBS_ERR_INVALID_ARG, "pbs_gemm: C is null");
   const bool bf16_out = c_fmt == PBS_FMT_BF16;
-  if (M == 0 || N == 0) return PBS_OK;
+  if (M == 0 || N == 0) {
+    if (!c_amax) return PBS_OK;
+    hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)c_amax);
+    return check_launch("pbs_gemm");
+  }
   if (K == 0) {
+    if (c_amax) hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)c_amax);
     const int64_t bytes = M * N * (bf16_out ? 2 : 4);
     hipLaunchKernelGGL(zero_c_kernel, dim3(1024), dim3(256), 0, stream, (uint8_t*)C, bytes);
     return check_launch("pbs_gemm");
@@ -911,6 +937,7 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
   g.tiles_n = (int)ceil_div(N, BN);
   g.a_sdiv = 1;
   g.b_sdiv = 1;
+  g.c_amax = (uint32_t*)c_amax;
 
   gemm_fn fn = nullptr;
   const char* name = "";
@@ -1053,6 +1080,27 @@ extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, 
   const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n);
   log_dispatch("%s layout=%d M=%lld N=%lld K=%lld out=%s tiles=%dx%d", name, (int)layout, (long long)M,
                (long long)N, (long long)K, bf16_out ? "bf16" : "f32", g.tiles_m, g.tiles_n);
+  if (c_amax) hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)c_amax);
   hipLaunchKernelGGL(fn, dim3(grid), dim3(NTHR), 0, stream, g);
   return check_launch("pbs_gemm");
+}
+
+extern "C" pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, int64_t N, int64_t K,
+                               const void* A, pbs_format a_fmt, const void* a_scale,
+                               const float* a_tensor_scale, const void* B, pbs_format b_fmt,
+                               const void* b_scale, const float* b_tensor_scale, void* C,
+                               pbs_format c_fmt, hipStream_t stream) {
+  return gemm_impl(recipe, layout, M, N, K, A, a_fmt, a_scale, a_tensor_scale, B, b_fmt, b_scale,
+                   b_tensor_scale, C, c_fmt, nullptr, stream);
+}
+
+extern "C" pbs_status pbs_gemm_amax(pbs_recipe recipe, pbs_layout layout, int64_t M, int64_t N, int64_t K,
+                                    const void* A, pbs_format a_fmt, const void* a_scale,
+                                    const float* a_tensor_scale, const void* B, pbs_format b_fmt,
+                                    const void* b_scale, const float* b_tensor_scale, void* C,
+                                    pbs_format c_fmt, float* c_amax, hipStream_t stream) {
+  PBS_REQUIRE(c_amax, PBS_ERR_INVALID_ARG, "pbs_gemm_amax: c_amax is null");
+  PBS_REQUIRE(((uintptr_t)c_amax & 3) == 0, PBS_ERR_INVALID_ARG, "pbs_gemm_amax: c_amax not 4-byte aligned");
+  return gemm_impl(recipe, layout, M, N, K, A, a_fmt, a_scale, a_tensor_scale, B, b_fmt, b_scale,
+                   b_tensor_scale, C, c_fmt, c_amax, stream);
 }

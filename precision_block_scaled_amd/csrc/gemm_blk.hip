@@ -94,15 +94,23 @@ __device__ __forceinline__ void store_blk(f32x16 (&acc)[4][2], const GemmArgs& g
         }
     __syncthreads();
     const int ch = lane & 15;
+    uint32_t mx = 0;
 #pragma unroll 4
     for (int it = 0; it < 16; ++it) {
       const int s = 64 * w + 4 * it + (lane >> 4);
       const uint4 val = *(const uint4*)(smem + s * KB_STG_BF16 + ch * 16);
       const int grow = m0 + s, gcol = n0 + ch * 8;
-      if (full || (grow < g.M && gcol < g.N))
+      if (full || (grow < g.M && gcol < g.N)) {
         *(uint4*)((uint16_t*)g.C + (int64_t)grow * g.ldc + gcol) = val;
+        if (g.c_amax) {
+          const uint32_t a = absmax_bf16x8(val);
+          mx = mx > a ? mx : a;
+        }
+      }
     }
+    if (g.c_amax) amax_fold_wave(mx, g.c_amax);
   } else {
+    uint32_t mx = 0;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       if (wm == p) {
@@ -124,10 +132,17 @@ __device__ __forceinline__ void store_blk(f32x16 (&acc)[4][2], const GemmArgs& g
         const int s = 32 * w + 2 * it + (lane >> 5);
         const uint4 val = *(const uint4*)(smem + s * KB_STG_F32 + (lane & 31) * 16);
         const int grow = m0 + 128 * p + s, gcol = n0 + (lane & 31) * 4;
-        if (full || (grow < g.M && gcol < g.N)) *(uint4*)((float*)g.C + (int64_t)grow * g.ldc + gcol) = val;
+        if (full || (grow < g.M && gcol < g.N)) {
+          *(uint4*)((float*)g.C + (int64_t)grow * g.ldc + gcol) = val;
+          if (g.c_amax) {
+            const uint32_t a = absmax_f32x4(val);
+            mx = mx > a ? mx : a;
+          }
+        }
       }
       if (p == 0) __syncthreads();
     }
+    if (g.c_amax) amax_fold_wave(mx, g.c_amax);
   }
 }
 

@@ -37,7 +37,42 @@ struct GemmArgs {
   int ldc;                // elements between rows of C
   int tiles_m, tiles_n;
   int a_sdiv, b_sdiv;     // MX scale rows: operand rows per stored scale row (1, or 128 for 128x128 blocks)
+  uint32_t* c_amax;       // optional: max |C| of the stored output (fp32 bits), folded in by the epilogue
 };
+
+// max |x| of the 8 bf16 / 4 fp32 values of a stored 16-byte chunk of C, as
+// fp32 bits (for non-negative IEEE values bit order is numeric order).
+__device__ __forceinline__ uint32_t absmax_bf16x8(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = (w[i] & 0x7FFFu) << 16, hi = w[i] & 0x7FFF0000u;
+    m = m > lo ? m : lo;
+    m = m > hi ? m : hi;
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint32_t absmax_f32x4(uint4 v) {
+  const uint32_t w[4] = {v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu, v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu};
+  const uint32_t a = w[0] > w[1] ? w[0] : w[1], b = w[2] > w[3] ? w[2] : w[3];
+  return a > b ? a : b;
+}
+
+// Fold a per-lane maximum into *out: wave reduction, then one atomic from
+// lane 0 only when the wave's maximum exceeds what *out already holds.
+__device__ __forceinline__ void amax_fold_wave(uint32_t v, uint32_t* out) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t u = (uint32_t)__shfl_xor((int)v, o, 64);
+    v = v > u ? v : u;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    const uint32_t cur = __builtin_nontemporal_load(out);
+    if (v > cur) atomicMax(out, v);
+  }
+}
 
 // LDS tile layout: row r, 16-byte chunk c lives at r * 128 + ((c ^ key(r)) << 4).
 // gfx950's LDS serves a 16-byte-per-lane access 16 lanes (256 bytes, 64

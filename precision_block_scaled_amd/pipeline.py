@@ -34,7 +34,7 @@ from . import (PBS_COL, PBS_DGRAD, PBS_FLAG_RHT16, PBS_FLAG_SR, PBS_FMT_BF16, PB
                PBS_RECIPE_MXFP4, PBS_RECIPE_MXFP8, PBS_RECIPE_NVFP4, PBS_ROW, PBS_WGRAD, pbs_amax,
                pbs_cast,
                pbs_delayed_init, pbs_delayed_scale, pbs_delayed_scale_inv, pbs_delayed_state_bytes,
-               pbs_delayed_update, pbs_gemm, pbs_scale_from_amax)
+               pbs_delayed_update, pbs_gemm, pbs_gemm_amax, pbs_scale_from_amax)
 
 RECIPES = {
     "bf16": PBS_RECIPE_BF16,
@@ -214,11 +214,13 @@ def quantize(recipe, x, src, orient, pass_, state=None, out=None, ws=None, strea
     return out
 
 
-def gemm(recipe, pass_, A, B, M, N, K, out_dtype=torch.bfloat16, C=None, stream=None):
+def gemm(recipe, pass_, A, B, M, N, K, out_dtype=torch.bfloat16, C=None, stream=None, c_amax=None):
     """C[M, N] for one pass from the two operands (QTensor for quantized recipes).
 
     For the bf16 recipe A and B are the natural-storage bf16 tensors of the
-    pass (fprop: X, W; dgrad: dY, W; wgrad: X, dY).
+    pass (fprop: X, W; dgrad: dY, W; wgrad: X, dY).  With ``c_amax`` (a
+    device fp32 tensor of one element) the epilogue also writes max |C| there
+    (pbs_gemm_amax).
     """
     dev = (A.codes if isinstance(A, QTensor) else A).device
     if C is None:
@@ -229,11 +231,14 @@ def gemm(recipe, pass_, A, B, M, N, K, out_dtype=torch.bfloat16, C=None, stream=
     if recipe == "bf16":
         a = A.codes if isinstance(A, QTensor) else A
         b = B.codes if isinstance(B, QTensor) else B
-        pbs_gemm(rec, lay, M, N, K, a, PBS_FMT_BF16, None, None, b, PBS_FMT_BF16, None, None, C, c_fmt,
-                 stream)
+        args = (rec, lay, M, N, K, a, PBS_FMT_BF16, None, None, b, PBS_FMT_BF16, None, None, C, c_fmt)
     else:
-        pbs_gemm(rec, lay, M, N, K, A.codes, A.fmt, A.scales, A.tensor_scale_inv, B.codes, B.fmt,
-                 B.scales, B.tensor_scale_inv, C, c_fmt, stream)
+        args = (rec, lay, M, N, K, A.codes, A.fmt, A.scales, A.tensor_scale_inv, B.codes, B.fmt,
+                B.scales, B.tensor_scale_inv, C, c_fmt)
+    if c_amax is None:
+        pbs_gemm(*args, stream)
+    else:
+        pbs_gemm_amax(*args, c_amax, stream)
     return C
 
 
