@@ -195,7 +195,7 @@ class Runner:
         return {k: float(np.median([a.elapsed_time(b) for a, b in v])) for k, v in out.items()}
 
 
-def quant_bandwidth(runner, iters=5):
+def quant_bandwidth(runner, iters=20):
     """GB/s of single cast passes on full-size operands (algorithmic bytes)."""
     torch, PL = runner.torch, runner.PL
     # X of MLP-down and dY of MLP-up: [15872, 16384] each, 520 MB, twice the
@@ -219,43 +219,40 @@ def quant_bandwidth(runner, iters=5):
     ]
     res = {}
     P = runner.P
-    amax = torch.zeros(4, device=runner.dev)
-    # amax pass
-    ts = []
-    for _ in range(iters):
+
+    def batch_ms(run):
+        # back-to-back passes between one pair of events: the host enqueues
+        # ahead of the GPU, so launch latency is not counted as pass time
+        run()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        P.pbs_amax(x, x.shape[0], x.shape[1], 0, 0, amax[0:1])
+        for _ in range(iters):
+            run()
         e1.record()
-        ts.append((e0, e1))
-    torch.cuda.synchronize()
-    ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    amax = torch.zeros(4, device=runner.dev)
+    ms = batch_ms(lambda: P.pbs_amax(x, x.shape[0], x.shape[1], 0, 0, amax[0:1]))
     res["amax"] = {"ms": round(ms, 4), "GBps": round(2.0 * n / ms / 1e6, 1)}
     for label, r, src, orient, p, bpe in cases:
         t = {"x": x, "dy": dy}[src]
         out = PL.quantize(r, t, src, orient, p)    # allocate + warm
         rows, cols = t.shape
-        ts = []
-        for _ in range(iters):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            rec = PL.RECIPES[r]
-            rmask = P.PBS_ROW if orient == "row" else P.PBS_COL
-            rc, rs, cc, cs = ((out.codes, out.scales, None, None) if orient == "row"
-                              else (None, None, out.codes, out.scales))
-            flags = 0
-            scale = None
-            if r in ("nvfp4", "mxfp4"):
-                flags = (P.PBS_FLAG_RHT16 if p == "wgrad" else 0) | (P.PBS_FLAG_SR if src == "dy" else 0)
-                scale = out._scal[1:2] if r == "nvfp4" else None
-            elif r == "fp8_current":
-                scale = out._scal[1:2]
-            P.pbs_cast(rec, t, rows, cols, PL.fmt_for(r, src), rmask, 0, flags, 42, scale, None,
-                       rc, rs, cc, cs)
-            e1.record()
-            ts.append((e0, e1))
-        torch.cuda.synchronize()
-        ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
+        rec = PL.RECIPES[r]
+        rmask = P.PBS_ROW if orient == "row" else P.PBS_COL
+        rc, rs, cc, cs = ((out.codes, out.scales, None, None) if orient == "row"
+                          else (None, None, out.codes, out.scales))
+        flags = 0
+        scale = None
+        if r in ("nvfp4", "mxfp4"):
+            flags = (P.PBS_FLAG_RHT16 if p == "wgrad" else 0) | (P.PBS_FLAG_SR if src == "dy" else 0)
+            scale = out._scal[1:2] if r == "nvfp4" else None
+        elif r == "fp8_current":
+            scale = out._scal[1:2]
+        ms = batch_ms(lambda: P.pbs_cast(rec, t, rows, cols, PL.fmt_for(r, src), rmask, 0, flags, 42, scale,
+                                         None, rc, rs, cc, cs))
         res[label] = {"ms": round(ms, 4), "GBps": round(bpe * t.numel() / ms / 1e6, 1)}
     return res
 
@@ -509,7 +506,11 @@ def main():
         "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "avg_launch_ms": round(avg_ms, 4), "launches": dk["launches"],
-                     "traffic": traffic},
+                     # HBM bytes per launch from the committed rocprofv3 counters (null once
+                     # the kernel's sources differ from those the counters were taken on)
+                     "traffic": round(traffic["bytes_per_launch"]) if traffic else None,
+                     "traffic_fetch_write": ([round(traffic["fetch_bytes_per_launch"]),
+                                              round(traffic["write_bytes_per_launch"])] if traffic else None)},
         "per_recipe": per_recipe,
         "next_recipes": nxt,
         "model": model,
