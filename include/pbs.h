@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PBS_VERSION 1
+#define PBS_VERSION 2   /* 2: FP8_BLOCK128_POW2 recipe, pbs_gemm_amax */
 
 typedef enum {
   PBS_OK = 0,

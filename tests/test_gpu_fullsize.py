@@ -15,7 +15,9 @@ tensors one by one in seconds, so it checks samples it computes exactly:
   of the whole tensor (after the Hadamard transform for NVFP4 Wgrad inputs);
 * GEMM outputs at 8 x 8 (m, n) pairs drawn from those rows, against the
   fp64 dot product of the oracle-dequantized rows, within
-  |err| <= 1e-5 sum|a b| (+ the 8-bit instruction's unit bound, + 1 bf16 ulp).
+  |err| <= 1e-5 sum|a b| (+ the 8-bit instruction's unit bound, + 1 bf16 ulp);
+* the GEMM epilogue's max |C| (pbs_gemm_amax) against the amax kernel's
+  pass over the whole stored C, bit for bit.
 """
 import functools
 
@@ -169,7 +171,10 @@ def run_pass(recipe, model, name, pass_):
         A, B = {"fprop": (xg, wg), "dgrad": (dyg, wg), "wgrad": (xg, dyg)}[pass_]
     else:
         A, B = PL.quantize_pass(recipe, pass_, xg, wg, dyg, states=states)
-    C = PL.gemm(recipe, pass_, A, B, M, N, K, out_dtype=torch.bfloat16)
+    c_amax = torch.full((1,), -1.0, device=dev)
+    C = PL.gemm(recipe, pass_, A, B, M, N, K, out_dtype=torch.bfloat16, c_amax=c_amax)
+    full_amax = torch.zeros(1, device=dev)
+    P.pbs_amax(C, M, N, 0, 0, full_amax)
     torch.cuda.synchronize()
 
     from oracle.passes import operand_roles
@@ -199,6 +204,9 @@ def run_pass(recipe, model, name, pass_):
                     g_tsi = q.tensor_scale_inv.cpu().numpy()[0]
                 if np.float32(g_tsi).view(np.uint32) != np.float32(o.tsi).view(np.uint32):
                     out.append(f"tensor scale_inv {g_tsi} vs {o.tsi}")
+    # the epilogue's max |C| equals the amax kernel's pass over the stored C
+    if c_amax.cpu().numpy().view(np.uint32)[0] != full_amax.cpu().numpy().view(np.uint32)[0]:
+        out.append(f"epilogue amax {c_amax.item()} vs amax of C {full_amax.item()}")
     rng = np.random.default_rng(7)
     ia = np.concatenate([[0, len(rows_a) - 1], rng.choice(len(rows_a), 6, replace=False)])
     ib = np.concatenate([[0, len(rows_b) - 1], rng.choice(len(rows_b), 6, replace=False)])
