@@ -107,6 +107,13 @@ def test_gemm_validation_codes():
             FAKE, P.PBS_FMT_E4M3, None, None, FAKE, P.PBS_FMT_F32, 0)
     _expect(1, g, P.PBS_RECIPE_BF16, 7, 64, 64, 64, FAKE, P.PBS_FMT_BF16, None, None, FAKE,
             P.PBS_FMT_BF16, None, None, FAKE, P.PBS_FMT_F32, 0)
+    # stored operand rows beyond 16 MiB (tiles address rows with 32-bit offsets) and dims beyond 2^30
+    _expect(2, g, P.PBS_RECIPE_BF16, P.PBS_FPROP, 64, 64, (16 << 20) // 2 + 64, FAKE, P.PBS_FMT_BF16, None,
+            None, FAKE, P.PBS_FMT_BF16, None, None, FAKE, P.PBS_FMT_F32, 0)
+    _expect(2, g, P.PBS_RECIPE_FP8_CURRENT, P.PBS_FPROP, 64, 64, (16 << 20) + 128, FAKE, P.PBS_FMT_E4M3, None,
+            FAKE, FAKE, P.PBS_FMT_E4M3, None, FAKE, FAKE, P.PBS_FMT_F32, 0)
+    _expect(2, g, P.PBS_RECIPE_BF16, P.PBS_FPROP, (1 << 30) + 16, 64, 64, FAKE, P.PBS_FMT_BF16, None, None,
+            FAKE, P.PBS_FMT_BF16, None, None, FAKE, P.PBS_FMT_F32, 0)
     # power-of-two sub-channel: 128x128 weight blocks need N % 128; scale words 4-byte aligned
     _expect(2, g, P.PBS_RECIPE_FP8_BLOCK128_POW2, P.PBS_FPROP, 64, 80, 128, FAKE, P.PBS_FMT_E4M3, FAKE, None,
             FAKE, P.PBS_FMT_E4M3, FAKE, None, FAKE, P.PBS_FMT_F32, 0)
