@@ -14,6 +14,8 @@
 #include "device.hpp"
 #include "host.hpp"
 
+#include <algorithm>
+
 namespace pbs {
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
@@ -208,7 +210,7 @@ pbs_status pbs_amax(const void* x_bf16, int64_t rows, int64_t cols, int flags, u
                 "pbs_amax: RHT16 needs rows %% 16 == 0 and cols %% 8 == 0 (got %lld x %lld)",
                 (long long)rows, (long long)cols);
     PBS_REQUIRE(((uintptr_t)x_bf16 & 15) == 0, PBS_ERR_INVALID_ARG, "pbs_amax: x not 16-byte aligned");
-    int grid = amax_grid((rows / 16) * (cols / 8), 2);
+    int grid = std::min(amax_grid((rows / 16) * (cols / 8), 2), 1024);   // one atomic per block
     log_dispatch("amax_rht_kernel rows=%lld cols=%lld grid=%d", (long long)rows, (long long)cols, grid);
     hipLaunchKernelGGL(amax_rht_kernel, dim3(grid), dim3(256), 0, stream, (const bf16_t*)x_bf16,
                        rows, cols, seed, out);
@@ -216,7 +218,9 @@ pbs_status pbs_amax(const void* x_bf16, int64_t rows, int64_t cols, int flags, u
     PBS_REQUIRE(((uintptr_t)x_bf16 & 15) == 0, PBS_ERR_INVALID_ARG, "pbs_amax: x not 16-byte aligned");
     const int64_t n8 = n / 8;
     const int tail_n = (int)(n - n8 * 8);
-    int grid = amax_grid(n8, 32);
+    // at most 1024 blocks: one same-address atomic per block at the end, so
+    // fewer, longer-lived blocks (1024 read as fast as 4096 in a probe)
+    int grid = std::min(amax_grid(n8, 32), 1024);
     log_dispatch("amax_bf16_kernel n=%lld grid=%d", (long long)n, grid);
     hipLaunchKernelGGL(amax_bf16_kernel, dim3(grid), dim3(256), 0, stream, (const uint4*)x_bf16, n8,
                        (const bf16_t*)x_bf16 + n8 * 8, tail_n, out);

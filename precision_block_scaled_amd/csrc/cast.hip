@@ -655,28 +655,6 @@ template <int RECIPE, int FMT, bool RHT, bool SR, bool AMAX>
 __global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
   __shared__ __align__(16) uint8_t tile[CT_R * CT_PITCH];
   const int t = threadIdx.x, lane = t & 63;
-  const int64_t r0 = (int64_t)blockIdx.y * CT_R, c0 = (int64_t)blockIdx.x * CT_C;
-  const int rlim = (int)min((int64_t)CT_R, a.R - r0);
-  const int clim = (int)min((int64_t)CT_C, a.C - c0);
-  // fill: 8 lanes per 128-byte row segment, 32 rows per pass, 8 passes
-  {
-    const int ch = t & 7;
-    uint4 v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (t >> 3) + 32 * i;
-      v[i] = make_uint4(0, 0, 0, 0);
-      if (row < rlim && ch * 8 < clim) v[i] = ld_nt16(a.x + (r0 + row) * a.C + c0 + ch * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (t >> 3) + 32 * i;
-      const int g = (2 * ch) ^ ((row >> 4) & 14);
-      // odd rows start 8 bytes into a 16-byte line: two 8-byte stores
-      *(uint2*)(tile + row * CT_PITCH + g * 8) = make_uint2(v[i].x, v[i].y);
-      *(uint2*)(tile + row * CT_PITCH + g * 8 + 8) = make_uint2(v[i].z, v[i].w);
-    }
-  }
   uint32_t rht_mask = 0;
   if (RHT) {
     // bit j of the mask from lane j (Philox counter (j, 0, 1, 0), bit 0 of word 0)
@@ -686,72 +664,104 @@ __global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
   }
   float tscale = 0.0f;
   if (RECIPE == R_TENSOR || RECIPE == R_NV) tscale = *a.scale;
-  __syncthreads();
-
-  const int rs = t & 15, cg = t >> 4;
-  // 16 rows x 4 columns: wv[i] = 4 bf16 of row 16 rs + i
-  uint2 wv[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int row = 16 * rs + i;
-    const int g = cg ^ ((row >> 4) & 14);
-    wv[i] = *(const uint2*)(tile + row * CT_PITCH + g * 8);
-  }
+  // Tiles in row-major order of the (rows / 256) x (cols / 64) tile grid.
+  // A 2D launch of that grid gives each workgroup its own tile; the fused-
+  // amax launch is 1D and shorter, and each workgroup walks tiles tile,
+  // tile + gridDim.x, ... so that only that many same-address atomics end it.
+  const int64_t gx = (a.C + CT_C - 1) / CT_C;
+  const int64_t ntiles = gx * ((a.R + CT_R - 1) / CT_R);
   uint32_t amx = 0;
+  for (int64_t tl = (int64_t)blockIdx.y * gridDim.x + blockIdx.x; tl < ntiles;
+       tl += (int64_t)gridDim.x * gridDim.y) {
+    const int64_t r0 = (tl / gx) * CT_R, c0 = (tl % gx) * CT_C;
+    const int rlim = (int)min((int64_t)CT_R, a.R - r0);
+    const int clim = (int)min((int64_t)CT_C, a.C - c0);
+    // fill: 8 lanes per 128-byte row segment, 32 rows per pass, 8 passes
+    {
+      const int ch = t & 7;
+      uint4 v[8];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float v[16];
+      for (int i = 0; i < 8; ++i) {
+        const int row = (t >> 3) + 32 * i;
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (row < rlim && ch * 8 < clim) v[i] = ld_nt16(a.x + (r0 + row) * a.C + c0 + ch * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = (t >> 3) + 32 * i;
+        const int g = (2 * ch) ^ ((row >> 4) & 14);
+        // odd rows start 8 bytes into a 16-byte line: two 8-byte stores
+        *(uint2*)(tile + row * CT_PITCH + g * 8) = make_uint2(v[i].x, v[i].y);
+        *(uint2*)(tile + row * CT_PITCH + g * 8 + 8) = make_uint2(v[i].z, v[i].w);
+      }
+    }
+    __syncthreads();
+
+    const int rs = t & 15, cg = t >> 4;
+    // 16 rows x 4 columns: wv[i] = 4 bf16 of row 16 rs + i
+    uint2 wv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint32_t word = (c < 2) ? wv[i].x : wv[i].y;
-      v[i] = __uint_as_float((c & 1) ? (word & 0xFFFF0000u) : (word << 16));
+      const int row = 16 * rs + i;
+      const int g = cg ^ ((row >> 4) & 14);
+      wv[i] = *(const uint2*)(tile + row * CT_PITCH + g * 8);
     }
-    const int col = 4 * cg + c;
-    const bool valid = (16 * rs < rlim) && (col < clim);
-    uint32_t mbits = 0;
-    if (RHT) {
-      rht16(v, rht_mask);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float v[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint32_t x = __float_as_uint(v[i]) & 0x7FFFFFFFu;
-        mbits = mbits > x ? mbits : x;
+        const uint32_t word = (c < 2) ? wv[i].x : wv[i].y;
+        v[i] = __uint_as_float((c & 1) ? (word & 0xFFFF0000u) : (word << 16));
       }
-    } else {
+      const int col = 4 * cg + c;
+      const bool valid = (16 * rs < rlim) && (col < clim);
+      uint32_t mbits = 0;
+      if (RHT) {
+        rht16(v, rht_mask);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t x = __float_as_uint(v[i]) & 0x7FFFFFFFu;
-        mbits = mbits > x ? mbits : x;
-      }
-    }
-    if (AMAX && valid) amx = amx > mbits ? amx : mbits;
-    const int64_t gc = c0 + col, gr = r0 + 16 * rs;
-    if (RECIPE == R_CHAN)   // the column's amax (fp32 bits), measured by chan_colmax_kernel
-      tscale = scale_from_amax(__uint_as_float(((const uint32_t*)a.col_scales)[valid ? gc : c0]), 448.0f);
-    uint32_t rnd[16];
-    if (SR) {
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t x = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+          mbits = mbits > x ? mbits : x;
+        }
+      } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint64_t idx = (uint64_t)((gr + i) * a.C + gc);
-        rnd[i] = philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
-                              (uint32_t)(a.seed >> 32));
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t x = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+          mbits = mbits > x ? mbits : x;
+        }
       }
+      if (AMAX && valid) amx = amx > mbits ? amx : mbits;
+      const int64_t gc = c0 + col, gr = r0 + 16 * rs;
+      if (RECIPE == R_CHAN)   // the column's amax (fp32 bits), measured by chan_colmax_kernel
+        tscale = scale_from_amax(__uint_as_float(((const uint32_t*)a.col_scales)[valid ? gc : c0]), 448.0f);
+      uint32_t rnd[16];
+      if (SR) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint64_t idx = (uint64_t)((gr + i) * a.C + gc);
+          rnd[i] = philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
+                                (uint32_t)(a.seed >> 32));
+        }
+      }
+      uint8_t* codes = (RECIPE == R_NV || RECIPE == R_MX4) ? a.col_codes + gc * (a.R / 2) + gr / 2
+                                                           : a.col_codes + gc * a.R + gr;
+      uint8_t* sc8 = nullptr;
+      float* sc32 = nullptr;
+      bool writer = true;
+      if (RECIPE == R_MX || RECIPE == R_MX4) {
+        sc8 = (uint8_t*)a.col_scales + gc * (a.R / 32) + gr / 32;
+        writer = (rs & 1) == 0;
+      } else if (RECIPE == R_NV) {
+        sc8 = (uint8_t*)a.col_scales + gc * (a.R / 16) + gr / 16;
+      } else if (RECIPE == R_BLOCK128 || RECIPE == R_B128P2) {
+        sc32 = (float*)a.col_scales + gc * (a.R / 128) + gr / 128;
+        writer = (rs & 7) == 0;
+      }
+      quantize_segment<RECIPE == R_CHAN ? R_TENSOR : RECIPE, FMT, SR>(v, mbits, tscale, valid, codes, sc8, sc32,
+                                                                       writer, rnd);
     }
-    uint8_t* codes = (RECIPE == R_NV || RECIPE == R_MX4) ? a.col_codes + gc * (a.R / 2) + gr / 2
-                                                         : a.col_codes + gc * a.R + gr;
-    uint8_t* sc8 = nullptr;
-    float* sc32 = nullptr;
-    bool writer = true;
-    if (RECIPE == R_MX || RECIPE == R_MX4) {
-      sc8 = (uint8_t*)a.col_scales + gc * (a.R / 32) + gr / 32;
-      writer = (rs & 1) == 0;
-    } else if (RECIPE == R_NV) {
-      sc8 = (uint8_t*)a.col_scales + gc * (a.R / 16) + gr / 16;
-    } else if (RECIPE == R_BLOCK128 || RECIPE == R_B128P2) {
-      sc32 = (float*)a.col_scales + gc * (a.R / 128) + gr / 128;
-      writer = (rs & 7) == 0;
-    }
-    quantize_segment<RECIPE == R_CHAN ? R_TENSOR : RECIPE, FMT, SR>(v, mbits, tscale, valid, codes, sc8, sc32,
-                                                                     writer, rnd);
+    __syncthreads();   // every read of this tile is done before the next fill
   }
   if (AMAX) {
     __shared__ uint32_t s_part[4];
@@ -1144,13 +1154,17 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
   if (fn.row) {
     const int64_t nseg = rows * cols / 16;
     // one pass of the wave loop per wave (measured best); with fused amax
-    // fewer, longer-lived workgroups (one atomic at most each)
-    const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(nseg, 1024), amax_out ? 2048 : (1 << 20));
+    // at most 1024 longer-lived workgroups: each ends in one same-address
+    // atomic at most, and thousands of those queue behind each other
+    const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(nseg, 1024), amax_out ? 1024 : (1 << 20));
     log_dispatch("%s_row recipe=%d fmt=%d flags=%d rows=%lld cols=%lld grid=%u", name, (int)recipe, (int)fmt,
                  flags, (long long)rows, (long long)cols, grid);
     hipLaunchKernelGGL(fn.row, dim3(grid), dim3(256), 0, stream, a, nseg);
   } else if (fn.col) {
+    // with fused amax a 1D grid of at most 1024 workgroups walks the tiles
+    // (one same-address atomic at most per workgroup)
     dim3 grid((unsigned)ceil_div(cols, CT_C), (unsigned)ceil_div(rows, CT_R));
+    if (amax_out) grid = dim3((unsigned)std::min<int64_t>((int64_t)grid.x * grid.y, 1024), 1);
     log_dispatch("%s_col recipe=%d fmt=%d flags=%d rows=%lld cols=%lld grid=%ux%u", name, (int)recipe,
                  (int)fmt, flags, (long long)rows, (long long)cols, grid.x, grid.y);
     hipLaunchKernelGGL(fn.col, grid, dim3(256), 0, stream, a);

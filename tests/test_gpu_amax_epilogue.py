@@ -92,3 +92,28 @@ def test_gemm_amax_empty_and_errors():
     with pytest.raises(P.PBSError):
         P.pbs_gemm_amax(P.PBS_RECIPE_BF16, P.PBS_FPROP, 32, 16, 64, A, P.PBS_FMT_BF16, None, None, A,
                         P.PBS_FMT_BF16, None, None, C, P.PBS_FMT_F32, None)
+
+
+@pytest.mark.parametrize("orient", ["row", "col"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fused_amax_cast_more_tiles_than_workgroups(orient, fmt):
+    """The per-tensor cast with its amax fused (delayed scaling) on a ragged
+    tensor large enough that each of its at most 1024 workgroups walks
+    several tiles (col copy) or segments (row copy): codes as the oracle's
+    cast with the same scale, amax exact."""
+    rows, cols = 2064, 8272                         # 9 x 130 col tiles, ragged in both
+    x = W.grads(rows, cols, seed=95) if fmt == "e5m2" else W.activations(rows, cols, seed=95)
+    s = np.float32(448.0 if fmt == "e4m3" else 57344.0) / R.amax(x) * np.float32(0.75)
+    scale = torch.tensor([s], dtype=torch.float32, device="cuda")
+    amax = torch.full((1,), -1.0, device="cuda")
+    out = torch.empty((rows, cols) if orient == "row" else (cols, rows), dtype=torch.uint8, device="cuda")
+    pfmt = P.PBS_FMT_E4M3 if fmt == "e4m3" else P.PBS_FMT_E5M2
+    rc, cc = (out, None) if orient == "row" else (None, out)
+    P.pbs_cast(P.PBS_RECIPE_FP8_DELAYED, to_gpu_bf16(x), rows, cols, pfmt, P.PBS_ROW if orient == "row" else P.PBS_COL,
+               0, 0, 0, scale, amax, rc, None, cc, None)
+    _sync()
+    want = R.cast_pertensor(x, np.float32(s), fmt, orient)
+    got = out.cpu().numpy()
+    bad = np.argwhere(got != want)
+    assert len(bad) == 0, f"{len(bad)} codes differ, first at {tuple(bad[0])}"
+    assert to_np_f32(amax)[0] == R.amax(x)
