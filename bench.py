@@ -257,6 +257,33 @@ def quant_bandwidth(runner, iters=20):
     return res
 
 
+def epilogue_amax_cost(runner, recipe="fp8_current", name="mlp_up", p="fprop", iters=10):
+    """One GEMM with and without the epilogue max |C| (pbs_gemm_amax), beside
+    the amax pass over C that it replaces."""
+    torch, PL, P = runner.torch, runner.PL, runner.P
+    A, B = runner.q[(recipe, name, p)]
+    M, N, K = next((M, N, K) for (n, pp, M, N, K) in runner.gemms if n == name and pp == p)
+    C = runner.C[(name, p)]
+    amax = torch.zeros(1, device=runner.dev)
+
+    def batch_ms(run):
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    plain = batch_ms(lambda: PL.gemm(recipe, p, A, B, M, N, K, C=C))
+    fused = batch_ms(lambda: PL.gemm(recipe, p, A, B, M, N, K, C=C, c_amax=amax))
+    pass_ = batch_ms(lambda: P.pbs_amax(C, M, N, 0, 0, amax))
+    return {"gemm": f"{recipe} {name}.{p} [{M}x{K}]x[{K}x{N}], bf16 out", "gemm_ms": round(plain, 4),
+            "gemm_with_amax_ms": round(fused, 4), "separate_amax_pass_ms": round(pass_, 4)}
+
+
 def per_gemm_times(events):
     """Per-(recipe, layer, pass) autocast and in-step GEMM times, and per-kernel totals."""
     per = {}
@@ -456,6 +483,7 @@ def main():
         log("pre-quantized GEMM timing")
         pre = runner.prequant_pass(recipes, a.prequant_iters)
     per_recipe = recipe_table(runner, recipes, per, pre)
+    epi = epilogue_amax_cost(runner) if (not a.no_extras and "fp8_current" in recipes) else None
     model = model_analysis(runner, recipes, per, pre)
 
     next_recipes = [r for r in a.next_recipes.split(",") if r]
@@ -515,6 +543,7 @@ def main():
         "next_recipes": nxt,
         "model": model,
         "quant_GBps": qbw,
+        "epilogue_amax": epi,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -278,7 +278,7 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], const GemmArgs& 
         }
       }
     }
-    if (g.c_amax) amax_fold_wave(mx, g.c_amax);
+    if (g.c_amax) amax_fold_wg(mx, g.c_amax, smem);
   } else {
     uint32_t mx = 0;
 #pragma unroll
@@ -309,7 +309,7 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], const GemmArgs& 
       }
       if (p == 0) __syncthreads();
     }
-    if (g.c_amax) amax_fold_wave(mx, g.c_amax);
+    if (g.c_amax) amax_fold_wg(mx, g.c_amax, smem);
   }
 }
 

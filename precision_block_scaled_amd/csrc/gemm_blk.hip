@@ -108,7 +108,7 @@ __device__ __forceinline__ void store_blk(f32x16 (&acc)[4][2], const GemmArgs& g
         }
       }
     }
-    if (g.c_amax) amax_fold_wave(mx, g.c_amax);
+    if (g.c_amax) amax_fold_wg(mx, g.c_amax, smem);
   } else {
     uint32_t mx = 0;
 #pragma unroll
@@ -142,7 +142,7 @@ __device__ __forceinline__ void store_blk(f32x16 (&acc)[4][2], const GemmArgs& g
       }
       if (p == 0) __syncthreads();
     }
-    if (g.c_amax) amax_fold_wave(mx, g.c_amax);
+    if (g.c_amax) amax_fold_wg(mx, g.c_amax, smem);
   }
 }
 

@@ -60,17 +60,30 @@ __device__ __forceinline__ uint32_t absmax_f32x4(uint4 v) {
   return a > b ? a : b;
 }
 
-// Fold a per-lane maximum into *out: wave reduction, then one atomic from
-// lane 0 only when the wave's maximum exceeds what *out already holds.
-__device__ __forceinline__ void amax_fold_wave(uint32_t v, uint32_t* out) {
+// Fold a per-lane maximum into *out: wave reduction, the workgroup's four
+// waves through the first 16 bytes of the (finished) epilogue staging area,
+// then one atomic from thread 0 only when the workgroup's maximum exceeds
+// what *out already holds.  Thousands of same-address atomics queue behind
+// each other, so there is at most one per workgroup.  No LDS object of its
+// own: a second one in the kernel makes the compiler wait for every LDS DMA
+// load in flight before each LDS read of the main loop.  Called by all
+// threads of the workgroup after its last read of `smem` (two barriers).
+__device__ __forceinline__ void amax_fold_wg(uint32_t v, uint32_t* out, uint8_t* smem) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const uint32_t u = (uint32_t)__shfl_xor((int)v, o, 64);
     v = v > u ? v : u;
   }
-  if ((threadIdx.x & 63) == 0) {
+  uint32_t* part = (uint32_t*)smem;
+  __syncthreads();                                   // every wave is done with the staging area
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = part[0];
+#pragma unroll
+    for (int i = 1; i < NTHR / 64; ++i) m = m > part[i] ? m : part[i];
     const uint32_t cur = __builtin_nontemporal_load(out);
-    if (v > cur) atomicMax(out, v);
+    if (m > cur) atomicMax(out, m);
   }
 }
 
