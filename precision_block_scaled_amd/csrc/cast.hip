@@ -578,11 +578,15 @@ __device__ __forceinline__ void wg_amax_fold(uint32_t v, uint32_t* out, uint32_t
 
 // Row copy: thread = 16-value segment of a row.  Each lane does U = 4
 // segments per step (the wave covers 256 consecutive segments), all loads
-// issued before any arithmetic.  No LDS.
+// issued before any arithmetic.  No LDS.  Segment s of the flat tensor is
+// values 16 s .. 16 s + 15 wherever the row breaks fall (the row length is
+// a multiple of 16), and every output is row-major with the blocks along
+// the row, so input, codes, block scales and the SR counter are all linear
+// in s: no row / column split is needed (the row length is a multiple of
+// the block, so a block never straddles rows).
 template <int RECIPE, int FMT, bool SR, bool AMAX>
 __global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg) {
   const int lane = threadIdx.x & 63;
-  const int64_t spr = a.C / 16;                         // segments per row
   const int64_t waves = (int64_t)gridDim.x * 4;
   const int64_t wave0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   float tscale = 0.0f;
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg)
       const int64_t s = wt * 64 * U + u * 64 + lane;
       ok[u] = s < nseg;
       const int64_t sc = ok[u] ? s : 0;
-      const bf16_t* p = a.x + (sc / spr) * a.C + (sc % spr) * 16;
+      const bf16_t* p = a.x + sc * 16;
       const uint4 v0 = ld_nt16(p), v1 = ld_nt16(p + 8);
       w[u][0] = v0.x; w[u][1] = v0.y; w[u][2] = v0.z; w[u][3] = v0.w;
       w[u][4] = v1.x; w[u][5] = v1.y; w[u][6] = v1.z; w[u][7] = v1.w;
@@ -605,7 +609,6 @@ __global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t s = wt * 64 * U + u * 64 + lane;
-      const int64_t row = s / spr, seg = s % spr;
       float v[16];
       bf16x16_to_f32(w[u], v);
       const uint32_t m16 = bf16_absmax16(w[u]);
@@ -614,24 +617,23 @@ __global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg)
       if (SR) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const uint64_t idx = (uint64_t)(row * a.C + seg * 16 + i);
+          const uint64_t idx = (uint64_t)(s * 16 + i);         // logical index r * C + c
           rnd[i] = philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
                                 (uint32_t)(a.seed >> 32));
         }
       }
-      uint8_t* codes = (RECIPE == R_NV || RECIPE == R_MX4) ? a.row_codes + row * (a.C / 2) + seg * 8
-                                                           : a.row_codes + row * a.C + seg * 16;
+      uint8_t* codes = (RECIPE == R_NV || RECIPE == R_MX4) ? a.row_codes + s * 8 : a.row_codes + s * 16;
       uint8_t* sc8 = nullptr;
       float* sc32 = nullptr;
       bool writer = true;
-      if (RECIPE == R_MX || RECIPE == R_MX4) {
-        sc8 = (uint8_t*)a.row_scales + row * (a.C / 32) + seg / 2;
-        writer = (seg & 1) == 0;
-      } else if (RECIPE == R_NV) {
-        sc8 = (uint8_t*)a.row_scales + row * (a.C / 16) + seg;
-      } else if (RECIPE == R_BLOCK128 || RECIPE == R_B128P2) {
-        sc32 = (float*)a.row_scales + row * (a.C / 128) + seg / 8;
-        writer = (seg & 7) == 0;
+      if (RECIPE == R_MX || RECIPE == R_MX4) {          // 32-value blocks: 2 segments
+        sc8 = (uint8_t*)a.row_scales + s / 2;
+        writer = (s & 1) == 0;
+      } else if (RECIPE == R_NV) {                      // 16-value blocks: 1 segment
+        sc8 = (uint8_t*)a.row_scales + s;
+      } else if (RECIPE == R_BLOCK128 || RECIPE == R_B128P2) {   // 128-value blocks: 8 segments
+        sc32 = (float*)a.row_scales + s / 8;
+        writer = (s & 7) == 0;
       }
       quantize_segment<RECIPE, FMT, SR>(v, m16 << 16, tscale, ok[u], codes, sc8, sc32, writer, rnd);
     }
