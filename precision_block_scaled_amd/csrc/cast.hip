@@ -66,11 +66,6 @@ struct CastArgs {
   uint64_t seed;
 };
 
-template <int FMT>
-__device__ __forceinline__ uint32_t enc_fp8(float v) {
-  return FMT == F_E4M3 ? enc_e4m3(v) : enc_e5m2(v);
-}
-
 __device__ __forceinline__ uint32_t lds_bits(const bf16_t* tile, int r, int c) {
   return (uint32_t)tile[r * LDS_STRIDE + c];
 }
@@ -103,15 +98,6 @@ __device__ __forceinline__ uint32_t max_abs_bits16(const uint32_t* b) {
   return m;
 }
 
-__device__ __forceinline__ void store16(uint8_t* dst, const uint32_t* code) {
-  uint4 w;
-  w.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-  w.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
-  w.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
-  w.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
-  *(uint4*)dst = w;
-}
-
 __device__ __forceinline__ uint2 pack_e2m1_16(const uint32_t* q) {
   uint2 w;
   w.x = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12) | (q[4] << 16) | (q[5] << 20) |
@@ -131,25 +117,83 @@ __device__ __forceinline__ uint32_t max16lanes(uint32_t v) {
   return v;
 }
 
+// Encoding by the gfx950 conversion instructions (v_cvt_pk_fp8_f32,
+// v_cvt_pk_bf8_f32, v_cvt_scalef32_pk_fp4_f32 with scale 1): they round to
+// nearest even, and clamping the input to the largest finite code first
+// makes them saturating.  Over every non-NaN fp32 input they return the same
+// codes as enc_e4m3 / enc_e5m2 / enc_e2m1 (checked exhaustively on gfx950).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+template <int FMT>
+__device__ __forceinline__ uint32_t hw_fp8x4(float a, float b, float c, float d) {
+  if (FMT == F_E4M3) {
+    const float L = 448.0f;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -L, L), __builtin_amdgcn_fmed3f(b, -L, L), 0,
+                                            false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, -L, L), __builtin_amdgcn_fmed3f(d, -L, L), w, true);
+    return (uint32_t)w;
+  } else {
+    const float L = 57344.0f;
+    int w = __builtin_amdgcn_cvt_pk_bf8_f32(__builtin_amdgcn_fmed3f(a, -L, L), __builtin_amdgcn_fmed3f(b, -L, L), 0,
+                                            false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(__builtin_amdgcn_fmed3f(c, -L, L), __builtin_amdgcn_fmed3f(d, -L, L), w, true);
+    return (uint32_t)w;
+  }
+}
+
+// 8 values -> 8 E2M1 codes, element 2k in the low nibble of byte k.
+__device__ __forceinline__ uint32_t hw_fp4x8(const float* v) {
+#define PBS_FP4_PAIR(w, k)                                                                         \
+  __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((w), __builtin_amdgcn_fmed3f(v[2 * (k)], -6.0f, 6.0f),    \
+                                           __builtin_amdgcn_fmed3f(v[2 * (k) + 1], -6.0f, 6.0f), 1.0f, (k))
+  uint32_t w = PBS_FP4_PAIR(0u, 0);
+  w = PBS_FP4_PAIR(w, 1);
+  w = PBS_FP4_PAIR(w, 2);
+  w = PBS_FP4_PAIR(w, 3);
+#undef PBS_FP4_PAIR
+  return w;
+}
+
+// 16 bf16 values (bit patterns) times s -> 16 FP8 codes.
+template <int FMT>
+__device__ __forceinline__ uint4 hw_fp8x16(const uint32_t* b, float s) {
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = bf16_to_float(b[i]) * s;
+  uint4 o;
+  o.x = hw_fp8x4<FMT>(v[0], v[1], v[2], v[3]);
+  o.y = hw_fp8x4<FMT>(v[4], v[5], v[6], v[7]);
+  o.z = hw_fp8x4<FMT>(v[8], v[9], v[10], v[11]);
+  o.w = hw_fp8x4<FMT>(v[12], v[13], v[14], v[15]);
+  return o;
+}
+
 // NVFP4 block: codes for 16 fp32 values with block max bits `abits`
 // (of |value|), global encode scale S.  Returns the E4M3 block scale code.
 template <bool SR>
 __device__ __forceinline__ uint32_t nvfp4_block(const float* v, uint32_t abits, float S,
-                                                const uint32_t* rnd, uint32_t* q) {
+                                                const uint32_t* rnd, uint2* packed) {
   const float a_b = __uint_as_float(abits);
   const float d_val = (a_b / 6.0f) * S;
   const uint32_t d_code = enc_e4m3(d_val);              // non-negative input: no sign bit
   const float d = dec_e4m3_pos(d_code);
+  uint32_t q[16];
   if (d == 0.0f) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) q[i] = (__float_as_uint(v[i]) >> 28) & 0x8u;
+    *packed = pack_e2m1_16(q);
   } else {
     float e_b = S / d;
     if (__float_as_uint(e_b) == 0x7F800000u) e_b = 3.40282346638528859812e+38f;
+    float x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float s = v[i] * e_b;
-      q[i] = SR ? sr_e2m1(s, rnd[i]) : enc_e2m1(s);
+    for (int i = 0; i < 16; ++i) x[i] = v[i] * e_b;
+    if (SR) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) q[i] = sr_e2m1(x[i], rnd[i]);
+      *packed = pack_e2m1_16(q);
+    } else {
+      *packed = make_uint2(hw_fp4x8(x), hw_fp4x8(x + 8));
     }
   }
   return d_code;
@@ -169,11 +213,9 @@ __device__ __forceinline__ void quantize_strip(const bf16_t* tile, int strip, in
   if (RECIPE == R_TENSOR) {
     const float s = tile_scale;
     for (int j = 0; j < len; j += 16) {
-      uint32_t b[16], code[16];
+      uint32_t b[16];
       read16<ROWDIR>(tile, strip, j, b);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) code[i] = enc_fp8<FMT>(bf16_to_float(b[i]) * s);
-      store16(out_codes + j, code);
+      *(uint4*)(out_codes + j) = hw_fp8x16<FMT>(b, s);
     }
   } else if (RECIPE == R_BLOCK128) {
     float s = tile_scale;
@@ -191,11 +233,9 @@ __device__ __forceinline__ void quantize_strip(const bf16_t* tile, int strip, in
       out_scales32[0] = 1.0f / s;
     }
     for (int j = 0; j < TILE; j += 16) {
-      uint32_t b[16], code[16];
+      uint32_t b[16];
       read16<ROWDIR>(tile, strip, j, b);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) code[i] = enc_e4m3(bf16_to_float(b[i]) * s);
-      store16(out_codes + j, code);
+      *(uint4*)(out_codes + j) = hw_fp8x16<F_E4M3>(b, s);
     }
   } else if (RECIPE == R_B128P2) {
     float s = tile_scale;
@@ -212,27 +252,21 @@ __device__ __forceinline__ void quantize_strip(const bf16_t* tile, int strip, in
     if (!W2D || scale_writer)   // s = 2^(127 - c): its exponent field is 254 - c
       *(uint32_t*)out_scales32 = (254u - (__float_as_uint(s) >> 23)) * 0x01010101u;
     for (int j = 0; j < TILE; j += 16) {
-      uint32_t b[16], code[16];
+      uint32_t b[16];
       read16<ROWDIR>(tile, strip, j, b);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) code[i] = enc_e4m3(bf16_to_float(b[i]) * s);
-      store16(out_codes + j, code);
+      *(uint4*)(out_codes + j) = hw_fp8x16<F_E4M3>(b, s);
     }
   } else if (RECIPE == R_MX) {
     for (int j = 0; j < len; j += 32) {
-      uint32_t b0[16], b1[16], code[16];
+      uint32_t b0[16], b1[16];
       read16<ROWDIR>(tile, strip, j, b0);
       read16<ROWDIR>(tile, strip, j + 16, b1);
       uint32_t m0 = max_abs_bits16(b0), m1 = max_abs_bits16(b1);
       const uint32_t c = mx_e8m0_from_bf16_amax(m0 > m1 ? m0 : m1);
       const float inv = mx_inv_scale(c);
       out_scales8[j / 32] = (uint8_t)c;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) code[i] = enc_e4m3(bf16_to_float(b0[i]) * inv);
-      store16(out_codes + j, code);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) code[i] = enc_e4m3(bf16_to_float(b1[i]) * inv);
-      store16(out_codes + j + 16, code);
+      *(uint4*)(out_codes + j) = hw_fp8x16<F_E4M3>(b0, inv);
+      *(uint4*)(out_codes + j + 16) = hw_fp8x16<F_E4M3>(b1, inv);
     }
   } else if (RECIPE == R_MX4) {
     for (int j = 0; j < len; j += 32) {
@@ -250,26 +284,29 @@ __device__ __forceinline__ void quantize_strip(const bf16_t* tile, int strip, in
       const uint32_t c = mx4_e8m0_from_f32_amax(m << 16);
       const float inv = mx_inv_scale(c);
       out_scales8[j / 32] = (uint8_t)c;
+      float x[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float x = v[i] * inv;
-        if (SR) {
+      for (int i = 0; i < 32; ++i) x[i] = v[i] * inv;
+      if (SR) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
           const int64_t gr = ROWDIR ? g_row0 : g_row0 + j + i;
           const int64_t gc = ROWDIR ? g_col0 + j + i : g_col0;
           const uint64_t idx = (uint64_t)(gr * a.C + gc);
-          q[i] = sr_e2m1(x, philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
-                                         (uint32_t)(a.seed >> 32)));
-        } else {
-          q[i] = enc_e2m1(x);
+          q[i] = sr_e2m1(x[i], philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
+                                            (uint32_t)(a.seed >> 32)));
         }
+        *(uint2*)(out_codes + j / 2) = pack_e2m1_16(q);
+        *(uint2*)(out_codes + j / 2 + 8) = pack_e2m1_16(q + 16);
+      } else {
+        *(uint2*)(out_codes + j / 2) = make_uint2(hw_fp4x8(x), hw_fp4x8(x + 8));
+        *(uint2*)(out_codes + j / 2 + 8) = make_uint2(hw_fp4x8(x + 16), hw_fp4x8(x + 24));
       }
-      *(uint2*)(out_codes + j / 2) = pack_e2m1_16(q);
-      *(uint2*)(out_codes + j / 2 + 8) = pack_e2m1_16(q + 16);
     }
   } else {  // R_NV
     const float S = tile_scale;
     for (int j = 0; j < len; j += 16) {
-      uint32_t b[16], q[16], rnd[16];
+      uint32_t b[16], rnd[16];
       float v[16];
       read16<ROWDIR>(tile, strip, j, b);
 #pragma unroll
@@ -293,8 +330,8 @@ __device__ __forceinline__ void quantize_strip(const bf16_t* tile, int strip, in
                                 (uint32_t)(a.seed >> 32));
         }
       }
-      const uint32_t dcode = nvfp4_block<SR>(v, m, S, rnd, q);
-      const uint2 w = pack_e2m1_16(q);
+      uint2 w;
+      const uint32_t dcode = nvfp4_block<SR>(v, m, S, rnd, &w);
       *(uint2*)(out_codes + j / 2) = w;
       if (!W2D || scale_writer) out_scales8[j / 16] = (uint8_t)dcode;
     }
@@ -414,38 +451,6 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
 // makes them saturating.  Over every non-NaN fp32 input they return the same
 // codes as enc_e4m3 / enc_e5m2 / enc_e2m1 (checked exhaustively on gfx950).
 // ---------------------------------------------------------------------------
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-template <int FMT>
-__device__ __forceinline__ uint32_t hw_fp8x4(float a, float b, float c, float d) {
-  if (FMT == F_E4M3) {
-    const float L = 448.0f;
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -L, L), __builtin_amdgcn_fmed3f(b, -L, L), 0,
-                                            false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, -L, L), __builtin_amdgcn_fmed3f(d, -L, L), w, true);
-    return (uint32_t)w;
-  } else {
-    const float L = 57344.0f;
-    int w = __builtin_amdgcn_cvt_pk_bf8_f32(__builtin_amdgcn_fmed3f(a, -L, L), __builtin_amdgcn_fmed3f(b, -L, L), 0,
-                                            false);
-    w = __builtin_amdgcn_cvt_pk_bf8_f32(__builtin_amdgcn_fmed3f(c, -L, L), __builtin_amdgcn_fmed3f(d, -L, L), w, true);
-    return (uint32_t)w;
-  }
-}
-
-// 8 values -> 8 E2M1 codes, element 2k in the low nibble of byte k.
-__device__ __forceinline__ uint32_t hw_fp4x8(const float* v) {
-#define PBS_FP4_PAIR(w, k)                                                                         \
-  __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((w), __builtin_amdgcn_fmed3f(v[2 * (k)], -6.0f, 6.0f),    \
-                                           __builtin_amdgcn_fmed3f(v[2 * (k) + 1], -6.0f, 6.0f), 1.0f, (k))
-  uint32_t w = PBS_FP4_PAIR(0u, 0);
-  w = PBS_FP4_PAIR(w, 1);
-  w = PBS_FP4_PAIR(w, 2);
-  w = PBS_FP4_PAIR(w, 3);
-#undef PBS_FP4_PAIR
-  return w;
-}
-
 // Max of the 15-bit magnitudes of 16 bf16 values held as 8 packed words.
 __device__ __forceinline__ uint32_t bf16_absmax16(const uint32_t* w) {
   u16x2 m = {0, 0};

@@ -151,12 +151,16 @@ class Workspace:
         return t
 
 
-def quantize(recipe, x, src, orient, pass_, state=None, out=None, ws=None, stream=None):
+def quantize(recipe, x, src, orient, pass_, state=None, out=None, ws=None, stream=None, known_amax=None):
     """Quantize bf16 tensor ``x`` [R, C] for use as the ``src`` operand of ``pass_``.
 
     Returns a QTensor whose stored shape is [R, C] (row) or [C, R] (col).
     ``out`` may be a QTensor from an earlier call with the same shape, reused
     in place.  ``state`` is a DelayedState for the delayed recipe.
+    ``known_amax`` (a device fp32 of one element holding max |x|, e.g. from
+    the epilogue of the GEMM that produced x) replaces the amax pass of the
+    per-tensor current-scaling and NVFP4 recipes; not with the Hadamard
+    transform, whose maximum is taken over the transformed values.
     """
     R, C = x.shape
     dev = x.device
@@ -178,8 +182,10 @@ def quantize(recipe, x, src, orient, pass_, state=None, out=None, ws=None, strea
                                   else (None, None, out.codes, out.scales))
     rec = RECIPES[recipe]
     if recipe == "fp8_current":
-        pbs_amax(x, R, C, 0, 0, scal[0:1], stream)
-        pbs_scale_from_amax(scal[0:1], FMAX[fmt], scal[1:2], scal[2:3], stream)
+        am = known_amax if known_amax is not None else scal[0:1]
+        if known_amax is None:
+            pbs_amax(x, R, C, 0, 0, am, stream)
+        pbs_scale_from_amax(am, FMAX[fmt], scal[1:2], scal[2:3], stream)
         pbs_cast(rec, x, R, C, fmt, rmask, 0, 0, 0, scal[1:2], None, row_c, row_s, col_c, col_s, stream)
         out.tensor_scale_inv = scal[2:3]
     elif recipe == "fp8_delayed":
@@ -194,8 +200,12 @@ def quantize(recipe, x, src, orient, pass_, state=None, out=None, ws=None, strea
     elif recipe == "nvfp4":
         rht = pass_ == "wgrad"
         flags = (PBS_FLAG_RHT16 if rht else 0) | (PBS_FLAG_SR if src == "dy" else 0)
-        pbs_amax(x, R, C, PBS_FLAG_RHT16 if rht else 0, RHT_SEED, scal[0:1], stream)
-        pbs_scale_from_amax(scal[0:1], NVFP4_FMAX, scal[1:2], scal[2:3], stream)
+        if known_amax is not None and rht:
+            raise ValueError("the Hadamard-transformed tensor's amax is not the producer's")
+        am = known_amax if known_amax is not None else scal[0:1]
+        if known_amax is None:
+            pbs_amax(x, R, C, PBS_FLAG_RHT16 if rht else 0, RHT_SEED, am, stream)
+        pbs_scale_from_amax(am, NVFP4_FMAX, scal[1:2], scal[2:3], stream)
         seed = SR_SEED if src == "dy" else RHT_SEED
         if rht and src == "dy" and RHT_SEED != SR_SEED:
             raise ValueError("one seed drives both the RHT signs and SR")

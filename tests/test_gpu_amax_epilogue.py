@@ -117,3 +117,25 @@ def test_fused_amax_cast_more_tiles_than_workgroups(orient, fmt):
     bad = np.argwhere(got != want)
     assert len(bad) == 0, f"{len(bad)} codes differ, first at {tuple(bad[0])}"
     assert to_np_f32(amax)[0] == R.amax(x)
+
+
+@pytest.mark.parametrize("recipe", ["fp8_current", "nvfp4"])
+def test_gemm_output_quantized_with_epilogue_amax(recipe):
+    """Y = X W^T with its max |Y| from the epilogue, then Y quantized with
+    current scaling (FP8) or NVFP4's tensor scale from that value and no amax
+    pass: the codes and scales are the oracle's quantization of the stored Y."""
+    from oracle.passes import quantize_operand
+    x = W.activations(512, 256, seed=96)
+    w = W.weights(384, 256, seed=97)
+    dy = W.grads(512, 384, seed=98)
+    A, B = PL.quantize_pass("fp8_current", "fprop", to_gpu_bf16(x), to_gpu_bf16(w), to_gpu_bf16(dy))
+    amax = torch.zeros(1, device="cuda")
+    Y = PL.gemm("fp8_current", "fprop", A, B, 512, 384, 256, out_dtype=torch.bfloat16, c_amax=amax)
+    q = PL.quantize(recipe, Y, "x", "row", "fprop", known_amax=amax)
+    _sync()
+    ybits = Y.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = quantize_operand(recipe, "x", "row", ybits, "fprop")
+    assert (q.codes.cpu().numpy() == want.codes).all()
+    if recipe == "nvfp4":
+        assert (q.scales.cpu().numpy() == want.scale).all()
+    assert q.tensor_scale_inv.cpu().numpy().view(np.uint32)[0] == np.float32(want.tensor_scale_inv).view(np.uint32)
