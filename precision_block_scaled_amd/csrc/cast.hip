@@ -348,16 +348,23 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
   const int rlim = (int)min((int64_t)TILE, a.R - r0);
   const int clim = (int)min((int64_t)TILE, a.C - c0);
 
-  // Stage the tile: 16 threads per 256-byte row, 8 rows per pass.
+  // Stage the tile: 16 threads per 256-byte row, 8 rows per pass; all 16
+  // loads of a thread in flight before the first LDS store (four at a time
+  // left a workgroup of 128 threads with too few bytes in flight).
   uint32_t mx = 0;
   {
     const int ch = t & 15;
-#pragma unroll 4
+    uint4 vv[16];
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = (t >> 4) + 8 * i;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < rlim && ch * 8 < clim)
-        v = ld_nt16(a.x + (r0 + row) * a.C + c0 + ch * 8);
+      vv[i] = make_uint4(0, 0, 0, 0);
+      if (row < rlim && ch * 8 < clim) vv[i] = ld_nt16(a.x + (r0 + row) * a.C + c0 + ch * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = (t >> 4) + 8 * i;
+      const uint4 v = vv[i];
       *(uint4*)&tile[row * LDS_STRIDE + ch * 8] = v;
       if (AMAX || ((RECIPE == R_BLOCK128 || RECIPE == R_B128P2) && W2D)) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
