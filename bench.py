@@ -257,6 +257,59 @@ def quant_bandwidth(runner, iters=20):
     return res
 
 
+class ClockSampler:
+    """Shader clock (MHz) of the GPU, read every 20 ms from the driver's
+    pp_dpm_sclk (the level marked '*'; 'S:' is the current fine-grained
+    clock) while the benchmark's GEMM-heavy phases run.  None where the file
+    is not readable."""
+
+    def __init__(self, period=0.02):
+        import glob
+        import threading
+        files = sorted(glob.glob("/sys/class/drm/card[0-9]*/device/pp_dpm_sclk"))
+        self.path = files[0] if len(files) == 1 else None     # one GPU per box: no guessing among several
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True) if self.path else None
+
+    def _read(self):
+        import re
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*Mhz", line, re.IGNORECASE)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._thread:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join(timeout=10)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"sclk_MHz_min": v[0], "sclk_MHz_median": v[len(v) // 2], "sclk_MHz_max": v[-1],
+                "samples": len(v), "source": f"{self.path}, every 20 ms from warm-up to the pre-quantized pass"}
+
+
 def epilogue_amax_cost(runner, recipe="fp8_current", name="mlp_up", p="fprop", iters=10):
     """One GEMM with and without the epilogue max |C| (pbs_gemm_amax), beside
     the amax pass over C that it replaces."""
@@ -459,6 +512,8 @@ def main():
     runner = Runner(layers, a.tokens, dev)
     total_flop = sum(2.0 * M * N * K for (_, _, M, N, K) in runner.gemms) * len(recipes)
 
+    clock = ClockSampler()      # shader clock over the GEMM-heavy part (warm-up to pre-quantized)
+    clock.__enter__()
     log(f"warmup {a.warmup} steps")
     for _ in range(a.warmup):
         runner.step(recipes)
@@ -486,6 +541,7 @@ def main():
     if not a.no_extras:
         log("pre-quantized GEMM timing")
         pre = runner.prequant_pass(recipes, a.prequant_iters)
+    clock.__exit__(None, None, None)
     per_recipe = recipe_table(runner, recipes, per, pre)
     epi = epilogue_amax_cost(runner) if (not a.no_extras and "fp8_current" in recipes) else None
     model = model_analysis(runner, recipes, per, pre)
@@ -548,6 +604,7 @@ def main():
         "model": model,
         "quant_GBps": qbw,
         "epilogue_amax": epi,
+        "gpu_clock": clock.summary(),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
