@@ -679,8 +679,8 @@ __global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
   float tscale = 0.0f;
   if (RECIPE == R_TENSOR || RECIPE == R_NV) tscale = *a.scale;
   // Tiles in row-major order of the (rows / 256) x (cols / 64) tile grid.
-  // A 2D launch of that grid gives each workgroup its own tile; the fused-
-  // amax launch is 1D and shorter, and each workgroup walks tiles tile,
+  // A launch with one workgroup per tile gives each its own tile; the fused-
+  // amax launch is shorter, and each workgroup walks tiles tile,
   // tile + gridDim.x, ... so that only that many same-address atomics end it.
   const int64_t gx = (a.C + CT_C - 1) / CT_C;
   const int64_t ntiles = gx * ((a.R + CT_R - 1) / CT_R);
@@ -978,7 +978,7 @@ static pbs_status cast_channel(const CastArgs& a, bool row, bool col, hipStream_
       log_dispatch("cast_channel_col rows=%lld cols=%lld colmax grid=%ux%u", (long long)a.R, (long long)a.C, g1.x,
                    g1.y);
       hipLaunchKernelGGL(chan_colmax_kernel, g1, dim3(256), 0, stream, a, (int)rpw);
-      const dim3 g2((unsigned)ceil_div(a.C, CT_C), (unsigned)ceil_div(a.R, CT_R));
+      const dim3 g2((unsigned)(ceil_div(a.C, CT_C) * ceil_div(a.R, CT_R)), 1);
       hipLaunchKernelGGL((cast_col_kernel<R_CHAN, F_E4M3, false, false, false>), g2, dim3(256), 0, stream, a);
       hipLaunchKernelGGL(chan_finalize_kernel, dim3((unsigned)ceil_div(a.C, 256)), dim3(256), 0, stream,
                          (float*)a.col_scales, a.C);
@@ -1175,12 +1175,13 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
                  flags, (long long)rows, (long long)cols, grid);
     hipLaunchKernelGGL(fn.row, dim3(grid), dim3(256), 0, stream, a, nseg);
   } else if (fn.col) {
-    // with fused amax a 1D grid of at most 1024 workgroups walks the tiles
-    // (one same-address atomic at most per workgroup)
-    dim3 grid((unsigned)ceil_div(cols, CT_C), (unsigned)ceil_div(rows, CT_R));
-    if (amax_out) grid = dim3((unsigned)std::min<int64_t>((int64_t)grid.x * grid.y, 1024), 1);
-    log_dispatch("%s_col recipe=%d fmt=%d flags=%d rows=%lld cols=%lld grid=%ux%u", name, (int)recipe,
-                 (int)fmt, flags, (long long)rows, (long long)cols, grid.x, grid.y);
+    // a 1D grid over the tiles in row-major tile order, one tile per
+    // workgroup; with fused amax at most 1024 workgroups walk the tiles (one
+    // same-address atomic at most per workgroup)
+    const int64_t ntiles = ceil_div(cols, CT_C) * ceil_div(rows, CT_R);
+    const dim3 grid((unsigned)std::min<int64_t>(ntiles, amax_out ? 1024 : (int64_t)1 << 30), 1);
+    log_dispatch("%s_col recipe=%d fmt=%d flags=%d rows=%lld cols=%lld grid=%u", name, (int)recipe,
+                 (int)fmt, flags, (long long)rows, (long long)cols, grid.x);
     hipLaunchKernelGGL(fn.col, grid, dim3(256), 0, stream, a);
   } else {
     dim3 grid((unsigned)ceil_div(cols, TILE), (unsigned)ceil_div(rows, TILE));
