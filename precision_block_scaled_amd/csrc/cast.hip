@@ -1,16 +1,18 @@
 // Quantize (cast) kernels for every recipe.
 //
-// One kernel template covers all recipes.  A workgroup of 128 threads
-// stages a 128 x 128 tile of the bf16 input in LDS (one coalesced HBM read),
-// then
-//   * the row copy: thread t quantizes row t of the tile (blocks along the
-//     columns) and writes it in place, and/or
-//   * the col copy: thread t quantizes column t of the tile (blocks along
-//     the rows) and writes it as row t of the transposed output,
-// so both copies come from one read of the input, and every 1D block (16,
-// 32 or 128 long) lies inside one thread's strip: block maxima need no
-// cross-thread reduction.  2D weight blocks (16x16 NVFP4) reduce across 16
-// neighbouring lanes; 128x128 tiles use the tile maximum.
+// Three kernel templates, each instantiated per recipe:
+//   * cast_row_kernel: the row copy with 1D blocks (every GEMM operand but
+//     2D-blocked weights): a lane owns 16-value segments, no LDS;
+//   * cast_col_kernel: the transposed copy with 1D blocks, through a
+//     256 x 64 tile in LDS;
+//   * cast_tile_kernel: 2D weight blocks and casts that produce both copies
+//     from one read.  A workgroup of 128 threads stages a 128 x 128 tile of
+//     the bf16 input in LDS, then thread t quantizes row t of the tile
+//     (row copy, blocks along the columns) and/or column t (col copy, written
+//     as row t of the transposed output), so every 1D block (16, 32 or 128
+//     long) lies inside one thread's strip; 16x16 NVFP4 blocks reduce across
+//     16 neighbouring lanes and 128x128 blocks use the tile maximum.
+// Channel-wise FP8 has its own row and column-maximum kernels (below).
 //
 // Recipes:
 //  per-tensor FP8 -- "Faster training throughput in FP8 precision with NVIDIA
