@@ -121,6 +121,22 @@ def test_gemm_validation_codes():
             None, FAKE, P.PBS_FMT_E4M3, FAKE, None, FAKE, P.PBS_FMT_F32, 0)
 
 
+def test_gemm_amax_validation_codes():
+    if not os.path.exists(P.lib_path):
+        pytest.skip("libpbs.so not built")
+    g = P.pbs_gemm_amax
+    # c_amax null or misaligned
+    _expect(1, g, P.PBS_RECIPE_BF16, P.PBS_FPROP, 64, 64, 64, FAKE, P.PBS_FMT_BF16, None, None, FAKE,
+            P.PBS_FMT_BF16, None, None, FAKE, P.PBS_FMT_F32, None, 0)
+    _expect(1, g, P.PBS_RECIPE_BF16, P.PBS_FPROP, 64, 64, 64, FAKE, P.PBS_FMT_BF16, None, None, FAKE,
+            P.PBS_FMT_BF16, None, None, FAKE, P.PBS_FMT_F32, FAKE + 2, 0)
+    # otherwise pbs_gemm's checks, still before anything is enqueued
+    _expect(2, g, P.PBS_RECIPE_BF16, P.PBS_FPROP, 100, 64, 64, FAKE, P.PBS_FMT_BF16, None, None, FAKE,
+            P.PBS_FMT_BF16, None, None, FAKE, P.PBS_FMT_F32, FAKE, 0)
+    _expect(3, g, P.PBS_RECIPE_MXFP8, P.PBS_FPROP, 64, 64, 128, FAKE, P.PBS_FMT_E5M2, FAKE, None, FAKE,
+            P.PBS_FMT_E4M3, FAKE, None, FAKE, P.PBS_FMT_F32, FAKE, 0)
+
+
 def test_scalar_entry_validation():
     if not os.path.exists(P.lib_path):
         pytest.skip("libpbs.so not built")
