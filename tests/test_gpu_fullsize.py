@@ -9,11 +9,13 @@ quantizes both operands on the GPU (autocast path of the pipeline) and runs
 with bf16 output.  The oracle cannot quantize and multiply 260M-element
 tensors one by one in seconds, so it checks samples it computes exactly:
 
-* whole 128-row groups of every quantized copy (first, a middle and the
-  last group; blocks never straddle a group), codes and scales bit for bit;
+* whole 128-row groups of every quantized copy (the first three, a middle
+  and the last group; blocks never straddle a group), codes and scales bit
+  for bit;
   per-tensor scales and the NVFP4 encode scale come from the oracle's amax
   of the whole tensor (after the Hadamard transform for NVFP4 Wgrad inputs);
-* GEMM outputs at 8 x 8 (m, n) pairs drawn from those rows, against the
+* GEMM outputs at about 11 x 11 (m, n) pairs drawn from those rows (first,
+  last, either side of the first 256-row tile boundary, random), against the
   fp64 dot product of the oracle-dequantized rows, within
   |err| <= 1e-5 sum|a b| (+ the 8-bit instruction's unit bound, + 1 bf16 ulp);
 * the GEMM epilogue's max |C| (pbs_gemm_amax) against the amax kernel's
@@ -65,9 +67,10 @@ def layer_inputs(model, name):
 
 
 def groups_of(n_rows):
-    """First, a middle and the last 128-row group of a copy with n_rows rows."""
+    """The first three, a middle and the last 128-row group of a copy with
+    n_rows rows (groups 1 and 2 straddle the first 256-row tile boundary)."""
     g = n_rows // 128
-    return sorted({0, g // 2, g - 1})
+    return sorted({0, 1, 2, g // 2, g - 1} & set(range(g)))
 
 
 def copy_rows(bits, orient, rows):
@@ -208,8 +211,11 @@ def run_pass(recipe, model, name, pass_):
     if c_amax.cpu().numpy().view(np.uint32)[0] != full_amax.cpu().numpy().view(np.uint32)[0]:
         out.append(f"epilogue amax {c_amax.item()} vs amax of C {full_amax.item()}")
     rng = np.random.default_rng(7)
-    ia = np.concatenate([[0, len(rows_a) - 1], rng.choice(len(rows_a), 6, replace=False)])
-    ib = np.concatenate([[0, len(rows_b) - 1], rng.choice(len(rows_b), 6, replace=False)])
+    # first and last rows, rows 255 / 256 / 257 (either side of the first 256-row tile boundary), random rows
+    edge_a = [int(np.searchsorted(rows_a, r)) for r in (255, 256, 257)]
+    edge_b = [int(np.searchsorted(rows_b, r)) for r in (255, 256, 257)]
+    ia = np.unique(np.concatenate([[0, len(rows_a) - 1], edge_a, rng.choice(len(rows_a), 6, replace=False)]))
+    ib = np.unique(np.concatenate([[0, len(rows_b) - 1], edge_b, rng.choice(len(rows_b), 6, replace=False)]))
     ah, bh = qa.deq[ia], qb.deq[ib]
     cref = ah @ bh.T
     bnd = np.abs(ah) @ np.abs(bh).T
