@@ -354,14 +354,65 @@ def per_gemm_times(events):
     return per, kern
 
 
+# matrix peak (TFLOP/s) of the instruction each recipe's GEMM runs on; exact
+# NVFP4 runs on the fp16 MFMA
+RECIPE_PEAK = {"bf16": 2516.6, "nvfp4": 2516.6, "mxfp4": 10066.3}
+
+
+def quant_bytes_per_element(recipe, src, k_len):
+    """Algorithmic HBM bytes per element to quantize one operand in autocast:
+    the bf16 read (twice when an amax pass must precede the cast), the codes
+    and the block scales written.  `src` is 'x', 'w' or 'dy'; `k_len` the
+    length of the copy's rows (channel scales)."""
+    w2d = src == "w"
+    if recipe == "bf16":
+        return 0.0
+    if recipe == "fp8_current":
+        return 2.0 + 3.0
+    if recipe == "fp8_delayed":
+        return 3.0
+    if recipe in ("fp8_block128", "fp8_block128_pow2"):
+        return 3.0 + (4.0 / 16384 if w2d else 4.0 / 128)
+    if recipe == "fp8_block128_1d1d":
+        return 3.0 + 4.0 / 128
+    if recipe == "fp8_block128_2d2d":
+        return 3.0 + 4.0 / 16384
+    if recipe == "mxfp8":
+        return 3.0 + 1.0 / 32
+    if recipe == "mxfp4":
+        return 2.5 + 1.0 / 32
+    if recipe == "nvfp4":
+        return 2.0 + 2.5 + (1.0 / 256 if w2d else 1.0 / 16)
+    if recipe == "fp8_channel":
+        return 3.0 + 4.0 / k_len
+    raise ValueError(recipe)
+
+
+def autocast_roofline_ms(runner, recipe):
+    """Per layer: GEMM flops at the recipe's matrix peak plus quantization
+    bytes at 8 TB/s, both operands of every GEMM quantized (autocast)."""
+    from precision_block_scaled_amd import pipeline as PL
+    peak = RECIPE_PEAK.get(recipe, 5033.2)
+    t = 0.0
+    for (_, p, M, N, K) in runner.gemms:
+        t += 2.0 * M * N * K / (peak * 1e12)
+        (sa, _), (sb, _) = PL.ROLES[p]
+        q = M * K * quant_bytes_per_element(recipe, sa, K) + N * K * quant_bytes_per_element(recipe, sb, K)
+        t += q / (HBM_GBPS * 1e9)
+    return t * 1e3
+
+
 def recipe_table(runner, recipes, per, pre):
     """ms per layer and TFLOP/s per recipe, autocast (and pre-quantized when timed)."""
     out = {}
     layer_flop = sum(2.0 * M * N * K for (_, _, M, N, K) in runner.gemms)
     for r in recipes:
         auto_ms = sum(float(np.median(per[(r, n, p)]["auto"])) for (n, p, *_) in runner.gemms)
+        roof = autocast_roofline_ms(runner, r)
         ent = {"autocast_ms_per_layer": round(auto_ms, 3),
-               "autocast_TFLOPs": round(layer_flop / (auto_ms * 1e-3) / 1e12, 1)}
+               "autocast_TFLOPs": round(layer_flop / (auto_ms * 1e-3) / 1e12, 1),
+               "autocast_roofline_ms_per_layer": round(roof, 3),
+               "autocast_roofline_frac": round(roof / auto_ms, 4)}
         if pre:
             pre_ms = sum(pre[(r, n, p)] for (n, p, *_) in runner.gemms)
             ent["prequant_ms_per_layer"] = round(pre_ms, 3)
