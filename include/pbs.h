@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PBS_VERSION 2   /* 2: FP8_BLOCK128_POW2 recipe, pbs_gemm_amax */
+#define PBS_VERSION 3   /* 3: pbs_rht_cast, pbs_debug_sr_encode */
 
 typedef enum {
   PBS_OK = 0,
@@ -232,6 +232,32 @@ pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t
                     void* col_scales, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
+ * pbs_rht_cast: the transposed (col) copy of a Wgrad operand of the 4-bit
+ * recipes, with the 16x16 random Hadamard transform applied first along
+ * the rows and, optionally, stochastic rounding of the E2M1 values ([LP]
+ * "Interpreting results for a real model": NVFP4 applies a random Hadamard
+ * transform to the Wgrad inputs and rounds gradients stochastically; [FP4]
+ * "Technical deep-dive": the two-level NVFP4 scaling).
+ *  recipe: PBS_RECIPE_NVFP4 or PBS_RECIPE_MXFP4.  x bf16 [rows, cols],
+ *    rows % 16 == 0 (each 16-row group of a column is transformed).
+ *  rht_seed: Philox4x32-10 key of the signs (sigma_j = bit 0 of word 0 of
+ *    Philox(counter (j, 0, 1, 0))), the same key as pbs_amax's seed for the
+ *    transformed maximum.
+ *  stochastic = 1: stochastic rounding with key sr_seed, counter = logical
+ *    element index r * cols + c of x; 0: round to nearest even (sr_seed
+ *    unused).
+ *  scale: NVFP4's device fp32 S_enc (pbs_scale_from_amax, fmax 2688, of
+ *    the transformed tensor's amax); unused for MXFP4.
+ *  col_codes [cols, rows / 2] packed E2M1, col_scales E4M3 [cols, rows / 16]
+ *    (NVFP4) or E8M0 [cols, rows / 32] (MXFP4), as pbs_cast's col copy.
+ *  pbs_cast(recipe, ..., PBS_COL, 0, PBS_FLAG_RHT16 | PBS_FLAG_SR, seed, ...)
+ *  is this call with rht_seed = sr_seed = seed.  Errors as pbs_cast.
+ * ------------------------------------------------------------------- */
+pbs_status pbs_rht_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t cols,
+                        uint64_t rht_seed, int stochastic, uint64_t sr_seed, const float* scale,
+                        void* col_codes, void* col_scales, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
  * pbs_gemm: C[M, N] = sum_k A[m, k] * B[n, k] with fp32 accumulation, in
  * the GEMM of `layout` ([LP] "Model configuration and training inputs":
  * every linear layer is an M x K x N product; "Using autocast mode vs
@@ -280,11 +306,13 @@ pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t
  *   MXFP4, NVFP4 and FP8_BLOCK128_POW2 block scales 4-byte aligned;
  *   FP8_CHANNEL scales
  *   16-byte aligned.
- * Accuracy: fp32 accumulation; the 8-bit instructions (FP8 recipes) sum
- *   each aligned group of 8 products in one step that keeps bits down to
- *   2^-13 of the group's largest product; BF16 and NVFP4 (decoded exactly to
- *   fp16 in registers) accumulate at fp32 precision; MXFP4 uses the same
- *   instruction as the FP8 recipes with E2M1 inputs.
+ * Accuracy: fp32 accumulation; the 8-bit instructions (FP8 recipes) truncate
+ *   each product of an aligned group of 8 toward zero to a multiple of
+ *   2^(e - 13), e the group's largest sum of operand exponents, and add the
+ *   exact sum of two such groups to the fp32 accumulator with one rounding
+ *   to nearest even; BF16 and NVFP4 (decoded exactly to fp16 in registers)
+ *   accumulate at fp32 precision; MXFP4 uses the same instruction as the
+ *   FP8 recipes with E2M1 inputs (whose products it keeps exactly).
  * C is overwritten; calls on one stream are ordered, nothing is allocated.
  * ------------------------------------------------------------------- */
 pbs_status pbs_gemm(pbs_recipe recipe, pbs_layout layout, int64_t M, int64_t N, int64_t K,
@@ -321,6 +349,19 @@ pbs_status pbs_gemm_amax(pbs_recipe recipe, pbs_layout layout, int64_t M, int64_
  * ------------------------------------------------------------------- */
 pbs_status pbs_quantized_bytes(pbs_recipe recipe, int64_t rows, int64_t cols, int weight_2d,
                                size_t* code_bytes, size_t* scale_bytes);
+
+/* ---------------------------------------------------------------------
+ * pbs_debug_sr_encode: test hook.  codes[i] = the device's stochastic
+ * E2M1 rounding of v[i] with the 32-bit random word r[i] (4-bit code, sign
+ * in bit 3, one per byte), the rule every SR cast applies ([LP]
+ * "Interpreting results for a real model": stochastic rounding of
+ * gradients): |v| >= 6 gives 6; otherwise, with lo <= |v| < hi adjacent
+ * E2M1 magnitudes, hi iff r < ceil((|v| - lo) / (hi - lo) * 2^32), else
+ * lo; the sign of v is kept.  v fp32 and r uint32 (4-byte aligned), codes
+ * uint8, n values; n == 0 enqueues nothing.
+ * ------------------------------------------------------------------- */
+pbs_status pbs_debug_sr_encode(const float* v, const uint32_t* r, uint8_t* codes, int64_t n,
+                               hipStream_t stream);
 
 const char* pbs_last_error(void);
 int pbs_version(void);

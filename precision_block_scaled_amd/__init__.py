@@ -24,7 +24,8 @@ __all__ = [
     "PBS_FLAG_RHT16", "PBS_FLAG_SR",
     "pbs_amax", "pbs_scale_from_amax", "pbs_delayed_state_bytes", "pbs_delayed_init",
     "pbs_delayed_update", "pbs_delayed_scale", "pbs_delayed_scale_inv", "pbs_cast",
-    "pbs_gemm", "pbs_gemm_amax", "pbs_quantized_bytes", "pbs_last_error", "pbs_version",
+    "pbs_rht_cast", "pbs_gemm", "pbs_gemm_amax", "pbs_quantized_bytes", "pbs_debug_sr_encode",
+    "pbs_last_error", "pbs_version",
 ]
 
 PBS_OK, PBS_ERR_INVALID_ARG, PBS_ERR_SHAPE, PBS_ERR_UNSUPPORTED, PBS_ERR_HIP = range(5)
@@ -52,6 +53,8 @@ SIGNATURES = {
     "pbs_delayed_scale_inv": (_vp, [_vp]),
     "pbs_cast": (_i32, [_i32, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _u64, _vp, _vp,
                         _vp, _vp, _vp, _vp, _vp]),
+    "pbs_rht_cast": (_i32, [_i32, _vp, _i64, _i64, _u64, _i32, _u64, _vp, _vp, _vp, _vp]),
+    "pbs_debug_sr_encode": (_i32, [_vp, _vp, _vp, _i64, _vp]),
     "pbs_gemm": (_i32, [_i32, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _vp,
                         _vp, _vp, _i32, _vp]),
     "pbs_gemm_amax": (_i32, [_i32, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _vp,
@@ -150,6 +153,16 @@ def pbs_cast(recipe, x, rows, cols, fmt, orient_mask, weight_2d, flags, seed, sc
     _check(lib().pbs_cast(recipe, _ptr(x), rows, cols, fmt, orient_mask, int(weight_2d), flags, seed,
                           _ptr(scale), _ptr(amax_out), _ptr(row_codes), _ptr(row_scales),
                           _ptr(col_codes), _ptr(col_scales), _stream(stream)))
+
+
+def pbs_rht_cast(recipe, x, rows, cols, rht_seed, stochastic, sr_seed, scale, col_codes, col_scales,
+                 stream=None):
+    _check(lib().pbs_rht_cast(recipe, _ptr(x), rows, cols, rht_seed, int(stochastic), sr_seed, _ptr(scale),
+                              _ptr(col_codes), _ptr(col_scales), _stream(stream)))
+
+
+def pbs_debug_sr_encode(v, r, codes, n, stream=None):
+    _check(lib().pbs_debug_sr_encode(_ptr(v), _ptr(r), _ptr(codes), n, _stream(stream)))
 
 
 def pbs_gemm(recipe, layout, M, N, K, A, a_fmt, a_scale, a_tensor_scale, B, b_fmt, b_scale,

@@ -65,7 +65,8 @@ struct CastArgs {
   void* row_scales;
   uint8_t* col_codes;
   void* col_scales;
-  uint64_t seed;
+  uint64_t seed;           // Philox key of stochastic rounding
+  uint64_t rht_seed;       // Philox key of the Hadamard transform's signs
 };
 
 __device__ __forceinline__ uint32_t lds_bits(const bf16_t* tile, int r, int c) {
@@ -122,8 +123,9 @@ __device__ __forceinline__ uint32_t max16lanes(uint32_t v) {
 // Encoding by the gfx950 conversion instructions (v_cvt_pk_fp8_f32,
 // v_cvt_pk_bf8_f32, v_cvt_scalef32_pk_fp4_f32 with scale 1): they round to
 // nearest even, and clamping the input to the largest finite code first
-// makes them saturating.  Over every non-NaN fp32 input they return the same
-// codes as enc_e4m3 / enc_e5m2 / enc_e2m1 (checked exhaustively on gfx950).
+// makes them saturating.  Compared on gfx950 with bit-level software
+// encoders of E4M3, E5M2 and E2M1 over every non-NaN fp32 input, they gave
+// the same code every time.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 template <int FMT>
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
   }
   if (RHT && t < 64) {
     uint32_t bit = 0;
-    if (t < 16) bit = philox_word0(t, 0u, 1u, 0u, (uint32_t)a.seed, (uint32_t)(a.seed >> 32)) & 1u;
+    if (t < 16) bit = philox_word0(t, 0u, 1u, 0u, (uint32_t)a.rht_seed, (uint32_t)(a.rht_seed >> 32)) & 1u;
     const uint64_t bal = __ballot(bit);
     if (t == 0) s_rht_mask = (uint32_t)bal;
   }
@@ -454,11 +456,8 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
 // step): NVFP4 blocks are one segment, MXFP8 blocks two neighbouring lanes,
 // 1x128 blocks eight, so block maxima reduce with at most three lane swaps.
 //
-// Encoding uses the gfx950 conversion instructions (v_cvt_pk_fp8_f32,
-// v_cvt_pk_bf8_f32, v_cvt_scalef32_pk_fp4_f32 with scale 1): they round to
-// nearest even, and clamping the input to the largest finite code first
-// makes them saturating.  Over every non-NaN fp32 input they return the same
-// codes as enc_e4m3 / enc_e5m2 / enc_e2m1 (checked exhaustively on gfx950).
+// Encoding uses the gfx950 conversion instructions, clamped first so that
+// they saturate (see hw_fp8x4 / hw_fp4x8 above).
 // ---------------------------------------------------------------------------
 // Max of the 15-bit magnitudes of 16 bf16 values held as 8 packed words.
 __device__ __forceinline__ uint32_t bf16_absmax16(const uint32_t* w) {
@@ -674,8 +673,8 @@ __global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
   uint32_t rht_mask = 0;
   if (RHT) {
     // bit j of the mask from lane j (Philox counter (j, 0, 1, 0), bit 0 of word 0)
-    const uint32_t bit = lane < 16 ? (philox_word0((uint32_t)lane, 0u, 1u, 0u, (uint32_t)a.seed,
-                                                   (uint32_t)(a.seed >> 32)) & 1u) : 0u;
+    const uint32_t bit = lane < 16 ? (philox_word0((uint32_t)lane, 0u, 1u, 0u, (uint32_t)a.rht_seed,
+                                                   (uint32_t)(a.rht_seed >> 32)) & 1u) : 0u;
     rht_mask = (uint32_t)__ballot(bit);
   }
   float tscale = 0.0f;
@@ -1019,11 +1018,12 @@ static CastPick pick_orient(int mask) {
 
 using namespace pbs;
 
-extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t cols,
-                               pbs_format fmt, int orient_mask, int weight_2d, int flags,
-                               uint64_t seed, const float* scale, float* amax_out, void* row_codes,
-                               void* row_scales, void* col_codes, void* col_scales,
-                               hipStream_t stream) {
+// pbs_cast and pbs_rht_cast: `seed` keys stochastic rounding, `rht_seed`
+// the Hadamard transform's signs.
+static pbs_status cast_impl(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t cols, pbs_format fmt,
+                            int orient_mask, int weight_2d, int flags, uint64_t seed, uint64_t rht_seed,
+                            const float* scale, float* amax_out, void* row_codes, void* row_scales,
+                            void* col_codes, void* col_scales, hipStream_t stream) {
   PBS_REQUIRE(orient_mask >= 1 && orient_mask <= 3, PBS_ERR_INVALID_ARG,
               "pbs_cast: orient_mask must be PBS_ROW, PBS_COL or both");
   PBS_REQUIRE((flags & ~(PBS_FLAG_RHT16 | PBS_FLAG_SR)) == 0, PBS_ERR_INVALID_ARG,
@@ -1064,6 +1064,7 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
   a.col_codes = (uint8_t*)col_codes;
   a.col_scales = col_scales;
   a.seed = seed;
+  a.rht_seed = rht_seed;
 
   CastPick fn;
   const char* name = "";
@@ -1195,4 +1196,52 @@ extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t ro
     hipLaunchKernelGGL(fn.tile, grid, dim3(128), 0, stream, a);
   }
   return check_launch("pbs_cast");
+}
+
+// Sanity of every pointer argument is checked by cast_impl; the Wgrad
+// operand of the 4-bit recipes is its transposed (col) copy.
+extern "C" pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t cols,
+                               pbs_format fmt, int orient_mask, int weight_2d, int flags,
+                               uint64_t seed, const float* scale, float* amax_out, void* row_codes,
+                               void* row_scales, void* col_codes, void* col_scales,
+                               hipStream_t stream) {
+  return cast_impl(recipe, x_bf16, rows, cols, fmt, orient_mask, weight_2d, flags, seed, seed, scale, amax_out,
+                   row_codes, row_scales, col_codes, col_scales, stream);
+}
+
+extern "C" pbs_status pbs_rht_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t cols,
+                                   uint64_t rht_seed, int stochastic, uint64_t sr_seed, const float* scale,
+                                   void* col_codes, void* col_scales, hipStream_t stream) {
+  PBS_REQUIRE(recipe == PBS_RECIPE_NVFP4 || recipe == PBS_RECIPE_MXFP4, PBS_ERR_UNSUPPORTED,
+              "pbs_rht_cast: the Hadamard transform applies to the NVFP4 and MXFP4 recipes only");
+  PBS_REQUIRE(stochastic == 0 || stochastic == 1, PBS_ERR_INVALID_ARG, "pbs_rht_cast: stochastic must be 0 or 1");
+  PBS_REQUIRE(rows % 16 == 0, PBS_ERR_SHAPE, "pbs_rht_cast: rows must be a multiple of 16 (got %lld)",
+              (long long)rows);
+  const int flags = PBS_FLAG_RHT16 | (stochastic ? PBS_FLAG_SR : 0);
+  return cast_impl(recipe, x_bf16, rows, cols, PBS_FMT_E2M1, PBS_COL, 0, flags, sr_seed, rht_seed, scale, nullptr,
+                   nullptr, nullptr, col_codes, col_scales, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Test hook: the device's stochastic E2M1 rounding on given values and
+// random words, one 4-bit code (sign in bit 3) per output byte.
+// ---------------------------------------------------------------------------
+namespace pbs {
+__global__ void sr_debug_kernel(const float* v, const uint32_t* r, uint8_t* out, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = (uint8_t)sr_e2m1(v[i], r[i]);
+}
+}  // namespace pbs
+
+extern "C" pbs_status pbs_debug_sr_encode(const float* v, const uint32_t* r, uint8_t* codes, int64_t n,
+                                          hipStream_t stream) {
+  PBS_REQUIRE(n >= 0, PBS_ERR_SHAPE, "pbs_debug_sr_encode: negative length");
+  PBS_REQUIRE(n == 0 || (v && r && codes), PBS_ERR_INVALID_ARG, "pbs_debug_sr_encode: null pointer");
+  PBS_REQUIRE(((uintptr_t)v & 3) == 0 && ((uintptr_t)r & 3) == 0, PBS_ERR_INVALID_ARG,
+              "pbs_debug_sr_encode: v and r must be 4-byte aligned");
+  if (n == 0) return PBS_OK;
+  const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(n, 256), 4096);
+  log_dispatch("sr_debug n=%lld grid=%u", (long long)n, grid);
+  hipLaunchKernelGGL(sr_debug_kernel, dim3(grid), dim3(256), 0, stream, v, r, codes, n);
+  return check_launch("pbs_debug_sr_encode");
 }

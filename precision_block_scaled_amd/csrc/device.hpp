@@ -1,12 +1,13 @@
-// Device helpers for the gfx950 kernels: bf16 access, bit-level encoders
-// for E4M3 / E5M2 / E2M1, E8M0 exponent selection, Philox4x32-10,
+// Device helpers for the gfx950 kernels: bf16 access, the bit-level E4M3
+// encoder of NVFP4 block scales, E8M0 exponent selection, Philox4x32-10,
 // stochastic rounding and the 16-point random Hadamard transform.
 //
-// Every encoder here works on the bits of an IEEE binary32 value: the
+// The E4M3 encoder works on the bits of an IEEE binary32 value: the
 // rounding of the value into the narrow format is a round-to-nearest-even
 // right shift of (exponent | mantissa), which carries into the exponent by
 // itself.  Saturation is a compare against the bit pattern of the largest
-// finite value.  Formats: "Optimizing Transformer models for low-precision
+// finite value.  (Element codes are produced by the hardware conversion
+// instructions, see the cast kernels.)  Formats: "Optimizing Transformer models for low-precision
 // training", "Technical deep-dive" (E4M3 / E5M2 bit splits); "Accelerate LLM
 // training with NVFP4 on Blackwell", "Technical deep-dive" (E2M1, values in
 // -6..6).  Rounding rule where the pages are silent: nearest, ties to even,
@@ -55,51 +56,6 @@ __device__ __forceinline__ uint32_t enc_e4m3(float v) {
     } else {
       uint32_t m = (a & 0x7FFFFFu) | (e ? 0x800000u : 0u);
       uint32_t s = 141u - (e ? e : 1u);
-      code = (s > 25u) ? 0u : rne_shr(m, s);
-    }
-  }
-  return sign | code;
-}
-
-// E5M2 (bias 15, max 57344 = 0x7B).  Normal: e >= 113, code =
-// (a - (112 << 23)) >> 21 rounded.  Subnormal: a / 2^-16 = m24 >> (134 - e).
-__device__ __forceinline__ uint32_t enc_e5m2(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a > 0x47600000u) {                 // > 57344
-    code = 0x7Bu;
-  } else {
-    uint32_t e = a >> 23;
-    if (e >= 113u) {
-      code = rne_shr(a - (112u << 23), 21u);
-    } else {
-      uint32_t m = (a & 0x7FFFFFu) | (e ? 0x800000u : 0u);
-      uint32_t s = 134u - (e ? e : 1u);
-      code = (s > 25u) ? 0u : rne_shr(m, s);
-    }
-  }
-  return sign | code;
-}
-
-// E2M1 (bias 1, max 6 = 0x7), 4-bit code with the sign in bit 3.
-// Normal: e >= 127 (1.0), code = (a - (126 << 23)) >> 22 rounded.
-// Subnormal (0.5 = code 1): a / 0.5 = m24 >> (149 - e).
-__device__ __forceinline__ uint32_t enc_e2m1(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 28) & 0x8u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a > 0x40C00000u) {                 // > 6
-    code = 0x7u;
-  } else {
-    uint32_t e = a >> 23;
-    if (e >= 127u) {
-      code = rne_shr(a - (126u << 23), 22u);
-    } else {
-      uint32_t m = (a & 0x7FFFFFu) | (e ? 0x800000u : 0u);
-      uint32_t s = 149u - (e ? e : 1u);
       code = (s > 25u) ? 0u : rne_shr(m, s);
     }
   }
