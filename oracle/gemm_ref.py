@@ -18,13 +18,16 @@ Acceptance (the tolerance the target states): |C_gpu - C_ref| <=
 place of C_ref when the GPU output is bf16.
 
 GEMMs that run on the 8-bit matrix instruction get one more term, from that
-instruction's own arithmetic (measured, not from the pages): it adds the
-products of each aligned group of 8 consecutive contraction indices after
-aligning them to the group's largest product and dropping everything below
-2**-13 of that product's binade; the group sums are then accumulated at
-fp32 precision.  Each group therefore loses less than 7 * 2**-13 of its
-largest |a * b|, which ``fp8_dot_unit_bound`` bounds by 2**-10 times the sum
-over groups of the largest |a * b| in the group.
+instruction's own arithmetic (measured on the GPU, not from the pages): in
+each aligned group of 8 consecutive contraction indices it truncates every
+product toward zero to a multiple of 2**(e - 13), where e is the largest
+sum of the two operands' binary exponents in the group (so 2**e is at most
+the group's largest |a * b|), and accumulates the group sums at fp32
+precision.  Each group therefore loses less than 7 * 2**-13 of its largest
+|a * b|, which ``fp8_dot_unit_bound`` bounds by 2**-10 times the sum over
+groups of the largest |a * b| in the group.  This term is a reading of the
+target's tolerance for hardware whose 8-bit dot unit truncates; the
+stated 1e-5 term alone is not met by it on outlier-heavy inputs.
 """
 from __future__ import annotations
 

@@ -949,20 +949,6 @@ def test_nvfp4_elements_bruteforce(seed):
                 assert codes[i, j] == want, (i, j, sr)
 
 
-def test_fp8_dot_unit_bound_bruteforce():
-    rng = np.random.default_rng(4)
-    from oracle.gemm_ref import fp8_dot_unit_bound
-    a = rng.standard_normal((5, 24))
-    b = rng.standard_normal((3, 24))
-    got = fp8_dot_unit_bound(a, b)
-    for i in range(5):
-        for j in range(3):
-            want = sum(max(abs(a[i, k] * b[j, k]) for k in range(g, g + 8)) for g in (0, 8, 16))
-            assert abs(got[i, j] - want * 2.0 ** -10) <= 1e-15 * want
-    # the bound covers the modelled loss: 7 terms truncated below 2**-13 of the group max
-    assert got.min() > 0
-
-
 def test_encode_saturates_overflowed_product():
     from oracle.formats import E4M3, E5M2, E2M1
     inf = np.float32(np.inf)
