@@ -3,25 +3,45 @@
 The CodonFM-5B layer at M = 31 x 512 = 15872 tokens, hidden 4096,
 intermediate 16384 ("How to optimize Transformer-based models for
 low-precision training", "Model configuration and training inputs"), with
-the benchmark's seeded inputs and its launch configuration (plus the same
-layer at 32768 tokens and a Llama-3-8B-shaped layer at 8192): each GEMM
-quantizes both operands on the GPU (autocast path of the pipeline) and runs
-with bf16 output.  The oracle cannot quantize and multiply 260M-element
-tensors one by one in seconds, so it checks samples it computes exactly:
+the benchmark's seeded inputs and its launch configuration, plus the same
+layer at 32 x 1024 = 32768 tokens and a Llama-3-8B-shaped layer at 8192
+tokens ("Using autocast mode vs pre-quantized mode" gives both token
+counts; "Faster training throughput in FP8 precision with NVIDIA NeMo",
+"Current scaling", names Llama 3 8B): each GEMM quantizes both operands on
+the GPU (the pipeline's autocast path) and runs with bf16 output.  The
+oracle cannot quantize and multiply 260M-element tensors in seconds, so it
+checks what it can compute exactly:
 
-* whole 128-row groups of every quantized copy (the first three, a middle
-  and the last group; blocks never straddle a group), codes and scales bit
-  for bit;
-  per-tensor scales and the NVFP4 encode scale come from the oracle's amax
-  of the whole tensor (after the Hadamard transform for NVFP4 Wgrad inputs);
-* GEMM outputs at about 11 x 11 (m, n) pairs drawn from those rows (first,
-  last, either side of the first 256-row tile boundary, random), against the
-  fp64 dot product of the oracle-dequantized rows, within
-  |err| <= 1e-5 sum|a b| (+ the 8-bit instruction's unit bound, + 1 bf16 ulp);
-* the GEMM epilogue's max |C| (pbs_gemm_amax) against the amax kernel's
-  pass over the whole stored C, bit for bit.
+* codes and scales, bit for bit, of every quantized row it computes: whole
+  128-row groups (the first three, a middle one, the last) and, on the
+  15872-token layer, one row in every 256-row tile of A and one in every
+  128 rows of B -- so every output tile of every GEMM kernel (256 x 256,
+  and 256 x 128 for the sub-channel kernel) holds checked outputs; blocks
+  never straddle what it quantizes (2D blocks bring their whole 128- or
+  16-row group).  Per-tensor and NVFP4 encode scales come from the oracle's
+  amax of the whole tensor (after the Hadamard transform for NVFP4 Wgrad
+  inputs);
+* GEMM outputs at those rows x columns against the fp64 dot product of the
+  oracle-dequantized rows, within |err| <= 1e-5 sum|a b| (+ the 8-bit
+  instruction's term for FP8-instruction recipes, + 1 bf16 ulp); for the
+  recipes on the unscaled 8-bit instruction (per-tensor current and delayed,
+  channel-wise) also bit for bit against the measured description of that
+  instruction (tests/fp8_dot_unit.py);
+* the GEMM epilogue's max |C| (pbs_gemm_amax) against the amax kernel's pass
+  over the whole stored C.
+
+How far the FP8-instruction outputs fall outside the stated 1e-5 term
+alone is collected per case; with PBS_REPORT_DIR set, the session writes it
+to fp8_exceedance.json there.
+
+The delayed-scaling trajectory (16 warm-up steps of tensors whose amax
+drifts x1.1 per step, then Dgrad and Wgrad at step 16 with E5M2 gradients)
+runs at full size on all four layers in test_delayed_trajectory_fullsize.
 """
+import concurrent.futures as cf
 import functools
+import json
+import os
 
 import numpy as np
 import pytest
@@ -31,18 +51,15 @@ import workloads as W
 import precision_block_scaled_amd as P
 from precision_block_scaled_amd import pipeline as PL
 from oracle import recipes as R
-from oracle.formats import bf16_to_f32
-from oracle.gemm_ref import check_gemm, fp8_dot_unit_bound
-from oracle.passes import BLOCK128_2D
+from oracle.formats import E4M3, E5M2, bf16_to_f32
+from oracle.gemm_ref import REL_TOL, check_gemm, fp8_dot_unit_bound
+from oracle.passes import BLOCK128_2D, operand_roles
 from oracle.philox import philox_word0_for_index
+from tests.fp8_dot_unit import dot_unit_gemm, to_bf16_rne
 from tests.gpu_util import to_gpu_bf16
 
 pytestmark = pytest.mark.gpu
 
-# model -> (tokens, layer shapes): the CodonFM-5B layer the benchmark times,
-# the same layer at 32 x 1024 tokens, and a Llama-3-8B-shaped layer (GQA
-# 32 q / 8 kv heads: QKV N = 6144; gated MLP: up N = 28672, down K = 14336)
-# at 8192 tokens
 L3 = W.LLAMA3_8B_LAYER
 MODELS = {
     "codonfm": (15872, W.layer_shapes(4096, 16384, 32)),
@@ -51,8 +68,12 @@ MODELS = {
                                        L3["gated"])),
 }
 FP8_MFMA = {"fp8_current", "fp8_delayed", "mxfp8", "fp8_channel", "fp8_block128_pow2"} | set(BLOCK128_2D)
+UNSCALED_FP8 = {"fp8_current", "fp8_delayed", "fp8_channel"}       # bit-exact against the description
 FMAX = {"e4m3": 448.0, "e5m2": 57344.0}
+FMTS = {"e4m3": E4M3, "e5m2": E5M2}
 SEED = 42
+THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+EXCEEDANCE = {}
 
 
 @functools.lru_cache(maxsize=2)
@@ -67,93 +88,255 @@ def layer_inputs(model, name):
 
 
 def groups_of(n_rows):
-    """The first three, a middle and the last 128-row group of a copy with
-    n_rows rows (groups 1 and 2 straddle the first 256-row tile boundary)."""
+    """The first three, a middle and the last 128-row group of a copy."""
     g = n_rows // 128
     return sorted({0, 1, 2, g // 2, g - 1} & set(range(g)))
 
 
-def copy_rows(bits, orient, rows):
-    """Rows `rows` of the copy of `bits` (source layout) in orientation `orient`, source layout slice."""
-    return bits[rows, :] if orient == "row" else bits[:, rows]
+def sample_rows(n_rows, period, dense):
+    """Output rows (or columns) whose outputs are checked: first and last,
+    255 / 256 / 257, and -- when `dense` -- one row in every `period` rows at
+    an offset that moves from tile to tile; otherwise 6 random ones."""
+    rows = {0, n_rows - 1} | {r for r in (255, 256, 257) if r < n_rows}
+    if dense:
+        for t in range((n_rows + period - 1) // period):
+            r = period * t + (37 * t + 11) % period
+            rows.add(min(r, n_rows - 1))
+    else:
+        rng = np.random.default_rng(7 + n_rows)
+        rows |= set(int(r) for r in rng.choice(n_rows, 6, replace=False))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def block_rows(recipe, src):
+    """Rows of a copy that one quantization block spans (2D blocks), else 1."""
+    if recipe in BLOCK128_2D and src in BLOCK128_2D[recipe]:
+        return 128
+    if src == "w" and recipe == "fp8_block128_pow2":
+        return 128
+    if src == "w" and recipe == "nvfp4":
+        return 16
+    return 1
 
 
 class OracleCopy:
-    """The oracle's quantization of whole 128-row groups of one copy."""
+    """The oracle's quantization of selected rows of one copy.
 
-    def __init__(self, recipe, src, orient, bits, pass_, dstate, rows):
-        self.recipe, self.rows = recipe, rows
-        sl = copy_rows(bits, orient, rows)
-        w2d = src in BLOCK128_2D.get(recipe, ()) or (src == "w" and recipe in ("nvfp4", "fp8_block128_pow2"))
+    quant_rows: every row quantized and compared (whole blocks); sample:
+    rows whose dequantized values feed the GEMM check (a subset).
+    """
+
+    def __init__(self, recipe, src, orient, bits, pass_, dstate, quant_rows, sample, tensor_amax):
+        self.recipe, self.src, self.orient = recipe, src, orient
+        self.br = block_rows(recipe, src)
+        self.w2d = self.br > 1
+        self.quant_rows = quant_rows
+        self.sample = sample
         self.tsi = None
-        self.scales = None
-        if recipe in ("fp8_current", "fp8_delayed"):
-            fmt = "e5m2" if src == "dy" else "e4m3"
-            if recipe == "fp8_current":
-                s, s_inv = R.scale_from_amax(R.amax(bits), FMAX[fmt])
-                self.codes = R.cast_pertensor(sl, s, fmt, orient)
-            else:
-                self.codes, s_inv, _ = dstate.cast(sl, orient)
-            self.tsi = np.float32(s_inv)
-            self.deq = R.dequant_pertensor(self.codes, fmt, self.tsi)
+        self.fmt = "e5m2" if (src == "dy" and recipe in ("fp8_current", "fp8_delayed")) else "e4m3"
+        self.bits_shape = bits.shape
+        self.scale = None
+        if recipe == "fp8_current":
+            self.scale, self.tsi = R.scale_from_amax(tensor_amax, FMAX[self.fmt])
+        elif recipe == "fp8_delayed":
+            self.tsi = np.float32(np.float32(1.0) / dstate.scale)
+            self.dstate = dstate
+        elif recipe == "nvfp4":
+            self.scale, self.tsi = R.nvfp4_tensor_scales(tensor_amax)
+        self.rht = recipe in ("nvfp4", "mxfp4") and pass_ == "wgrad"
+        self.sr = recipe in ("nvfp4", "mxfp4") and src == "dy"
+        # the selected rows in one gather, quantized in chunks of whole blocks
+        # in threads (numpy releases the GIL)
+        sel = bits[quant_rows, :] if orient == "row" else bits[:, quant_rows]
+        n = len(quant_rows)
+        step = max(1, -(-n // (2 * THREADS)))
+        step = -(-step // self.br) * self.br
+        chunks = [(c0, min(len(quant_rows), c0 + step)) for c0 in range(0, len(quant_rows), step)]
+        with cf.ThreadPoolExecutor(THREADS) as ex:
+            parts = list(ex.map(lambda c: self._quantize(sel, quant_rows, *c), chunks))
+        self.codes = np.concatenate([p[0] for p in parts])
+        self.scales = None if parts[0][1] is None else np.concatenate([p[1] for p in parts])
+        deq = {}
+        raw = {}
+        rs = {}
+        for p in parts:
+            deq.update(p[2])
+            raw.update(p[3])
+            rs.update(p[4])
+        self.deq = np.stack([deq[int(r)] for r in sample])
+        self.raw = np.stack([raw[int(r)] for r in sample]) if raw else None
+        self.row_scale = np.array([rs[int(r)] for r in sample], np.float32) if rs else None
+
+    def _sr_random(self, rows):
+        M, N = self.bits_shape
+        r = np.asarray(rows, dtype=np.uint64)
+        if self.orient == "row":
+            idx = r[:, None] * np.uint64(N) + np.arange(N, dtype=np.uint64)[None, :]
+        else:
+            idx = np.arange(M, dtype=np.uint64)[None, :] * np.uint64(N) + r[:, None]
+        return philox_word0_for_index(idx, SEED)
+
+    def _quantize(self, sel, rows_all, i0, i1):
+        """(codes, scales, {row: deq}, {row: raw code values}, {row: channel scale}) for the
+        selected copy rows at positions i0..i1-1 (rows rows_all[i0:i1])."""
+        recipe = self.recipe
+        sl = sel[i0:i1, :] if self.orient == "row" else sel[:, i0:i1]
+        rows = rows_all[i0:i1]
+        pos = {int(r): i for i, r in enumerate(rows)}
+        want = [int(r) for r in self.sample if int(r) in pos]
+        loc = [pos[r] for r in want]
+        scales = None
+        raw = {}
+        rs = {}
+        if recipe == "fp8_current":
+            codes = R.cast_pertensor(sl, self.scale, self.fmt, self.orient)
+            deq = R.dequant_pertensor(codes, self.fmt, self.tsi)
+            dec = FMTS[self.fmt].decode(codes)
+            raw = {r: dec[i] for r, i in zip(want, loc)}
+        elif recipe == "fp8_delayed":
+            codes, _, _ = self.dstate.cast(sl, self.orient)
+            deq = R.dequant_pertensor(codes, self.fmt, self.tsi)
+            dec = FMTS[self.fmt].decode(codes)
+            raw = {r: dec[i] for r, i in zip(want, loc)}
         elif recipe in BLOCK128_2D:
-            self.codes, self.scales = R.quantize_block128(sl, orient, weight_2d=w2d)
-            self.deq = R.dequant_block128(self.codes, self.scales, w2d)
-        elif recipe == "fp8_block128_pow2":             # scales compared as E8M0 codes
-            self.codes, self.scales = R.quantize_block128_pow2(sl, orient, weight_2d=w2d)
-            self.deq = R.dequant_block128_pow2(self.codes, self.scales, w2d)
-        elif recipe == "fp8_channel":                   # a copy row's scale is its own
-            self.codes, self.scales = R.quantize_channel(sl, orient)
-            self.deq = R.dequant_channel(self.codes, self.scales)
+            codes, scales = R.quantize_block128(sl, self.orient, weight_2d=self.w2d)
+            deq = R.dequant_block128(codes, scales, self.w2d)
+        elif recipe == "fp8_block128_pow2":
+            codes, scales = R.quantize_block128_pow2(sl, self.orient, weight_2d=self.w2d)
+            deq = R.dequant_block128_pow2(codes, scales, self.w2d)
+        elif recipe == "fp8_channel":
+            codes, scales = R.quantize_channel(sl, self.orient)
+            deq = R.dequant_channel(codes, scales)
+            dec = E4M3.decode(codes)
+            raw = {r: dec[i] for r, i in zip(want, loc)}
+            rs = {r: scales[i] for r, i in zip(want, loc)}
         elif recipe == "mxfp8":
-            self.codes, self.scales = R.quantize_mxfp8(sl, orient)
-            self.deq = R.dequant_mxfp8(self.codes, self.scales)
+            codes, scales = R.quantize_mxfp8(sl, self.orient)
+            deq = R.dequant_mxfp8(codes, scales)
         elif recipe in ("nvfp4", "mxfp4"):
-            rht = pass_ == "wgrad"
             t = bf16_to_f32(sl)
-            if rht:
+            if self.rht:
                 t = R.rht16_along_rows(t, SEED)          # col slices hold whole columns
-            t_o = t if orient == "row" else np.ascontiguousarray(t.T)
-            sr = None
-            if src == "dy":
-                M, N = bits.shape
-                r = np.asarray(rows, dtype=np.uint64)
-                if orient == "row":
-                    idx = r[:, None] * np.uint64(N) + np.arange(N, dtype=np.uint64)[None, :]
-                else:
-                    idx = np.arange(M, dtype=np.uint64)[None, :] * np.uint64(N) + r[:, None]
-                sr = philox_word0_for_index(idx, SEED)
+            t_o = t if self.orient == "row" else np.ascontiguousarray(t.T)
+            sr = self._sr_random(rows) if self.sr else None
             if recipe == "nvfp4":
-                A = R.amax(R.rht16_along_rows(bf16_to_f32(bits), SEED) if rht else bits)
-                S_enc, S_dec = R.nvfp4_tensor_scales(A)
-                self.codes, self.scales = R.quantize_nvfp4(t_o, S_enc, weight_2d=w2d, sr_random=sr)
-                self.tsi = np.float32(S_dec)
-                self.deq = R.dequant_nvfp4(self.codes, self.scales, self.tsi, w2d)
+                codes, scales = R.quantize_nvfp4(t_o, self.scale, weight_2d=self.w2d, sr_random=sr)
+                deq = R.dequant_nvfp4(codes, scales, self.tsi, self.w2d)
             else:
-                self.codes, self.scales = R.quantize_mxfp4(t_o, sr_random=sr)
-                self.deq = R.dequant_mxfp4(self.codes, self.scales)
+                codes, scales = R.quantize_mxfp4(t_o, sr_random=sr)
+                deq = R.dequant_mxfp4(codes, scales)
         else:  # bf16: the operand is the natural-layout tensor
-            self.codes = sl if orient == "row" else np.ascontiguousarray(sl.T)
-            self.deq = bf16_to_f32(self.codes).astype(np.float64)
-        self.w2d = w2d
+            codes = sl if self.orient == "row" else np.ascontiguousarray(sl.T)
+            deq = bf16_to_f32(codes).astype(np.float64)
+        return codes, scales, {r: deq[i] for r, i in zip(want, loc)}, raw, rs
 
 
-def gpu_rows(q, rows, w2d):
-    """Codes and scales of the GPU copy q for whole 128-row groups `rows`."""
+def gpu_rows(q, rows, br):
+    """Codes and scales of the GPU copy q for rows `rows` (whole blocks)."""
     idx = torch.from_numpy(np.asarray(rows, dtype=np.int64)).to(q.codes.device)
     codes = q.codes[idx].cpu().numpy()
     sc = None
     if q.scales is not None:
-        if w2d:
-            div = 128 if q.recipe in BLOCK128_2D or q.recipe == "fp8_block128_pow2" else 16
-            g = torch.from_numpy(np.unique(np.asarray(rows) // div).astype(np.int64)).to(q.codes.device)
+        if br > 1:
+            g = torch.from_numpy(np.unique(np.asarray(rows) // br).astype(np.int64)).to(q.codes.device)
             sc = q.scales[g].cpu().numpy()
         else:
             sc = q.scales[idx].cpu().numpy()
     return codes, sc
 
 
-def run_pass(recipe, model, name, pass_):
+def quant_rows_for(n_rows, sample, br, extra_groups=True):
+    """Rows to quantize: the sample's whole blocks, plus the fixed 128-row groups."""
+    rows = set()
+    for r in sample:
+        b0 = (int(r) // br) * br
+        rows.update(range(b0, b0 + br))
+    if extra_groups:
+        for g in groups_of(n_rows):
+            rows.update(range(128 * g, 128 * g + 128))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _threaded_max(fn, n, axis_len):
+    parts = np.array_split(np.arange(axis_len), min(THREADS, axis_len))
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        return np.float32(max(ex.map(lambda c: fn(c[0], c[-1] + 1), [p for p in parts if len(p)])))
+
+
+@functools.lru_cache(maxsize=8)
+def _amax_cached(model, name, src, rht):
+    bits = dict(zip(("x", "w", "dy"), layer_inputs(model, name)))[src]
+    if not rht:      # the maximum of row chunks is the maximum of the tensor
+        return _threaded_max(lambda r0, r1: R.amax(bits[r0:r1]), THREADS, bits.shape[0])
+    # the Hadamard transform runs down each column: column chunks
+    return _threaded_max(lambda c0, c1: R.amax(R.rht16_along_rows(bf16_to_f32(bits[:, c0:c1]), SEED)),
+                         THREADS, bits.shape[1])
+
+
+def tensor_amax(recipe, model, name, src, rht):
+    """The tensor maximum the per-tensor and NVFP4 encode scales need (else None)."""
+    if recipe == "fp8_current" or recipe == "nvfp4":
+        return _amax_cached(model, name, src, rht and recipe == "nvfp4")
+    return None
+
+
+def check_copy(q, o, states, sname, what):
+    out = []
+    codes, sc = gpu_rows(q, o.quant_rows, o.br)
+    if (codes != o.codes).any():
+        i = tuple(np.argwhere(codes != o.codes)[0])
+        out.append(f"{what} codes differ at {i}: {codes[i]} vs {o.codes[i]}")
+    if o.recipe == "fp8_block128_pow2":            # each word: the E8M0 code in all four bytes
+        if (sc.view(np.uint32) != o.scales.astype(np.uint32) * np.uint32(0x01010101)).any():
+            out.append(f"{what} block scale words differ")
+    elif o.scales is not None and (sc.view(np.uint8) != np.ascontiguousarray(o.scales).view(np.uint8)).any():
+        out.append(f"{what} block scales differ")
+    if o.tsi is not None:
+        if isinstance(q.tensor_scale_inv, int):   # delayed: the state's scale_inv word
+            g_tsi = states[sname].buf[4:8].cpu().numpy().view(np.float32)[0]
+        else:
+            g_tsi = q.tensor_scale_inv.cpu().numpy()[0]
+        if np.float32(g_tsi).view(np.uint32) != np.float32(o.tsi).view(np.uint32):
+            out.append(f"{what} tensor scale_inv {g_tsi} vs {o.tsi}")
+    return out
+
+
+def check_outputs(recipe, C, qa, qb, key):
+    """The GEMM outputs at the sampled rows x columns."""
+    out = []
+    ia = torch.from_numpy(qa.sample).cuda()
+    ib = torch.from_numpy(qb.sample).cuda()
+    c = C[ia][:, ib].float().cpu().numpy()
+    ah, bh = qa.deq, qb.deq
+    cref = ah @ bh.T
+    bnd = np.abs(ah) @ np.abs(bh).T
+    extra = fp8_dot_unit_bound(ah, bh) if recipe in FP8_MFMA else None
+    ok, tol, err = check_gemm(c, cref, bnd, True, extra)
+    if not ok.all():
+        i = tuple(np.argwhere(~ok)[0])
+        out.append(f"GEMM {(~ok).sum()} of {ok.size} outside bound; got {c[i]} want {cref[i]} tol {tol[i]}")
+    if recipe in FP8_MFMA:
+        ratio = err / np.maximum(REL_TOL * bnd, 1e-300)
+        EXCEEDANCE[key] = {"outputs": int(c.size), "max_err_over_1e-5_sum_abs": float(ratio.max()),
+                           "outputs_over_stated_term": int((err > REL_TOL * bnd + 0).sum()),
+                           "outputs_over_stated_term_plus_bf16_ulp": int((~check_gemm(c, cref, bnd, True)[0]).sum())}
+    if recipe in UNSCALED_FP8:
+        chunks = np.array_split(np.arange(qa.raw.shape[0]), min(THREADS, qa.raw.shape[0]))
+        with cf.ThreadPoolExecutor(THREADS) as ex:
+            acc = np.concatenate(list(ex.map(lambda c: dot_unit_gemm(qa.raw[c], qb.raw, qa.fmt, qb.fmt), chunks)))
+        if recipe == "fp8_channel":
+            post = (qa.row_scale[:, None] * qb.row_scale[None, :]).astype(np.float32)
+        else:
+            post = np.float32(np.float32(qa.tsi) * np.float32(qb.tsi))
+        want = to_bf16_rne((acc * post).astype(np.float32))
+        if (want != c).any():
+            i = tuple(np.argwhere(want != c)[0])
+            out.append(f"{(want != c).sum()} of {c.size} outputs differ from the 8-bit instruction's "
+                       f"description; first {i}: {c[i]!r} vs {want[i]!r}")
+    return out
+
+
+def run_pass(recipe, model, name, pass_, dense):
     x, w, dy = layer_inputs(model, name)
     src = {"x": x, "w": w, "dy": dy}
     dev = "cuda"
@@ -180,70 +363,131 @@ def run_pass(recipe, model, name, pass_):
     P.pbs_amax(C, M, N, 0, 0, full_amax)
     torch.cuda.synchronize()
 
-    from oracle.passes import operand_roles
     (sa, oa), (sb, ob) = operand_roles(pass_)
     if recipe == "bf16":
         oa, ob = {"fprop": ("row", "row"), "dgrad": ("row", "col"), "wgrad": ("col", "col")}[pass_]
+    # one row in every 256-row tile of A, one in every 128 rows of B
+    samp_a = sample_rows(M, 256, dense)
+    samp_b = sample_rows(N, 128, dense)
+    rht = recipe in ("nvfp4", "mxfp4") and pass_ == "wgrad"
+    qa = OracleCopy(recipe, sa, oa, src[sa], pass_, ostates.get(sa), quant_rows_for(M, samp_a, block_rows(recipe, sa)),
+                    samp_a, tensor_amax(recipe, model, name, sa, rht))
+    qb = OracleCopy(recipe, sb, ob, src[sb], pass_, ostates.get(sb), quant_rows_for(N, samp_b, block_rows(recipe, sb)),
+                    samp_b, tensor_amax(recipe, model, name, sb, rht))
     out = []
-    rows_a = np.concatenate([np.arange(128 * g, 128 * g + 128) for g in groups_of(M)])
-    rows_b = np.concatenate([np.arange(128 * g, 128 * g + 128) for g in groups_of(N)])
-    qa = OracleCopy(recipe, sa, oa, src[sa], pass_, ostates.get(sa), rows_a)
-    qb = OracleCopy(recipe, sb, ob, src[sb], pass_, ostates.get(sb), rows_b)
     if recipe != "bf16":
-        for q, o, rows, sname in ((A, qa, rows_a, sa), (B, qb, rows_b, sb)):
-            codes, sc = gpu_rows(q, rows, o.w2d)
-            if (codes != o.codes).any():
-                i = tuple(np.argwhere(codes != o.codes)[0])
-                out.append(f"codes differ at sampled {i}: {codes[i]} vs {o.codes[i]}")
-            if recipe == "fp8_block128_pow2":            # each word: the E8M0 code in all four bytes
-                if (sc.view(np.uint32) != o.scales.astype(np.uint32) * np.uint32(0x01010101)).any():
-                    out.append("block scale words differ")
-            elif o.scales is not None and (sc.view(np.uint8) != np.ascontiguousarray(o.scales).view(np.uint8)).any():
-                out.append("block scales differ")
-            if o.tsi is not None:
-                if isinstance(q.tensor_scale_inv, int):   # delayed: the state's scale_inv word
-                    g_tsi = states[sname].buf[4:8].cpu().numpy().view(np.float32)[0]
-                else:
-                    g_tsi = q.tensor_scale_inv.cpu().numpy()[0]
-                if np.float32(g_tsi).view(np.uint32) != np.float32(o.tsi).view(np.uint32):
-                    out.append(f"tensor scale_inv {g_tsi} vs {o.tsi}")
-    # the epilogue's max |C| equals the amax kernel's pass over the stored C
+        out += check_copy(A, qa, states, sa, "A")
+        out += check_copy(B, qb, states, sb, "B")
     if c_amax.cpu().numpy().view(np.uint32)[0] != full_amax.cpu().numpy().view(np.uint32)[0]:
         out.append(f"epilogue amax {c_amax.item()} vs amax of C {full_amax.item()}")
-    rng = np.random.default_rng(7)
-    # first and last rows, rows 255 / 256 / 257 (either side of the first 256-row tile boundary), random rows
-    edge_a = [int(np.searchsorted(rows_a, r)) for r in (255, 256, 257)]
-    edge_b = [int(np.searchsorted(rows_b, r)) for r in (255, 256, 257)]
-    ia = np.unique(np.concatenate([[0, len(rows_a) - 1], edge_a, rng.choice(len(rows_a), 6, replace=False)]))
-    ib = np.unique(np.concatenate([[0, len(rows_b) - 1], edge_b, rng.choice(len(rows_b), 6, replace=False)]))
-    ah, bh = qa.deq[ia], qb.deq[ib]
-    cref = ah @ bh.T
-    bnd = np.abs(ah) @ np.abs(bh).T
-    extra = fp8_dot_unit_bound(ah, bh) if recipe in FP8_MFMA else None
-    c = C[torch.from_numpy(rows_a[ia]).cuda()][:, torch.from_numpy(rows_b[ib]).cuda()]
-    c = c.float().cpu().numpy()
-    ok, tol, err = check_gemm(c, cref, bnd, True, extra)
-    if not ok.all():
-        i = tuple(np.argwhere(~ok)[0])
-        out.append(f"GEMM {(~ok).sum()} of {ok.size} outside bound; got {c[i]} want {cref[i]} tol {tol[i]}")
+    out += check_outputs(recipe, C, qa, qb, f"{model}.{name}.{pass_}.{recipe}")
     return out
 
 
 RECIPES = ["bf16", "fp8_current", "fp8_delayed", "fp8_block128", "mxfp8", "nvfp4"]
-CASES = ([("codonfm", n, r) for n in ("qkv", "attn_out", "mlp_up", "mlp_down") for r in RECIPES]
-         + [("llama3_8b", n, r) for n in ("qkv", "attn_out", "mlp_up", "mlp_down") for r in RECIPES]
-         + [("codonfm_32k", n, r) for n in ("mlp_up", "mlp_down") for r in ("mxfp8", "nvfp4", "fp8_block128")]
-         + [(m, n, r) for r in ("mxfp4", "fp8_channel") for m in ("codonfm", "llama3_8b")
-            for n in ("qkv", "attn_out", "mlp_up", "mlp_down")]
-         + [("codonfm", n, r) for r in ("fp8_block128_1d1d", "fp8_block128_2d2d")
-            for n in ("qkv", "attn_out", "mlp_up", "mlp_down")]
-         + [(m, n, "fp8_block128_pow2") for m in ("codonfm", "llama3_8b")
-            for n in ("qkv", "attn_out", "mlp_up", "mlp_down")])
+LAYERS = ("qkv", "attn_out", "mlp_up", "mlp_down")
+CASES = ([("codonfm", n, r) for n in LAYERS for r in RECIPES]
+         + [("codonfm_32k", n, r) for n in LAYERS for r in RECIPES]
+         + [("llama3_8b", n, r) for n in LAYERS for r in RECIPES]
+         + [(m, n, r) for r in ("mxfp4", "fp8_channel") for m in ("codonfm", "llama3_8b") for n in LAYERS]
+         + [("codonfm", n, r) for r in ("fp8_block128_1d1d", "fp8_block128_2d2d") for n in LAYERS]
+         + [(m, n, "fp8_block128_pow2") for m in ("codonfm", "llama3_8b") for n in LAYERS])
 
 
 @pytest.mark.parametrize("model,name,recipe", CASES)
 def test_fullsize_layer(model, name, recipe):
+    # every output tile is sampled on the benchmark's own layer and recipes
+    dense = model == "codonfm" and recipe in RECIPES
     problems = []
     for pass_ in ("fprop", "dgrad", "wgrad"):
-        problems += [f"{pass_}: {p}" for p in run_pass(recipe, model, name, pass_)]
+        problems += [f"{pass_}: {p}" for p in run_pass(recipe, model, name, pass_, dense)]
     assert not problems, f"{model} {name} {recipe}: " + "; ".join(problems)
+
+
+# ---------------------------------------------------------------------------
+# Delayed scaling at full size: 16 warm-up steps, then Dgrad and Wgrad
+# ---------------------------------------------------------------------------
+def _drift_gpu(base, step):
+    """bf16(fp32(x) * fp32(1.1**step)) on the GPU (torch rounds to nearest even)."""
+    return (base.float() * float(W.drift_factor(step))).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("name", LAYERS)
+def test_delayed_trajectory_fullsize(name):
+    """Every tensor of the layer drifts: step s holds bf16(fp32(x) *
+    fp32(1.1**s)).  Steps 0..15 cast each tensor with the state's scale and
+    measure its amax in the same pass; the state is updated once per step.
+    At step 16 the amax exceeds every history entry by 1.1x, so the largest
+    values saturate.  The oracle's histories follow from the closed form
+    amax_s = bf16(fp32(amax_0) * fp32(1.1**s)) (rounding is monotone)."""
+    x, w, dy = layer_inputs("codonfm", name)
+    base = {"x": x, "w": w, "dy": dy}
+    dev = "cuda"
+    gbase = {k: to_gpu_bf16(v) for k, v in base.items()}
+    fmts = {"x": P.PBS_FMT_E4M3, "w": P.PBS_FMT_E4M3, "dy": P.PBS_FMT_E5M2}
+    states = {k: PL.DelayedState(fmts[k], dev) for k in base}
+    ostates = {k: R.DelayedScaling("e5m2" if k == "dy" else "e4m3") for k in base}
+    a0 = {k: R.amax(v) for k, v in base.items()}
+    orient = {"x": "col", "w": "row", "dy": "row"}
+    problems = []
+    for step in range(16):
+        for k in base:
+            xs = _drift_gpu(gbase[k], step)
+            PL.quantize("fp8_delayed", xs, k, orient[k], "fprop", state=states[k])
+            states[k].update()
+            amax_s = bf16_to_f32(W.drift(W.f32_to_bf16_bits(np.float32(a0[k])), step))
+            ostates[k].update(amax_s)
+        torch.cuda.synchronize()
+    for k in base:
+        hist = states[k].buf[16:16 + 64].view(torch.float32).cpu().numpy()
+        if not (hist == ostates[k].hist).all():
+            problems.append(f"{k}: history after 16 steps differs")
+    # step 16: Dgrad (dY row x W col) and Wgrad (X col x dY col)
+    g16 = {k: _drift_gpu(gbase[k], 16) for k in base}
+    for k in base:                        # the input the oracle sees: same rows, drifted on the host
+        rows = np.array([0, 1, base[k].shape[0] // 2, base[k].shape[0] - 1])
+        got = g16[k][torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+        if (got != W.drift(base[k][rows], 16)).any():
+            problems.append(f"{k}: GPU drift differs from the input generator's")
+    for pass_ in ("dgrad", "wgrad"):
+        M, N, K = PL.pass_dims(pass_, x.shape[0], x.shape[1], w.shape[0])
+        A, B = PL.quantize_pass("fp8_delayed", pass_, g16["x"], g16["w"], g16["dy"], states=states)
+        C = PL.gemm("fp8_delayed", pass_, A, B, M, N, K, out_dtype=torch.bfloat16)
+        amax16 = {k: states[k].amax.item() for k in ("x", "w", "dy")}
+        torch.cuda.synchronize()
+        (sa, oa), (sb, ob) = operand_roles(pass_)
+        samp_a, samp_b = sample_rows(M, 256, True), sample_rows(N, 128, True)
+        qa = OracleCopy("fp8_delayed", sa, oa, _Drifted(base[sa], 16), pass_, ostates[sa],
+                        quant_rows_for(M, samp_a, 1), samp_a, None)
+        qb = OracleCopy("fp8_delayed", sb, ob, _Drifted(base[sb], 16), pass_, ostates[sb],
+                        quant_rows_for(N, samp_b, 1), samp_b, None)
+        problems += [f"{pass_}: {p}" for p in check_copy(A, qa, states, sa, "A")]
+        problems += [f"{pass_}: {p}" for p in check_copy(B, qb, states, sb, "B")]
+        problems += [f"{pass_}: {p}" for p in check_outputs("fp8_delayed", C, qa, qb,
+                                                              f"codonfm.{name}.{pass_}.fp8_delayed_step16")]
+        for k in (sa, sb):
+            want = bf16_to_f32(W.drift(W.f32_to_bf16_bits(np.float32(a0[k])), 16))
+            if amax16[k] != want:
+                problems.append(f"{pass_}: step-16 amax of {k} {amax16[k]} vs {want}")
+    assert not problems, f"{name}: " + "; ".join(problems)
+
+
+class _Drifted:
+    """Lazy view of drift(base, step): slices are drifted when taken."""
+
+    def __init__(self, base, step):
+        self.base, self.step = base, step
+        self.shape = base.shape
+
+    def __getitem__(self, key):
+        return W.drift(self.base[key], self.step)
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _exceedance_report():
+    yield
+    d = os.environ.get("PBS_REPORT_DIR")
+    if d and EXCEEDANCE:
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, "fp8_exceedance.json"), "w") as f:
+            json.dump(EXCEEDANCE, f, indent=1, sort_keys=True)
