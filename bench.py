@@ -1,22 +1,29 @@
-"""Benchmark: quantize-then-GEMM over the 12 GEMMs of a CodonFM-5B layer.
+"""Benchmark: quantize-then-GEMM over the 12 GEMMs of a Transformer layer.
 
 Workload ("How to optimize Transformer-based models for low-precision
 training", "Model configuration and training inputs" and "Using autocast
-mode vs pre-quantized mode"): hidden 4096, intermediate 16384, 32 heads,
-micro-batch 31 x sequence 512 = 15872 tokens; QKV, attention-out, MLP-up and
-MLP-down in Fprop, Dgrad and Wgrad = 12 GEMMs.
+mode vs pre-quantized mode"): a model configuration (hidden size,
+intermediate size, attention heads and key/value heads, gated MLP or not)
+and a batch (micro-batch x sequence length tokens) give the QKV,
+attention-out, MLP-up and MLP-down linear layers, each in Fprop, Dgrad and
+Wgrad: 12 GEMMs.  The default is the CodonFM-5B layer: hidden 4096,
+intermediate 16384, 32 heads, micro-batch 31 x sequence 512 = 15872 tokens.
 
 One step = every recipe (BF16, FP8 current, FP8 delayed, FP8 1x128/128x128,
 MXFP8, NVFP4) over the 12 GEMMs in autocast mode: each GEMM quantizes both
 of its operands from bf16 (amax, scale, cast, RHT, SR as the recipe needs)
-and then runs the GEMM, bf16 output.  Inputs are seeded synthetic tensors
-resident in HBM before timing starts; each layer has its own X, W and dY.
+and then runs the GEMM, bf16 output.  With --pre-quantize the step times the
+GEMMs alone on operands quantized beforehand.  Inputs are seeded synthetic
+tensors resident in HBM before timing starts; each layer has its own X, W
+and dY.
 
 Printed: one JSON line.  ``value`` = total GEMM FLOP of the step / step time
-(TFLOP/s), plus per-recipe ms/layer and TFLOP/s in autocast and pre-quantized
-modes, quantize-pass GB/s, the roofline of the dominant kernel (timed with
-HIP events on the stream it runs on), and the CPU oracle timed on a bounded
-sample of the same workload.
+(TFLOP/s), plus per-recipe ms/layer and TFLOP/s in autocast, pre-quantized
+(operands hot in the caches, and cold) and layer-autocast modes,
+quantize-pass GB/s, the roofline of the dominant kernel (timed with HIP
+events on the stream it runs on), the same sweep on the CodonFM layer at
+32 x 1024 tokens and on a Llama-3-8B-shaped layer at 8192 tokens, and the
+CPU oracle timed on a bounded sample of the workload beside the GPU.
 """
 from __future__ import annotations
 
@@ -101,10 +108,21 @@ def upload_bf16(bits, dev):
     return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
 
 
-def build_layer_tensors(tokens, dev):
+# model configurations: the pages' CodonFM-5B layer, and a Llama-3-8B-shaped
+# layer (GQA 32 query / 8 key-value heads, gated MLP)
+MODELS = {
+    "codonfm": dict(hidden=4096, intermediate=16384, heads=32, kv_heads=32, gated=False, micro_batch=31,
+                    seq_len=512),
+    "llama3_8b": dict(hidden=4096, intermediate=14336, heads=32, kv_heads=8, gated=True, micro_batch=1,
+                      seq_len=8192),
+}
+
+
+def build_layer_tensors(cfg, tokens, dev):
     import workloads as W
     layers = {}
-    for i, ls in enumerate(W.layer_shapes(4096, 16384, 32)):
+    shapes = W.layer_shapes(cfg["hidden"], cfg["intermediate"], cfg["heads"], cfg["kv_heads"], cfg["gated"])
+    for i, ls in enumerate(shapes):
         x = upload_bf16(W.activations(tokens, ls.k_in, seed=10 + i), dev)
         w = upload_bf16(W.weights(ls.n_out, ls.k_in, seed=20 + i), dev)
         dy = upload_bf16(W.grads(tokens, ls.n_out, seed=30 + i), dev)
@@ -155,7 +173,11 @@ class Runner:
         self.PL.gemm(recipe, p, A, B, M, N, K, C=self.C[(name, p)])
 
     def step(self, recipes, events=None):
-        """One autocast pass over all recipes x 12 GEMMs.  events: list to append timing."""
+        """One autocast pass over all recipes x 12 GEMMs.  events: list to append timing.
+
+        Delayed scaling: every GEMM casts with the state's scale and measures
+        amax in the same pass; each tensor's state is updated once per step,
+        after its last consumer (the scale of a step comes from earlier steps)."""
         torch = self.torch
         for r in recipes:
             for (name, p, M, N, K) in self.gemms:
@@ -169,14 +191,31 @@ class Runner:
                 if events is not None:
                     e2.record()
                     events.append((r, name, p, M, N, K, e0, e1, e2))
-                if r == "fp8_delayed":
-                    for s in st:
-                        s.update()
+            if r == "fp8_delayed":
+                for s in self.states.values():
+                    s.update()
 
-    def prequant_pass(self, recipes, iters):
-        """GEMM-only timing with operands quantized once beforehand."""
+    def gemm_step(self, recipes, events):
+        """One pre-quantized pass: the 12 GEMMs of every recipe on the operands
+        the last autocast step quantized (events as in step, e0 == e1)."""
+        torch = self.torch
+        for r in recipes:
+            for (name, p, M, N, K) in self.gemms:
+                A, B = (self.operands(r, name, p)[:2] if r == "bf16" else self.q[(r, name, p)])
+                e0, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                e0.record()
+                self.run_gemm(r, name, p, A, B, M, N, K)
+                e2.record()
+                events.append((r, name, p, M, N, K, e0, e0, e2))
+
+    def prequant_pass(self, recipes, iters, cold=False):
+        """GEMM-only timing with operands quantized once beforehand: {(recipe,
+        layer, pass): (median ms, min ms)}.  Back to back, an operand that fits
+        the 256 MB last-level cache stays there; with `cold` a 1 GiB scratch
+        write between iterations (outside the events) evicts it first."""
         torch = self.torch
         out = {}
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=self.dev) if cold else None
         for r in recipes:
             for (name, p, M, N, K) in self.gemms:
                 if r == "bf16":
@@ -185,6 +224,8 @@ class Runner:
                     A, B = self.q[(r, name, p)]
                 ts = []
                 for _ in range(iters):
+                    if cold:
+                        scratch.zero_()
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     e0.record()
                     self.run_gemm(r, name, p, A, B, M, N, K)
@@ -192,7 +233,77 @@ class Runner:
                     ts.append((e0, e1))
                 out[(r, name, p)] = ts
         torch.cuda.synchronize()
-        return {k: float(np.median([a.elapsed_time(b) for a, b in v])) for k, v in out.items()}
+        res = {}
+        for k, v in out.items():
+            t = [a.elapsed_time(b) for a, b in v]
+            res[k] = (float(np.median(t)), float(np.min(t)))
+        return res
+
+    def layer_step(self, recipes, events, producer_amax=True):
+        """Layer autocast: each of X, W and dY is quantized once per layer --
+        both copies from one read wherever the two copies get the same
+        treatment -- and then the layer's three GEMMs run.  With
+        `producer_amax` the per-tensor maxima of X and dY come from the
+        epilogue of the GEMMs that produce them (pbs_gemm_amax: each layer's
+        Fprop and Dgrad fold max |C| into their epilogue for the next and the
+        previous layer), so current scaling and NVFP4 read X and dY once
+        (the maximum of the Hadamard-transformed tensors still takes a pass).
+        events: appends (recipe, layer, ms-event pair)."""
+        torch, PL, P = self.torch, self.PL, self.P
+        for r in recipes:
+            for name, (x, w, dy, ls) in self.layers.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                cp = self.lq.get((r, name))
+                st = {k: self.states[(name, k)] for k in ("x", "w", "dy")}
+                known = self.known_amax[name] if producer_amax and r in ("fp8_current", "nvfp4") else {}
+                amx = self.c_amax if r in ("fp8_current", "nvfp4") else None
+                if r == "bf16":
+                    q = {("x", "row"): x, ("w", "row"): w, ("dy", "row"): dy}
+                else:
+                    q = {} if cp is None else cp
+                    for s_, t in (("x", x), ("w", w), ("dy", dy)):
+                        if r in ("nvfp4", "mxfp4") and s_ != "w":
+                            pr = "fprop" if s_ == "x" else "dgrad"
+                            q[(s_, "row")] = PL.quantize(r, t, s_, "row", pr, st[s_], q.get((s_, "row")),
+                                                         known_amax=known.get(s_))
+                            q[(s_, "col")] = PL.quantize(r, t, s_, "col", "wgrad", st[s_], q.get((s_, "col")))
+                        else:
+                            prev = (q[(s_, "row")], q[(s_, "col")]) if (s_, "row") in q else None
+                            q[(s_, "row")], q[(s_, "col")] = PL.quantize_both(r, t, s_, st[s_], prev,
+                                                                             known_amax=known.get(s_))
+                    self.lq[(r, name)] = q
+                for (n_, p, M, N, K) in self.gemms:
+                    if n_ != name:
+                        continue
+                    if r == "bf16":
+                        A, B = {"fprop": (x, w), "dgrad": (dy, w), "wgrad": (x, dy)}[p]
+                    else:
+                        (sa, oa), (sb, ob) = PL.ROLES[p]
+                        A, B = q[(sa, oa)], q[(sb, ob)]
+                    PL.gemm(r, p, A, B, M, N, K, C=self.C[(name, p)],
+                            c_amax=amx if (amx is not None and p != "wgrad") else None)
+                e1.record()
+                events.append((r, name, e0, e1))
+                if r == "fp8_delayed":
+                    for s_ in ("x", "w", "dy"):
+                        st[s_].update()
+
+    def prepare_layer_mode(self):
+        """Buffers of the layer mode, and the maxima of X and dY that the
+        producing GEMMs' epilogues would hand over (measured once, untimed)."""
+        torch, P = self.torch, self.P
+        self.lq = {}
+        self.c_amax = torch.zeros(1, device=self.dev)
+        self.known_amax = {}
+        for name, (x, w, dy, ls) in self.layers.items():
+            ka = {}
+            for s_, t in (("x", x), ("dy", dy)):
+                a = torch.zeros(1, device=self.dev)
+                P.pbs_amax(t, t.shape[0], t.shape[1], 0, 0, a)
+                ka[s_] = a
+            self.known_amax[name] = ka
+        torch.cuda.synchronize()
 
 
 def quant_bandwidth(runner, iters=20):
@@ -357,6 +468,9 @@ def per_gemm_times(events):
 # matrix peak (TFLOP/s) of the instruction each recipe's GEMM runs on; exact
 # NVFP4 runs on the fp16 MFMA
 RECIPE_PEAK = {"bf16": 2516.6, "nvfp4": 2516.6, "mxfp4": 10066.3}
+# the format's own dense peak where it differs from the instruction's: NVFP4
+# is a 4-bit format (FP4 matrix rate), though its exact path issues fp16 MFMAs
+FORMAT_PEAK = {"nvfp4": 10066.3}
 
 
 def quant_bytes_per_element(recipe, src, k_len):
@@ -388,11 +502,11 @@ def quant_bytes_per_element(recipe, src, k_len):
     raise ValueError(recipe)
 
 
-def autocast_roofline_ms(runner, recipe):
+def autocast_roofline_ms(runner, recipe, peak=None):
     """Per layer: GEMM flops at the recipe's matrix peak plus quantization
     bytes at 8 TB/s, both operands of every GEMM quantized (autocast)."""
     from precision_block_scaled_amd import pipeline as PL
-    peak = RECIPE_PEAK.get(recipe, 5033.2)
+    peak = peak or RECIPE_PEAK.get(recipe, 5033.2)
     t = 0.0
     for (_, p, M, N, K) in runner.gemms:
         t += 2.0 * M * N * K / (peak * 1e12)
@@ -402,22 +516,75 @@ def autocast_roofline_ms(runner, recipe):
     return t * 1e3
 
 
-def recipe_table(runner, recipes, per, pre):
-    """ms per layer and TFLOP/s per recipe, autocast (and pre-quantized when timed)."""
+def layer_roofline_ms(runner, recipe):
+    """Per layer in layer-autocast mode: GEMM flops at the recipe's matrix
+    peak plus one read of X, W and dY and the writes of both copies of each
+    (the 4-bit recipes read X and dY once more for the Hadamard copy and its
+    maximum; the maxima of X and dY come from the producers' epilogues)."""
+    peak = RECIPE_PEAK.get(recipe, 5033.2)
+    t = sum(2.0 * M * N * K for (_, _, M, N, K) in runner.gemms) / (peak * 1e12)
+    if recipe == "bf16":
+        return t * 1e3
+    out_b = {"fp8_current": 1.0, "fp8_delayed": 1.0, "fp8_block128": 1.0 + 4 / 128, "mxfp8": 1.0 + 1 / 32,
+             "nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32, "fp8_channel": 1.0, "fp8_block128_pow2": 1.0 + 4 / 128,
+             "fp8_block128_1d1d": 1.0 + 4 / 128, "fp8_block128_2d2d": 1.0}[recipe]
+    q = 0.0
+    for (x, w, dy, ls) in runner.layers.values():
+        for t_, src in ((x, "x"), (w, "w"), (dy, "dy")):
+            n = t_.numel()
+            reads = 2.0
+            if recipe in ("nvfp4", "mxfp4") and src != "w":
+                reads = 2.0 * (3 if recipe == "nvfp4" else 2)     # row cast, RHT amax (NVFP4), RHT col cast
+            if recipe == "fp8_current" and src == "w":
+                reads = 4.0                                        # amax pass, then the cast
+            if recipe == "nvfp4" and src == "w":
+                reads = 4.0
+            q += n * (reads + 2 * out_b)
+    return (t + q / (HBM_GBPS * 1e9)) * 1e3
+
+
+def recipe_table(runner, recipes, per, pre, cold=None, layer=None):
+    """ms per layer and TFLOP/s per recipe: autocast (median and min over the
+    timed steps), pre-quantized (median and min, operands hot in the caches;
+    and with the caches flushed when `cold` is given), layer autocast; the
+    fraction of each mode's roofline (for NVFP4 against the fp16 matrix
+    rate it runs on and against the FP4 format's peak)."""
     out = {}
     layer_flop = sum(2.0 * M * N * K for (_, _, M, N, K) in runner.gemms)
+    tf = lambda ms: round(layer_flop / (ms * 1e-3) / 1e12, 1)
     for r in recipes:
         auto_ms = sum(float(np.median(per[(r, n, p)]["auto"])) for (n, p, *_) in runner.gemms)
+        auto_min = sum(float(np.min(per[(r, n, p)]["auto"])) for (n, p, *_) in runner.gemms)
         roof = autocast_roofline_ms(runner, r)
-        ent = {"autocast_ms_per_layer": round(auto_ms, 3),
-               "autocast_TFLOPs": round(layer_flop / (auto_ms * 1e-3) / 1e12, 1),
+        ent = {"autocast_ms_per_layer": round(auto_ms, 3), "autocast_min_ms_per_layer": round(auto_min, 3),
+               "autocast_TFLOPs": tf(auto_ms),
                "autocast_roofline_ms_per_layer": round(roof, 3),
                "autocast_roofline_frac": round(roof / auto_ms, 4)}
+        if r in FORMAT_PEAK:
+            roof_f = autocast_roofline_ms(runner, r, peak=FORMAT_PEAK[r])
+            ent["autocast_roofline_frac_format_peak"] = round(roof_f / auto_ms, 4)
         if pre:
-            pre_ms = sum(pre[(r, n, p)] for (n, p, *_) in runner.gemms)
+            pre_ms = sum(pre[(r, n, p)][0] for (n, p, *_) in runner.gemms)
+            pre_min = sum(pre[(r, n, p)][1] for (n, p, *_) in runner.gemms)
+            peak = RECIPE_PEAK.get(r, 5033.2)
             ent["prequant_ms_per_layer"] = round(pre_ms, 3)
-            ent["prequant_TFLOPs"] = round(layer_flop / (pre_ms * 1e-3) / 1e12, 1)
-            ent["ms_per_gemm_prequant"] = {f"{n}.{p}": round(pre[(r, n, p)], 4) for (n, p, *_) in runner.gemms}
+            ent["prequant_min_ms_per_layer"] = round(pre_min, 3)
+            ent["prequant_TFLOPs"] = tf(pre_ms)
+            ent["prequant_frac_of_peak"] = round(layer_flop / (pre_ms * 1e-3) / 1e12 / peak, 4)
+            if r in FORMAT_PEAK:
+                ent["prequant_frac_of_format_peak"] = round(layer_flop / (pre_ms * 1e-3) / 1e12 / FORMAT_PEAK[r], 4)
+            ent["ms_per_gemm_prequant"] = {f"{n}.{p}": round(pre[(r, n, p)][0], 4) for (n, p, *_) in runner.gemms}
+            ent["ms_per_gemm_prequant_min"] = {f"{n}.{p}": round(pre[(r, n, p)][1], 4) for (n, p, *_) in runner.gemms}
+        if cold:
+            cold_ms = sum(cold[(r, n, p)][0] for (n, p, *_) in runner.gemms)
+            ent["prequant_cold_ms_per_layer"] = round(cold_ms, 3)
+            ent["prequant_cold_TFLOPs"] = tf(cold_ms)
+        if layer and r in layer:
+            ent["layer_autocast_ms_per_layer"] = round(layer[r], 3)
+            ent["layer_autocast_TFLOPs"] = tf(layer[r])
+            lroof = layer_roofline_ms(runner, r)
+            ent["layer_autocast_roofline_ms_per_layer"] = round(lroof, 3)
+            ent["layer_autocast_roofline_frac"] = round(lroof / layer[r], 4)
         out[r] = ent
     return out
 
@@ -439,10 +606,10 @@ def model_analysis(runner, recipes, per, pre, layers=24):
         if "bf16" in auto:
             e["speedup_vs_bf16_autocast"] = round(auto["bf16"] / auto[r], 3)
         if pre:
-            pm = sum(pre[(r, n, p)] for (n, p, *_) in runner.gemms)
+            pm = sum(pre[(r, n, p)][0] for (n, p, *_) in runner.gemms)
             e["prequant_ms_per_model"] = round(layers * pm, 2)
             if "bf16" in recipes:
-                pb = sum(pre[("bf16", n, p)] for (n, p, *_) in runner.gemms)
+                pb = sum(pre[("bf16", n, p)][0] for (n, p, *_) in runner.gemms)
                 e["speedup_vs_bf16_prequant"] = round(pb / pm, 3)
         # stored weight bytes of the layer (codes + block scales + fp32 tensor scalars)
         wb = 0
@@ -460,20 +627,64 @@ def model_analysis(runner, recipes, per, pre, layers=24):
         out["mxfp8_over_nvfp4_fprop_autocast"] = {n: round(med("mxfp8", n, "fprop") / med("nvfp4", n, "fprop"), 3)
                                                   for n in names}
     if pre:
-        out["dgrad_over_fprop_prequant"] = {r: {n: round(pre[(r, n, "dgrad")] / pre[(r, n, "fprop")], 3) for n in names}
+        out["dgrad_over_fprop_prequant"] = {r: {n: round(pre[(r, n, "dgrad")][0] / pre[(r, n, "fprop")][0], 3) for n in names}
                                             for r in recipes}
     return out
 
 
-def cpu_baseline(seconds_target=12.0):
-    """The CPU oracle on a bounded sample of the workload: autocast Fprop of the
-    attention-out layer (W [4096, 4096]) for the first `rows` tokens, every
-    recipe (quantize X and W, fp64 GEMM over the dequantized operands),
-    repeated until about `seconds_target` seconds of host time."""
+def host_info():
+    """Host CPU facts for the oracle baseline."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        import threadpoolctl
+        blas = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=None)
+    except Exception:
+        pass
+    return {"cpu_count": os.cpu_count(), "affinity_cores": cores, "cpu_model": model, "blas_threads": blas}
+
+
+def _threads():
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(16, os.cpu_count() or 1))
+
+
+def cpu_baseline(runner, per, pre, quant_gbps, seconds_target=8.0):
+    """The CPU oracle beside the GPU, on bounded samples of the same workload.
+
+    * value: autocast Fprop of the attention-out layer (W [4096, 4096]) for
+      256 tokens, all six recipes (oracle quantize of X and W, then the fp64
+      GEMM over the dequantized operands), repeated for about
+      `seconds_target` seconds: TFLOP/s of the oracle doing what a step does;
+    * per recipe, the oracle's quantization of a [512, 16384] slice of the
+      MLP-down activations (row chunks over the host's threads): GB/s in the
+      same algorithmic bytes as the GPU's quantize passes, and the GPU/CPU
+      ratio where the GPU timed the same cast;
+    * the fp64 GEMM of each of the 12 GEMMs on a 256-row slice (full K and
+      N), extrapolated to the full M, beside the GPU's per-GEMM autocast
+      time of each recipe; one full-shape fp64 GEMM (MLP-down Fprop)
+      calibrates the extrapolation."""
+    import concurrent.futures as cf
     import workloads as W
     from oracle import recipes as R
     from oracle.passes import pass_operands
     from oracle.gemm_ref import gemm_ref
+    info = host_info()
+    nthr = _threads()
     rows = 256
     x = W.activations(rows, 4096, seed=11)
     w = W.weights(4096, 4096, seed=21)
@@ -493,20 +704,125 @@ def cpu_baseline(seconds_target=12.0):
             flop += 2.0 * rows * 4096 * 4096
         passes += 1
     dt = time.perf_counter() - t0
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        blas_threads = max((i.get("num_threads", 1) for i in info), default=1)
-    except Exception:
-        blas_threads = None
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads or cores,
+
+    # quantization of a [512, 16384] activation slice, row chunks in threads
+    xq = W.activations(512, 16384, seed=13)
+    chunks = np.array_split(np.arange(512), nthr)
+    quant = {}
+    label = {"fp8_current": "fp8_tensor_cast_row", "fp8_block128": "fp8_block128_cast_row",
+             "mxfp8": "mxfp8_cast_row", "nvfp4": "nvfp4_cast_row"}
+    from oracle.formats import bf16_to_f32
+    S_nv = R.nvfp4_tensor_scales(R.amax(xq))[0]
+    s_cur = R.scale_from_amax(R.amax(xq), 448.0)[0]
+    casts = {"fp8_current": lambda c: R.cast_pertensor(xq[c], s_cur, "e4m3", "row"),
+             "fp8_block128": lambda c: R.quantize_block128(xq[c], "row"),
+             "mxfp8": lambda c: R.quantize_mxfp8(xq[c], "row"),
+             "nvfp4": lambda c: R.quantize_nvfp4(bf16_to_f32(xq[c]), S_nv)}
+    for r, fn in casts.items():
+        tq = time.perf_counter()
+        with cf.ThreadPoolExecutor(nthr) as ex:
+            list(ex.map(fn, chunks))
+        tq = time.perf_counter() - tq
+        # the cast's own bytes (without the amax pass), as the GPU's GB/s counts them
+        bpe = quant_bytes_per_element(r, "x", 16384) - (2.0 if r in ("fp8_current", "nvfp4") else 0.0)
+        gbps = bpe * xq.size / tq / 1e9
+        e = {"ms": round(tq * 1e3, 2), "GBps": round(gbps, 3), "elements": int(xq.size), "threads": nthr}
+        g = quant_gbps.get(label[r], {}).get("GBps") if quant_gbps else None
+        if g:
+            e["gpu_GBps"] = g
+            e["gpu_over_cpu"] = round(g / gbps, 1)
+        quant[r] = e
+
+    # fp64 GEMMs: 256-row slices of the 12 GEMMs, extrapolated to the full M
+    rng = np.random.default_rng(0)
+    gemms = {}
+    t_oracle_layer = 0.0
+    for (name, p, M, N, K) in runner.gemms:
+        a = rng.standard_normal((256, K))
+        b = rng.standard_normal((N, K))
+        tg = time.perf_counter()
+        a @ b.T
+        tg = time.perf_counter() - tg
+        ext = tg * M / 256 * 1e3
+        t_oracle_layer += ext
+        gemms[f"{name}.{p}"] = {"oracle_fp64_ms_extrapolated": round(ext, 1)}
+    gpu_layer = {r: sum(float(np.median(per[(r, n, p)]["auto"])) for (n, p, *_) in runner.gemms)
+                 for r in RECIPES if (r, runner.gemms[0][0], runner.gemms[0][1]) in per}
+    for (name, p, M, N, K) in runner.gemms:
+        gemms[f"{name}.{p}"]["gpu_autocast_ms"] = {r: round(float(np.median(per[(r, name, p)]["auto"])), 4)
+                                                   for r in gpu_layer}
+    # one full-shape calibration: MLP-down Fprop
+    calib = None
+    md = next((g for g in runner.gemms if g[0] == "mlp_down" and g[1] == "fprop"), None)
+    if md is not None:
+        _, _, M, N, K = md
+        a = rng.standard_normal((M, K))
+        b = rng.standard_normal((N, K))
+        tg = time.perf_counter()
+        a @ b.T
+        tg = time.perf_counter() - tg
+        del a, b
+        calib = {"gemm": f"mlp_down.fprop [{M}x{K}]x[{K}x{N}] fp64, full shape", "ms": round(tg * 1e3, 1),
+                 "extrapolated_from_256_rows_ms": gemms["mlp_down.fprop"]["oracle_fp64_ms_extrapolated"]}
+    layer_flop = sum(2.0 * M * N * K for (_, _, M, N, K) in runner.gemms)
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": info["blas_threads"] or info["affinity_cores"],
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"autocast Fprop of attn-out (W 4096x4096) for {rows} tokens, all 6 recipes: "
-                      f"oracle quantize of X and W + fp64 GEMM, {passes} passes"}
+                      f"oracle quantize of X and W + fp64 GEMM, {passes} passes",
+            "host": info,
+            "quantize_512x16384_activations": quant,
+            "fp64_gemm_per_layer_ms_extrapolated": round(t_oracle_layer, 1),
+            "fp64_gemm_TFLOPs": round(layer_flop / (t_oracle_layer * 1e-3) / 1e12, 3),
+            "gpu_autocast_ms_per_layer": {r: round(v, 3) for r, v in gpu_layer.items()},
+            "gpu_over_cpu_per_layer": {r: round(t_oracle_layer / v, 1) for r, v in gpu_layer.items()},
+            "per_gemm": gemms, "calibration": calib}
+
+
+def fp8_exceedance(runner, recipes, group_rows=128):
+    """How far the FP8-instruction GEMMs land outside the stated tolerance
+    1e-5 * sum|a b| alone (the oracle accepts them with the 8-bit dot unit's
+    term added): the Fprop GEMM of every layer, its outputs at one 128-row
+    group of X x one 128-row group of W (the middle ones), against the
+    oracle's fp64 product of those rows quantized on the host."""
+    import workloads as W
+    from oracle import recipes as R
+    from oracle.gemm_ref import REL_TOL, check_gemm, fp8_dot_unit_bound
+    from oracle.passes import quantize_operand
+    torch, PL = runner.torch, runner.PL
+    out = {}
+    for r in recipes:
+        if r in ("bf16", "nvfp4", "mxfp4"):
+            continue
+        worst, over, total, outside = 0.0, 0, 0, 0
+        for (name, p, M, N, K) in runner.gemms:
+            if p != "fprop" or (r, name, p) not in runner.q:
+                continue
+            x, w, dy, ls = runner.layers[name]
+            A, B = runner.q[(r, name, p)]
+            C = PL.gemm(r, p, A, B, M, N, K)
+            ra = np.arange(group_rows) + (M // group_rows // 2) * group_rows
+            rb = np.arange(group_rows) + (N // group_rows // 2) * group_rows
+            c = C[torch.from_numpy(ra).to(C.device)][:, torch.from_numpy(rb).to(C.device)].float().cpu().numpy()
+            xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
+            wb = w.view(torch.int16).cpu().numpy().view(np.uint16)
+            if r in ("fp8_current", "fp8_delayed"):
+                sa = R.scale_from_amax(R.amax(xb), 448.0)
+                sb = R.scale_from_amax(R.amax(wb), 448.0)
+                ah = R.dequant_pertensor(R.cast_pertensor(xb[ra], sa[0], "e4m3"), "e4m3", sa[1])
+                bh = R.dequant_pertensor(R.cast_pertensor(wb[rb], sb[0], "e4m3"), "e4m3", sb[1])
+            else:
+                ah = quantize_operand(r, "x", "row", xb[ra], "fprop").dequant()
+                bh = quantize_operand(r, "w", "row", wb[rb], "fprop").dequant()
+            cref = ah @ bh.T
+            base = np.abs(ah) @ np.abs(bh).T
+            err = np.abs(c.astype(np.float64) - cref)
+            worst = max(worst, float((err / np.maximum(REL_TOL * base, 1e-300)).max()))
+            over += int((~check_gemm(c, cref, base, True)[0]).sum())
+            outside += int((~check_gemm(c, cref, base, True, fp8_dot_unit_bound(ah, bh))[0]).sum())
+            total += c.size
+        out[r] = {"outputs": total, "max_err_over_1e-5_sum_abs": round(worst, 3),
+                  "outputs_over_stated_bound": over, "outputs_outside_oracle_tolerance": outside}
+    return out
 
 
 def load_traffic(kernel_name):
@@ -523,18 +839,88 @@ def load_traffic(kernel_name):
     return rec
 
 
+def timed_steps(runner, recipes, warmup, steps, prequant_mode):
+    """Warm-up, then `steps` timed steps bracketed by device synchronisation.
+    Returns (wall ms per step, events).  In pre-quantized mode the operands
+    are quantized once by the warm-up and each step runs the GEMMs only."""
+    torch = runner.torch
+    for _ in range(max(1, warmup) if prequant_mode else warmup):
+        runner.step(recipes)
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if prequant_mode:
+            runner.gemm_step(recipes, events)
+        else:
+            runner.step(recipes, events)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps, events
+
+
+def layer_mode(runner, recipes, warmup, steps):
+    """ms per layer of the layer-autocast mode, per recipe (median of steps)."""
+    torch = runner.torch
+    runner.prepare_layer_mode()
+    for _ in range(warmup):
+        runner.layer_step(recipes, [])
+    ev = []
+    for _ in range(steps):
+        runner.layer_step(recipes, ev)
+    torch.cuda.synchronize()
+    acc = {}
+    for (r, name, e0, e1) in ev:
+        acc.setdefault(r, {}).setdefault(name, []).append(e0.elapsed_time(e1))
+    return {r: sum(float(np.median(v)) for v in d.values()) for r, d in acc.items()}
+
+
+def sweep(cfg, tokens, recipes, dev, warmup, steps, iters):
+    """The six recipes on another configuration (autocast and pre-quantized
+    ms per layer, TFLOP/s and roofline fractions), reported apart from value."""
+    torch = __import__("torch")
+    layers = build_layer_tensors(cfg, tokens, dev)
+    runner = Runner(layers, tokens, dev)
+    ms_step, events = timed_steps(runner, recipes, warmup, steps, False)
+    per, _ = per_gemm_times(events)
+    pre = runner.prequant_pass(recipes, iters)
+    tab = recipe_table(runner, recipes, per, pre)
+    for r in tab:
+        tab[r].pop("ms_per_gemm_prequant_min", None)
+    out = {"tokens": tokens, **{k: cfg[k] for k in ("hidden", "intermediate", "heads", "kv_heads", "gated")},
+           "gemm_shapes_MNK": {f"{n}.{p}": [M, N, K] for (n, p, M, N, K) in runner.gemms},
+           "layer_TFLOP": round(sum(2.0 * M * N * K for (_, _, M, N, K) in runner.gemms) / 1e12, 3),
+           "ms_per_step": round(ms_step, 3), "per_recipe": tab}
+    del runner, layers
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--tokens", type=int, default=15872)
+    # model configuration and batch, as the pages' benchmark takes them
+    ap.add_argument("--model", choices=sorted(MODELS), default="codonfm",
+                    help="preset the flags below are defaults of")
+    ap.add_argument("--hidden_size", "--hidden-size", type=int, default=None)
+    ap.add_argument("--intermediate_size", "--intermediate-size", type=int, default=None)
+    ap.add_argument("--num_attention_heads", "--num-attention-heads", type=int, default=None)
+    ap.add_argument("--num_key_value_heads", "--num-key-value-heads", type=int, default=None)
+    ap.add_argument("--gated", choices=("yes", "no"), default=None, help="gated MLP (up projection 2x wide)")
+    ap.add_argument("--micro_batch_size", "--micro-batch-size", type=int, default=None)
+    ap.add_argument("--sequence_length", "--sequence-length", type=int, default=None)
+    ap.add_argument("--tokens", type=int, default=None, help="tokens per step (overrides micro-batch x sequence)")
+    ap.add_argument("--pre-quantize", "--pre_quantize", action="store_true",
+                    help="time the GEMMs alone on operands quantized before the timed steps")
     ap.add_argument("--recipes", default=",".join(RECIPES))
     ap.add_argument("--next-recipes", default=",".join(NEXT_RECIPES),
                     help="recipes beyond the six, timed after the step and reported apart")
     ap.add_argument("--prequant-iters", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip pre-quant and GB/s passes")
+    ap.add_argument("--no-extras", action="store_true", help="skip every pass after the timed steps")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the 32768-token CodonFM and 8192-token Llama-3-8B sweeps")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     a = ap.parse_args()
@@ -542,6 +928,17 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); the multi-GPU "
               "sharding of this path is a design note, not built.", file=sys.stderr)
         sys.exit(2)
+    cfg = dict(MODELS[a.model])
+    for key, val in (("hidden", a.hidden_size), ("intermediate", a.intermediate_size),
+                     ("heads", a.num_attention_heads), ("kv_heads", a.num_key_value_heads),
+                     ("micro_batch", a.micro_batch_size), ("seq_len", a.sequence_length)):
+        if val is not None:
+            cfg[key] = val
+    if a.num_attention_heads is not None and a.num_key_value_heads is None and a.model == "codonfm":
+        cfg["kv_heads"] = cfg["heads"]
+    if a.gated is not None:
+        cfg["gated"] = a.gated == "yes"
+    tokens = a.tokens if a.tokens is not None else cfg["micro_batch"] * cfg["seq_len"]
 
     import torch
     dev = torch.device("cuda:0")
@@ -558,27 +955,15 @@ def main():
     import precision_block_scaled_amd as P
     P.lib()
     recipes = [r for r in a.recipes.split(",") if r]
-    log("generating inputs")
-    layers = build_layer_tensors(a.tokens, dev)
-    runner = Runner(layers, a.tokens, dev)
+    log(f"generating inputs: {a.model} {cfg} tokens={tokens}")
+    layers = build_layer_tensors(cfg, tokens, dev)
+    runner = Runner(layers, tokens, dev)
     total_flop = sum(2.0 * M * N * K for (_, _, M, N, K) in runner.gemms) * len(recipes)
 
     clock = ClockSampler()      # shader clock over the GEMM-heavy part (warm-up to pre-quantized)
     clock.__enter__()
-    log(f"warmup {a.warmup} steps")
-    for _ in range(a.warmup):
-        runner.step(recipes)
-    torch.cuda.synchronize()
-
-    log(f"timing {a.steps} steps")
-    events = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
-        runner.step(recipes, events)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / a.steps
+    log(f"warmup {a.warmup}, timing {a.steps} steps ({'pre-quantized' if a.pre_quantize else 'autocast'})")
+    ms_step, events = timed_steps(runner, recipes, a.warmup, a.steps, a.pre_quantize)
 
     per, kern = per_gemm_times(events)
     dom = max(kern.items(), key=lambda kv: kv[1]["ms"])
@@ -588,12 +973,21 @@ def main():
     peak = PEAK_TFLOPS[dk["dtype"]]
     traffic = load_traffic(dom_name)
 
-    pre = {}
+    pre, cold, lay = {}, {}, {}
     if not a.no_extras:
-        log("pre-quantized GEMM timing")
+        if a.pre_quantize:          # the timed steps were the GEMMs alone: fill the autocast table too
+            ev_a = []
+            for _ in range(a.steps):
+                runner.step(recipes, ev_a)
+            torch.cuda.synchronize()
+            per, _ = per_gemm_times(ev_a)
+        log("pre-quantized GEMM timing (operands hot, then with the caches flushed)")
         pre = runner.prequant_pass(recipes, a.prequant_iters)
+        cold = runner.prequant_pass(recipes, a.prequant_iters, cold=True)
+        log("layer autocast (each tensor quantized once per layer)")
+        lay = layer_mode(runner, recipes, a.warmup, a.steps)
     clock.__exit__(None, None, None)
-    per_recipe = recipe_table(runner, recipes, per, pre)
+    per_recipe = recipe_table(runner, recipes, per, pre, cold, lay)
     epi = epilogue_amax_cost(runner) if (not a.no_extras and "fp8_current" in recipes) else None
     model = model_analysis(runner, recipes, per, pre)
 
@@ -601,30 +995,52 @@ def main():
     nxt = {}
     if not a.no_extras and next_recipes:
         log(f"next recipes {next_recipes} (reported apart from value)")
-        for _ in range(a.warmup):
-            runner.step(next_recipes)
-        ev2 = []
-        for _ in range(a.steps):
-            runner.step(next_recipes, ev2)
-        torch.cuda.synchronize()
+        _, ev2 = timed_steps(runner, next_recipes, a.warmup, a.steps, False)
         per2, kern2 = per_gemm_times(ev2)
         pre2 = runner.prequant_pass(next_recipes, a.prequant_iters)
-        nxt = recipe_table(runner, next_recipes, per2, pre2)
+        lay2 = layer_mode(runner, next_recipes, a.warmup, a.steps)
+        nxt = recipe_table(runner, next_recipes, per2, pre2, None, lay2)
         for key, k in kern2.items():
             tf = k["flop"] / (k["ms"] * 1e-3) / 1e12
             nxt.setdefault("kernels", {})[key] = {
                 "avg_launch_ms": round(k["ms"] / k["launches"], 4), "achieved_TFLOPs": round(tf, 1),
                 "peak": PEAK_TFLOPS[k["dtype"]], "frac": round(tf / PEAK_TFLOPS[k["dtype"]], 4)}
     qbw = {}
+    exceed = None
     if not a.no_extras:
         log("quantize-pass bandwidth")
         qbw = quant_bandwidth(runner)
+        if not a.no_cpu_baseline:
+            log("FP8-instruction outputs against the stated tolerance (oracle on sampled rows)")
+            exceed = fp8_exceedance(runner, recipes + [r for r in next_recipes if r not in recipes])
 
     cpu = None
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline()
+        cpu = cpu_baseline(runner, per, pre, qbw)
 
+    sweeps = {}
+    if not a.no_extras and not a.no_sweep:
+        del runner, layers
+        torch.cuda.empty_cache()
+        for label, mname, tok in (("codonfm_32768_tokens", "codonfm", 32768), ("llama3_8b_8192_tokens", "llama3_8b", 8192)):
+            log(f"sweep {label}")
+            sweeps[label] = sweep(MODELS[mname], tok, recipes, dev, 1, max(2, a.steps // 2), max(2, a.prequant_iters // 2))
+
+    roof = {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 1),
+            "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "avg_launch_ms": round(avg_ms, 4), "launches": dk["launches"],
+            # HBM bytes per launch from the committed rocprofv3 counters (null once
+            # the kernel's sources differ from those the counters were taken on)
+            "traffic": round(traffic["bytes_per_launch"]) if traffic else None,
+            "traffic_fetch_write": ([round(traffic["fetch_bytes_per_launch"]),
+                                     round(traffic["write_bytes_per_launch"])] if traffic else None)}
+    if dom_name.startswith("gemm_nvfp4"):       # the 4-bit format's own peak, beside the fp16 instruction's
+        roof["format_peak_fp4"] = PEAK_TFLOPS["fp4"]
+        roof["frac_of_format_peak_fp4"] = round(achieved / PEAK_TFLOPS["fp4"], 4)
+    layer_desc = ("CodonFM-5B layer" if a.model == "codonfm" and cfg == MODELS["codonfm"] else
+                  f"{a.model}-shaped layer (hidden {cfg['hidden']}, intermediate {cfg['intermediate']}, "
+                  f"heads {cfg['heads']}/{cfg['kv_heads']} kv, gated {cfg['gated']})")
     line = {
         "metric": "TFLOPS & ms/GEMM over 12 layer shapes (M=15872) per recipe; quant GB/s",
         "value": round(total_flop / (ms_step * 1e-3) / 1e12, 2),
@@ -638,23 +1054,21 @@ def main():
         "vs_baseline": None,
         "dtype": "mixed: bf16 | fp8 (e4m3/e5m2) | nvfp4 decoded to fp16",
         "data": "synthetic (seeded N(0,1)+8 outlier channels x100, N(0,0.02^2), Student-t(3)x1e-3)",
-        "config": {"workload": "CodonFM-5B layer, 12 GEMMs (QKV/attn-out/MLP-up/MLP-down x "
-                               "Fprop/Dgrad/Wgrad), autocast, every recipe",
-                   "tokens": a.tokens, "hidden": 4096, "intermediate": 16384,
+        "config": {"workload": f"{layer_desc}, 12 GEMMs (QKV/attn-out/MLP-up/MLP-down x Fprop/Dgrad/Wgrad), "
+                               f"{'pre-quantized' if a.pre_quantize else 'autocast'}, every recipe",
+                   "tokens": tokens, "hidden": cfg["hidden"], "intermediate": cfg["intermediate"],
+                   "heads": cfg["heads"], "kv_heads": cfg["kv_heads"], "gated": cfg["gated"],
+                   "micro_batch": cfg["micro_batch"], "seq_len": cfg["seq_len"],
+                   "mode": "pre-quantized" if a.pre_quantize else "autocast",
                    "recipes": recipes, "gemm_out": "bf16", "parallelism": "single GPU"},
-        "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 1),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "avg_launch_ms": round(avg_ms, 4), "launches": dk["launches"],
-                     # HBM bytes per launch from the committed rocprofv3 counters (null once
-                     # the kernel's sources differ from those the counters were taken on)
-                     "traffic": round(traffic["bytes_per_launch"]) if traffic else None,
-                     "traffic_fetch_write": ([round(traffic["fetch_bytes_per_launch"]),
-                                              round(traffic["write_bytes_per_launch"])] if traffic else None)},
+        "roofline": roof,
         "per_recipe": per_recipe,
         "next_recipes": nxt,
         "model": model,
+        "sweep": sweeps,
         "quant_GBps": qbw,
         "epilogue_amax": epi,
+        "fp8_tolerance_exceedance": exceed,
         "gpu_clock": clock.summary(),
         "cpu_baseline": cpu,
     }

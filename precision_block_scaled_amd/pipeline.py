@@ -125,6 +125,11 @@ class DelayedState:
         pbs_delayed_init(self.buf, hist_len, stream)
 
     @property
+    def scale_inv(self):
+        """The state's scale_inv word as a one-element device tensor (a view)."""
+        return self.buf[4:8].view(torch.float32)
+
+    @property
     def scale_ptr(self):
         return pbs_delayed_scale(self.buf)
 
@@ -151,53 +156,49 @@ class Workspace:
         return t
 
 
-def quantize(recipe, x, src, orient, pass_, state=None, out=None, ws=None, stream=None, known_amax=None):
-    """Quantize bf16 tensor ``x`` [R, C] for use as the ``src`` operand of ``pass_``.
+def _copy_scalar(dst, src, stream=None):
+    """Stream-ordered device-to-device copy of one fp32 (no arithmetic)."""
+    if stream is None:
+        dst.copy_(src)
+        return
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream)
+    with torch.cuda.stream(stream):
+        dst.copy_(src)
 
-    Returns a QTensor whose stored shape is [R, C] (row) or [C, R] (col).
-    ``out`` may be a QTensor from an earlier call with the same shape, reused
-    in place.  ``state`` is a DelayedState for the delayed recipe.
-    ``known_amax`` (a device fp32 of one element holding max |x|, e.g. from
-    the epilogue of the GEMM that produced x) replaces the amax pass of the
-    per-tensor current-scaling and NVFP4 recipes; not with the Hadamard
-    transform, whose maximum is taken over the transformed values.
-    """
+
+def _new_scalars(dev):
+    return torch.zeros(3, dtype=torch.float32, device=dev)   # amax, scale, scale_inv
+
+
+def _cast_into(recipe, x, src, pass_, rmask, bufs, scal, w2d, state, stream, known_amax):
+    """The amax / scale / cast calls of one recipe into the copies `bufs`
+    (row codes, row scales, col codes, col scales; unused ones None).
+    Returns the device tensor scale_inv the copies carry (or None)."""
     R, C = x.shape
-    dev = x.device
-    rows, cols = (R, C) if orient == "row" else (C, R)
     fmt = fmt_for(recipe, src)
-    if recipe == "bf16":
-        if orient != "row":
-            raise ValueError("bf16 operands are consumed in natural storage")
-        return QTensor("bf16", PBS_FMT_BF16, R, C, x)
-    w2d = src in TWO_D.get(recipe, ())
-    if out is None:
-        codes, sc = _empty_copy(recipe, rows, cols, w2d, dev)
-        scal = torch.zeros(3, dtype=torch.float32, device=dev)   # amax, scale, scale_inv
-        out = QTensor(recipe, fmt, rows, cols, codes, sc, scal[2:3], w2d)
-        out._scal = scal
-    scal = out._scal
-    rmask = PBS_ROW if orient == "row" else PBS_COL
-    row_c, row_s, col_c, col_s = ((out.codes, out.scales, None, None) if orient == "row"
-                                  else (None, None, out.codes, out.scales))
     rec = RECIPES[recipe]
+    row_c, row_s, col_c, col_s = bufs
     if recipe == "fp8_current":
         am = known_amax if known_amax is not None else scal[0:1]
         if known_amax is None:
             pbs_amax(x, R, C, 0, 0, am, stream)
         pbs_scale_from_amax(am, FMAX[fmt], scal[1:2], scal[2:3], stream)
         pbs_cast(rec, x, R, C, fmt, rmask, 0, 0, 0, scal[1:2], None, row_c, row_s, col_c, col_s, stream)
-        out.tensor_scale_inv = scal[2:3]
-    elif recipe == "fp8_delayed":
+        return scal[2:3]
+    if recipe == "fp8_delayed":
         if state is None:
             raise ValueError("delayed scaling needs a DelayedState")
         pbs_cast(rec, x, R, C, fmt, rmask, 0, 0, 0, state.scale_ptr, state.amax, row_c, row_s,
                  col_c, col_s, stream)
-        out.tensor_scale_inv = state.scale_inv_ptr
-    elif recipe in SUBCHANNEL + ("mxfp8", "fp8_channel", "fp8_block128_pow2"):
-        pbs_cast(rec, x, R, C, fmt, rmask, int(w2d), 0, 0, None, None, row_c, row_s, col_c, col_s,
-                 stream)
-    elif recipe == "nvfp4":
+        # the copy keeps the scale it was cast with: a stream-ordered 4-byte
+        # device copy of the state's scale_inv, which later updates replace
+        _copy_scalar(scal[2:3], state.scale_inv, stream)
+        return scal[2:3]
+    if recipe in SUBCHANNEL + ("mxfp8", "fp8_channel", "fp8_block128_pow2"):
+        pbs_cast(rec, x, R, C, fmt, rmask, int(w2d), 0, 0, None, None, row_c, row_s, col_c, col_s, stream)
+        return None
+    if recipe == "nvfp4":
         rht = pass_ == "wgrad"
         flags = (PBS_FLAG_RHT16 if rht else 0) | (PBS_FLAG_SR if src == "dy" else 0)
         if known_amax is not None and rht:
@@ -211,17 +212,73 @@ def quantize(recipe, x, src, orient, pass_, state=None, out=None, ws=None, strea
             raise ValueError("one seed drives both the RHT signs and SR")
         pbs_cast(rec, x, R, C, fmt, rmask, int(w2d), flags, seed, scal[1:2], None, row_c, row_s,
                  col_c, col_s, stream)
-        out.tensor_scale_inv = scal[2:3]
-    elif recipe == "mxfp4":
+        return scal[2:3]
+    if recipe == "mxfp4":
         flags = (PBS_FLAG_RHT16 if pass_ == "wgrad" else 0) | (PBS_FLAG_SR if src == "dy" else 0)
         if flags == (PBS_FLAG_RHT16 | PBS_FLAG_SR) and RHT_SEED != SR_SEED:
             raise ValueError("one seed drives both the RHT signs and SR")
         pbs_cast(rec, x, R, C, fmt, rmask, 0, flags, SR_SEED if src == "dy" else RHT_SEED, None, None,
                  row_c, row_s, col_c, col_s, stream)
-        out.tensor_scale_inv = None
-    else:
-        raise ValueError(recipe)
+        return None
+    raise ValueError(recipe)
+
+
+def quantize(recipe, x, src, orient, pass_, state=None, out=None, ws=None, stream=None, known_amax=None):
+    """Quantize bf16 tensor ``x`` [R, C] for use as the ``src`` operand of ``pass_``.
+
+    Returns a QTensor whose stored shape is [R, C] (row) or [C, R] (col).
+    ``out`` may be a QTensor from an earlier call with the same shape, reused
+    in place.  ``state`` is a DelayedState for the delayed recipe.
+    ``known_amax`` (a device fp32 of one element holding max |x|, e.g. from
+    the epilogue of the GEMM that produced x) replaces the amax pass of the
+    per-tensor current-scaling and NVFP4 recipes; not with the Hadamard
+    transform, whose maximum is taken over the transformed values.
+    """
+    R, C = x.shape
+    rows, cols = (R, C) if orient == "row" else (C, R)
+    if recipe == "bf16":
+        if orient != "row":
+            raise ValueError("bf16 operands are consumed in natural storage")
+        return QTensor("bf16", PBS_FMT_BF16, R, C, x)
+    w2d = src in TWO_D.get(recipe, ())
+    if out is None:
+        codes, sc = _empty_copy(recipe, rows, cols, w2d, x.device)
+        scal = _new_scalars(x.device)
+        out = QTensor(recipe, fmt_for(recipe, src), rows, cols, codes, sc, scal[2:3], w2d)
+        out._scal = scal
+    bufs = ((out.codes, out.scales, None, None) if orient == "row" else (None, None, out.codes, out.scales))
+    rmask = PBS_ROW if orient == "row" else PBS_COL
+    out.tensor_scale_inv = _cast_into(recipe, x, src, pass_, rmask, bufs, out._scal, w2d, state, stream,
+                                      known_amax)
     return out
+
+
+def quantize_both(recipe, x, src, state=None, outs=None, stream=None, known_amax=None):
+    """Row and col copies of bf16 ``x`` [R, C] from one read of x (pbs_cast
+    with both orientations), for a tensor whose two copies get the same
+    treatment: every recipe's weights, and the activations and gradients of
+    every recipe but the 4-bit ones (whose col copies take the Hadamard
+    transform, and whose gradients round stochastically).  Returns
+    (row QTensor [R, C], col QTensor [C, R]); ``outs`` may be such a pair,
+    reused in place."""
+    if recipe == "bf16":
+        raise ValueError("bf16 operands are consumed in natural storage")
+    if recipe in ("nvfp4", "mxfp4") and src != "w":
+        raise ValueError("the 4-bit recipes' activation and gradient copies differ (Hadamard, SR)")
+    R, C = x.shape
+    w2d = src in TWO_D.get(recipe, ())
+    if outs is None:
+        rc, rs = _empty_copy(recipe, R, C, w2d, x.device)
+        cc, cs = _empty_copy(recipe, C, R, w2d, x.device)
+        scal = _new_scalars(x.device)
+        fmt = fmt_for(recipe, src)
+        outs = (QTensor(recipe, fmt, R, C, rc, rs, scal[2:3], w2d), QTensor(recipe, fmt, C, R, cc, cs, scal[2:3], w2d))
+        outs[0]._scal = outs[1]._scal = scal
+    row, col = outs
+    tsi = _cast_into(recipe, x, src, "fprop", PBS_ROW | PBS_COL, (row.codes, row.scales, col.codes, col.scales),
+                     row._scal, w2d, state, stream, known_amax)
+    row.tensor_scale_inv = col.tensor_scale_inv = tsi
+    return row, col
 
 
 def gemm(recipe, pass_, A, B, M, N, K, out_dtype=torch.bfloat16, C=None, stream=None, c_amax=None):
