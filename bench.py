@@ -327,6 +327,12 @@ def quant_bandwidth(runner, iters=20):
         # copy); the col copy reads x twice (column maxima, then the cast)
         ("fp8_channel_cast_row", "fp8_channel", "x", "row", "fprop", 2 + 1 + 4 / 16384),
         ("fp8_channel_cast_col", "fp8_channel", "x", "col", "wgrad", 2 + 1 + 4 / 15872),
+        # both copies from one read (the layer-autocast casts): bf16 read once,
+        # two copies written
+        ("fp8_tensor_cast_rowcol", "fp8_current", "x", "both", "fprop", 2 + 2 * 1.0),
+        ("fp8_block128_cast_rowcol", "fp8_block128", "x", "both", "fprop", 2 + 2 * (1 + 4 / 128)),
+        ("mxfp8_cast_rowcol", "mxfp8", "x", "both", "fprop", 2 + 2 * (1 + 1 / 32)),
+        ("fp8_tensor_cast_col", "fp8_current", "x", "col", "wgrad", 3.0),
     ]
     res = {}
     P = runner.P
@@ -349,12 +355,18 @@ def quant_bandwidth(runner, iters=20):
     res["amax"] = {"ms": round(ms, 4), "GBps": round(2.0 * n / ms / 1e6, 1)}
     for label, r, src, orient, p, bpe in cases:
         t = {"x": x, "dy": dy}[src]
-        out = PL.quantize(r, t, src, orient, p)    # allocate + warm
         rows, cols = t.shape
         rec = PL.RECIPES[r]
-        rmask = P.PBS_ROW if orient == "row" else P.PBS_COL
-        rc, rs, cc, cs = ((out.codes, out.scales, None, None) if orient == "row"
-                          else (None, None, out.codes, out.scales))
+        if orient == "both":
+            rq, cq = PL.quantize_both(r, t, src)    # allocate + warm
+            out = rq
+            rmask = P.PBS_ROW | P.PBS_COL
+            rc, rs, cc, cs = rq.codes, rq.scales, cq.codes, cq.scales
+        else:
+            out = PL.quantize(r, t, src, orient, p)    # allocate + warm
+            rmask = P.PBS_ROW if orient == "row" else P.PBS_COL
+            rc, rs, cc, cs = ((out.codes, out.scales, None, None) if orient == "row"
+                              else (None, None, out.codes, out.scales))
         flags = 0
         scale = None
         if r in ("nvfp4", "mxfp4"):

@@ -221,9 +221,9 @@ float* pbs_delayed_scale_inv(void* state); /* device address of `scale_inv` */
  *    it twice (column maxima, then the cast) and uses col_scales as the
  *    running maxima in between.  `scale` unused.
  *  Outputs for an orientation not in orient_mask may be NULL.
- *  2D-block casts (weight_2d = 1) and two-copy casts (orient_mask =
- *  PBS_ROW | PBS_COL) take at most 65535 x 128 rows (else PBS_ERR_SHAPE);
- *  single-copy 1D casts have no such limit.
+ *  2D-block casts (weight_2d = 1) and two-copy casts with stochastic
+ *  rounding take at most 65535 x 128 rows (else PBS_ERR_SHAPE); other 1D
+ *  casts, two-copy ones included, have no such limit.
  * ------------------------------------------------------------------- */
 pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t cols,
                     pbs_format fmt, int orient_mask, int weight_2d, int flags,

@@ -1,12 +1,14 @@
 // Quantize (cast) kernels for every recipe.
 //
-// Three kernel templates, each instantiated per recipe:
+// Four kernel templates, each instantiated per recipe:
 //   * cast_row_kernel: the row copy with 1D blocks (every GEMM operand but
 //     2D-blocked weights): a lane owns 16-value segments, no LDS;
-//   * cast_col_kernel: the transposed copy with 1D blocks, through a
-//     256 x 64 tile in LDS;
-//   * cast_tile_kernel: 2D weight blocks and casts that produce both copies
-//     from one read.  A workgroup of 128 threads stages a 128 x 128 tile of
+//   * cast_rc_kernel: the transposed (col) copy with 1D blocks, alone or
+//     with the row copy from the same read, through a 256 x 128 tile in LDS;
+//   * cast_col_kernel: the col copy with the Hadamard transform or
+//     stochastic rounding, through a 256 x 64 tile in LDS;
+//   * cast_tile_kernel: 2D weight blocks, and both copies from one read
+//     with stochastic rounding.  A workgroup of 128 threads stages a 128 x 128 tile of
 //     the bf16 input in LDS, then thread t quantizes row t of the tile
 //     (row copy, blocks along the columns) and/or column t (col copy, written
 //     as row t of the transposed output), so every 1D block (16, 32 or 128
@@ -785,6 +787,233 @@ __global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Col copy, alone or with the row copy from the same read, for 1D blocks
+// without the Hadamard transform or stochastic rounding.  A workgroup
+// stages a 256-row x 128-column tile of x in LDS (two 64-column halves laid
+// out as cast_col_kernel's tile, so the column reads stay conflict-free);
+// every row of the tile is read as one 256-byte piece (a read probe of this
+// pattern streams faster than 128-byte pieces).  Fill: lane ch = t % 16
+// holds 8 values of columns 8 ch .. 8 ch + 7 of rows t / 16 + 16 i; with
+// ROW it quantizes them on the spot -- the lanes of one row piece are 16
+// neighbouring lanes, so a block of 16, 32 or 128 values is 2, 4 or 16 lanes
+// -- and stores the row copy's codes (16 lanes write 128 contiguous bytes).
+// Then the col copy as in cast_col_kernel, once per half.
+// ---------------------------------------------------------------------------
+// The 256 x 128 tile (two halves) with a grid of at most 1024 workgroups:
+// 64-column tiles made the two-copy cast 35% slower (8 lanes per 128-byte
+// row piece of the row copy), 512 or 2048 workgroups no faster.
+constexpr int RC_NH = 2;
+constexpr int RC_GRID = 1024;
+
+// Quantize 8 row values v (fp32) held by a lane, with the row block spread
+// over 2 (NVFP4), 4 (MX) or 16 (1x128) neighbouring lanes; writes the codes
+// (8 bytes, or 4 for E2M1) and, from the block's first lane, its scale.
+template <int RECIPE, int FMT>
+__device__ __forceinline__ void quantize_row8(const float* v, uint32_t mbits, float tscale, bool valid, int ch,
+                                              uint8_t* codes, uint8_t* sc8, float* sc32) {
+  if (RECIPE == R_NV || RECIPE == R_MX4) {
+    uint32_t w;
+    bool writer;
+    uint32_t scode;
+    if (RECIPE == R_NV) {
+      const uint32_t m = group_max<2>(mbits);
+      const float S = tscale;
+      scode = enc_e4m3((__uint_as_float(m) / 6.0f) * S);
+      const float d = dec_e4m3_pos(scode);
+      if (d == 0.0f) {
+        w = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w |= ((__float_as_uint(v[i]) >> 28) & 0x8u) << (4 * i);
+      } else {
+        float e_b = S / d;
+        if (__float_as_uint(e_b) == 0x7F800000u) e_b = 3.40282346638528859812e+38f;
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = v[i] * e_b;
+        w = hw_fp4x8(x);
+      }
+      writer = (ch & 1) == 0;
+    } else {
+      scode = mx4_e8m0_from_f32_amax(group_max<4>(mbits));
+      const float s = mx_inv_scale(scode);
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = v[i] * s;
+      w = hw_fp4x8(x);
+      writer = (ch & 3) == 0;
+    }
+    if (valid) {
+      *(uint32_t*)codes = w;
+      if (writer) *sc8 = (uint8_t)scode;
+    }
+    return;
+  }
+  float s = tscale;
+  bool writer = false;
+  uint32_t word = 0;
+  if (RECIPE == R_MX) {
+    const uint32_t c = mx_e8m0_from_bf16_amax(group_max<4>(mbits) >> 16);
+    s = mx_inv_scale(c);
+    writer = (ch & 3) == 0;
+    word = c;
+  } else if (RECIPE == R_BLOCK128) {
+    s = scale_from_amax(__uint_as_float(group_max<16>(mbits)), 448.0f);
+    writer = ch == 0;
+  } else if (RECIPE == R_B128P2) {
+    const uint32_t c = mx_e8m0_from_bf16_amax(group_max<16>(mbits) >> 16);
+    s = mx_inv_scale(c);
+    writer = ch == 0;
+    word = c * 0x01010101u;
+  }
+  uint2 o;
+  o.x = hw_fp8x4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+  o.y = hw_fp8x4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+  if (valid) {
+    *(uint2*)codes = o;
+    if (writer) {
+      if (RECIPE == R_MX) *sc8 = (uint8_t)word;
+      else if (RECIPE == R_BLOCK128) *sc32 = 1.0f / s;
+      else if (RECIPE == R_B128P2) *(uint32_t*)sc32 = word;
+    }
+  }
+}
+
+template <int RECIPE, int FMT, bool ROW, bool AMAX, int NH>
+__global__ __launch_bounds__(256) void cast_rc_kernel(CastArgs a) {
+  static_assert(NH == 1 || NH == 2, "one or two 64-column halves");
+  constexpr int TC = 64 * NH;               // tile columns
+  constexpr int LPR = 8 * NH;               // lanes per row piece
+  constexpr int RPP = 256 / LPR;            // rows per fill pass
+  constexpr int NP = CT_R / RPP;            // fill passes (loads per lane)
+  __shared__ __align__(16) uint8_t tile[NH * CT_R * CT_PITCH];
+  const int t = threadIdx.x;
+  float tscale = 0.0f;
+  if (RECIPE == R_TENSOR || RECIPE == R_NV) tscale = *a.scale;
+  constexpr bool E2M1 = RECIPE == R_NV || RECIPE == R_MX4;
+  const int64_t gx = (a.C + TC - 1) / TC;
+  const int64_t ntiles = gx * ((a.R + CT_R - 1) / CT_R);
+  const int ch = t % LPR;
+  const int half = ch >> 3, c8 = ch & 7;
+  uint32_t amx = 0;
+  // The workgroup walks tiles tl, tl + gridDim.x, ...; the loads of the next
+  // tile are issued before the col phase of the current one, so they are in
+  // flight while it computes.
+  uint4 v[NP];
+  auto issue = [&](int64_t tl) {
+    const int64_t r0 = (tl / gx) * CT_R, c0 = (tl % gx) * TC;
+    const int rlim = (int)min((int64_t)CT_R, a.R - r0);
+    const bool cvalid = ch * 8 < (int)min((int64_t)TC, a.C - c0);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int row = t / LPR + RPP * i;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (row < rlim && cvalid) v[i] = ld_nt16(a.x + (r0 + row) * a.C + c0 + ch * 8);
+    }
+  };
+  if ((int64_t)blockIdx.x < ntiles) issue(blockIdx.x);
+  for (int64_t tl = blockIdx.x; tl < ntiles; tl += gridDim.x) {
+    const int64_t r0 = (tl / gx) * CT_R, c0 = (tl % gx) * TC;
+    const int rlim = (int)min((int64_t)CT_R, a.R - r0);
+    const int clim = (int)min((int64_t)TC, a.C - c0);
+    // fill: LPR lanes per row piece (8 values each), RPP rows per pass
+    {
+      const bool cvalid = ch * 8 < clim;
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int row = t / LPR + RPP * i;
+        uint8_t* th = tile + half * (CT_R * CT_PITCH);
+        const int g = (2 * c8) ^ ((row >> 4) & 14);
+        *(uint2*)(th + row * CT_PITCH + g * 8) = make_uint2(v[i].x, v[i].y);
+        *(uint2*)(th + row * CT_PITCH + g * 8 + 8) = make_uint2(v[i].z, v[i].w);
+        const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        u16x2 m2 = {0, 0};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w4[k] & 0x7FFF7FFFu));
+        const uint32_t m16 = m2.x > m2.y ? m2.x : m2.y;
+        if (AMAX) amx = amx > m16 ? amx : m16;
+        if (ROW) {
+          float f[8];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            f[2 * k] = __uint_as_float(w4[k] << 16);
+            f[2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
+          }
+          const bool valid = row < rlim && cvalid;
+          const int64_t gr = r0 + row, gcol = c0 + ch * 8;
+          uint8_t* codes = E2M1 ? a.row_codes + gr * (a.C / 2) + gcol / 2 : a.row_codes + gr * a.C + gcol;
+          uint8_t* sc8 = nullptr;
+          float* sc32 = nullptr;
+          if (RECIPE == R_MX || RECIPE == R_MX4) sc8 = (uint8_t*)a.row_scales + gr * (a.C / 32) + gcol / 32;
+          if (RECIPE == R_NV) sc8 = (uint8_t*)a.row_scales + gr * (a.C / 16) + gcol / 16;
+          if (RECIPE == R_BLOCK128 || RECIPE == R_B128P2) sc32 = (float*)a.row_scales + gr * (a.C / 128) + gcol / 128;
+          quantize_row8<RECIPE, FMT>(f, m16 << 16, tscale, valid, ch, codes, sc8, sc32);
+        }
+      }
+    }
+    // the tile's LDS writes are visible to every wave (the global stores of
+    // the row copy need not have landed)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (tl + (int64_t)gridDim.x < ntiles) issue(tl + gridDim.x);
+
+    // col copy: thread t takes rows 16 (t % 16) .. + 15 of 4 columns of each half
+    const int rs = t & 15, cg = t >> 4;
+#pragma unroll
+    for (int half = 0; half < NH; ++half) {
+      const uint8_t* th = tile + half * (CT_R * CT_PITCH);
+      uint2 wv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 16 * rs + i;
+        const int g = cg ^ ((row >> 4) & 14);
+        wv[i] = *(const uint2*)(th + row * CT_PITCH + g * 8);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float cv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t word = (c < 2) ? wv[i].x : wv[i].y;
+          cv[i] = __uint_as_float((c & 1) ? (word & 0xFFFF0000u) : (word << 16));
+        }
+        const int col = 64 * half + 4 * cg + c;
+        const bool valid = (16 * rs < rlim) && (col < clim);
+        uint32_t mbits = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t x = __float_as_uint(cv[i]) & 0x7FFFFFFFu;
+          mbits = mbits > x ? mbits : x;
+        }
+        const int64_t gc = c0 + col, gr = r0 + 16 * rs;
+        uint8_t* codes = E2M1 ? a.col_codes + gc * (a.R / 2) + gr / 2 : a.col_codes + gc * a.R + gr;
+        uint8_t* sc8 = nullptr;
+        float* sc32 = nullptr;
+        bool writer = true;
+        if (RECIPE == R_MX || RECIPE == R_MX4) {
+          sc8 = (uint8_t*)a.col_scales + gc * (a.R / 32) + gr / 32;
+          writer = (rs & 1) == 0;
+        } else if (RECIPE == R_NV) {
+          sc8 = (uint8_t*)a.col_scales + gc * (a.R / 16) + gr / 16;
+        } else if (RECIPE == R_BLOCK128 || RECIPE == R_B128P2) {
+          sc32 = (float*)a.col_scales + gc * (a.R / 128) + gr / 128;
+          writer = (rs & 7) == 0;
+        }
+        quantize_segment<RECIPE, FMT, false>(cv, mbits, tscale, valid, codes, sc8, sc32, writer, nullptr);
+      }
+    }
+    // every LDS read of this tile is done before the next fill
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  if (AMAX) {
+    __shared__ uint32_t s_part[4];
+    wg_amax_fold(amx << 16, a.amax_out, s_part);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Channel-wise FP8: one scale per row of the copy.
 //
 // Row copy: a team of T lanes (one wave, or the whole 256-thread workgroup
@@ -999,14 +1228,28 @@ typedef void (*cast_row_fn)(CastArgs, int64_t);
 // Kernel choice: single-orientation casts with 1D blocks take the row / col
 // kernels; 2D weight blocks and two-copy casts take the tile kernel.
 struct CastPick {
-  cast_fn tile = nullptr, col = nullptr;
+  cast_fn tile = nullptr, col = nullptr, rc = nullptr;
   cast_row_fn row = nullptr;
+  int rc_cols = 0;                          // tile width of the row+col kernel
 };
 
+// 1D blocks: the row kernel for a row copy; the 256 x 128 row+col kernel for
+// a plain col copy and for both copies from one read; the 256 x 64 col
+// kernel for col copies with the Hadamard transform or stochastic rounding;
+// the 128 x 128 tile kernel for 2D blocks and two stochastically rounded
+// copies.
 template <int RECIPE, int FMT, bool W2D, bool RHT, bool SR, bool AMAX>
 static CastPick pick_orient(int mask) {
   CastPick p;
   if (!W2D && mask == PBS_ROW && !RHT) p.row = cast_row_kernel<RECIPE, FMT, SR, AMAX>;
+  else if (!W2D && !RHT && !SR && mask == PBS_COL) {
+    p.rc = cast_rc_kernel<RECIPE, FMT, false, AMAX, RC_NH>;
+    p.rc_cols = 64 * RC_NH;
+  } else if (!W2D && !RHT && !SR && mask == (PBS_ROW | PBS_COL)) {   // a 1x128 row block needs 128 columns
+    constexpr int nh = (RECIPE == R_BLOCK128 || RECIPE == R_B128P2) ? 2 : RC_NH;
+    p.rc = cast_rc_kernel<RECIPE, FMT, true, AMAX, nh>;
+    p.rc_cols = 64 * nh;
+  }
   else if (!W2D && mask == PBS_COL) p.col = cast_col_kernel<RECIPE, FMT, RHT, SR, AMAX>;
   else if (mask == PBS_ROW) p.tile = cast_tile_kernel<RECIPE, FMT, true, false, W2D, false, SR, AMAX>;
   else if (mask == PBS_COL) p.tile = cast_tile_kernel<RECIPE, FMT, false, true, W2D, RHT, SR, AMAX>;
@@ -1179,6 +1422,15 @@ static pbs_status cast_impl(pbs_recipe recipe, const void* x_bf16, int64_t rows,
     log_dispatch("%s_row recipe=%d fmt=%d flags=%d rows=%lld cols=%lld grid=%u", name, (int)recipe, (int)fmt,
                  flags, (long long)rows, (long long)cols, grid);
     hipLaunchKernelGGL(fn.row, dim3(grid), dim3(256), 0, stream, a, nseg);
+  } else if (fn.rc) {
+    // a 1D grid of at most RC_GRID workgroups walking the 256 x 128 tiles
+    // (each prefetches its next tile; with fused amax at most that many
+    // same-address atomics end the pass)
+    const int64_t ntiles = ceil_div(cols, fn.rc_cols) * ceil_div(rows, CT_R);
+    const dim3 grid((unsigned)std::min<int64_t>(ntiles, RC_GRID), 1);
+    log_dispatch("%s_%s recipe=%d fmt=%d rows=%lld cols=%lld grid=%u", name, row ? "rowcol" : "col", (int)recipe,
+                 (int)fmt, (long long)rows, (long long)cols, grid.x);
+    hipLaunchKernelGGL(fn.rc, grid, dim3(256), 0, stream, a);
   } else if (fn.col) {
     // a 1D grid over the tiles in row-major tile order, one tile per
     // workgroup; with fused amax at most 1024 workgroups walk the tiles (one
