@@ -30,9 +30,9 @@ checks what it can compute exactly:
 * the GEMM epilogue's max |C| (pbs_gemm_amax) against the amax kernel's pass
   over the whole stored C.
 
-How far the FP8-instruction outputs fall outside the stated 1e-5 term
-alone is collected per case; with PBS_REPORT_DIR set, the session writes it
-to fp8_exceedance.json there.
+How far the FP8-instruction outputs fall outside the stated bound alone
+(1e-5 sum|ab| + 1 bf16 ulp) is collected per case; with PBS_REPORT_DIR set,
+the session writes it to fp8_exceedance.json there.
 
 The delayed-scaling trajectory (16 warm-up steps of tensors whose amax
 drifts x1.1 per step, then Dgrad and Wgrad at step 16 with E5M2 gradients)
@@ -52,7 +52,7 @@ import precision_block_scaled_amd as P
 from precision_block_scaled_amd import pipeline as PL
 from oracle import recipes as R
 from oracle.formats import E4M3, E5M2, bf16_to_f32
-from oracle.gemm_ref import REL_TOL, check_gemm, fp8_dot_unit_bound
+from oracle.gemm_ref import check_gemm, fp8_dot_unit_bound
 from oracle.passes import BLOCK128_2D, operand_roles
 from oracle.philox import philox_word0_for_index
 from tests.fp8_dot_unit import dot_unit_gemm, to_bf16_rne
@@ -316,10 +316,10 @@ def check_outputs(recipe, C, qa, qb, key):
         i = tuple(np.argwhere(~ok)[0])
         out.append(f"GEMM {(~ok).sum()} of {ok.size} outside bound; got {c[i]} want {cref[i]} tol {tol[i]}")
     if recipe in FP8_MFMA:
-        ratio = err / np.maximum(REL_TOL * bnd, 1e-300)
-        EXCEEDANCE[key] = {"outputs": int(c.size), "max_err_over_1e-5_sum_abs": float(ratio.max()),
-                           "outputs_over_stated_term": int((err > REL_TOL * bnd + 0).sum()),
-                           "outputs_over_stated_term_plus_bf16_ulp": int((~check_gemm(c, cref, bnd, True)[0]).sum())}
+        # the stated bound for bf16 output: 1e-5 sum|ab| + one bf16 ulp of C_ref
+        ok0, tol0, _ = check_gemm(c, cref, bnd, True)
+        EXCEEDANCE[key] = {"outputs": int(c.size), "max_err_over_stated_bound": float((err / tol0).max()),
+                           "outputs_over_stated_bound": int((~ok0).sum())}
     if recipe in UNSCALED_FP8:
         chunks = np.array_split(np.arange(qa.raw.shape[0]), min(THREADS, qa.raw.shape[0]))
         with cf.ThreadPoolExecutor(THREADS) as ex:
