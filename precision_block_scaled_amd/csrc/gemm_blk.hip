@@ -235,21 +235,21 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_blk_kernel(GemmArgs g) {
   // raw scale words of the stage (read by inline assembly): a_scale of the
   // lane's row in each row tile, and b_scale -- one word for 128x128 weight
   // blocks, else the lane's 16 columns of each column tile.
-  i32x8 fb[2][2], fa[2];
+  i32x8 fb[2][2], fa[2][2];
   uint32_t asw[4];
   i32x4 bsw[2][4];
-  float fac[4];          // per row tile: a_scale (times the weight scale for 128x128 blocks)
-  float bsv[2][16];      // 1x128 B blocks: b_scale of the lane's columns
+  float fac[4] = {};     // per row tile: a_scale (times the weight scale for 128x128 blocks)
+  float bsv[2][16] = {}; // 1x128 B blocks: b_scale of the lane's columns
   typedef __attribute__((address_space(3))) const float* lds_f32_p;
   auto read_fb = [&](int kt, int j) {
     const uint8_t* lbq = tB(kt % KB_NSTAGE) + wn * 8192;
 #pragma unroll
     for (int h = 0; h < 2; ++h) fb[j][h] = read2(lbq + j * 4096, lb, ((uint32_t)(((4 * h) ^ (2 * j)) << 4)) ^ bx);
   };
-  auto read_fa = [&](int kt, int i) {
+  auto read_fa = [&](int kt, int i) {       // into fa[i & 1]
     const uint8_t* la = tA(kt % KB_NSTAGE) + wm * 16384;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) fa[h] = read2(la + i * 4096, lb, (uint32_t)(((4 * h) ^ (2 * i)) << 4));
+    for (int h = 0; h < 2; ++h) fa[i & 1][h] = read2(la + i * 4096, lb, (uint32_t)(((4 * h) ^ (2 * i)) << 4));
   };
   auto load_scales = [&](int kt) {
     const lds_f32_p pa_ = (lds_f32_p)(ringA(kt % KB_NSLOT) + wm * 128 + lr);
@@ -316,17 +316,29 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_blk_kernel(GemmArgs g) {
     load_scales(0);
   }
 
+  // Partial products of the two tiles in flight; tile 7 of a stage is
+  // folded during tile 0 of the next (zeros before the first stage).
+  f32x16 part[2] = {};
+  // fold values r0 .. r0 + 7 of tile tt with the current stage's scales
+  auto fold8 = [&](int tt, int r0) {
+    const int i = tt >> 1, j = tt & 1;
+#pragma unroll
+    for (int r = r0; r < r0 + 8; ++r)
+      acc[i][j][r] = __builtin_fmaf(part[tt & 1][r], B2D ? fac[i] : fac[i] * bsv[j][r], acc[i][j][r]);
+  };
+
   // One K stage.  MORE: stage kt + 2 exists and its tiles are loaded during
   // tiles 0-5 of this one; NEXT: stage kt + 1 exists (its scale words are
   // loaded here).  Tiles t = (i, j) = (t / 2, t % 2): tile t multiplies into
   // part[t % 2] while tile t - 1 is folded, acc += part * a_scale[m] *
-  // b_scale[n].  A fragments of row tile i + 1 are read once tile (i, 1) has
-  // issued.  After tile 5 every wave waits for the next stage's data and
-  // meets at a barrier (this stage's tile buffer is no longer read by then),
-  // so tiles 6-7 read the next stage's first operands and scale words as
-  // their registers free up, and the next stage starts without an LDS round
-  // trip.  The last two stages are peeled so that every stage is
-  // straight-line code and the fenced schedule holds.
+  // b_scale[n]; tile 0 folds the previous stage's tile 7 before this
+  // stage's scales replace that stage's.  A fragments of row tile i + 1 are
+  // read into the other buffer once tile (i, 0) has issued.  After tile 5
+  // every wave waits for the next stage's data and meets at a barrier (this
+  // stage's tile buffer is no longer read by then), so tiles 6-7 read the
+  // next stage's first operands as their registers free up, and the next
+  // stage starts without an LDS round trip.  The last two stages are peeled
+  // so that every stage is straight-line code and the fenced schedule holds.
   auto stage = [&](int kt, auto more_c, auto next_c) {
     constexpr bool MORE = decltype(more_c)::value;
     constexpr bool NEXT = decltype(next_c)::value;
@@ -335,14 +347,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_blk_kernel(GemmArgs g) {
       a_nx = load_word_untracked(pa + kt + 1);
       b_nx = load_word_untracked(pb + kt + 1);
     }
-    f32x16 part[2];
-    // fold values r0 .. r0 + 7 of tile tt
-    auto fold8 = [&](int tt, int r0) {
-      const int i = tt >> 1, j = tt & 1;
-#pragma unroll
-      for (int r = r0; r < r0 + 8; ++r)
-        acc[i][j][r] = __builtin_fmaf(part[tt & 1][r], B2D ? fac[i] : fac[i] * bsv[j][r], acc[i][j][r]);
-    };
     const f32x16 zero = {};
     // Each MFMA is followed by half a fold of the previous tile, so the
     // vector unit works while the matrix core does and the second MFMA of a
@@ -351,16 +355,17 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_blk_kernel(GemmArgs g) {
     for (int tt = 0; tt < 8; ++tt) {
       const int i = tt >> 1, j = tt & 1;
       // transposed tile: B rows are the instruction's rows, A rows its columns
-      part[tt & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][0], fa[0], zero, 0, 0, 0, 0, 0, 0);
+      part[tt & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][0], fa[i & 1][0], zero, 0, 0, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (tt == 0) finish_scales();
-      if (tt > 0) fold8(tt - 1, 0);
+      fold8((tt + 7) & 7, 0);
       if (MORE && tt < 6) issue_tile(kt + 2, 2 * tt);
       __builtin_amdgcn_sched_barrier(0);
-      part[tt & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][1], fa[1], part[tt & 1], 0, 0, 0, 0, 0, 0);
+      part[tt & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][1], fa[i & 1][1], part[tt & 1], 0, 0, 0, 0,
+                                                                     0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (tt > 0) fold8(tt - 1, 8);
-      if (j == 1 && i < 3) read_fa(kt, i + 1);
+      fold8((tt + 7) & 7, 8);
+      if (tt == 0) finish_scales();
+      if (j == 0 && i < 3) read_fa(kt, i + 1);     // the other buffer: row tile i - 1 is done
       if (MORE && tt < 6) issue_tile(kt + 2, 2 * tt + 1);
       if (tt == 5 && NEXT) {
         if (MORE) wait_vm_ahead();
@@ -368,22 +373,22 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_blk_kernel(GemmArgs g) {
         put_scales(kt + 1, a_nx, b_nx);
         barrier_lds();
       }
-      if (tt == 6 && NEXT) read_fb(kt + 1, 0);     // fb[0] is free once tile (3, 0) has issued
-      if (tt == 7 && NEXT) {                       // fa, fb[1] are free after tile (3, 1)
-        read_fb(kt + 1, 1);
+      if (tt == 6 && NEXT) {                       // fb[0] is free once tile (3, 0) has issued, fa[0]
+        read_fb(kt + 1, 0);                        // after row tile 2
         read_fa(kt + 1, 0);
       }
+      if (tt == 7 && NEXT) read_fb(kt + 1, 1);     // fb[1] is free after tile (3, 1)
       __builtin_amdgcn_sched_barrier(0);
     }
-    fold8(7, 0);
-    fold8(7, 8);
-    if (NEXT) load_scales(kt + 1);                 // every fold of this stage is done
+    if (NEXT) load_scales(kt + 1);                 // fac / bsv still hold this stage's scales
   };
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
   for (int kt = 0; kt < nk - 2; ++kt) stage(kt, T_{}, T_{});
   if (nk >= 2) stage(nk - 2, F_{}, T_{});
   stage(nk - 1, F_{}, F_{});
+  fold8(7, 0);
+  fold8(7, 8);
   __syncthreads();                                   // the epilogue reuses the tile buffers
   store_blk<OUT_BF16>(acc, g, smem, m0, n0, w, wm, wn, lane);
 }
