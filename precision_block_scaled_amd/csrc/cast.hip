@@ -1410,7 +1410,9 @@ static pbs_status cast_impl(pbs_recipe recipe, const void* x_bf16, int64_t rows,
       return set_error(PBS_ERR_INVALID_ARG, "pbs_cast: unknown recipe %d", (int)recipe);
   }
   PBS_REQUIRE(!fn.tile || ceil_div(rows, TILE) <= 65535, PBS_ERR_SHAPE,
-              "pbs_cast: 2D-block and two-copy casts take at most 65535 x 128 rows (got %lld)", (long long)rows);
+              "pbs_cast: 2D-block casts and two-copy casts with stochastic rounding take at most 65535 x 128 rows "
+              "(got %lld)",
+              (long long)rows);
   if (amax_out) hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)amax_out);
   if (rows == 0 || cols == 0) return check_launch("pbs_cast");
   if (fn.row) {

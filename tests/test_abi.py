@@ -75,11 +75,12 @@ def test_cast_validation_codes():
             FAKE, None, None, 0)
     _expect(1, c, P.PBS_RECIPE_FP8_BLOCK128_POW2, FAKE, 64, 128, P.PBS_FMT_E4M3, 1, 0, 0, 0, None, None, FAKE,
             FAKE + 2, None, None, 0)
-    # 2D-block and two-copy casts: at most 65535 tiles of 128 rows
+    # 2D-block casts and two-copy casts with stochastic rounding: at most 65535 tiles of 128 rows (the
+    # other two-copy casts walk their tiles in a persistent grid and pass validation at that height)
     _expect(2, c, P.PBS_RECIPE_FP8_BLOCK128, FAKE, 128 * 65536, 128, P.PBS_FMT_E4M3, 1, 1, 0, 0, None, None, FAKE,
             FAKE, None, None, 0)
-    _expect(2, c, P.PBS_RECIPE_MXFP8, FAKE, 128 * 65536, 128, P.PBS_FMT_E4M3, 3, 0, 0, 0, None, None, FAKE,
-            FAKE, FAKE, FAKE, 0)
+    _expect(2, c, P.PBS_RECIPE_NVFP4, FAKE, 128 * 65536, 128, P.PBS_FMT_E2M1, 3, 0, P.PBS_FLAG_SR, 0, FAKE, None,
+            FAKE, FAKE, FAKE, FAKE, 0)
     # per-tensor FP8 needs the scale
     _expect(1, c, P.PBS_RECIPE_FP8_CURRENT, FAKE, 64, 64, P.PBS_FMT_E4M3, 1, 0, 0, 0, None, None, FAKE,
             None, None, None, 0)
