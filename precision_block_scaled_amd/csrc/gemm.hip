@@ -940,6 +940,7 @@ static pbs_status gemm_impl(pbs_recipe recipe, pbs_layout layout, int64_t M, int
   g.c_amax = (uint32_t*)c_amax;
 
   gemm_fn fn = nullptr;
+  int nthr = NTHR;                     // threads per workgroup of the chosen kernel
   const char* name = "";
   const bool w2d = layout != PBS_WGRAD;     // weights carry 2D block scales
   switch (recipe) {
@@ -992,7 +993,8 @@ static pbs_status gemm_impl(pbs_recipe recipe, pbs_layout layout, int64_t M, int
       PBS_REQUIRE(K % 128 == 0, PBS_ERR_SHAPE, "pbs_gemm: FP8_BLOCK128 needs K %% 128 == 0");
       PBS_REQUIRE(!w2d || N % 128 == 0, PBS_ERR_SHAPE, "pbs_gemm: 128x128 weight blocks need N %% 128 == 0");
       g.lda = K; g.ldb = K;
-      g.tiles_n = (int)ceil_div(N, 128);          // gemm_blk.hip: 256 x 128 tiles
+      g.tiles_n = (int)ceil_div(N, BLK_BN);       // gemm_blk.hip: 256 x 256 tiles, 8 waves
+      nthr = BLK_THR;
       fn = blk_kernel_for(false, w2d, bf16_out);
       name = "gemm_fp8_block128";
       break;
@@ -1007,7 +1009,8 @@ static pbs_status gemm_impl(pbs_recipe recipe, pbs_layout layout, int64_t M, int
       PBS_REQUIRE(!two || (M % 128 == 0 && N % 128 == 0), PBS_ERR_SHAPE,
                   "pbs_gemm: 128x128 blocks on both operands need M and N %% 128 == 0");
       g.lda = K; g.ldb = K;
-      g.tiles_n = (int)ceil_div(N, 128);
+      g.tiles_n = (int)ceil_div(N, BLK_BN);
+      nthr = BLK_THR;
       fn = blk_kernel_for(two, two, bf16_out);
       name = two ? "gemm_fp8_block128_2d2d" : "gemm_fp8_block128_1d1d";
       break;
@@ -1081,7 +1084,7 @@ static pbs_status gemm_impl(pbs_recipe recipe, pbs_layout layout, int64_t M, int
   log_dispatch("%s layout=%d M=%lld N=%lld K=%lld out=%s tiles=%dx%d", name, (int)layout, (long long)M,
                (long long)N, (long long)K, bf16_out ? "bf16" : "f32", g.tiles_m, g.tiles_n);
   if (c_amax) hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(64), 0, stream, (uint32_t*)c_amax);
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(NTHR), 0, stream, g);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(nthr), 0, stream, g);
   return check_launch("pbs_gemm");
 }
 

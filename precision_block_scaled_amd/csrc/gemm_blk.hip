@@ -10,21 +10,25 @@
 // matrix instruction's E8M0 scale: every 128-long K block is multiplied on
 // the matrix cores into fresh registers (two v_mfma_f32_32x32x64_f8f6f4 per
 // 32x32 tile) and folded into the result by the vector unit, one fp32 FMA
-// per output value and block.  That fold, not the matrix core, bounds the
-// recipe unless it costs no more than the products it folds.
+// per output value and block.  Per wave and K block that is 16 MFMAs (1024
+// matrix-core cycles) against 128 FMAs (512 vector cycles), plus 128 scale
+// products for 1x128 B blocks.  The fold reads what the matrix core just
+// wrote, so one wave alone leaves the matrix core idle whenever its
+// instruction stream waits on that dependency, an LDS read or a barrier.
 //
-// So this kernel keeps everything the fold touches in VGPRs: a 256 x 128
-// output tile per workgroup, 4 waves of 128 x 64 (2 x 2), 128 accumulators
-// per lane, and the MFMAs write their partial products to VGPRs (this file
-// is built with -amdgpu-mfma-vgpr-form).  Per wave and K block: 16 MFMAs
-// (1024 matrix-core cycles) against 128 FMAs, plus 64 scale products for
-// 128x128 weight blocks (the wave's 64 columns share one weight scale) or
-// 128 for 1x128 Wgrad blocks.  The fold of tile t-1 runs while tile t
-// multiplies.
+// So every SIMD runs two waves: a 256 x 256 output tile per workgroup, 8
+// waves of 128 x 64 (2 along M x 4 along N), and while one wave folds or
+// waits the other's MFMAs run.  Each wave keeps everything the fold touches
+// in VGPRs -- 128 accumulators per lane, and the MFMAs write their partial
+// products to VGPRs (this file is built with -amdgpu-mfma-vgpr-form) -- in
+// the 256 registers two waves per SIMD leave it.  The fold of tile t-1 runs
+// while tile t multiplies.
 //
-// Staging: three LDS stage buffers of 48 KB (A 256 rows, B 128 rows, 128 B
-// each, swizzled as in the other GEMMs) and a 3-deep scale-row ring, loads
-// for stage k+2 spread over the MFMAs of stage k, one barrier per stage.
+// Staging: two LDS stage buffers of 64 KB (A and B, 256 rows x 128 B each,
+// swizzled as in the other GEMMs) and a 2-deep scale-row ring, all filled by
+// LDS-DMA.  The loads of stage k+2 are issued in the last two tiles of stage
+// k, as soon as every wave is done reading stage k's buffer, and waited for
+// in the middle of stage k+1.  One barrier per stage.
 #include "device.hpp"
 #include "gemm_common.hpp"
 #include "host.hpp"
@@ -33,20 +37,22 @@
 
 namespace pbs {
 
-constexpr int KB_BN = 128;                         // output columns per workgroup
-constexpr int KB_TB = KB_BN * ROWB;                // 16 KB of B per stage
-constexpr int KB_STAGE = TILEB + KB_TB;            // 48 KB per stage
-constexpr int KB_NSTAGE = 3;
+constexpr int KB_THR = BLK_THR;                     // 8 waves per workgroup
+constexpr int KB_NW = KB_THR / 64;
+constexpr int KB_BN = BLK_BN;                      // output columns per workgroup
+constexpr int KB_STAGE = 2 * TILEB;                // A and B: 64 KB per stage
+constexpr int KB_NSTAGE = 2;
 constexpr int KB_RING = KB_NSTAGE * KB_STAGE;      // scale ring after the stage buffers
-constexpr int KB_NSLOT = 3;
-constexpr int KB_SLOT = (BM + KB_BN + KB_BN) * 4;  // a_scale[256], b_scale[128], a sink for waves 2-3
-constexpr int KB_STG_BF16 = 272;                   // epilogue staging pitch, bf16 (256 rows)
-constexpr int KB_STG_F32 = 528;                    // epilogue staging pitch, fp32 (128 rows a pass)
-constexpr int KB_SMEM = cmax(KB_RING + KB_NSLOT * KB_SLOT, cmax(256 * KB_STG_BF16, 128 * KB_STG_F32));
-constexpr int KB_VM_TILES = 8 + 4;                 // tile loads per lane per stage: A, B
+constexpr int KB_NSLOT = 2;
+constexpr int KB_SLOT = (BM + KB_BN) * 4;          // a_scale[256], b_scale[256]
+constexpr int KB_STG_BF16 = 2 * KB_BN + 16;        // epilogue staging pitch in bytes, bf16 (256 rows)
+constexpr int KB_STG_F32 = 4 * KB_BN + 16;         // fp32 (128 rows a pass)
+constexpr int KB_SMEM = cmax(KB_RING + KB_NSLOT * KB_SLOT, cmax(BM * KB_STG_BF16, 128 * KB_STG_F32));
+static_assert(KB_SMEM <= 160 * 1024, "LDS");
 
-// B tile: 128 rows, 4 loads per lane; load i of wave w fills rows
-// 32 w + 8 i .. + 7 (same chunk ownership as Direct).
+// Tile loads: 256 rows, 4 loads per lane; load i of wave w (0-7) fills rows
+// 32 w + 8 i .. + 7; lane l owns row 32 w + 8 i + l / 8, physical chunk l % 8
+// (the logical chunk that the swizzle places there).
 struct Direct4 {
   const uint8_t* base;
   uint32_t off[4];
@@ -77,9 +83,11 @@ __device__ __forceinline__ void direct4_item(const Direct4& d, int kt, uint8_t* 
 // store) and every lane then writes 16 contiguous bytes of C.
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_blk(f32x16 (&acc)[4][2], const GemmArgs& g, uint8_t* smem, int m0, int n0,
-                                          int w, int wm, int wn, int lane) {
+                                          int wm, int wn, int lane) {
+  const int t = threadIdx.x;
   const int lr = lane & 31, lg = lane >> 5;
   const bool full = (m0 + BM <= g.M) && (n0 + KB_BN <= g.N);
+  uint32_t mx = 0;
   if constexpr (OUT_BF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -93,11 +101,10 @@ __device__ __forceinline__ void store_blk(f32x16 (&acc)[4][2], const GemmArgs& g
               make_uint2(pk_bf16(acc[i][j][4 * q], acc[i][j][4 * q + 1]), pk_bf16(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
         }
     __syncthreads();
-    const int ch = lane & 15;
-    uint32_t mx = 0;
+    const int ch = t & 31;                           // 16-byte chunk of a 512-byte row
 #pragma unroll 4
     for (int it = 0; it < 16; ++it) {
-      const int s = 64 * w + 4 * it + (lane >> 4);
+      const int s = 16 * it + (t >> 5);
       const uint4 val = *(const uint4*)(smem + s * KB_STG_BF16 + ch * 16);
       const int grow = m0 + s, gcol = n0 + ch * 8;
       if (full || (grow < g.M && gcol < g.N)) {
@@ -108,9 +115,7 @@ __device__ __forceinline__ void store_blk(f32x16 (&acc)[4][2], const GemmArgs& g
         }
       }
     }
-    if (g.c_amax) amax_fold_wg(mx, g.c_amax, smem);
   } else {
-    uint32_t mx = 0;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       if (wm == p) {
@@ -127,11 +132,12 @@ __device__ __forceinline__ void store_blk(f32x16 (&acc)[4][2], const GemmArgs& g
             }
       }
       __syncthreads();
+      const int ch = t & 63;                         // 16-byte chunk of a 1 KB row
 #pragma unroll 4
       for (int it = 0; it < 16; ++it) {
-        const int s = 32 * w + 2 * it + (lane >> 5);
-        const uint4 val = *(const uint4*)(smem + s * KB_STG_F32 + (lane & 31) * 16);
-        const int grow = m0 + 128 * p + s, gcol = n0 + (lane & 31) * 4;
+        const int s = 8 * it + (t >> 6);
+        const uint4 val = *(const uint4*)(smem + s * KB_STG_F32 + ch * 16);
+        const int grow = m0 + 128 * p + s, gcol = n0 + ch * 4;
         if (full || (grow < g.M && gcol < g.N)) {
           *(uint4*)((float*)g.C + (int64_t)grow * g.ldc + gcol) = val;
           if (g.c_amax) {
@@ -142,80 +148,62 @@ __device__ __forceinline__ void store_blk(f32x16 (&acc)[4][2], const GemmArgs& g
       }
       if (p == 0) __syncthreads();
     }
-    if (g.c_amax) amax_fold_wg(mx, g.c_amax, smem);
   }
+  if (g.c_amax) amax_fold_wg<KB_NW>(mx, g.c_amax, smem);
 }
 
-// Waits of a stage that loaded the tiles of the stage after next: first for
-// this lane's loads of the next stage and the scale words loaded at the start
-// of this one (the KB_VM_TILES tile loads issued after them may stay in
-// flight), later for its LDS writes before a plain s_barrier (a
-// __syncthreads() would also wait for the loads in flight).  LDS reads of
-// this stage have all been consumed by its MFMAs by then.
-__device__ __forceinline__ void wait_vm_ahead() { asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); }
+// The wait in the middle of a stage for this lane's loads of the next stage
+// (nothing else is in flight then), and for its LDS accesses before a plain
+// s_barrier (a __syncthreads() would do the same here, but says less).
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// One dword from global memory into a register, as inline assembly: the
-// compiler does not track it, and the stage's explicit waits cover it.
-__device__ __forceinline__ float load_word_untracked(const float* p) {
-  float v;
-  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-
 template <bool A2D, bool B2D, bool OUT_BF16>
-__global__ __launch_bounds__(NTHR, 1) void gemm_blk_kernel(GemmArgs g) {
-  static_assert(KB_VM_TILES == 12, "wait_vm_ahead counts 12 tile loads per stage");
+__global__ __launch_bounds__(KB_THR, 1) void gemm_blk_kernel(GemmArgs g) {
   __shared__ __align__(16) uint8_t smem[KB_SMEM];
 
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w >> 2, wn = w & 3;
   const int lr = lane & 31, lg = lane >> 5;
   int tm, tn;
   tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * KB_BN;
   const int nk = g.K / 128;
 
-  auto tA = [&](int s) { return smem + s * KB_STAGE; };
-  auto tB = [&](int s) { return smem + s * KB_STAGE + TILEB; };
-  auto ringA = [&](int s) { return (float*)(smem + KB_RING + s * KB_SLOT); };
-  auto ringB = [&](int s) { return (float*)(smem + KB_RING + s * KB_SLOT + BM * 4); };
+  auto tA = [&](int s) { return smem + (s & 1) * KB_STAGE; };
+  auto tB = [&](int s) { return smem + (s & 1) * KB_STAGE + TILEB; };
+  auto ringA = [&](int s) { return (float*)(smem + KB_RING + (s & 1) * KB_SLOT); };
+  auto ringB = [&](int s) { return (float*)(smem + KB_RING + (s & 1) * KB_SLOT + BM * 4); };
 
-  Direct da;
-  Direct4 db;
-  direct_init(da, g.A, g.lda, m0, g.M, w);
+  Direct4 da, db;
+  direct4_init(da, g.A, g.lda, m0, g.M, w);
   direct4_init(db, g.B, g.ldb, n0, g.N, w);
-  auto issue_tile = [&](int kt, int v) {     // tile load v (of 12) of stage kt: A 0-7, B 8-11
-    const int s = kt % KB_NSTAGE;
-    if (v < 8) direct_item(da, kt, tA(s), w, v);
-    else direct4_item(db, kt, tB(s), w, v - 8);
-  };
-
-  // Scale rows go through registers: lane (w, l) owns a_scale of tile row
-  // 64 w + l and b_scale of tile row 64 (w & 1) + l; the words of stage k + 1
-  // are loaded at the start of stage k and written into the LDS ring at its
-  // end (waves 2-3 write their b_scale copy into the slot's sink).  Loads,
-  // ring writes and ring reads are inline assembly with explicit waits: as
-  // plain accesses the compiler cannot tell them apart from the tile loads
-  // in flight and makes each wait for all of them.
+  // Scale rows go into the ring by LDS-DMA like the tiles: lane (w, l) of
+  // waves 0-3 loads the a_scale word of tile row 64 w + l, of waves 4-7 the
+  // b_scale word of tile row 64 (w - 4) + l.
   const int sstride = g.K / 128;
-  int ra = m0 + 64 * w + lane, rb = n0 + 64 * (w & 1) + lane;
-  ra = ra < g.M ? ra : g.M - 1;
-  rb = rb < g.N ? rb : g.N - 1;
-  const float* pa = (const float*)g.a_scale + (int64_t)(A2D ? ra / 128 : ra) * sstride;
-  const float* pb = (const float*)g.b_scale + (int64_t)(B2D ? rb / 128 : rb) * sstride;
-  auto put_scales = [&](int kt, float a, float b) {
-    typedef __attribute__((address_space(3))) float* lds_f32_w;
-    const int r = kt % KB_NSLOT;
-    const lds_f32_w pa_ = (lds_f32_w)(ringA(r) + 64 * w + lane);
-    const lds_f32_w pb_ = (lds_f32_w)(ringB(r) + (w < 2 ? 0 : KB_BN) + 64 * (w & 1) + lane);
-    asm volatile("ds_write_b32 %0, %1" ::"v"(pa_), "v"(a) : "memory");
-    asm volatile("ds_write_b32 %0, %1" ::"v"(pb_), "v"(b) : "memory");
+  const float* ps;
+  {
+    const bool on_a = w < 4;
+    int r = on_a ? m0 + 64 * w + lane : n0 + 64 * (w - 4) + lane;
+    const int lim = on_a ? g.M : g.N;
+    r = r < lim ? r : lim - 1;
+    const bool twod = on_a ? A2D : B2D;
+    ps = (const float*)(on_a ? g.a_scale : g.b_scale) + (int64_t)(twod ? r / 128 : r) * sstride;
+  }
+  // load v (of 9) of stage kt: A tiles 0-3, B tiles 4-7, the scale word 8
+  auto issue_item = [&](int kt, int v) {
+    if (v < 4) {
+      direct4_item(da, kt, tA(kt), w, v);
+    } else if (v < 8) {
+      direct4_item(db, kt, tB(kt), w, v - 4);
+    } else {
+      __builtin_amdgcn_global_load_lds(ps + kt, (lds_ptr_t)(ringA(kt) + 64 * w), 4, 0, 0);
+    }
   };
 
   f32x16 acc[4][2];
@@ -227,170 +215,176 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_blk_kernel(GemmArgs g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const uint32_t lb = (uint32_t)(lr * 128 + ((lg ^ swz_key(lr)) << 4));
-  // B rows 64 wn + 32 j + lr have key(lr) ^ 2 j ^ 4 wn
-  const uint32_t bx = (uint32_t)(wn << 6);
+  // B rows 64 wn + 32 j + lr have key(lr) ^ 2 j ^ 4 (wn & 1)
+  const uint32_t bx = (uint32_t)((wn & 1) << 6);
 
   // Operands of the current stage, carried across stages: B fragments of the
   // wave's two column tiles, A fragments of the current row tile, and the
-  // raw scale words of the stage (read by inline assembly): a_scale of the
-  // lane's row in each row tile, and b_scale -- one word for 128x128 weight
-  // blocks, else the lane's 16 columns of each column tile.
-  i32x8 fb[2][2], fa[2][2];
+  // scale words of the stage: a_scale of the lane's
+  // row in each row tile, and b_scale -- one word for 128x128 weight blocks
+  // (the wave's 64 columns lie in one block), else the lane's 16 columns of
+  // each column tile.
+  i32x8 fb[2][2], fa[2];
   uint32_t asw[4];
-  i32x4 bsw[2][4];
+  i32x4 bsw[2][4];        // 1x128 B blocks: b_scale of the lane's columns (fp32 bits)
   float fac[4] = {};     // per row tile: a_scale (times the weight scale for 128x128 blocks)
-  float bsv[2][16] = {}; // 1x128 B blocks: b_scale of the lane's columns
-  typedef __attribute__((address_space(3))) const float* lds_f32_p;
   auto read_fb = [&](int kt, int j) {
-    const uint8_t* lbq = tB(kt % KB_NSTAGE) + wn * 8192;
+    const uint8_t* lbq = tB(kt) + wn * 8192;
 #pragma unroll
     for (int h = 0; h < 2; ++h) fb[j][h] = read2(lbq + j * 4096, lb, ((uint32_t)(((4 * h) ^ (2 * j)) << 4)) ^ bx);
   };
-  auto read_fa = [&](int kt, int i) {       // into fa[i & 1]
-    const uint8_t* la = tA(kt % KB_NSTAGE) + wm * 16384;
+  auto read_fa = [&](int kt, int i) {
+    const uint8_t* la = tA(kt) + wm * 16384;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) fa[i & 1][h] = read2(la + i * 4096, lb, (uint32_t)(((4 * h) ^ (2 * i)) << 4));
+    for (int h = 0; h < 2; ++h) fa[h] = read2(la + i * 4096, lb, (uint32_t)(((4 * h) ^ (2 * i)) << 4));
   };
+  // The scale words of stage kt from the ring: a_scale and the first column
+  // tile's b_scale (load_scales), the second column tile's b_scale for 1x128
+  // B blocks (load_scales_b1: read once the previous stage's last fold has
+  // used the old values).
   auto load_scales = [&](int kt) {
-    const lds_f32_p pa_ = (lds_f32_p)(ringA(kt % KB_NSLOT) + wm * 128 + lr);
+    const float* qa = ringA(kt) + wm * 128 + lr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(asw[i]) : "v"(pa_), "i"(128 * i));
+    for (int i = 0; i < 4; ++i) asw[i] = __float_as_uint(qa[32 * i]);
     if (B2D) {
-      const lds_f32_p pb_ = (lds_f32_p)ringB(kt % KB_NSLOT);
-      asm volatile("ds_read_b32 %0, %1" : "=v"(bsw[0][0].x) : "v"(pb_));
+      bsw[0][0].x = __float_as_uint(ringB(kt)[64 * wn]);
     } else {
-      const lds_f32_p pb_ = (lds_f32_p)(ringB(kt % KB_NSLOT) + wn * 64 + 4 * lg);
+      const float* qb = ringB(kt) + wn * 64 + 4 * lg;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(bsw[j][q]) : "v"(pb_), "i"(128 * j + 32 * q));
+      for (int q = 0; q < 4; ++q) bsw[0][q] = *(const i32x4*)(qb + 8 * q);
     }
   };
-  // Wait for the scale reads (the wait names their results as operands, so
-  // nothing that uses them is scheduled before it) and form the factors.
-  auto finish_scales = [&]() {
-    if (B2D) {
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(asw[0]), "+v"(asw[1]), "+v"(asw[2]), "+v"(asw[3]), "+v"(bsw[0][0].x)::"memory");
-      const float bs = __uint_as_float(bsw[0][0].x);
+  auto load_scales_b1 = [&](int kt) {
+    if (!B2D) {
+      const float* qb = ringB(kt) + wn * 64 + 4 * lg + 32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fac[i] = __uint_as_float(asw[i]) * bs;
-    } else {
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(asw[0]), "+v"(asw[1]), "+v"(asw[2]), "+v"(asw[3]), "+v"(bsw[0][0]), "+v"(bsw[0][1]),
-                     "+v"(bsw[0][2]), "+v"(bsw[0][3]), "+v"(bsw[1][0]), "+v"(bsw[1][1]), "+v"(bsw[1][2]),
-                     "+v"(bsw[1][3])::"memory");
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fac[i] = __uint_as_float(asw[i]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = __builtin_bit_cast(float4, bsw[j][q]);
-          bsv[j][4 * q] = v.x;
-          bsv[j][4 * q + 1] = v.y;
-          bsv[j][4 * q + 2] = v.z;
-          bsv[j][4 * q + 3] = v.w;
-        }
+      for (int q = 0; q < 4; ++q) bsw[1][q] = *(const i32x4*)(qb + 8 * q);
     }
+  };
+  // The row-tile factors from the raw words (1x128 B blocks are read from
+  // bsw by the fold itself).
+  auto finish_scales = [&]() {
+    const float bs = B2D ? __uint_as_float(bsw[0][0].x) : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fac[i] = B2D ? __uint_as_float(asw[i]) * bs : __uint_as_float(asw[i]);
   };
 
-  // Prologue: scale words and tiles of stage 0, tiles of stage 1, then the
-  // operands of stage 0.
+  // Prologue: the loads of stages 0 and 1, then the operands of stage 0.
+  // Stage 1's 9 loads may stay in flight -- unless the kernel spills (1x128
+  // B blocks can: their scale words take 32 more registers), since spill
+  // traffic would make a counted wait miscount.
   {
-    const float a0 = pa[0], b0 = pb[0];
 #pragma unroll
-    for (int v = 0; v < KB_VM_TILES; ++v) issue_tile(0, v);
+    for (int v = 0; v < 9; ++v) issue_item(0, v);
     if (nk > 1) {
 #pragma unroll
-      for (int v = 0; v < KB_VM_TILES; ++v) issue_tile(1, v);
+      for (int v = 0; v < 9; ++v) issue_item(1, v);
     }
-    put_scales(0, a0, b0);
-    if (nk > 1) wait_vm_ahead();
+    if (B2D && nk > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     else wait_vm0();
     barrier_lds();
     read_fb(0, 0);
     read_fb(0, 1);
     read_fa(0, 0);
-    load_scales(0);
+    load_scales(0);                                  // load_scales_b1(0) in stage 0
   }
 
-  // Partial products of the two tiles in flight; tile 7 of a stage is
-  // folded during tile 0 of the next (zeros before the first stage).
-  f32x16 part[2] = {};
+  // Partial products in flight.  With 128x128 weight blocks, two tiles: tile
+  // t multiplies while tile t - 1 is folded, and tile 7 of a stage is folded
+  // during tile 0 of the next (zeros before the first stage).  1x128 B
+  // blocks need 32 more registers for their scales, so they keep one tile
+  // and fold it right after its MFMAs; the SIMD's other wave fills the gap.
+  constexpr int NP = B2D ? 2 : 1;
+  f32x16 part[NP] = {};
   // fold values r0 .. r0 + 7 of tile tt with the current stage's scales
   auto fold8 = [&](int tt, int r0) {
     const int i = tt >> 1, j = tt & 1;
 #pragma unroll
     for (int r = r0; r < r0 + 8; ++r)
-      acc[i][j][r] = __builtin_fmaf(part[tt & 1][r], B2D ? fac[i] : fac[i] * bsv[j][r], acc[i][j][r]);
+      acc[i][j][r] = B2D ? __builtin_fmaf(part[tt % NP][r], fac[i], acc[i][j][r])
+                         : __builtin_fmaf(part[tt % NP][r] * __builtin_bit_cast(float4, bsw[j][r >> 2])[r & 3], fac[i],
+                                          acc[i][j][r]);
   };
 
-  // One K stage.  MORE: stage kt + 2 exists and its tiles are loaded during
-  // tiles 0-5 of this one; NEXT: stage kt + 1 exists (its scale words are
-  // loaded here).  Tiles t = (i, j) = (t / 2, t % 2): tile t multiplies into
-  // part[t % 2] while tile t - 1 is folded, acc += part * a_scale[m] *
-  // b_scale[n]; tile 0 folds the previous stage's tile 7 before this
-  // stage's scales replace that stage's.  A fragments of row tile i + 1 are
-  // read into the other buffer once tile (i, 0) has issued.  After tile 5
-  // every wave waits for the next stage's data and meets at a barrier (this
-  // stage's tile buffer is no longer read by then), so tiles 6-7 read the
-  // next stage's first operands as their registers free up, and the next
-  // stage starts without an LDS round trip.  The last two stages are peeled
-  // so that every stage is straight-line code and the fenced schedule holds.
-  auto stage = [&](int kt, auto more_c, auto next_c) {
-    constexpr bool MORE = decltype(more_c)::value;
+  // One K stage.  ISSUE: stage kt + 2 exists and its loads are issued in
+  // tiles 6-7 of this one, into this stage's buffer and ring slot; NEXT:
+  // stage kt + 1 exists.  Tiles t = (i, j) = (t / 2, t % 2): tile t
+  // multiplies into part[t % 2] while tile t - 1 is folded, acc += part *
+  // a_scale[m] * b_scale[n]; tile 0 folds the previous stage's tile 7 before
+  // this stage's scales replace that stage's.  A fragments of row tile i + 1
+  // are read once tile (i, 1) has issued (the other wave of the SIMD covers
+  // the LDS latency).  After tile
+  // 5 every wave waits for the next stage's data and meets at a barrier (this
+  // stage's buffer is no longer read by then), so tiles 6-7 read the next
+  // stage's first operands as their registers free up and refill this
+  // stage's buffer, and the next stage starts without an LDS round trip.  The
+  // last stages are peeled so that every stage is straight-line code and the
+  // fenced schedule holds.
+  auto stage = [&](int kt, auto issue_c, auto next_c) {
+    constexpr bool ISSUE = decltype(issue_c)::value;
     constexpr bool NEXT = decltype(next_c)::value;
-    float a_nx = 0.0f, b_nx = 0.0f;
-    if (NEXT) {
-      a_nx = load_word_untracked(pa + kt + 1);
-      b_nx = load_word_untracked(pb + kt + 1);
-    }
     const f32x16 zero = {};
-    // Each MFMA is followed by half a fold of the previous tile, so the
-    // vector unit works while the matrix core does and the second MFMA of a
-    // tile (which accumulates onto the first) finds the first one done.
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       const int i = tt >> 1, j = tt & 1;
       // transposed tile: B rows are the instruction's rows, A rows its columns
-      part[tt & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][0], fa[i & 1][0], zero, 0, 0, 0, 0, 0, 0);
+      part[tt % NP] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][0], fa[0], zero, 0, 0, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      fold8((tt + 7) & 7, 0);
-      if (MORE && tt < 6) issue_tile(kt + 2, 2 * tt);
+      if (NP == 2) fold8((tt + 7) & 7, 0);
+      if (ISSUE && tt == 6) {
+#pragma unroll
+        for (int v = 0; v < 3; ++v) issue_item(kt + 2, v);
+      }
+      if (ISSUE && tt == 7) {
+#pragma unroll
+        for (int v = 5; v < 7; ++v) issue_item(kt + 2, v);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      part[tt & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][1], fa[i & 1][1], part[tt & 1], 0, 0, 0, 0,
-                                                                     0, 0);
+      part[tt % NP] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][1], fa[1], part[tt % NP], 0, 0, 0, 0,
+                                                                      0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      fold8((tt + 7) & 7, 8);
-      if (tt == 0) finish_scales();
-      if (j == 0 && i < 3) read_fa(kt, i + 1);     // the other buffer: row tile i - 1 is done
-      if (MORE && tt < 6) issue_tile(kt + 2, 2 * tt + 1);
+      if (NP == 2) fold8((tt + 7) & 7, 8);
+      if (tt == 0) {                               // the previous stage's scales are done with
+        finish_scales();
+        load_scales_b1(kt);
+      }
+      if (NP == 1) {
+        fold8(tt, 0);
+        fold8(tt, 8);
+      }
+      if (j == 1 && i < 3) read_fa(kt, i + 1);     // row tile i is done
+      if (ISSUE && tt == 6) {
+#pragma unroll
+        for (int v = 3; v < 5; ++v) issue_item(kt + 2, v);
+      }
+      if (ISSUE && tt == 7) {
+#pragma unroll
+        for (int v = 7; v < 9; ++v) issue_item(kt + 2, v);
+      }
       if (tt == 5 && NEXT) {
-        if (MORE) wait_vm_ahead();
-        else wait_vm0();
-        put_scales(kt + 1, a_nx, b_nx);
+        wait_vm0();
         barrier_lds();
       }
-      if (tt == 6 && NEXT) {                       // fb[0] is free once tile (3, 0) has issued, fa[0]
-        read_fb(kt + 1, 0);                        // after row tile 2
+      if (tt == 6 && NEXT) read_fb(kt + 1, 0);     // fb[0] is free once tile (3, 0) has issued
+      if (tt == 7 && NEXT) {                       // fa, fb[1] are free after tile (3, 1)
+        read_fb(kt + 1, 1);
         read_fa(kt + 1, 0);
       }
-      if (tt == 7 && NEXT) read_fb(kt + 1, 1);     // fb[1] is free after tile (3, 1)
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (NEXT) load_scales(kt + 1);                 // fac / bsv still hold this stage's scales
+    if (NEXT) load_scales(kt + 1);                 // fac and bsw[1] still hold this stage's scales
   };
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
   for (int kt = 0; kt < nk - 2; ++kt) stage(kt, T_{}, T_{});
   if (nk >= 2) stage(nk - 2, F_{}, T_{});
   stage(nk - 1, F_{}, F_{});
-  fold8(7, 0);
-  fold8(7, 8);
+  if (NP == 2) {
+    fold8(7, 0);
+    fold8(7, 8);
+  }
   __syncthreads();                                   // the epilogue reuses the tile buffers
-  store_blk<OUT_BF16>(acc, g, smem, m0, n0, w, wm, wn, lane);
+  store_blk<OUT_BF16>(acc, g, smem, m0, n0, wm, wn, lane);
 }
 
 gemm_fn blk_kernel_for(bool a2d, bool b2d, bool bf16_out) {

@@ -60,14 +60,15 @@ __device__ __forceinline__ uint32_t absmax_f32x4(uint4 v) {
   return a > b ? a : b;
 }
 
-// Fold a per-lane maximum into *out: wave reduction, the workgroup's four
-// waves through the first 16 bytes of the (finished) epilogue staging area,
+// Fold a per-lane maximum into *out: wave reduction, the workgroup's NW
+// waves through the first 4 NW bytes of the (finished) epilogue staging area,
 // then one atomic from thread 0 only when the workgroup's maximum exceeds
 // what *out already holds.  Thousands of same-address atomics queue behind
 // each other, so there is at most one per workgroup.  No LDS object of its
 // own: a second one in the kernel makes the compiler wait for every LDS DMA
 // load in flight before each LDS read of the main loop.  Called by all
 // threads of the workgroup after its last read of `smem` (two barriers).
+template <int NW = NTHR / 64>
 __device__ __forceinline__ void amax_fold_wg(uint32_t v, uint32_t* out, uint8_t* smem) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -81,7 +82,7 @@ __device__ __forceinline__ void amax_fold_wg(uint32_t v, uint32_t* out, uint8_t*
   if (threadIdx.x == 0) {
     uint32_t m = part[0];
 #pragma unroll
-    for (int i = 1; i < NTHR / 64; ++i) m = m > part[i] ? m : part[i];
+    for (int i = 1; i < NW; ++i) m = m > part[i] ? m : part[i];
     const uint32_t cur = __builtin_nontemporal_load(out);
     if (m > cur) atomicMax(out, m);
   }
@@ -188,7 +189,9 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
 typedef void (*gemm_fn)(GemmArgs);
 
 // Sub-channel (block-128) FP8 kernel of gemm_blk.hip: 128x128 (a2d / b2d)
-// or 1x128 blocks for A and B (a2d implies b2d), bf16 or fp32 output.
+// or 1x128 blocks for A and B (a2d implies b2d), bf16 or fp32 output;
+// BLK_THR threads per workgroup, BM x BLK_BN output tiles.
+constexpr int BLK_THR = 512, BLK_BN = 256;
 gemm_fn blk_kernel_for(bool a2d, bool b2d, bool bf16_out);
 
 }  // namespace pbs
