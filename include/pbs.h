@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PBS_VERSION 3   /* 3: pbs_rht_cast, pbs_debug_sr_encode */
+#define PBS_VERSION 4   /* 3: pbs_rht_cast, pbs_debug_sr_encode; 4: four SR words per Philox call */
 
 typedef enum {
   PBS_OK = 0,
@@ -203,7 +203,8 @@ float* pbs_delayed_scale_inv(void* state); /* device address of `scale_inv` */
  *    this tensor's amax, taken after the RHT when it is used).
  *    flags: PBS_FLAG_RHT16 (col copy only, rows % 16 == 0; sign seed
  *    `seed`), PBS_FLAG_SR (stochastic rounding with Philox4x32-10, key =
- *    `seed`, counter = logical element index r * cols + c of x).
+ *    `seed`: logical element i = r * cols + c of x takes word i % 4 of the
+ *    call with counter (i / 4, 0, 0)).
  *  recipe MXFP4 ([FP4] "Technical deep-dive": the 32-value MX format that
  *    NVFP4's 16-value blocks refine): fmt E2M1, codes packed as for NVFP4;
  *    E8M0 scale bytes per 1x32 block along the contraction axis, [rows,
@@ -243,8 +244,9 @@ pbs_status pbs_cast(pbs_recipe recipe, const void* x_bf16, int64_t rows, int64_t
  *  rht_seed: Philox4x32-10 key of the signs (sigma_j = bit 0 of word 0 of
  *    Philox(counter (j, 0, 1, 0))), the same key as pbs_amax's seed for the
  *    transformed maximum.
- *  stochastic = 1: stochastic rounding with key sr_seed, counter = logical
- *    element index r * cols + c of x; 0: round to nearest even (sr_seed
+ *  stochastic = 1: stochastic rounding with key sr_seed, words as for
+ *    pbs_cast's PBS_FLAG_SR (element i = r * cols + c of x: word i % 4 of
+ *    the call with counter i / 4); 0: round to nearest even (sr_seed
  *    unused).
  *  scale: NVFP4's device fp32 S_enc (pbs_scale_from_amax, fmax 2688, of
  *    the transformed tensor's amax); unused for MXFP4.

@@ -8,9 +8,10 @@ S-box: two 32x32->64 multiplications per round, a Feistel-like permutation
 of the four counter words, a Weyl key schedule), with N=4 words of W=32 bits
 and R=10 rounds.  The stochastic rounding of gradients named in "How to
 optimize Transformer-based models for low-precision training",
-"Interpreting results for a real model", uses it with key (42, 0) and the
-element index as counter (the plainest reading of a counter-based
-generator keyed by a seed).
+"Interpreting results for a real model", uses it with key (42, 0); element
+i of the gradient takes word i % 4 of the call with counter i // 4 (the
+plainest reading of a counter-based generator keyed by a seed that spends
+every word it makes).
 
 One round, for counter (c0, c1, c2, c3) and key (k0, k1):
   (hi0, lo0) = M0 * c0        (hi1, lo1) = M1 * c2      (64-bit products)
@@ -50,10 +51,16 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
     return tuple(x.astype(np.uint32) for x in (c0, c1, c2, c3))
 
 
-def philox_word0_for_index(idx, seed=42):
-    """Word 0 of Philox4x32-10(key=(seed lo, seed hi), counter=(idx lo, idx hi, 0, 0))."""
+def philox_word_for_index(idx, seed=42):
+    """The stochastic-rounding word of element idx: word idx % 4 of
+    Philox4x32-10(key=(seed lo, seed hi), counter=(q lo, q hi, 0, 0)), q = idx // 4.
+
+    One call of the generator yields four 32-bit words; four consecutive
+    indices share a call, so a stream of n words costs n / 4 calls.
+    """
     idx = np.asarray(idx, dtype=np.uint64)
-    lo = idx & _MASK32
-    hi = idx >> np.uint64(32)
+    q = idx >> np.uint64(2)
+    k = (idx & np.uint64(3)).astype(np.int64)
     seed = int(seed)
-    return philox4x32_10(lo, hi, 0, 0, seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)[0]
+    w = philox4x32_10(q & _MASK32, q >> np.uint64(32), 0, 0, seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    return np.choose(k, w).astype(np.uint32)

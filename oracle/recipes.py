@@ -23,7 +23,7 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import E2M1, E4M3, E5M2, FORMATS, bf16_to_f32, e8m0_decode
-from .philox import philox4x32_10, philox_word0_for_index
+from .philox import philox4x32_10, philox_word_for_index
 
 FLT_MAX = np.float32(np.finfo(np.float32).max)
 FMAX = {"e4m3": 448.0, "e5m2": 57344.0}
@@ -355,12 +355,13 @@ def quantize_nvfp4(t, S_enc, weight_2d=False, sr_random=None):
 def sr_random_for(shape_mn, orient, seed=42):
     """Per-element SR random words for a gradient dY of logical shape [M, N].
 
-    Counter = logical element index m * N + n of dY, whatever copy is being
-    produced; returned in the layout of the requested copy.
+    Element (m, n) takes word i % 4 of the Philox call with counter i // 4,
+    i = m * N + n its logical index in dY, whatever copy is being produced;
+    returned in the layout of the requested copy.
     """
     M, N = shape_mn
     idx = np.arange(M * N, dtype=np.uint64).reshape(M, N)
-    r = philox_word0_for_index(idx, seed)
+    r = philox_word_for_index(idx, seed)
     return r if orient == "row" else np.ascontiguousarray(r.T)
 
 

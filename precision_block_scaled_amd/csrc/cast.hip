@@ -35,7 +35,8 @@
 //    random Hadamard transform on the Wgrad inputs, stochastic rounding of
 //    gradients.  d = enc_E4M3(fp32(fp32(amax_b / 6) * S_enc)), e_b =
 //    fp32(S_enc / d), codes = enc_E2M1(fp32(x * e_b)) or its stochastic
-//    rounding with Philox4x32-10 (counter = logical element index).
+//    rounding with Philox4x32-10 (logical element i takes word i % 4 of the
+//    call with counter i / 4).
 //  channel-wise FP8 -- "Faster training throughput in FP8 precision with
 //    NVIDIA NeMo", "Scaling recipe granularity" (per-channel scaling): one
 //    scale per row of each contraction-contiguous copy, s_r = fp32(448 /
@@ -210,6 +211,29 @@ __device__ __forceinline__ uint32_t nvfp4_block(const float* v, uint32_t abits, 
 //  strip: index of the strip in the tile (= thread id)
 //  out_codes: start of this strip's output row segment
 //  g_row/g_col of element 0 of the strip (for the SR counter)
+// Stochastic-rounding words of values j .. j + N - 1 of a strip: a row strip
+// (ROWDIR) of logical row g_row0 from column g_col0 (a multiple of 4, as j
+// is), one call per 4 values; a column strip of column g_col0 from row
+// g_row0, one call per value, whose word the column picks.
+template <bool ROWDIR, int N>
+__device__ __forceinline__ void sr_strip_words(const CastArgs& a, int64_t g_row0, int64_t g_col0, int j,
+                                               uint32_t* rnd) {
+  if (ROWDIR) {
+    const uint64_t q0 = (uint64_t)(g_row0 * a.C + g_col0 + j) >> 2;
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+      const uint4 r4 = sr_words4(q0 + k, a.seed);
+      rnd[4 * k] = r4.x;
+      rnd[4 * k + 1] = r4.y;
+      rnd[4 * k + 2] = r4.z;
+      rnd[4 * k + 3] = r4.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) rnd[i] = sr_word((uint64_t)((g_row0 + j + i) * a.C + g_col0), a.seed);
+  }
+}
+
 template <int RECIPE, int FMT, bool ROWDIR, bool W2D, bool RHT, bool SR>
 __device__ __forceinline__ void quantize_strip(const bf16_t* tile, int strip, int len,
                                                const CastArgs& a, float tile_scale,
@@ -294,14 +318,10 @@ __device__ __forceinline__ void quantize_strip(const bf16_t* tile, int strip, in
 #pragma unroll
       for (int i = 0; i < 32; ++i) x[i] = v[i] * inv;
       if (SR) {
+        uint32_t rnd[32];
+        sr_strip_words<ROWDIR, 32>(a, g_row0, g_col0, j, rnd);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int64_t gr = ROWDIR ? g_row0 : g_row0 + j + i;
-          const int64_t gc = ROWDIR ? g_col0 + j + i : g_col0;
-          const uint64_t idx = (uint64_t)(gr * a.C + gc);
-          q[i] = sr_e2m1(x[i], philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
-                                            (uint32_t)(a.seed >> 32)));
-        }
+        for (int i = 0; i < 32; ++i) q[i] = sr_e2m1(x[i], rnd[i]);
         *(uint2*)(out_codes + j / 2) = pack_e2m1_16(q);
         *(uint2*)(out_codes + j / 2 + 8) = pack_e2m1_16(q + 16);
       } else {
@@ -325,17 +345,7 @@ __device__ __forceinline__ void quantize_strip(const bf16_t* tile, int strip, in
         m = m > x ? m : x;
       }
       if (W2D) m = max16lanes(m);
-      if (SR) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          // element i of this segment sits at logical (row, col) of x
-          const int64_t gr = ROWDIR ? g_row0 : g_row0 + j + i;
-          const int64_t gc = ROWDIR ? g_col0 + j + i : g_col0;
-          const uint64_t idx = (uint64_t)(gr * a.C + gc);
-          rnd[i] = philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
-                                (uint32_t)(a.seed >> 32));
-        }
-      }
+      if (SR) sr_strip_words<ROWDIR, 16>(a, g_row0, g_col0, j, rnd);
       uint2 w;
       const uint32_t dcode = nvfp4_block<SR>(v, m, S, rnd, &w);
       *(uint2*)(out_codes + j / 2) = w;
@@ -629,12 +639,14 @@ __global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg)
       const uint32_t m16 = bf16_absmax16(w[u]);
       if (AMAX && ok[u]) amx = amx > m16 ? amx : m16;
       uint32_t rnd[16];
-      if (SR) {
+      if (SR) {                                   // logical indices 16 s .. 16 s + 15: four calls
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint64_t idx = (uint64_t)(s * 16 + i);         // logical index r * C + c
-          rnd[i] = philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
-                                (uint32_t)(a.seed >> 32));
+        for (int k = 0; k < 4; ++k) {
+          const uint4 r4 = sr_words4((uint64_t)(s * 4 + k), a.seed);
+          rnd[4 * k] = r4.x;
+          rnd[4 * k + 1] = r4.y;
+          rnd[4 * k + 2] = r4.z;
+          rnd[4 * k + 3] = r4.w;
         }
       }
       uint8_t* codes = (RECIPE == R_NV || RECIPE == R_MX4) ? a.row_codes + s * 8 : a.row_codes + s * 16;
@@ -669,7 +681,7 @@ __global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg)
 constexpr int CT_R = 256, CT_C = 64, CT_PITCH = 136;
 
 template <int RECIPE, int FMT, bool RHT, bool SR, bool AMAX>
-__global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
+__global__ __launch_bounds__(256, 2) void cast_col_kernel(CastArgs a) {
   __shared__ __align__(16) uint8_t tile[CT_R * CT_PITCH];
   const int t = threadIdx.x, lane = t & 63;
   uint32_t rht_mask = 0;
@@ -723,6 +735,23 @@ __global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
       const int g = cg ^ ((row >> 4) & 14);
       wv[i] = *(const uint2*)(tile + row * CT_PITCH + g * 8);
     }
+    // stochastic rounding: the thread's 4 columns 4 cg .. 4 cg + 3 are one
+    // aligned group of a row of x, so one call per row serves all four
+    // (one call in flight at a time: hoisting all sixteen multiplies the live
+    // registers, and occupancy hides the chain's latency better)
+    uint32_t rndc[4][16];
+    if (SR) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint64_t idx = (uint64_t)((r0 + 16 * rs + i) * a.C + c0 + 4 * cg);
+        const uint4 r4 = sr_words4(idx >> 2, a.seed);
+        rndc[0][i] = r4.x;
+        rndc[1][i] = r4.y;
+        rndc[2][i] = r4.z;
+        rndc[3][i] = r4.w;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float v[16];
@@ -752,15 +781,6 @@ __global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
       const int64_t gc = c0 + col, gr = r0 + 16 * rs;
       if (RECIPE == R_CHAN)   // the column's amax (fp32 bits), measured by chan_colmax_kernel
         tscale = scale_from_amax(__uint_as_float(((const uint32_t*)a.col_scales)[valid ? gc : c0]), 448.0f);
-      uint32_t rnd[16];
-      if (SR) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint64_t idx = (uint64_t)((gr + i) * a.C + gc);
-          rnd[i] = philox_word0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, (uint32_t)a.seed,
-                                (uint32_t)(a.seed >> 32));
-        }
-      }
       uint8_t* codes = (RECIPE == R_NV || RECIPE == R_MX4) ? a.col_codes + gc * (a.R / 2) + gr / 2
                                                            : a.col_codes + gc * a.R + gr;
       uint8_t* sc8 = nullptr;
@@ -776,7 +796,8 @@ __global__ __launch_bounds__(256) void cast_col_kernel(CastArgs a) {
         writer = (rs & 7) == 0;
       }
       quantize_segment<RECIPE == R_CHAN ? R_TENSOR : RECIPE, FMT, SR>(v, mbits, tscale, valid, codes, sc8, sc32,
-                                                                       writer, rnd);
+                                                                       writer, rndc[c]);
+      if (SR) __builtin_amdgcn_sched_barrier(0);   // one column at a time: the words already hold 64 registers
     }
     __syncthreads();   // every read of this tile is done before the next fill
   }

@@ -109,10 +109,9 @@ __device__ __forceinline__ float mx_inv_scale(uint32_t c) {
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
 // Easy as 1, 2, 3", SC'11): ten rounds of two 32x32->64 products and a
 // word permutation, key bumped by the Weyl constants between rounds.
-// Only word 0 of the output is used.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2,
-                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     // one 32x32->64 product each (v_mad_u64_u32), not separate lo / hi halves
@@ -124,7 +123,26 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
-  return c0;
+  return make_uint4(c0, c1, c2, c3);
+}
+
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                 uint32_t k1) {
+  return philox4x32_10(c0, c1, c2, c3, k0, k1).x;
+}
+
+// Stochastic-rounding words: logical element i of x (row-major index
+// r * C + c) takes word i % 4 of the call with counter (i / 4, 0, 0), so four
+// consecutive elements of a row share one call.  sr_words4(q) is the call
+// for elements 4 q .. 4 q + 3, sr_word(i) one element's word.
+__device__ __forceinline__ uint4 sr_words4(uint64_t q, uint64_t seed) {
+  return philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), 0u, 0u, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t sr_word(uint64_t i, uint64_t seed) {
+  const uint4 w = sr_words4(i >> 2, seed);
+  const uint32_t k = (uint32_t)i & 3u;
+  return k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w;
 }
 
 // Stochastic rounding of v to E2M1 with the 32-bit random r: |v| >= 6 gives

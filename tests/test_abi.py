@@ -22,7 +22,7 @@ def declared_functions():
 def test_library_built_and_loads():
     if not os.path.exists(P.lib_path):
         pytest.skip("libpbs.so not built (run __graft_entry__.build())")
-    assert P.pbs_version() == 3
+    assert P.pbs_version() == 4
 
 
 def test_every_declared_symbol_is_exported():

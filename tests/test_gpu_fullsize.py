@@ -54,7 +54,7 @@ from oracle import recipes as R
 from oracle.formats import E4M3, E5M2, bf16_to_f32
 from oracle.gemm_ref import check_gemm, fp8_dot_unit_bound
 from oracle.passes import BLOCK128_2D, operand_roles
-from oracle.philox import philox_word0_for_index
+from oracle.philox import philox_word_for_index
 from tests.fp8_dot_unit import dot_unit_gemm, to_bf16_rne
 from tests.gpu_util import to_gpu_bf16
 
@@ -174,7 +174,7 @@ class OracleCopy:
             idx = r[:, None] * np.uint64(N) + np.arange(N, dtype=np.uint64)[None, :]
         else:
             idx = np.arange(M, dtype=np.uint64)[None, :] * np.uint64(N) + r[:, None]
-        return philox_word0_for_index(idx, SEED)
+        return philox_word_for_index(idx, SEED)
 
     def _quantize(self, sel, rows_all, i0, i1):
         """(codes, scales, {row: deq}, {row: raw code values}, {row: channel scale}) for the

