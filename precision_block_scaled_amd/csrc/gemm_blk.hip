@@ -218,170 +218,233 @@ __global__ __launch_bounds__(KB_THR, 1) void gemm_blk_kernel(GemmArgs g) {
   // B rows 64 wn + 32 j + lr have key(lr) ^ 2 j ^ 4 (wn & 1)
   const uint32_t bx = (uint32_t)((wn & 1) << 6);
 
-  // Operands of the current stage, carried across stages: B fragments of the
-  // wave's two column tiles, A fragments of the current row tile, and the
-  // scale words of the stage: a_scale of the lane's
-  // row in each row tile, and b_scale -- one word for 128x128 weight blocks
-  // (the wave's 64 columns lie in one block), else the lane's 16 columns of
-  // each column tile.
-  i32x8 fb[2][2], fa[2];
-  uint32_t asw[4];
-  i32x4 bsw[2][4];        // 1x128 B blocks: b_scale of the lane's columns (fp32 bits)
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  uint32_t asw[4];       // a_scale words of the lane's row in each row tile (fp32 bits)
   float fac[4] = {};     // per row tile: a_scale (times the weight scale for 128x128 blocks)
-  auto read_fb = [&](int kt, int j) {
-    const uint8_t* lbq = tB(kt) + wn * 8192;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) fb[j][h] = read2(lbq + j * 4096, lb, ((uint32_t)(((4 * h) ^ (2 * j)) << 4)) ^ bx);
-  };
-  auto read_fa = [&](int kt, int i) {
-    const uint8_t* la = tA(kt) + wm * 16384;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) fa[h] = read2(la + i * 4096, lb, (uint32_t)(((4 * h) ^ (2 * i)) << 4));
-  };
-  // The scale words of stage kt from the ring: a_scale and the first column
-  // tile's b_scale (load_scales), the second column tile's b_scale for 1x128
-  // B blocks (load_scales_b1: read once the previous stage's last fold has
-  // used the old values).
-  auto load_scales = [&](int kt) {
+  auto read_asw = [&](int kt) {
     const float* qa = ringA(kt) + wm * 128 + lr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) asw[i] = __float_as_uint(qa[32 * i]);
-    if (B2D) {
-      bsw[0][0].x = __float_as_uint(ringB(kt)[64 * wn]);
-    } else {
-      const float* qb = ringB(kt) + wn * 64 + 4 * lg;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) bsw[0][q] = *(const i32x4*)(qb + 8 * q);
-    }
   };
-  auto load_scales_b1 = [&](int kt) {
-    if (!B2D) {
-      const float* qb = ringB(kt) + wn * 64 + 4 * lg + 32;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) bsw[1][q] = *(const i32x4*)(qb + 8 * q);
-    }
-  };
-  // The row-tile factors from the raw words (1x128 B blocks are read from
-  // bsw by the fold itself).
-  auto finish_scales = [&]() {
-    const float bs = B2D ? __uint_as_float(bsw[0][0].x) : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fac[i] = B2D ? __uint_as_float(asw[i]) * bs : __uint_as_float(asw[i]);
-  };
+  // The prologue issues the loads of stages 0 and 1 and waits for stage 0
+  // with stage 1's 9 loads in flight: a counted wait, right only while the
+  // kernel does not spill (spill traffic is counted too); the static check
+  // of this file holds every variant to that.
 
-  // Prologue: the loads of stages 0 and 1, then the operands of stage 0.
-  // Stage 1's 9 loads may stay in flight -- unless the kernel spills (1x128
-  // B blocks can: their scale words take 32 more registers), since spill
-  // traffic would make a counted wait miscount.
-  {
+  if constexpr (B2D) {
+    // Operands of the current stage, carried across stages: B fragments of
+    // the wave's two column tiles, A fragments of the current row tile, the
+    // a_scale words and the one b_scale word of the wave's 64 columns (they
+    // lie in one 128x128 block).
+    i32x8 fb[2][2], fa[2];
+    uint32_t bsw = 0;
+    auto read_fb = [&](int kt, int j) {
+      const uint8_t* lbq = tB(kt) + wn * 8192;
 #pragma unroll
-    for (int v = 0; v < 9; ++v) issue_item(0, v);
-    if (nk > 1) {
+      for (int h = 0; h < 2; ++h) fb[j][h] = read2(lbq + j * 4096, lb, ((uint32_t)(((4 * h) ^ (2 * j)) << 4)) ^ bx);
+    };
+    auto read_fa = [&](int kt, int i) {
+      const uint8_t* la = tA(kt) + wm * 16384;
 #pragma unroll
-      for (int v = 0; v < 9; ++v) issue_item(1, v);
-    }
-    if (B2D && nk > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else wait_vm0();
-    barrier_lds();
-    read_fb(0, 0);
-    read_fb(0, 1);
-    read_fa(0, 0);
-    load_scales(0);                                  // load_scales_b1(0) in stage 0
-  }
+      for (int h = 0; h < 2; ++h) fa[h] = read2(la + i * 4096, lb, (uint32_t)(((4 * h) ^ (2 * i)) << 4));
+    };
+    auto load_scales = [&](int kt) {
+      read_asw(kt);
+      bsw = __float_as_uint(ringB(kt)[64 * wn]);
+    };
+    auto finish_scales = [&]() {
+      const float bs = __uint_as_float(bsw);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fac[i] = __uint_as_float(asw[i]) * bs;
+    };
 
-  // Partial products in flight.  With 128x128 weight blocks, two tiles: tile
-  // t multiplies while tile t - 1 is folded, and tile 7 of a stage is folded
-  // during tile 0 of the next (zeros before the first stage).  1x128 B
-  // blocks need 32 more registers for their scales, so they keep one tile
-  // and fold it right after its MFMAs; the SIMD's other wave fills the gap.
-  constexpr int NP = B2D ? 2 : 1;
-  f32x16 part[NP] = {};
-  // fold values r0 .. r0 + 7 of tile tt with the current stage's scales
-  auto fold8 = [&](int tt, int r0) {
-    const int i = tt >> 1, j = tt & 1;
+    {
 #pragma unroll
-    for (int r = r0; r < r0 + 8; ++r)
-      acc[i][j][r] = B2D ? __builtin_fmaf(part[tt % NP][r], fac[i], acc[i][j][r])
-                         : __builtin_fmaf(part[tt % NP][r] * __builtin_bit_cast(float4, bsw[j][r >> 2])[r & 3], fac[i],
-                                          acc[i][j][r]);
-  };
-
-  // One K stage.  ISSUE: stage kt + 2 exists and its loads are issued in
-  // tiles 6-7 of this one, into this stage's buffer and ring slot; NEXT:
-  // stage kt + 1 exists.  Tiles t = (i, j) = (t / 2, t % 2): tile t
-  // multiplies into part[t % 2] while tile t - 1 is folded, acc += part *
-  // a_scale[m] * b_scale[n]; tile 0 folds the previous stage's tile 7 before
-  // this stage's scales replace that stage's.  A fragments of row tile i + 1
-  // are read once tile (i, 1) has issued (the other wave of the SIMD covers
-  // the LDS latency).  After tile
-  // 5 every wave waits for the next stage's data and meets at a barrier (this
-  // stage's buffer is no longer read by then), so tiles 6-7 read the next
-  // stage's first operands as their registers free up and refill this
-  // stage's buffer, and the next stage starts without an LDS round trip.  The
-  // last stages are peeled so that every stage is straight-line code and the
-  // fenced schedule holds.
-  auto stage = [&](int kt, auto issue_c, auto next_c) {
-    constexpr bool ISSUE = decltype(issue_c)::value;
-    constexpr bool NEXT = decltype(next_c)::value;
-    const f32x16 zero = {};
+      for (int v = 0; v < 9; ++v) issue_item(0, v);
+      if (nk > 1) {
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const int i = tt >> 1, j = tt & 1;
-      // transposed tile: B rows are the instruction's rows, A rows its columns
-      part[tt % NP] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][0], fa[0], zero, 0, 0, 0, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (NP == 2) fold8((tt + 7) & 7, 0);
-      if (ISSUE && tt == 6) {
-#pragma unroll
-        for (int v = 0; v < 3; ++v) issue_item(kt + 2, v);
-      }
-      if (ISSUE && tt == 7) {
-#pragma unroll
-        for (int v = 5; v < 7; ++v) issue_item(kt + 2, v);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      part[tt % NP] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][1], fa[1], part[tt % NP], 0, 0, 0, 0,
-                                                                      0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (NP == 2) fold8((tt + 7) & 7, 8);
-      if (tt == 0) {                               // the previous stage's scales are done with
-        finish_scales();
-        load_scales_b1(kt);
-      }
-      if (NP == 1) {
-        fold8(tt, 0);
-        fold8(tt, 8);
-      }
-      if (j == 1 && i < 3) read_fa(kt, i + 1);     // row tile i is done
-      if (ISSUE && tt == 6) {
-#pragma unroll
-        for (int v = 3; v < 5; ++v) issue_item(kt + 2, v);
-      }
-      if (ISSUE && tt == 7) {
-#pragma unroll
-        for (int v = 7; v < 9; ++v) issue_item(kt + 2, v);
-      }
-      if (tt == 5 && NEXT) {
+        for (int v = 0; v < 9; ++v) issue_item(1, v);
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      } else {
         wait_vm0();
-        barrier_lds();
       }
-      if (tt == 6 && NEXT) read_fb(kt + 1, 0);     // fb[0] is free once tile (3, 0) has issued
-      if (tt == 7 && NEXT) {                       // fa, fb[1] are free after tile (3, 1)
-        read_fb(kt + 1, 1);
-        read_fa(kt + 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      barrier_lds();
+      read_fb(0, 0);
+      read_fb(0, 1);
+      read_fa(0, 0);
+      load_scales(0);
     }
-    if (NEXT) load_scales(kt + 1);                 // fac and bsw[1] still hold this stage's scales
-  };
-  using T_ = std::integral_constant<bool, true>;
-  using F_ = std::integral_constant<bool, false>;
-  for (int kt = 0; kt < nk - 2; ++kt) stage(kt, T_{}, T_{});
-  if (nk >= 2) stage(nk - 2, F_{}, T_{});
-  stage(nk - 1, F_{}, F_{});
-  if (NP == 2) {
+
+    // Partial products of the two tiles in flight: tile t multiplies while
+    // tile t - 1 is folded, and tile 7 of a stage is folded during tile 0 of
+    // the next (zeros before the first stage).
+    f32x16 part[2] = {};
+    auto fold8 = [&](int tt, int r0) {           // values r0 .. r0 + 7 of tile tt
+      const int i = tt >> 1, j = tt & 1;
+#pragma unroll
+      for (int r = r0; r < r0 + 8; ++r) acc[i][j][r] = __builtin_fmaf(part[tt & 1][r], fac[i], acc[i][j][r]);
+    };
+
+    // One K stage.  ISSUE: stage kt + 2 exists and its loads are issued in
+    // tiles 6-7 of this one, into this stage's buffer and ring slot; NEXT:
+    // stage kt + 1 exists.  Tiles t = (i, j) = (t / 2, t % 2): tile t
+    // multiplies into part[t % 2] while tile t - 1 is folded, acc += part *
+    // a_scale[m] * b_scale[n]; tile 0 folds the previous stage's tile 7
+    // before this stage's scales replace that stage's.  A fragments of row
+    // tile i + 1 are read once tile (i, 1) has issued (the other wave of the
+    // SIMD covers the LDS latency).  After tile 5 every wave waits for the
+    // next stage's data and meets at a barrier (this stage's buffer is no
+    // longer read by then), so tiles 6-7 read the next stage's first operands
+    // as their registers free up and refill this stage's buffer, and the next
+    // stage starts without an LDS round trip.  The last stages are peeled so
+    // that every stage is straight-line code and the fenced schedule holds.
+    auto stage = [&](int kt, auto issue_c, auto next_c) {
+      constexpr bool ISSUE = decltype(issue_c)::value;
+      constexpr bool NEXT = decltype(next_c)::value;
+      const f32x16 zero = {};
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const int i = tt >> 1, j = tt & 1;
+        // transposed tile: B rows are the instruction's rows, A rows its columns
+        part[tt & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][0], fa[0], zero, 0, 0, 0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        fold8((tt + 7) & 7, 0);
+        if (ISSUE && tt == 6) {
+#pragma unroll
+          for (int v = 0; v < 3; ++v) issue_item(kt + 2, v);
+        }
+        if (ISSUE && tt == 7) {
+#pragma unroll
+          for (int v = 5; v < 7; ++v) issue_item(kt + 2, v);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        part[tt & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][1], fa[1], part[tt & 1], 0, 0, 0, 0, 0,
+                                                                       0);
+        __builtin_amdgcn_sched_barrier(0);
+        fold8((tt + 7) & 7, 8);
+        if (tt == 0) finish_scales();              // the previous stage's scales are done with
+        if (j == 1 && i < 3) read_fa(kt, i + 1);   // row tile i is done
+        if (ISSUE && tt == 6) {
+#pragma unroll
+          for (int v = 3; v < 5; ++v) issue_item(kt + 2, v);
+        }
+        if (ISSUE && tt == 7) {
+#pragma unroll
+          for (int v = 7; v < 9; ++v) issue_item(kt + 2, v);
+        }
+        if (tt == 5 && NEXT) {
+          wait_vm0();
+          barrier_lds();
+        }
+        if (tt == 6 && NEXT) read_fb(kt + 1, 0);   // fb[0] is free once tile (3, 0) has issued
+        if (tt == 7 && NEXT) {                     // fa, fb[1] are free after tile (3, 1)
+          read_fb(kt + 1, 1);
+          read_fa(kt + 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (NEXT) load_scales(kt + 1);               // fac still holds this stage's scales
+    };
+    for (int kt = 0; kt < nk - 2; ++kt) stage(kt, T_{}, T_{});
+    if (nk >= 2) stage(nk - 2, F_{}, T_{});
+    stage(nk - 1, F_{}, F_{});
     fold8(7, 0);
     fold8(7, 8);
+  } else {
+    // 1x128 B blocks: the lane's 16 columns of a column tile have 16
+    // different b_scale words.  Tiles go column tile by column tile, t =
+    // (i, j) = (t % 4, t / 4), so that only one column tile's words are held
+    // (16 registers rather than 32, which keeps the wave within its 256
+    // without spilling), at the cost of reading the A fragments twice per
+    // stage; each tile's partial products are folded right after its MFMAs
+    // (the SIMD's other wave covers the wait), the A fragments of the next
+    // tile are read into the other of two buffers meanwhile.
+    i32x8 gb[2], ga[2][2];
+    i32x4 bw[4];
+    auto read_gb = [&](int kt, int j) {
+      const uint8_t* lbq = tB(kt) + wn * 8192;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) gb[h] = read2(lbq + j * 4096, lb, ((uint32_t)(((4 * h) ^ (2 * j)) << 4)) ^ bx);
+    };
+    auto read_ga = [&](int kt, int i, int slot) {
+      const uint8_t* la = tA(kt) + wm * 16384;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ga[slot][h] = read2(la + i * 4096, lb, (uint32_t)(((4 * h) ^ (2 * i)) << 4));
+    };
+    auto read_bw = [&](int kt, int j) {
+      const float* qb = ringB(kt) + wn * 64 + 32 * j + 4 * lg;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bw[q] = *(const i32x4*)(qb + 8 * q);
+    };
+
+    {
+#pragma unroll
+      for (int v = 0; v < 9; ++v) issue_item(0, v);
+      if (nk > 1) {
+#pragma unroll
+        for (int v = 0; v < 9; ++v) issue_item(1, v);
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      } else {
+        wait_vm0();
+      }
+      barrier_lds();
+      read_gb(0, 0);
+      read_ga(0, 0, 0);
+      read_bw(0, 0);
+      read_asw(0);
+    }
+
+    // One K stage, ISSUE / NEXT as for 128x128 blocks.  After tile 6 (whose
+    // A read for tile 7 is this stage's last read of its buffer) every wave
+    // waits for the next stage's data and meets at a barrier; tiles 6-7 then
+    // refill this stage's buffer and tile 7 reads the next stage's first
+    // operands and scale words.
+    auto stage = [&](int kt, auto issue_c, auto next_c) {
+      constexpr bool ISSUE = decltype(issue_c)::value;
+      constexpr bool NEXT = decltype(next_c)::value;
+      const f32x16 zero = {};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fac[i] = __uint_as_float(asw[i]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int i = t & 3, j = t >> 2, sl = t & 1;
+        f32x16 part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(gb[0], ga[sl][0], zero, 0, 0, 0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(gb[1], ga[sl][1], part, 0, 0, 0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t < 7) read_ga(kt, (t + 1) & 3, sl ^ 1);   // the other buffer: tile t - 1 is done
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[i][j][r] = __builtin_fmaf(part[r] * __builtin_bit_cast(float4, bw[r >> 2])[r & 3], fac[i], acc[i][j][r]);
+        if (t == 3) {                               // column tile 0 is done
+          read_gb(kt, 1);
+          read_bw(kt, 1);
+        }
+        if (t == 6 && NEXT) {
+          wait_vm0();
+          barrier_lds();
+        }
+        if (ISSUE && t == 6) {
+#pragma unroll
+          for (int v = 0; v < 5; ++v) issue_item(kt + 2, v);
+        }
+        if (ISSUE && t == 7) {
+#pragma unroll
+          for (int v = 5; v < 9; ++v) issue_item(kt + 2, v);
+        }
+        if (t == 7 && NEXT) {
+          read_gb(kt + 1, 0);
+          read_ga(kt + 1, 0, 0);
+          read_bw(kt + 1, 0);
+          read_asw(kt + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    for (int kt = 0; kt < nk - 2; ++kt) stage(kt, T_{}, T_{});
+    if (nk >= 2) stage(nk - 2, F_{}, T_{});
+    stage(nk - 1, F_{}, F_{});
   }
   __syncthreads();                                   // the epilogue reuses the tile buffers
   store_blk<OUT_BF16>(acc, g, smem, m0, n0, wm, wn, lane);

@@ -8,12 +8,12 @@ counted wait is right only if the compiler emits exactly the kernel's own
 loads before it and no spill traffic (scratch accesses also count), so it is
 used only where the kernel does not spill.  This test compiles the file for
 gfx950 with the library's own flags and checks, on the assembly of every
-instantiation: no scratch for 128x128 B blocks; the K loop's vector-memory
-instructions are exactly one stage's loads, after its one vmcnt(0); the
-prologue issues 18 loads before vmcnt(9), or waits with vmcnt(0) only
-(1x128 B blocks, whose 32 more scale registers may spill); and no
-inline-assembly load result is touched before a wait covers it (the file
-has none today; the check guards the pattern).
+instantiation: no scratch; the K loop's vector-memory instructions are
+exactly one stage's loads, after its one vmcnt(0); the prologue issues 18
+loads before vmcnt(9); and no inline-assembly load result is touched before
+a wait covers it (the file has none today; the check guards the pattern).
+check_waits(body, counted=False) is the rule for a kernel that may spill:
+vmcnt(0) only.
 """
 import os
 import re
@@ -186,19 +186,12 @@ def asm_lines():
     return _compile()
 
 
-def _b2d(name):
-    """gemm_blk_kernel<A2D, B2D, OUT_BF16>: the second template argument."""
-    return re.search(r"ILb[01]ELb([01])E", name).group(1) == "1"
-
-
 def test_counted_waits_match_the_loads(asm_lines):
     ks = kernels(asm_lines)
     assert len(ks) == 6, sorted(ks)
     for name, (body, scratch) in ks.items():
-        counted = _b2d(name)
-        if counted:
-            assert scratch == 0, f"{name}: {scratch} bytes of scratch; its counted wait needs none"
-        bad = check_waits(body, counted)
+        assert scratch == 0, f"{name}: {scratch} bytes of scratch; its counted wait needs none"
+        bad = check_waits(body, True)
         assert not bad, f"{name}: " + "; ".join(bad)
 
 
