@@ -77,8 +77,9 @@ def kernel_key(recipe, pass_):
 
 # the sources each kernel family is built from: its HBM counters stay valid
 # while these files are unchanged
-KERNEL_SOURCES = {
-    "gemm_": ("gemm.hip", "gemm_blk.hip", "gemm_common.hpp", "device.hpp", "host.hpp"),
+KERNEL_SOURCES = {    # first matching prefix wins
+    "gemm_fp8_block128": ("gemm.hip", "gemm_blk.hip", "gemm_common.hpp", "device.hpp", "host.hpp"),
+    "gemm_": ("gemm.hip", "gemm_common.hpp", "device.hpp", "host.hpp"),
     "cast_": ("cast.hip", "device.hpp", "host.hpp"),
     "chan_": ("cast.hip", "device.hpp", "host.hpp"),
     "amax": ("amax.hip", "device.hpp", "host.hpp"),
