@@ -143,6 +143,18 @@ struct Frags {
 // per-lane part of that address is lm = (8 lg + j / 4) * 512 + 64 (j / 4) +
 // 16 (2 h' + (j % 4) / 2) + 8 (j % 2) + 256 wm (h' = lr / 16, j = lr % 16);
 // tile i XORs 64 i into it (the chunk swizzle 4 (k & 3) = 4 (j / 4)).
+// One transposing read.  The compiler makes an LDS read wait for every
+// LDS-DMA load in flight unless the read carries alias information; a
+// restrict-qualified pointer gives it some, and the compiler then separates
+// the read from the loads by their addresses, as it does for the plain
+// ds_read_b128 of K-major tiles (the loads in flight fill the other stage
+// buffer; the stage's own loads were waited for at the barrier).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i16x4 read_tr16(const uint8_t* __restrict__ p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
 template <int H, int LD>
 __device__ __forceinline__ void op_read(i32x4 (&x)[4][2], int d, const uint8_t* base, uint32_t lb) {
   if (LD == LD_KMAJOR) {
@@ -152,10 +164,7 @@ __device__ __forceinline__ void op_read(i32x4 (&x)[4][2], int d, const uint8_t* 
   } else {
     const int tile = d >> 2, s = (d >> 1) & 1, q = d & 1;
     const int S = 2 * H + s;
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const uint8_t* p = base + (16 * S + 4 * q) * 512 + (lb ^ (uint32_t)(64 * tile));
-    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    const i16x4 v = read_tr16(base + (16 * S + 4 * q) * 512 + (lb ^ (uint32_t)(64 * tile)));
     const int2 w2 = __builtin_bit_cast(int2, v);
     if (q == 0) {
       x[tile][s].x = w2.x;
@@ -434,15 +443,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
   constexpr int DS_NEXT = DS_HALF + (MX ? 8 : 0);
   // MXFP4: phase A also reads the stage's second scale dword (used in phase C)
   constexpr int DS_A = DS_HALF + (OP == OP_FP4 ? 8 : 0);
-  // The compiler makes a transposing LDS read wait for every LDS-DMA load
-  // still in flight.  With an MN-major operand the schedule therefore keeps
-  // them apart: phase A reads on its second half of MFMAs (the previous
-  // loads have landed by then), phase C reads on its first half and issues
-  // the loads on its second half.
-  constexpr bool SPLIT = LDA == LD_MNMAJOR || LDB == LD_MNMAJOR;
-  constexpr int A_DS0 = SPLIT ? NMFMA / 2 : 0;        // first MFMA carrying phase A's reads
-  constexpr int C_VM0 = SPLIT ? NMFMA / 2 : 0;        // first MFMA carrying phase C's loads
-
   Frags f0, f1;
   // MX scale words of the tiles: MXFP8 one dword per row and stage (mxa /
   // mxb, the next stage's in nxa / nxb); MXFP4 dword 0 in mxa / mxb (phase
@@ -507,12 +507,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
     for (int m = 0; m < NMFMA; ++m) {
       mfma_one<OP, SC, AFMT, BFMT>(acc, f0, mxa, mxb, 0, lg, m);
       __builtin_amdgcn_sched_barrier(0);
-      if (m >= A_DS0) {
 #pragma unroll
-        for (int d = share_lo(DS_A, HALF, m - A_DS0); d < share_hi(DS_A, HALF, m - A_DS0); ++d) {
-          if (d < DS_HALF) frag_read<1, LDA, LDB>(f1, d, curA, curB, lba, lbb);
-          else mx_item(m1a, m1b, kt, d - DS_HALF, 1);
-        }
+      for (int d = share_lo(DS_A, HALF, m); d < share_hi(DS_A, HALF, m); ++d) {
+        if (d < DS_HALF) frag_read<1, LDA, LDB>(f1, d, curA, curB, lba, lbb);
+        else mx_item(m1a, m1b, kt, d - DS_HALF, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -539,11 +537,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_kernel(GemmArgs g) {
         else if (OP == OP_FP4) mx_item(mxa, mxb, kt + 1, d - DS_HALF, 0);
         else mx_item(nxa, nxb, kt + 1, d - DS_HALF, 0);
       }
-      if (m >= C_VM0) {
 #pragma unroll
-        for (int v = share_lo(NVM, NMFMA - C_VM0, m - C_VM0); v < share_hi(NVM, NMFMA - C_VM0, m - C_VM0); ++v)
-          issue_item(kt + 2, v);
-      }
+      for (int v = share_lo(NVM, NMFMA, m); v < share_hi(NVM, NMFMA, m); ++v) issue_item(kt + 2, v);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (NEXT && MX && OP != OP_FP4) {
