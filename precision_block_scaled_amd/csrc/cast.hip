@@ -161,6 +161,24 @@ __device__ __forceinline__ uint32_t hw_fp4x8(const float* v) {
   return w;
 }
 
+// NVFP4 block scale: the E4M3 code of d_val >= 0 (saturating at 448, as
+// enc_E4M3 with its clamp), its exact value d, and the encode factor e_b =
+// fp32(S / d) (FLT_MAX where the quotient overflows).  A block whose scale
+// rounds to 0 gets e_b = 0, so its codes are the signed zeros of its values.
+struct NvScale4 {
+  uint32_t code;
+  float e_b;
+};
+__device__ __forceinline__ NvScale4 nv_block_scale(float d_val, float S) {
+  NvScale4 r;
+  r.code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(d_val, 0.0f, 448.0f), 0.0f, 0, false) &
+           0xFFu;
+  const float d = __builtin_amdgcn_cvt_f32_fp8((int)r.code, 0);
+  const float e_b = fminf(S / d, 3.40282346638528859812e+38f);
+  r.e_b = d == 0.0f ? 0.0f : e_b;
+  return r;
+}
+
 // 16 bf16 values (bit patterns) times s -> 16 FP8 codes.
 template <int FMT>
 __device__ __forceinline__ uint4 hw_fp8x16(const uint32_t* b, float s) {
@@ -181,20 +199,16 @@ template <bool SR>
 __device__ __forceinline__ uint32_t nvfp4_block(const float* v, uint32_t abits, float S,
                                                 const uint32_t* rnd, uint2* packed) {
   const float a_b = __uint_as_float(abits);
-  const float d_val = (a_b / 6.0f) * S;
-  const uint32_t d_code = enc_e4m3(d_val);              // non-negative input: no sign bit
-  const float d = dec_e4m3_pos(d_code);
+  const NvScale4 sc = nv_block_scale((a_b / 6.0f) * S, S);
   uint32_t q[16];
-  if (d == 0.0f) {
+  if (sc.e_b == 0.0f) {     // the signed zeros, without the multiplies (fewer live registers under SR)
 #pragma unroll
     for (int i = 0; i < 16; ++i) q[i] = (__float_as_uint(v[i]) >> 28) & 0x8u;
     *packed = pack_e2m1_16(q);
   } else {
-    float e_b = S / d;
-    if (__float_as_uint(e_b) == 0x7F800000u) e_b = 3.40282346638528859812e+38f;
     float x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = v[i] * e_b;
+    for (int i = 0; i < 16; ++i) x[i] = v[i] * sc.e_b;
     if (SR) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) q[i] = sr_e2m1(x[i], rnd[i]);
@@ -203,7 +217,7 @@ __device__ __forceinline__ uint32_t nvfp4_block(const float* v, uint32_t abits, 
       *packed = make_uint2(hw_fp4x8(x), hw_fp4x8(x + 8));
     }
   }
-  return d_code;
+  return sc.code;
 }
 
 // Quantize one strip (a tile row if ROWDIR, else a tile column) of `len`
@@ -551,32 +565,8 @@ __device__ __forceinline__ void quantize_segment(const float* v, uint32_t mbits,
     }
     if (valid) *(uint2*)codes = o;
   } else {  // R_NV
-    const float S = tscale;
-    const float a_b = __uint_as_float(mbits);
-    const uint32_t d_code = enc_e4m3((a_b / 6.0f) * S);
-    const float d = dec_e4m3_pos(d_code);
     uint2 o;
-    if (d == 0.0f) {
-      uint32_t q[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) q[i] = (__float_as_uint(v[i]) >> 28) & 0x8u;
-      o = pack_e2m1_16(q);
-    } else {
-      float e_b = S / d;
-      if (__float_as_uint(e_b) == 0x7F800000u) e_b = 3.40282346638528859812e+38f;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = v[i] * e_b;
-      if (SR) {
-        uint32_t q[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) q[i] = sr_e2m1(x[i], rnd[i]);
-        o = pack_e2m1_16(q);
-      } else {
-        o.x = hw_fp4x8(x);
-        o.y = hw_fp4x8(x + 8);
-      }
-    }
+    const uint32_t d_code = nvfp4_block<SR>(v, mbits, tscale, rnd, &o);
     if (valid) {
       *(uint2*)codes = o;
       *sc8 = (uint8_t)d_code;
@@ -601,14 +591,91 @@ __device__ __forceinline__ void wg_amax_fold(uint32_t v, uint32_t* out, uint32_t
   }
 }
 
-// Row copy: thread = 16-value segment of a row.  Each lane does U = 4
-// segments per step (the wave covers 256 consecutive segments), all loads
-// issued before any arithmetic.  No LDS.  Segment s of the flat tensor is
-// values 16 s .. 16 s + 15 wherever the row breaks fall (the row length is
-// a multiple of 16), and every output is row-major with the blocks along
-// the row, so input, codes, block scales and the SR counter are all linear
-// in s: no row / column split is needed (the row length is a multiple of
-// the block, so a block never straddles rows).
+// Quantize 8 row values v (fp32) held by a lane, with the row block spread
+// over 2 (NVFP4), 4 (MX) or 16 (1x128) neighbouring lanes (ch: the lane's
+// place among 16 such lanes); writes the codes (8 bytes, or 4 for E2M1) and,
+// from the block's first lane, its scale.  SR (E2M1 recipes): rnd holds the
+// values' stochastic-rounding words.
+template <int RECIPE, int FMT, bool SR = false>
+__device__ __forceinline__ void quantize_row8(const float* v, uint32_t mbits, float tscale, bool valid, int ch,
+                                              uint8_t* codes, uint8_t* sc8, float* sc32,
+                                              const uint32_t* rnd = nullptr) {
+  auto e2m1x8 = [&](const float* x) {
+    if (!SR) return hw_fp4x8(x);
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= sr_e2m1(x[i], rnd[i]) << (4 * i);
+    return w;
+  };
+  if (RECIPE == R_NV || RECIPE == R_MX4) {
+    uint32_t w;
+    bool writer;
+    uint32_t scode;
+    if (RECIPE == R_NV) {
+      const uint32_t m = group_max<2>(mbits);
+      const float S = tscale;
+      const NvScale4 sc = nv_block_scale((__uint_as_float(m) / 6.0f) * S, S);
+      scode = sc.code;
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = v[i] * sc.e_b;
+      w = e2m1x8(x);
+      writer = (ch & 1) == 0;
+    } else {
+      scode = mx4_e8m0_from_f32_amax(group_max<4>(mbits));
+      const float s = mx_inv_scale(scode);
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = v[i] * s;
+      w = e2m1x8(x);
+      writer = (ch & 3) == 0;
+    }
+    if (valid) {
+      *(uint32_t*)codes = w;
+      if (writer) *sc8 = (uint8_t)scode;
+    }
+    return;
+  }
+  float s = tscale;
+  bool writer = false;
+  uint32_t word = 0;
+  if (RECIPE == R_MX) {
+    const uint32_t c = mx_e8m0_from_bf16_amax(group_max<4>(mbits) >> 16);
+    s = mx_inv_scale(c);
+    writer = (ch & 3) == 0;
+    word = c;
+  } else if (RECIPE == R_BLOCK128) {
+    s = scale_from_amax(__uint_as_float(group_max<16>(mbits)), 448.0f);
+    writer = ch == 0;
+  } else if (RECIPE == R_B128P2) {
+    const uint32_t c = mx_e8m0_from_bf16_amax(group_max<16>(mbits) >> 16);
+    s = mx_inv_scale(c);
+    writer = ch == 0;
+    word = c * 0x01010101u;
+  }
+  uint2 o;
+  o.x = hw_fp8x4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+  o.y = hw_fp8x4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+  if (valid) {
+    *(uint2*)codes = o;
+    if (writer) {
+      if (RECIPE == R_MX) *sc8 = (uint8_t)word;
+      else if (RECIPE == R_BLOCK128) *sc32 = 1.0f / s;
+      else if (RECIPE == R_B128P2) *(uint32_t*)sc32 = word;
+    }
+  }
+}
+
+// Row copy: a lane quantizes units of 8 consecutive values (one 16-byte
+// load), U = 8 units per step; unit q of the flat tensor is values 8 q ..
+// 8 q + 7, and the 64 lanes of one load instruction take 64 consecutive
+// units, so every load reads 1 KB of contiguous input (32 bytes per lane as
+// two 16-byte loads, every instruction touching 2 KB, streamed 6% slower).
+// Every output is row-major with the blocks along the row and the row
+// length is a multiple of the block, so input, codes, block scales and the
+// SR counter are all linear in q, a block of 16, 32 or 128 values is 2, 4 or
+// 16 neighbouring lanes (never straddling a row), and a block is either
+// wholly inside the tensor or wholly past its end.  No LDS.
 template <int RECIPE, int FMT, bool SR, bool AMAX>
 __global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg) {
   const int lane = threadIdx.x & 63;
@@ -616,53 +683,46 @@ __global__ __launch_bounds__(256) void cast_row_kernel(CastArgs a, int64_t nseg)
   const int64_t wave0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   float tscale = 0.0f;
   if (RECIPE == R_TENSOR || RECIPE == R_NV) tscale = *a.scale;
+  constexpr bool E2M1 = RECIPE == R_NV || RECIPE == R_MX4;
+  const int64_t nu = 2 * nseg;
   uint32_t amx = 0;
-  constexpr int U = 4;
-  for (int64_t wt = wave0; wt * 64 * U < nseg; wt += waves) {
-    uint32_t w[U][8];
-    bool ok[U];
+  constexpr int U = 8;
+  for (int64_t wt = wave0; wt * 64 * U < nu; wt += waves) {
+    uint4 w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t s = wt * 64 * U + u * 64 + lane;
-      ok[u] = s < nseg;
-      const int64_t sc = ok[u] ? s : 0;
-      const bf16_t* p = a.x + sc * 16;
-      const uint4 v0 = ld_nt16(p), v1 = ld_nt16(p + 8);
-      w[u][0] = v0.x; w[u][1] = v0.y; w[u][2] = v0.z; w[u][3] = v0.w;
-      w[u][4] = v1.x; w[u][5] = v1.y; w[u][6] = v1.z; w[u][7] = v1.w;
+      const int64_t q = wt * 64 * U + u * 64 + lane;
+      w[u] = ld_nt16(a.x + (q < nu ? q : 0) * 8);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t s = wt * 64 * U + u * 64 + lane;
-      float v[16];
-      bf16x16_to_f32(w[u], v);
-      const uint32_t m16 = bf16_absmax16(w[u]);
-      if (AMAX && ok[u]) amx = amx > m16 ? amx : m16;
-      uint32_t rnd[16];
-      if (SR) {                                   // logical indices 16 s .. 16 s + 15: four calls
+      const int64_t q = wt * 64 * U + u * 64 + lane;
+      const bool valid = q < nu;
+      const uint32_t w4[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+      u16x2 m2 = {0, 0};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint4 r4 = sr_words4((uint64_t)(s * 4 + k), a.seed);
-          rnd[4 * k] = r4.x;
-          rnd[4 * k + 1] = r4.y;
-          rnd[4 * k + 2] = r4.z;
-          rnd[4 * k + 3] = r4.w;
-        }
+      for (int k = 0; k < 4; ++k) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w4[k] & 0x7FFF7FFFu));
+      const uint32_t m8 = m2.x > m2.y ? m2.x : m2.y;
+      if (AMAX && valid) amx = amx > m8 ? amx : m8;
+      float f[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        f[2 * k] = __uint_as_float(w4[k] << 16);
+        f[2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
       }
-      uint8_t* codes = (RECIPE == R_NV || RECIPE == R_MX4) ? a.row_codes + s * 8 : a.row_codes + s * 16;
+      uint32_t rnd[8];
+      if (SR) {                                   // logical indices 8 q .. 8 q + 7: two calls
+        const uint4 r0 = sr_words4((uint64_t)(2 * q), a.seed), r1 = sr_words4((uint64_t)(2 * q + 1), a.seed);
+        rnd[0] = r0.x; rnd[1] = r0.y; rnd[2] = r0.z; rnd[3] = r0.w;
+        rnd[4] = r1.x; rnd[5] = r1.y; rnd[6] = r1.z; rnd[7] = r1.w;
+      }
+      uint8_t* codes = a.row_codes + q * (E2M1 ? 4 : 8);
       uint8_t* sc8 = nullptr;
       float* sc32 = nullptr;
-      bool writer = true;
-      if (RECIPE == R_MX || RECIPE == R_MX4) {          // 32-value blocks: 2 segments
-        sc8 = (uint8_t*)a.row_scales + s / 2;
-        writer = (s & 1) == 0;
-      } else if (RECIPE == R_NV) {                      // 16-value blocks: 1 segment
-        sc8 = (uint8_t*)a.row_scales + s;
-      } else if (RECIPE == R_BLOCK128 || RECIPE == R_B128P2) {   // 128-value blocks: 8 segments
-        sc32 = (float*)a.row_scales + s / 8;
-        writer = (s & 7) == 0;
-      }
-      quantize_segment<RECIPE, FMT, SR>(v, m16 << 16, tscale, ok[u], codes, sc8, sc32, writer, rnd);
+      if (RECIPE == R_MX || RECIPE == R_MX4) sc8 = (uint8_t*)a.row_scales + q / 4;
+      else if (RECIPE == R_NV) sc8 = (uint8_t*)a.row_scales + q / 2;
+      else if (RECIPE == R_BLOCK128 || RECIPE == R_B128P2) sc32 = (float*)a.row_scales + q / 16;
+      quantize_row8<RECIPE, FMT, SR>(f, m8 << 16, tscale, valid, lane & 15, codes, sc8, sc32, rnd);
     }
   }
   if (AMAX) {
@@ -825,79 +885,6 @@ __global__ __launch_bounds__(256, 2) void cast_col_kernel(CastArgs a) {
 // row piece of the row copy), 512 or 2048 workgroups no faster.
 constexpr int RC_NH = 2;
 constexpr int RC_GRID = 1024;
-
-// Quantize 8 row values v (fp32) held by a lane, with the row block spread
-// over 2 (NVFP4), 4 (MX) or 16 (1x128) neighbouring lanes; writes the codes
-// (8 bytes, or 4 for E2M1) and, from the block's first lane, its scale.
-template <int RECIPE, int FMT>
-__device__ __forceinline__ void quantize_row8(const float* v, uint32_t mbits, float tscale, bool valid, int ch,
-                                              uint8_t* codes, uint8_t* sc8, float* sc32) {
-  if (RECIPE == R_NV || RECIPE == R_MX4) {
-    uint32_t w;
-    bool writer;
-    uint32_t scode;
-    if (RECIPE == R_NV) {
-      const uint32_t m = group_max<2>(mbits);
-      const float S = tscale;
-      scode = enc_e4m3((__uint_as_float(m) / 6.0f) * S);
-      const float d = dec_e4m3_pos(scode);
-      if (d == 0.0f) {
-        w = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w |= ((__float_as_uint(v[i]) >> 28) & 0x8u) << (4 * i);
-      } else {
-        float e_b = S / d;
-        if (__float_as_uint(e_b) == 0x7F800000u) e_b = 3.40282346638528859812e+38f;
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = v[i] * e_b;
-        w = hw_fp4x8(x);
-      }
-      writer = (ch & 1) == 0;
-    } else {
-      scode = mx4_e8m0_from_f32_amax(group_max<4>(mbits));
-      const float s = mx_inv_scale(scode);
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = v[i] * s;
-      w = hw_fp4x8(x);
-      writer = (ch & 3) == 0;
-    }
-    if (valid) {
-      *(uint32_t*)codes = w;
-      if (writer) *sc8 = (uint8_t)scode;
-    }
-    return;
-  }
-  float s = tscale;
-  bool writer = false;
-  uint32_t word = 0;
-  if (RECIPE == R_MX) {
-    const uint32_t c = mx_e8m0_from_bf16_amax(group_max<4>(mbits) >> 16);
-    s = mx_inv_scale(c);
-    writer = (ch & 3) == 0;
-    word = c;
-  } else if (RECIPE == R_BLOCK128) {
-    s = scale_from_amax(__uint_as_float(group_max<16>(mbits)), 448.0f);
-    writer = ch == 0;
-  } else if (RECIPE == R_B128P2) {
-    const uint32_t c = mx_e8m0_from_bf16_amax(group_max<16>(mbits) >> 16);
-    s = mx_inv_scale(c);
-    writer = ch == 0;
-    word = c * 0x01010101u;
-  }
-  uint2 o;
-  o.x = hw_fp8x4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
-  o.y = hw_fp8x4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
-  if (valid) {
-    *(uint2*)codes = o;
-    if (writer) {
-      if (RECIPE == R_MX) *sc8 = (uint8_t)word;
-      else if (RECIPE == R_BLOCK128) *sc32 = 1.0f / s;
-      else if (RECIPE == R_B128P2) *(uint32_t*)sc32 = word;
-    }
-  }
-}
 
 template <int RECIPE, int FMT, bool ROW, bool AMAX, int NH>
 __global__ __launch_bounds__(256) void cast_rc_kernel(CastArgs a) {

@@ -30,52 +30,6 @@ __device__ __forceinline__ uint4 ld_nt16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Round-to-nearest-even right shift of x by s (1 <= s <= 31).
-__device__ __forceinline__ uint32_t rne_shr(uint32_t x, uint32_t s) {
-  uint32_t q = x >> s;
-  uint32_t r = x & ((1u << s) - 1u);
-  uint32_t h = 1u << (s - 1u);
-  return q + (uint32_t)((r > h) | ((r == h) & (q & 1u)));
-}
-
-// E4M3 (bias 7, max 448 = 0x7E).  Normal results: fp32 biased exponent
-// e >= 121 (2^-6); the E4M3 code is (e - 120) << 3 | top 3 mantissa bits,
-// i.e. (a - (120 << 23)) >> 20 rounded.  Subnormal results: a / 2^-9
-// rounded, = m24 >> (141 - e).
-__device__ __forceinline__ uint32_t enc_e4m3(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a > 0x43E00000u) {                 // > 448
-    code = 0x7Eu;
-  } else {
-    uint32_t e = a >> 23;
-    if (e >= 121u) {
-      code = rne_shr(a - (120u << 23), 20u);
-    } else {
-      uint32_t m = (a & 0x7FFFFFu) | (e ? 0x800000u : 0u);
-      uint32_t s = 141u - (e ? e : 1u);
-      code = (s > 25u) ? 0u : rne_shr(m, s);
-    }
-  }
-  return sign | code;
-}
-
-// Exact value of a non-negative E4M3 code (0..0x7E) as float.
-__device__ __forceinline__ float dec_e4m3_pos(uint32_t c) {
-  uint32_t e = c >> 3, m = c & 7u;
-  if (e == 0) return (float)m * 0.001953125f;             // m * 2^-9, exact
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
-}
-
-// Magnitude of an E2M1 code's low 3 bits as float (0, .5, 1, 1.5, 2, 3, 4, 6).
-__device__ __forceinline__ float dec_e2m1_mag(uint32_t c) {
-  uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  if (e == 0) return m ? 0.5f : 0.0f;
-  return __uint_as_float(((e + 126u) << 23) | (m << 22));
-}
-
 // MXFP8 block exponent: E8M0 code of the smallest e in [-127, 127] with
 // amax <= 448 * 2^e, from the bf16 bits of a non-negative block maximum.
 // amax = 1.f * 2^(E-127): e = E - 135 if f <= 0.75, else E - 134.
