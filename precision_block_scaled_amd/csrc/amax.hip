@@ -91,7 +91,13 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint4* __restrict_
 }
 
 // amax of the RHT16 output along the rows: one work item = one group of 16
-// rows x 8 columns (sixteen 16-byte loads, coalesced across the wave).
+// rows x 8 columns (sixteen 16-byte loads, coalesced across the wave).  The
+// transform's arithmetic is trimmed to what the maximum needs, with the same
+// result bit for bit: the sign flips go onto the packed bf16 words (both
+// values of a word are in one row, so they share sigma_r), and the exact
+// multiply by 1/4 is applied once to the final maximum -- rounding x / 4 is
+// monotone in |x|, so the maximum of the rounded values is the rounding of
+// the maximum.
 __global__ __launch_bounds__(256) void amax_rht_kernel(const bf16_t* __restrict__ x, int64_t rows,
                                                        int64_t cols, uint64_t seed, uint32_t* out) {
   __shared__ uint32_t s_mask;
@@ -103,7 +109,7 @@ __global__ __launch_bounds__(256) void amax_rht_kernel(const bf16_t* __restrict_
     if (threadIdx.x == 0) s_mask = (uint32_t)b;
   }
   __syncthreads();
-  const uint32_t sign_mask = s_mask;
+  const uint32_t sign_mask = __builtin_amdgcn_readfirstlane(s_mask);
   const int64_t c8n = cols / 8;
   const int64_t items = (rows / 16) * c8n;
   uint32_t m = 0;
@@ -115,21 +121,42 @@ __global__ __launch_bounds__(256) void amax_rht_kernel(const bf16_t* __restrict_
 #pragma unroll
     for (int r = 0; r < 16; ++r) v[r] = ld_nt16(p + r * cols);
 #pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t sx = ((sign_mask >> r) & 1u) ? 0x80008000u : 0u;
+      v[r].x ^= sx;
+      v[r].y ^= sx;
+      v[r].z ^= sx;
+      v[r].w ^= sx;
+    }
+#pragma unroll
     for (int c = 0; c < 8; ++c) {
       float u[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        uint32_t w = (c < 2) ? v[r].x : (c < 4) ? v[r].y : (c < 6) ? v[r].z : v[r].w;
-        u[r] = bf16_to_float((c & 1) ? (w >> 16) : (w & 0xFFFFu));
+        const uint32_t w = (c < 2) ? v[r].x : (c < 4) ? v[r].y : (c < 6) ? v[r].z : v[r].w;
+        u[r] = __uint_as_float((c & 1) ? (w & 0xFFFF0000u) : (w << 16));
       }
-      rht16(u, sign_mask);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        uint32_t a = __float_as_uint(u[r]) & 0x7FFFFFFFu;
-        m = m > a ? m : a;
+      for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if ((i & h) == 0) {
+            const float a = u[i], b = u[i + h];
+            u[i] = a + b;
+            u[i + h] = a - b;
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const uint32_t a = __float_as_uint(u[r]) & 0x7FFFFFFFu, b = __float_as_uint(u[r + 1]) & 0x7FFFFFFFu;
+        const uint32_t ab = a > b ? a : b;
+        m = m > ab ? m : ab;
       }
     }
   }
+  // the 1/4 of the transform, on the maximum (inf stays inf; NaN bits stay NaN)
+  m = __float_as_uint(__uint_as_float(m) * 0.25f) & 0x7FFFFFFFu;
   block_max_atomic(m, out);
 }
 

@@ -113,15 +113,33 @@ __device__ __forceinline__ uint2 pack_e2m1_16(const uint32_t* q) {
   return w;
 }
 
-// Max over the 16 lanes that share bits 4..5 of the lane id.
-__device__ __forceinline__ uint32_t max16lanes(uint32_t v) {
+// Max over aligned groups of G lanes.  Within a 16-lane row the exchanges
+// are DPP moves (vector ALU, no LDS permute): quad_perm [1,0,3,2] and
+// [2,3,0,1] reduce each quad, row_half_mirror (lane i <-> 7 - i of each
+// 8-lane half) brings in the other quad of the half, row_mirror (i <-> 15 -
+// i) the other half of the row.  Wider groups exchange through __shfl_xor.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t x) {
+  const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+  return x > y ? x : y;
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+  if (G >= 2) v = dpp_max<0xB1>(v);
+  if (G >= 4) v = dpp_max<0x4E>(v);
+  if (G >= 8) v = dpp_max<0x141>(v);
+  if (G >= 16) v = dpp_max<0x140>(v);
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    uint32_t w = (uint32_t)__shfl_xor((int)v, o, 64);
-    v = v > w ? v : w;
+  for (int o = 16; o < G; o <<= 1) {
+    const uint32_t u = (uint32_t)__shfl_xor((int)v, o, 64);
+    v = v > u ? v : u;
   }
   return v;
 }
+
+// Max over the 16 lanes that share bits 4..5 of the lane id.
+__device__ __forceinline__ uint32_t max16lanes(uint32_t v) { return group_max<16>(v); }
 
 // Encoding by the gfx950 conversion instructions (v_cvt_pk_fp8_f32,
 // v_cvt_pk_bf8_f32, v_cvt_scalef32_pk_fp4_f32 with scale 1): they round to
@@ -491,17 +509,6 @@ __device__ __forceinline__ uint32_t bf16_absmax16(const uint32_t* w) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
   return m.x > m.y ? m.x : m.y;
-}
-
-// Max over lane groups of 2 or 8 (xor 1, 2, 4).
-template <int G>
-__device__ __forceinline__ uint32_t group_max(uint32_t v) {
-#pragma unroll
-  for (int o = 1; o < G; o <<= 1) {
-    const uint32_t u = (uint32_t)__shfl_xor((int)v, o, 64);
-    v = v > u ? v : u;
-  }
-  return v;
 }
 
 __device__ __forceinline__ void bf16x16_to_f32(const uint32_t* w, float* v) {
