@@ -2,7 +2,8 @@
 //
 // Four kernel templates, each instantiated per recipe:
 //   * cast_row_kernel: the row copy with 1D blocks (every GEMM operand but
-//     2D-blocked weights): a lane owns 16-value segments, no LDS;
+//     2D-blocked weights): a lane quantizes 8 consecutive values at a time,
+//     no LDS;
 //   * cast_rc_kernel: the transposed (col) copy with 1D blocks, alone or
 //     with the row copy from the same read, through a 256 x 128 tile in LDS;
 //   * cast_col_kernel: the col copy with the Hadamard transform or
@@ -496,9 +497,12 @@ __global__ __launch_bounds__(128) void cast_tile_kernel(CastArgs a) {
 
 // ---------------------------------------------------------------------------
 // Single-orientation casts with 1D blocks: the common case of a cast per
-// GEMM operand.  Both kernels work on 16-value segments (one per lane and
-// step): NVFP4 blocks are one segment, MXFP8 blocks two neighbouring lanes,
-// 1x128 blocks eight, so block maxima reduce with at most three lane swaps.
+// GEMM operand.  The row copy works on 8-value units (quantize_row8: a block
+// of 16, 32 or 128 values is 2, 4 or 16 neighbouring lanes); the col copy
+// (cast_rc_kernel below) and the Hadamard / stochastic-rounding col copy
+// (cast_col_kernel) on 16-value segments of a column (quantize_segment:
+// NVFP4 blocks are one segment, MX blocks two neighbouring lanes, 1x128
+// blocks eight).  Block maxima reduce across lanes with DPP moves.
 //
 // Encoding uses the gfx950 conversion instructions, clamped first so that
 // they saturate (see hw_fp8x4 / hw_fp4x8 above).
