@@ -150,6 +150,24 @@ __device__ __forceinline__ uint32_t max16lanes(uint32_t v) { return group_max<16
 // the same code every time.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
+// Max of the 15-bit magnitudes of 8 bf16 values (one 16-byte load).
+__device__ __forceinline__ uint32_t bf16_absmax8(const uint4& w) {
+  const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+  u16x2 m2 = {0, 0};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w4[k] & 0x7FFF7FFFu));
+  return m2.x > m2.y ? m2.x : m2.y;
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4& w, float* f) {
+  const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f[2 * k] = __uint_as_float(w4[k] << 16);
+    f[2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
+  }
+}
+
 template <int FMT>
 __device__ __forceinline__ uint32_t hw_fp8x4(float a, float b, float c, float d) {
   if (FMT == F_E4M3) {
@@ -1059,22 +1077,18 @@ __global__ __launch_bounds__(256) void chan_row_kernel(CastArgs a) {
   __shared__ uint32_t s_part[4];
   uint32_t m = 0;
   if (NCH > 0) {
-    uint32_t w[NCH > 0 ? NCH : 1][8];
+    // 8-value units j T + tl of the row (one 16-byte load each, so the
+    // lanes of a load instruction read contiguous input)
+    const int64_t upr = 2 * spr;
+    uint4 w[NCH > 0 ? 2 * NCH : 1];
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int64_t sg = (int64_t)j * T + tl;
-      if (live && sg < spr) {
-        const uint4 v0 = ld_nt16(xr + sg * 16), v1 = ld_nt16(xr + sg * 16 + 8);
-        w[j][0] = v0.x; w[j][1] = v0.y; w[j][2] = v0.z; w[j][3] = v0.w;
-        w[j][4] = v1.x; w[j][5] = v1.y; w[j][6] = v1.z; w[j][7] = v1.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[j][i] = 0u;
-      }
+    for (int j = 0; j < 2 * NCH; ++j) {
+      const int64_t q = (int64_t)j * T + tl;
+      w[j] = (live && q < upr) ? ld_nt16(xr + q * 8) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const uint32_t mj = bf16_absmax16(w[j]);
+    for (int j = 0; j < 2 * NCH; ++j) {
+      const uint32_t mj = bf16_absmax8(w[j]);
       m = m > mj ? m : mj;
     }
     m = group_max<64>(m);
@@ -1087,12 +1101,11 @@ __global__ __launch_bounds__(256) void chan_row_kernel(CastArgs a) {
     }
     const float s = scale_from_amax(__uint_as_float(m << 16), 448.0f);
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int64_t sg = (int64_t)j * T + tl;
-      float v[16];
-      bf16x16_to_f32(w[j], v);
-      quantize_segment<R_TENSOR, F_E4M3, false>(v, 0u, s, live && sg < spr, cr + sg * 16, nullptr, nullptr,
-                                                false, nullptr);
+    for (int j = 0; j < 2 * NCH; ++j) {
+      const int64_t q = (int64_t)j * T + tl;
+      float f[8];
+      bf16x8_to_f32(w[j], f);
+      quantize_row8<R_TENSOR, F_E4M3>(f, 0u, s, live && q < upr, 0, cr + q * 8, nullptr, nullptr);
     }
     if (live && tl == 0) ((float*)a.row_scales)[row] = 1.0f / s;
   } else {
