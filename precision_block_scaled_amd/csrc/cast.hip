@@ -1054,11 +1054,11 @@ __global__ __launch_bounds__(256) void cast_rc_kernel(CastArgs a) {
 // Channel-wise FP8: one scale per row of the copy.
 //
 // Row copy: a team of T lanes (one wave, or the whole 256-thread workgroup
-// for long rows) owns a row; lane l holds the row's 16-value segments
-// l, l + T, ... (up to NCH of them) in registers, so the row is read from
-// HBM once: max over the team, scale, encode, store.  Rows longer than
-// 256 * 16 * 16 values (NCH = 0) are read twice (the second read mostly
-// from L2).
+// for long rows) owns a row; lane l holds the row's 8-value units l, l + T,
+// ... (up to 2 NCH of them, one 16-byte load each) in registers, so the row
+// is read from HBM once: max over the team, scale, encode, store.  Rows
+// longer than 256 * 16 * 16 values (NCH = 0) are read twice (the second
+// read mostly from L2).
 //
 // Col copy: one scale per column of x.  chan_colmax_kernel folds column
 // maxima into col_scales (fp32 bits, cleared first); cast_col_kernel
