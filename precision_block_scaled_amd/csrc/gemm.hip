@@ -671,10 +671,14 @@ __device__ __forceinline__ void nv_scale_item(const NvScale& s, int kt, uint8_t*
 // 8 E2M1 codes (element 2k in the low nibble of byte k) times an fp16 scale,
 // as the fp16 operand of one K=16 step.
 __device__ __forceinline__ i32x4 nv_decode(uint32_t raw, f16x2 sc) {
-  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 0) * sc;
-  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 1) * sc;
-  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 2) * sc;
-  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 3) * sc;
+  // the four conversions first, then the four multiplies: each multiply
+  // waits for its conversion's result, and four independent chains hide
+  // that latency where one register reused for every pair would not
+  const f16x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 0);
+  const f16x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 1);
+  const f16x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 2);
+  const f16x2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 3);
+  const f16x2 p0 = c0 * sc, p1 = c1 * sc, p2 = c2 * sc, p3 = c3 * sc;
   i32x4 r;
   r.x = __builtin_bit_cast(int, p0);
   r.y = __builtin_bit_cast(int, p1);
