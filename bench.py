@@ -13,7 +13,10 @@ One step = every recipe (BF16, FP8 current, FP8 delayed, FP8 1x128/128x128,
 MXFP8, NVFP4) over the 12 GEMMs in autocast mode: each GEMM quantizes both
 of its operands from bf16 (amax, scale, cast, RHT, SR as the recipe needs)
 and then runs the GEMM, bf16 output.  With --pre-quantize the step times the
-GEMMs alone on operands quantized beforehand.  Inputs are seeded synthetic
+GEMMs alone on operands quantized beforehand.  As in the pages' tool,
+--no-fp8 drops MXFP8, --no-fp4 the 4-bit recipes, --num_hidden_layers sets
+the layer count of the model-level projection, and -o writes the per-GEMM
+speedup-over-BF16 chart of the timed mode.  Inputs are seeded synthetic
 tensors resident in HBM before timing starts; each layer has its own X, W
 and dY.
 
@@ -113,9 +116,9 @@ def upload_bf16(bits, dev):
 # layer (GQA 32 query / 8 key-value heads, gated MLP)
 MODELS = {
     "codonfm": dict(hidden=4096, intermediate=16384, heads=32, kv_heads=32, gated=False, micro_batch=31,
-                    seq_len=512),
+                    seq_len=512, num_layers=24),
     "llama3_8b": dict(hidden=4096, intermediate=14336, heads=32, kv_heads=8, gated=True, micro_batch=1,
-                      seq_len=8192),
+                      seq_len=8192, num_layers=32),
 }
 
 
@@ -607,7 +610,7 @@ def model_analysis(runner, recipes, per, pre, layers=24):
     Transformer-based models for low-precision training", "Using autocast mode
     vs pre-quantized mode" and "Interpreting results for a real model"):
     per-recipe speedup over BF16 in both modes, the model's GEMM time for its
-    24 identical layers, the MXFP8 / NVFP4 Fprop ratio per layer, the Dgrad /
+    `layers` identical layers, the MXFP8 / NVFP4 Fprop ratio per layer, the Dgrad /
     Fprop asymmetry per layer, and the weight bytes each recipe stores."""
     P = runner.P
     names = [ls.name for (_, _, _, ls) in runner.layers.values()]
@@ -643,6 +646,50 @@ def model_analysis(runner, recipes, per, pre, layers=24):
         out["dgrad_over_fprop_prequant"] = {r: {n: round(pre[(r, n, "dgrad")][0] / pre[(r, n, "fprop")][0], 3) for n in names}
                                             for r in recipes}
     return out
+
+
+def speedup_table(runner, recipes, per, pre=None):
+    """Per GEMM of the layer, in runner.gemms order: {recipe: [value, ...]},
+    the speedup over BF16 in the timed mode (autocast median, or
+    pre-quantized when `pre` is given) when BF16 was run (BF16 itself then
+    left out), else TFLOP/s.  Returns (labels, table, "speedup" | "TFLOP/s")."""
+    ms = (lambda r, n, p: pre[(r, n, p)][0]) if pre else (lambda r, n, p: float(np.median(per[(r, n, p)]["auto"])))
+    labels = [f"{n}.{p}" for (n, p, *_) in runner.gemms]
+    if "bf16" in recipes:
+        tab = {r: [ms("bf16", n, p) / ms(r, n, p) for (n, p, *_) in runner.gemms] for r in recipes if r != "bf16"}
+        return labels, tab, "speedup"
+    tab = {r: [2.0 * M * N * K / (ms(r, n, p) * 1e-3) / 1e12 for (n, p, M, N, K) in runner.gemms] for r in recipes}
+    return labels, tab, "TFLOP/s"
+
+
+def write_speedup_plot(path, runner, recipes, per, pre, title):
+    """The chart the pages' benchmark writes with -o ("How to optimize
+    Transformer-based models for low-precision training", "Model
+    configuration and training inputs"): for each of the layer's GEMMs
+    (Fprop, Dgrad, Wgrad of QKV, attention-out, MLP-up, MLP-down) one bar per
+    recipe, from speedup_table.  Returns the path written."""
+    import matplotlib
+    matplotlib.use("Agg")
+    import matplotlib.pyplot as plt
+    labels, tab, kind = speedup_table(runner, recipes, per, pre)
+    n = max(1, len(tab))
+    fig, ax = plt.subplots(figsize=(max(8.0, 0.3 * len(labels) * n), 4.8))
+    width = 0.8 / n
+    xs = np.arange(len(labels))
+    for i, (r, ys) in enumerate(tab.items()):
+        ax.bar(xs + (i - (n - 1) / 2) * width, ys, width, label=r)
+    if kind == "speedup":
+        ax.axhline(1.0, color="black", linewidth=0.8)
+    ax.set_xticks(xs)
+    ax.set_xticklabels([l.replace(".", "\n") for l in labels], fontsize=7)
+    ax.set_ylabel("speedup over BF16" if kind == "speedup" else "TFLOP/s")
+    ax.set_title(title, fontsize=9)
+    ax.legend(fontsize=7, ncol=min(n, 6))
+    fig.tight_layout()
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    fig.savefig(path, dpi=120)
+    plt.close(fig)
+    return path
 
 
 def host_info():
@@ -920,6 +967,8 @@ def main():
     ap.add_argument("--intermediate_size", "--intermediate-size", type=int, default=None)
     ap.add_argument("--num_attention_heads", "--num-attention-heads", type=int, default=None)
     ap.add_argument("--num_key_value_heads", "--num-key-value-heads", type=int, default=None)
+    ap.add_argument("--num_hidden_layers", "--num-hidden-layers", type=int, default=None,
+                    help="layers of the model-level projection (identical layers)")
     ap.add_argument("--gated", choices=("yes", "no"), default=None, help="gated MLP (up projection 2x wide)")
     ap.add_argument("--micro_batch_size", "--micro-batch-size", type=int, default=None)
     ap.add_argument("--sequence_length", "--sequence-length", type=int, default=None)
@@ -927,6 +976,11 @@ def main():
     ap.add_argument("--pre-quantize", "--pre_quantize", action="store_true",
                     help="time the GEMMs alone on operands quantized before the timed steps")
     ap.add_argument("--recipes", default=",".join(RECIPES))
+    ap.add_argument("--no-fp8", "--no_fp8", action="store_true", help="drop MXFP8 from the recipes")
+    ap.add_argument("--no-fp4", "--no_fp4", action="store_true",
+                    help="drop the 4-bit recipes (NVFP4, and MXFP4 of the next recipes)")
+    ap.add_argument("-o", "--output", default=None,
+                    help="write the per-GEMM speedup-over-BF16 chart of the timed mode to this image file")
     ap.add_argument("--next-recipes", default=",".join(NEXT_RECIPES),
                     help="recipes beyond the six, timed after the step and reported apart")
     ap.add_argument("--prequant-iters", type=int, default=5)
@@ -944,7 +998,8 @@ def main():
     cfg = dict(MODELS[a.model])
     for key, val in (("hidden", a.hidden_size), ("intermediate", a.intermediate_size),
                      ("heads", a.num_attention_heads), ("kv_heads", a.num_key_value_heads),
-                     ("micro_batch", a.micro_batch_size), ("seq_len", a.sequence_length)):
+                     ("micro_batch", a.micro_batch_size), ("seq_len", a.sequence_length),
+                     ("num_layers", a.num_hidden_layers)):
         if val is not None:
             cfg[key] = val
     if a.num_attention_heads is not None and a.num_key_value_heads is None and a.model == "codonfm":
@@ -967,7 +1022,8 @@ def main():
 
     import precision_block_scaled_amd as P
     P.lib()
-    recipes = [r for r in a.recipes.split(",") if r]
+    dropped = ({"mxfp8"} if a.no_fp8 else set()) | ({"nvfp4", "mxfp4"} if a.no_fp4 else set())
+    recipes = [r for r in a.recipes.split(",") if r and r not in dropped]
     log(f"generating inputs: {a.model} {cfg} tokens={tokens}")
     layers = build_layer_tensors(cfg, tokens, dev)
     runner = Runner(layers, tokens, dev)
@@ -1002,9 +1058,19 @@ def main():
     clock.__exit__(None, None, None)
     per_recipe = recipe_table(runner, recipes, per, pre, cold, lay)
     epi = epilogue_amax_cost(runner) if (not a.no_extras and "fp8_current" in recipes) else None
-    model = model_analysis(runner, recipes, per, pre)
+    model = model_analysis(runner, recipes, per, pre, layers=cfg["num_layers"])
+    plot_path = None
+    if a.output:
+        mode = "pre-quantized" if a.pre_quantize else "autocast"
+        if a.pre_quantize and not pre:
+            log("-o: the pre-quantized chart needs the pre-quantized pass (not run with --no-extras)")
+        else:
+            plot_path = write_speedup_plot(
+                a.output, runner, recipes, per, pre if a.pre_quantize else None,
+                f"{a.model}: hidden {cfg['hidden']}, intermediate {cfg['intermediate']}, {tokens} tokens, {mode}")
+            log(f"wrote {plot_path}")
 
-    next_recipes = [r for r in a.next_recipes.split(",") if r]
+    next_recipes = [r for r in a.next_recipes.split(",") if r and r not in dropped]
     nxt = {}
     if not a.no_extras and next_recipes:
         log(f"next recipes {next_recipes} (reported apart from value)")
@@ -1051,7 +1117,8 @@ def main():
     if dom_name.startswith("gemm_nvfp4"):       # the 4-bit format's own peak, beside the fp16 instruction's
         roof["format_peak_fp4"] = PEAK_TFLOPS["fp4"]
         roof["frac_of_format_peak_fp4"] = round(achieved / PEAK_TFLOPS["fp4"], 4)
-    layer_desc = ("CodonFM-5B layer" if a.model == "codonfm" and cfg == MODELS["codonfm"] else
+    same_layer = all(cfg[k] == MODELS["codonfm"][k] for k in ("hidden", "intermediate", "heads", "kv_heads", "gated"))
+    layer_desc = ("CodonFM-5B layer" if a.model == "codonfm" and same_layer else
                   f"{a.model}-shaped layer (hidden {cfg['hidden']}, intermediate {cfg['intermediate']}, "
                   f"heads {cfg['heads']}/{cfg['kv_heads']} kv, gated {cfg['gated']})")
     line = {
