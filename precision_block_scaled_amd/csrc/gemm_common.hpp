@@ -105,20 +105,27 @@ __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" :
 // past the end re-read the last valid row; their results are never stored).
 // ---------------------------------------------------------------------------
 
-// K-major, direct to LDS (global_load_lds_dwordx4, no registers): load i (of
-// 8) of wave w fills LDS rows 64 w + 8 i .. + 7; lane l owns row
+// K-major, direct to LDS (buffer_load_dwordx4 ... lds, no registers): load i
+// (of 8) of wave w fills LDS rows 64 w + 8 i .. + 7; lane l owns row
 // 64 w + 8 i + l / 8, physical chunk l % 8, i.e. the logical chunk that the
-// swizzle places there.  The tile's row base is wave-uniform; each lane keeps
-// eight 32-bit offsets (row * ld < 2^32 is checked on the host).
+// swizzle places there.  The tile's rows are one buffer resource (base = its
+// first row, range = the bytes to the operand's end, at most 2^32 - 1), so a
+// load is that resource, the lane's 32-bit offset and the stage's byte offset
+// in a scalar register: no per-lane 64-bit address arithmetic (row * ld <
+// 2^32 is checked on the host).
 struct Direct {
-  const uint8_t* base;
+  __amdgpu_buffer_rsrc_t r;
   uint32_t off[8];
 };
+
+constexpr int BUF_RSRC_WORD3 = 0x00020000;   // raw, untyped gfx9 buffer (32-bit data format field)
 
 __device__ __forceinline__ void direct_init(Direct& d, const uint8_t* p, int64_t ld, int rows0, int nrows,
                                             int w) {
   const int lane = threadIdx.x & 63;
-  d.base = p + (int64_t)rows0 * ld;
+  const int64_t span = (int64_t)(nrows - rows0) * ld;
+  d.r = __builtin_amdgcn_make_buffer_rsrc((void*)(p + (int64_t)rows0 * ld), (short)0,
+                                          (int)(uint32_t)(span < 0xFFFFFFFFll ? span : 0xFFFFFFFFll), BUF_RSRC_WORD3);
   const int lim = nrows - rows0 - 1;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -129,16 +136,9 @@ __device__ __forceinline__ void direct_init(Direct& d, const uint8_t* p, int64_t
   }
 }
 
-__device__ __forceinline__ void direct_issue(const Direct& d, int kt, uint8_t* tile, int w) {
-  const uint8_t* g = d.base + (int64_t)kt * ROWB;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_global_load_lds(g + d.off[i], (lds_ptr_t)(tile + (w * 8 + i) * 1024), 16, 0, 0);
-}
-
 __device__ __forceinline__ void direct_item(const Direct& d, int kt, uint8_t* tile, int w, int i) {
-  const uint8_t* g = d.base + (int64_t)kt * ROWB;
-  __builtin_amdgcn_global_load_lds(g + d.off[i], (lds_ptr_t)(tile + (w * 8 + i) * 1024), 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.r, (lds_ptr_t)(tile + (w * 8 + i) * 1024), 16, d.off[i],
+                                           (uint32_t)(kt * ROWB), 0, 0);
 }
 
 // One dword per tile row per stage (MX scales: 4 E8M0 bytes; block-128: one

@@ -105,7 +105,8 @@ def loop_blocks(body):
 
 def check_barrier_waits(block):
     """Violations of 'every s_barrier of this block follows a vmcnt(0) with no
-    vector-memory load issued between the two'."""
+    vector-memory load issued between the two' (a weaker vmcnt(N) wait in
+    between, such as the compiler's own for the barrier, changes nothing)."""
     bad = []
     for i, line in enumerate(block):
         if _op(line) != "s_barrier":
@@ -113,14 +114,12 @@ def check_barrier_waits(block):
         for prev in reversed(block[:i]):
             op = _op(prev)
             if op.startswith(("global_load", "buffer_load", "scratch_load", "flat_load")):
-                bad.append(f"{prev.strip()!r} issued after the last wait before the barrier")
+                bad.append(f"{prev.strip()!r} issued after the last vmcnt(0) before the barrier")
                 break
-            if op == "s_waitcnt" and "vmcnt" in prev:
-                if "vmcnt(0)" not in prev:
-                    bad.append(f"the barrier's wait is {prev.strip()!r}, not vmcnt(0)")
+            if op == "s_waitcnt" and "vmcnt(0)" in prev:
                 break
         else:
-            bad.append("a barrier with no vmcnt wait before it in its block")
+            bad.append("a barrier with no vmcnt(0) before it in its block")
     return bad
 
 
@@ -130,20 +129,17 @@ def _salu(op):
 
 def check_loop_waits(loop):
     """Violations of 'the loop waits for loads only at its s_barrier': every
-    vmcnt wait is vmcnt(0) and reaches the barrier through waits and scalar
-    instructions only (the kernel's explicit wait and the compiler's own
-    for the barrier may both be there, back to back)."""
+    vmcnt wait reaches the barrier through waits and scalar instructions only
+    (the kernel's explicit vmcnt(0) and the compiler's own wait for the
+    barrier may both be there, back to back), and one of them is vmcnt(0)."""
     bad = []
     waits = [(i, l) for i, l in enumerate(loop) if _op(l) == "s_waitcnt" and "vmcnt" in l]
-    if not waits:
-        return ["no vmcnt wait in the K loop"]
+    if not any("vmcnt(0)" in l for _, l in waits):
+        return ["no vmcnt(0) wait in the K loop"]
     for i, l in waits:
-        if "vmcnt(0)" not in l:
-            bad.append(f"the K loop waits with {l.strip()!r}, not vmcnt(0)")
-            continue
         nxt = next((m for m in loop[i + 1:] if _op(m) and not _salu(_op(m))), "")
         if _op(nxt) != "s_barrier":
-            bad.append(f"a vmcnt(0) of the K loop is followed by {nxt.strip()!r}, not its s_barrier")
+            bad.append(f"the K loop waits with {l.strip()!r} away from its barrier (next: {nxt.strip()!r})")
     return bad
 
 
@@ -203,6 +199,10 @@ def test_barrier_checker_catches_an_unguarded_barrier():
     assert check_barrier_waits([l.replace("vmcnt(0)", "vmcnt(4)") for l in good])
     late = good[:3] + ["\tglobal_load_lds_dwordx4 v1, s[0:1]"] + good[3:]
     assert check_barrier_waits(late)
+    late_buf = good[:3] + ["\tbuffer_load_dwordx4 v1, s[4:7], s2 offen lds"] + good[3:]
+    assert check_barrier_waits(late_buf)
+    weaker_after = good[:3] + ["\ts_waitcnt vmcnt(2) lgkmcnt(0)"] + good[4:]
+    assert check_barrier_waits(weaker_after) == []
     body = [".LBB0_2:                                ;   in Loop: Header=BB0_3 Depth=1", "\tv_mfma_x a[0:15]",
             ".LBB0_3:                                ; =>This Inner Loop Header: Depth=1"] + good[1:] + [
             "\ts_cbranch_scc0 .LBB0_2", ".LBB0_4:"]
@@ -224,3 +224,5 @@ def test_checker_catches_a_wait_before_the_barrier_phase():
     assert check_loop_waits(counted)
     no_barrier = [l for l in good if "s_barrier" not in l]
     assert check_loop_waits(no_barrier)
+    both = head + ["\ts_waitcnt vmcnt(0)", "\ts_add_i32 s36, s38, s30", "\ts_waitcnt vmcnt(2) lgkmcnt(0)"] + good[3:]
+    assert check_loop_waits(both) == []
