@@ -101,23 +101,24 @@ __device__ __forceinline__ uint32_t sr_word(uint64_t i, uint64_t seed) {
 
 // Stochastic rounding of v to E2M1 with the 32-bit random r: |v| >= 6 gives
 // 6; otherwise with lo <= |v| < hi adjacent E2M1 magnitudes, round up iff
-// r < ceil((|v| - lo) / (hi - lo) * 2^32).  |v| - lo is exact (Sterbenz or
-// lo = 0) and the scaling by 2^32 / (hi - lo) is a power of two, so the
-// threshold is computed exactly.  Branch-free: below 2 the grid step is 0.5
-// (lo = floor(2|v|) / 2), in [2, 4) it is 1, in [4, 6) it is 2.
+// r < ceil((|v| - lo) / (hi - lo) * 2^32).  Computed on the fp32 bit pattern
+// ua of |v|, exactly: from 1 up, an E2M1 step covers the upper or lower half
+// of a binade (steps 0.5, 1, 2 in [1, 2), [2, 4), [4, 8)), so lo's code is
+// (ua >> 22) - 252 and the position within the step is the 22 mantissa bits
+// below the halving bit, i.e. the threshold is ua << 10 (mod 2^32); in
+// [0.5, 1) lo = 0.5 (code 1) and the position is the whole 23-bit mantissa,
+// ua << 9; below 0.5 lo = 0 and the threshold is ceil(|v| * 2^33), exact in
+// fp32.  A NaN saturates like |v| >= 6 (the code above 6's bit pattern),
+// as the oracle's rule does.
 __device__ __forceinline__ uint32_t sr_e2m1(float v, uint32_t r) {
   const uint32_t u = __float_as_uint(v);
+  const uint32_t ua = u & 0x7FFFFFFFu;
   const uint32_t sign = (u >> 28) & 0x8u;
-  const float a = __uint_as_float(u & 0x7FFFFFFFu);
-  const bool r1 = a < 2.0f, r2 = a < 4.0f;
-  const float f1 = floorf(a * 2.0f);                   // exact: a * 2 is exact
-  const float f2 = floorf(a);
-  const float lo = r1 ? f1 * 0.5f : (r2 ? f2 : 4.0f);
-  const uint32_t lo_code = r1 ? (uint32_t)f1 : (r2 ? (f2 < 3.0f ? 4u : 5u) : 6u);
-  const float scale = r1 ? 8589934592.0f : (r2 ? 4294967296.0f : 2147483648.0f);   // 2^32 / step
-  const float T = ceilf((a - lo) * scale);             // 0 <= T <= 2^32, exact
-  const bool up = (T >= 4294967296.0f) || (r < (uint32_t)T);
-  const uint32_t code = a >= 6.0f ? 7u : lo_code + (up ? 1u : 0u);
+  const bool ge1 = ua >= 0x3F800000u, ge05 = ua >= 0x3F000000u;
+  const uint32_t lo = ge1 ? (ua >> 22) - 252u : (ge05 ? 1u : 0u);
+  const uint32_t T =
+      ge1 ? (ua << 10) : (ge05 ? (ua << 9) : (uint32_t)ceilf(__uint_as_float(ua) * 8589934592.0f));
+  const uint32_t code = ua >= 0x40C00000u ? 7u : lo + (r < T ? 1u : 0u);
   return sign | code;
 }
 

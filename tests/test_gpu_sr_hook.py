@@ -100,5 +100,16 @@ def test_grid_values_never_move_and_saturation():
         assert (got == want).all(), r
 
 
+def test_nan_saturates_as_the_oracle_does():
+    """A NaN (either sign bit) takes the largest magnitude, as in the oracle,
+    whatever the random word."""
+    v = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF], np.uint32).view(np.float32)
+    for r in (0, 1, 2 ** 31, 2 ** 32 - 1):
+        rs = np.full(len(v), r, np.uint32)
+        got = _device_sr(v, rs)
+        assert (got == R.sr_e2m1(v, rs)).all(), (r, got)
+        assert (got & 7 == 7).all()
+
+
 def test_empty_call_enqueues_nothing():
     P.pbs_debug_sr_encode(None, None, None, 0)
