@@ -772,6 +772,11 @@ constexpr int CT_R = 256, CT_C = 64, CT_PITCH = 136;
 template <int RECIPE, int FMT, bool RHT, bool SR, bool AMAX>
 __global__ __launch_bounds__(256, 2) void cast_col_kernel(CastArgs a) {
   __shared__ __align__(16) uint8_t tile[CT_R * CT_PITCH];
+  // MXFP4 with stochastic rounding: the random words of columns 2 and 3 wait
+  // in LDS (word j of thread t at j * 256 + t, each thread its own slots)
+  // instead of 32 registers, which kept that variant from spilling
+  constexpr bool WORDS_LDS = SR && RECIPE == R_MX4;
+  __shared__ uint32_t wlds[WORDS_LDS ? 32 * 256 : 1];
   const int t = threadIdx.x, lane = t & 63;
   uint32_t rht_mask = 0;
   if (RHT) {
@@ -828,7 +833,7 @@ __global__ __launch_bounds__(256, 2) void cast_col_kernel(CastArgs a) {
     // aligned group of a row of x, so one call per row serves all four
     // (one call in flight at a time: hoisting all sixteen multiplies the live
     // registers, and occupancy hides the chain's latency better)
-    uint32_t rndc[4][16];
+    uint32_t rndc[WORDS_LDS ? 2 : 4][16];
     if (SR) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -836,8 +841,13 @@ __global__ __launch_bounds__(256, 2) void cast_col_kernel(CastArgs a) {
         const uint4 r4 = sr_words4(idx >> 2, a.seed);
         rndc[0][i] = r4.x;
         rndc[1][i] = r4.y;
-        rndc[2][i] = r4.z;
-        rndc[3][i] = r4.w;
+        if constexpr (WORDS_LDS) {
+          wlds[i * 256 + t] = r4.z;
+          wlds[(16 + i) * 256 + t] = r4.w;
+        } else {
+          rndc[WORDS_LDS ? 0 : 2][i] = r4.z;
+          rndc[WORDS_LDS ? 1 : 3][i] = r4.w;
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -884,8 +894,15 @@ __global__ __launch_bounds__(256, 2) void cast_col_kernel(CastArgs a) {
         sc32 = (float*)a.col_scales + gc * (a.R / 128) + gr / 128;
         writer = (rs & 7) == 0;
       }
+      uint32_t rl[16];
+      const uint32_t* rnd = rndc[c & (WORDS_LDS ? 1 : 3)];
+      if (WORDS_LDS && c >= 2) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rl[i] = wlds[((c - 2) * 16 + i) * 256 + t];
+        rnd = rl;
+      }
       quantize_segment<RECIPE == R_CHAN ? R_TENSOR : RECIPE, FMT, SR>(v, mbits, tscale, valid, codes, sc8, sc32,
-                                                                       writer, rndc[c]);
+                                                                       writer, rnd);
       if (SR) __builtin_amdgcn_sched_barrier(0);   // one column at a time: the words already hold 64 registers
     }
     __syncthreads();   // every read of this tile is done before the next fill
